@@ -1,0 +1,192 @@
+"""fp64 CPU oracle of block-sparse masked softmax attention (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the yardstick the HIP path is checked against.  Only the
+test suite, the smoke check and the CPU-baseline leg of the benchmark may import
+it; the product path never does.  It shares no code with the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this module
+only marshals numpy / torch CPU arrays into it.  What it computes, and the readings
+of the pages it follows, are stated in the header of ``oracle.c``:
+"Writing Pallas Kernels for JAX", section "Writing the Kernel Logic: Load, Compute,
+Store" (masked scaled-dot-product softmax times V), and "Pallas-Triton kernels and
+kernel auto-tuning", section "Flash Attention" (the tiled method is exact, so the
+oracle is the plain operator).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    _lib = configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def configure(lib):
+    """Declare the C signatures on a loaded oracle library and return it."""
+    p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.oracle_fwd.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p, p, i32]
+    lib.oracle_fwd.restype = i32
+    lib.oracle_fwd_rows.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32,
+                                    p, i64, p, p, i32]
+    lib.oracle_fwd_rows.restype = i32
+    lib.oracle_probs.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p]
+    lib.oracle_probs.restype = i32
+    lib.oracle_compact.argtypes = [p, i64, i64, p, p]
+    lib.oracle_compact.restype = i64
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
+    return lib
+
+
+def _as_raw(x):
+    """Return (contiguous numpy array of raw element bits, dtype code).
+
+    Accepts numpy float32/float64 arrays and torch CPU tensors of float32,
+    float64 or bfloat16 (passed as their raw 16-bit patterns; the C code widens
+    them exactly)."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        if x.device.type != "cpu":
+            raise ValueError("oracle inputs must live on the CPU")
+        x = x.contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy(), BF16
+        if x.dtype == torch.float32:
+            return x.numpy(), F32
+        if x.dtype == torch.float64:
+            return x.numpy(), F64
+        raise TypeError("unsupported tensor dtype %s" % x.dtype)
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.float64:
+        return x, F64
+    raise TypeError("unsupported array dtype %s" % x.dtype)
+
+
+def _mask_u8(mask):
+    try:
+        import torch
+        if isinstance(mask, torch.Tensor):
+            mask = mask.contiguous().to(torch.uint8).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+
+
+def _shape(q, mask, block_q, block_k):
+    B, H, S, D = q.shape
+    n_q, n_k = S // block_q, S // block_k
+    if tuple(mask.shape) != (B, H, n_q, n_k):
+        raise ValueError("mask shape %s != %s" % (tuple(mask.shape), (B, H, n_q, n_k)))
+    return B, H, S, D
+
+
+def fwd(q, k, v, mask, block_q, block_k, scale, nthreads=0):
+    """Full forward.  q, k, v: [B,H,S,D]; mask: [B,H,S/block_q,S/block_k].
+    Returns (out float64 [B,H,S,D], lse float64 [B,H,S])."""
+    lib = _load()
+    qa, dt = _as_raw(q)
+    ka, dt2 = _as_raw(k)
+    va, dt3 = _as_raw(v)
+    if not (dt == dt2 == dt3):
+        raise TypeError("q, k, v must share a dtype")
+    m = _mask_u8(mask)
+    B, H, S, D = _shape(qa, m, block_q, block_k)
+    out = np.empty((B, H, S, D), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    rc = lib.oracle_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, m.ctypes.data,
+                        B, H, S, D, block_q, block_k, float(np.float32(scale)),
+                        out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_fwd failed with code %d" % rc)
+    return out, lse
+
+
+def fwd_rows(q, k, v, mask, block_q, block_k, scale, rows, nthreads=0):
+    """Selected rows: rows are flat indices (b*H + h)*S + s.
+    Returns (out float64 [n, D], lse float64 [n])."""
+    lib = _load()
+    qa, dt = _as_raw(q)
+    ka, _ = _as_raw(k)
+    va, _ = _as_raw(v)
+    m = _mask_u8(mask)
+    B, H, S, D = _shape(qa, m, block_q, block_k)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    out = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_fwd_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, m.ctypes.data,
+                             B, H, S, D, block_q, block_k, float(np.float32(scale)),
+                             rows.ctypes.data, n, out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_fwd_rows failed with code %d" % rc)
+    return out, lse
+
+
+def probs(q, k, v, mask, block_q, block_k, scale):
+    """Dense softmax weights P [B,H,S,S] (zero where masked) for tiny shapes."""
+    lib = _load()
+    qa, dt = _as_raw(q)
+    ka, _ = _as_raw(k)
+    va, _ = _as_raw(v)
+    m = _mask_u8(mask)
+    B, H, S, D = _shape(qa, m, block_q, block_k)
+    P = np.empty((B, H, S, S), dtype=np.float64)
+    rc = lib.oracle_probs(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, m.ctypes.data,
+                          B, H, S, D, block_q, block_k, float(np.float32(scale)), P.ctypes.data)
+    if rc:
+        raise ValueError("oracle_probs failed with code %d" % rc)
+    return P
+
+
+def compact(mask):
+    """CSR compaction of a block mask [..., n_k] flattened to rows.
+    Returns (row_ptr int32 [R+1], col_idx int32 [nnz])."""
+    lib = _load()
+    m = _mask_u8(mask)
+    n_k = m.shape[-1]
+    R = m.size // n_k
+    row_ptr = np.empty(R + 1, dtype=np.int32)
+    col_idx = np.empty(max(R * n_k, 1), dtype=np.int32)
+    nnz = lib.oracle_compact(m.ctypes.data, R, n_k, row_ptr.ctypes.data, col_idx.ctypes.data)
+    if nnz < 0:
+        raise ValueError("oracle_compact failed")
+    return row_ptr, col_idx[:nnz].copy()
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())

@@ -1,0 +1,284 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for block-sparse masked softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the yardstick the GPU path is checked
+ * against; it is never part of the product path.  Only the test suite, the smoke
+ * check and the CPU-baseline leg of the benchmark load it.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * What it computes (the operation the pages define):
+ *   "Writing Pallas Kernels for JAX" (rajatpandit.com), section "Writing the Kernel
+ *   Logic: Load, Compute, Store": scores are the scaled dot products of query rows
+ *   with key rows; where the block mask is 0 the score is pushed to -inf before a
+ *   row softmax; the softmax weights multiply V.  "Pallas-Triton kernels and kernel
+ *   auto-tuning" (robertdyro.com), section "Flash Attention": the tiled method
+ *   computes that operator exactly, so the oracle is the plain definition, not
+ *   the tiled algorithm.
+ *
+ * Readings (where the pages leave a step open):
+ *   - The softmax is over the whole row of keys, not per tile.  The per-tile
+ *     softmax printed in the Pallas kernel listing is not attention; the oracle
+ *     follows the exact operator.
+ *   - The mask is block level: mask[b][h][qi][kj] != 0 activates the key block
+ *     kj (keys kj*block_k .. kj*block_k+block_k-1) for every query in query block
+ *     qi (queries qi*block_q .. qi*block_q+block_q-1).
+ *   - A row with no active key has out = 0 and lse = -inf (a literal softmax over
+ *     an all -inf row is undefined).
+ *   - lse is the natural logarithm of the row's sum of exp(score).
+ *   - Inputs are widened exactly to double; scale is the caller's fp32 value
+ *     widened, applied as scale * (q . k).
+ *
+ * Two passes per row, with no online rescaling and no tiling:
+ *   pass 1: s_j = scale * sum_d q[r][d] * k[j][d]   (d ascending, j ascending over
+ *           the active keys), m = max_j s_j;
+ *   pass 2: e_j = exp(s_j - m), l = sum_j e_j, out[r][:] = sum_j e_j v[j][:] / l,
+ *           lse[r] = m + log(l).
+ * Skipping inactive keys equals the literal -inf form exactly: those terms add
+ * exact zeros and never change the max.
+ *
+ * Compaction (the block-list form of the mask): for each mask row in (b, h, qi)
+ * row-major order, the ascending list of kj with mask != 0; row_ptr[0] = 0 and
+ * row_ptr[r+1] = row_ptr[r] + count of row r.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+
+typedef struct {
+    const void* q;
+    const void* k;
+    const void* v;
+    int dtype;
+    const uint8_t* mask;
+    int64_t B, H, S, D;
+    int64_t block_q, block_k, n_q, n_k;
+    double scale;
+} problem;
+
+/* Exact widening of one element to double.  bf16 is the top 16 bits of an fp32. */
+static double widen(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORC_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return ((const double*)base)[idx];
+}
+
+static int check(const problem* p) {
+    if (!p->q || !p->k || !p->v || !p->mask) return 1;
+    if (p->B <= 0 || p->H <= 0 || p->S <= 0 || p->D <= 0) return 2;
+    if (p->block_q <= 0 || p->block_k <= 0) return 2;
+    if (p->S % p->block_q != 0 || p->S % p->block_k != 0) return 2;
+    if (p->dtype < ORC_F32 || p->dtype > ORC_F64) return 3;
+    return 0;
+}
+
+/* One query row: bh = b*H + h, s = query position.  sbuf holds S doubles,
+ * acc holds D doubles. */
+static void oracle_row(const problem* p, int64_t bh, int64_t s, double* out_row,
+                       double* lse_out, double* sbuf, double* acc) {
+    const int64_t D = p->D;
+    const int64_t qi = s / p->block_q;
+    const uint8_t* mrow = p->mask + (bh * p->n_q + qi) * p->n_k;
+    const int64_t qbase = (bh * p->S + s) * D;
+
+    /* pass 1: scores of the active keys, ascending, and their max */
+    int64_t n = 0;
+    double m = -INFINITY;
+    for (int64_t kj = 0; kj < p->n_k; ++kj) {
+        if (!mrow[kj]) continue;
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            const int64_t kbase = (bh * p->S + j) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dot += widen(p->q, p->dtype, qbase + d) * widen(p->k, p->dtype, kbase + d);
+            const double sj = p->scale * dot;
+            sbuf[n++] = sj;
+            if (sj > m) m = sj;
+        }
+    }
+    if (n == 0) {
+        for (int64_t d = 0; d < D; ++d) out_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+
+    /* pass 2: exponentials, their sum, and the weighted sum of V rows */
+    double l = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        sbuf[t] = exp(sbuf[t] - m);
+        l += sbuf[t];
+    }
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    int64_t t = 0;
+    for (int64_t kj = 0; kj < p->n_k; ++kj) {
+        if (!mrow[kj]) continue;
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            const int64_t vbase = (bh * p->S + j) * D;
+            const double e = sbuf[t++];
+            for (int64_t d = 0; d < D; ++d) acc[d] += e * widen(p->v, p->dtype, vbase + d);
+        }
+    }
+    for (int64_t d = 0; d < D; ++d) out_row[d] = acc[d] / l;
+    *lse_out = m + log(l);
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+static problem make_problem(const void* q, const void* k, const void* v, int dtype,
+                            const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D,
+                            int64_t block_q, int64_t block_k, float scale) {
+    problem p;
+    p.q = q; p.k = k; p.v = v; p.dtype = dtype; p.mask = mask;
+    p.B = B; p.H = H; p.S = S; p.D = D;
+    p.block_q = block_q; p.block_k = block_k;
+    p.n_q = block_q > 0 ? S / block_q : 0;
+    p.n_k = block_k > 0 ? S / block_k : 0;
+    p.scale = (double)scale;
+    return p;
+}
+
+/* Full forward: out is double[B][H][S][D], lse is double[B][H][S].
+ * Returns 0 on success, nonzero on a bad argument (nothing written). */
+int oracle_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+               int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+               float scale, double* out, double* lse, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    int rc = check(&p);
+    if (rc) return rc;
+    if (!out || !lse) return 1;
+    set_threads(nthreads);
+    const int64_t rows = B * H * S;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!sbuf || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r)
+                oracle_row(&p, r / S, r % S, out + r * D, lse + r, sbuf, acc);
+        }
+        free(sbuf);
+        free(acc);
+    }
+    return failed ? 9 : 0;
+}
+
+/* Selected rows only: rows[i] is a flat row index (b*H + h)*S + s.
+ * out_rows is double[n_rows][D], lse_rows is double[n_rows]. */
+int oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+                    int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+                    float scale, const int64_t* rows, int64_t n_rows, double* out_rows,
+                    double* lse_rows, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    int rc = check(&p);
+    if (rc) return rc;
+    if (!rows || !out_rows || !lse_rows) return 1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= B * H * S) return 2;
+    set_threads(nthreads);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!sbuf || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < n_rows; ++i)
+                oracle_row(&p, rows[i] / S, rows[i] % S, out_rows + i * D, lse_rows + i, sbuf, acc);
+        }
+        free(sbuf);
+        free(acc);
+    }
+    return failed ? 9 : 0;
+}
+
+/* Dense probability matrix P[b][h][s][j] (zero where masked), for tiny shapes:
+ * the row softmax weights exp(s_j - m)/l of the definition above.  An empty row
+ * is all zeros. */
+int oracle_probs(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+                 int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+                 float scale, double* P) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    int rc = check(&p);
+    if (rc) return rc;
+    if (!P) return 1;
+    double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!sbuf) return 9;
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        for (int64_t s = 0; s < S; ++s) {
+            double* prow = P + (bh * S + s) * S;
+            for (int64_t j = 0; j < S; ++j) prow[j] = 0.0;
+            const int64_t qi = s / block_q;
+            const uint8_t* mrow = mask + (bh * p.n_q + qi) * p.n_k;
+            const int64_t qbase = (bh * S + s) * D;
+            double m = -INFINITY;
+            int64_t n = 0;
+            for (int64_t j = 0; j < S; ++j) {
+                sbuf[j] = -INFINITY;
+                if (!mrow[j / block_k]) continue;
+                const int64_t kbase = (bh * S + j) * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += widen(q, dtype, qbase + d) * widen(k, dtype, kbase + d);
+                sbuf[j] = p.scale * dot;
+                if (sbuf[j] > m) m = sbuf[j];
+                ++n;
+            }
+            if (n == 0) continue;
+            double l = 0.0;
+            for (int64_t j = 0; j < S; ++j)
+                if (mrow[j / block_k]) l += exp(sbuf[j] - m);
+            for (int64_t j = 0; j < S; ++j)
+                if (mrow[j / block_k]) prow[j] = exp(sbuf[j] - m) / l;
+        }
+    }
+    free(sbuf);
+    return 0;
+}
+
+/* Compaction of a block mask with n_rows rows of n_k bytes into CSR.
+ * row_ptr holds n_rows+1 entries; col_idx must hold n_rows*n_k entries.
+ * Returns the number of active blocks (nnz), or -1 on a bad argument. */
+int64_t oracle_compact(const uint8_t* mask, int64_t n_rows, int64_t n_k, int32_t* row_ptr,
+                       int32_t* col_idx) {
+    if (!mask || !row_ptr || !col_idx || n_rows < 0 || n_k <= 0) return -1;
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        for (int64_t kj = 0; kj < n_k; ++kj)
+            if (mask[r * n_k + kj]) col_idx[nnz++] = (int32_t)kj;
+        row_ptr[r + 1] = (int32_t)nnz;
+    }
+    return nnz;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

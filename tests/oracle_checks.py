@@ -1,0 +1,299 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check takes the oracle's Python API (a module or object with fwd, fwd_rows,
+probs, compact) so the same checks run on the real oracle (test_oracle_pins.py)
+and on deliberately broken copies of it (test_oracle_mutants.py).
+
+What pins what:
+  hand_example      hand-derived values of a 4-token example (tests/golden)
+  brute_force       dense literal -inf softmax in NumPy + scipy logsumexp
+  sdpa_dense        torch scaled_dot_product_attention (fp64, CPU) for an all-ones mask
+  sdpa_block_causal torch SDPA with the expanded lower-triangular block mask
+  block_diagonal    block-diagonal mask == independent dense attention per block
+  probs_sum         softmax weights are >= 0, zero where masked, rows sum to 1
+  constant_v        V == c gives out == c on every non-empty row
+  zero_query        Q == 0 (or scale == 0): out = mean of the visible V rows,
+                    lse = ln(number of visible keys)
+  empty_rows        a row with no active block gives out == 0 exactly, lse == -inf
+  linearity         out(a V1 + b V2) == a out(V1) + b out(V2)
+  key_permutation   permuting keys (with their V rows) inside an active block
+                    changes neither out nor lse
+  shift             K + 1 c^T leaves out unchanged and adds scale*(q.c) to lse;
+                    with a large c it also checks the max subtraction
+  rows_match_full   the selected-rows entry point equals the full forward
+  bf16_widening     bf16 inputs give the same result as their exact fp64 values
+  compact_brute     CSR compaction equals np.nonzero per row
+"""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from brute import brute_compact, brute_fwd, expand_mask
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TOL = 1e-12
+
+
+def _rand(shape, seed, dtype=torch.float64):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float64).to(dtype)
+
+
+def _mask(B, H, nq, nk, p, seed, empty_rows=()):
+    g = torch.Generator().manual_seed(seed)
+    m = (torch.rand(B, H, nq, nk, generator=g) < p).to(torch.uint8)
+    for (b, h, i) in empty_rows:
+        m[b, h, i, :] = 0
+    return m
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fin_a, fin_b = np.isfinite(a), np.isfinite(b)
+    assert np.array_equal(fin_a, fin_b), (what, "finite pattern differs")
+    assert np.array_equal(a[~fin_a], b[~fin_b]), (what, "non-finite values differ")
+    if fin_a.any():
+        err = np.max(np.abs(a[fin_a] - b[fin_b]))
+        scale = max(1.0, float(np.max(np.abs(b[fin_b]))))
+        assert err <= tol * scale, (what, float(err))
+
+
+def hand_example(orc):
+    ex = json.load(open(os.path.join(HERE, "golden", "hand_example.json")))
+    q = np.array(ex["q"], dtype=np.float64)
+    k = np.array(ex["k"], dtype=np.float64)
+    v = np.array(ex["v"], dtype=np.float64)
+    mask = np.array(ex["mask"], dtype=np.uint8)
+    out, lse = orc.fwd(q, k, v, mask, ex["block_q"], ex["block_k"], ex["scale"])
+    want_lse = np.array([[[float(x) for x in row] for row in h] for h in ex["lse"]])
+    _close(out, np.array(ex["out"]), 1e-12, "out")
+    _close(lse, want_lse, 1e-12, "lse")
+
+
+CASES = [
+    # B, H, S, D, block_q, block_k, p, seed, dtype, scale
+    (1, 1, 8, 4, 2, 2, 0.6, 1, torch.float64, 0.7),
+    (2, 3, 16, 8, 4, 2, 0.5, 2, torch.float64, 0.35),
+    (1, 2, 12, 5, 3, 4, 0.5, 3, torch.float32, 1.3),
+    (2, 2, 32, 16, 8, 16, 0.5, 4, torch.bfloat16, 0.25),
+    (1, 2, 24, 6, 6, 4, 0.4, 5, torch.float64, -0.9),
+]
+
+
+def brute_force(orc):
+    for (B, H, S, D, bq, bk, p, seed, dt, scale) in CASES:
+        q = _rand((B, H, S, D), seed, dt)
+        k = _rand((B, H, S, D), seed + 100, dt)
+        v = _rand((B, H, S, D), seed + 200, dt)
+        mask = _mask(B, H, S // bq, S // bk, p, seed, empty_rows=[(0, 0, 1)])
+        out, lse = orc.fwd(q, k, v, mask, bq, bk, scale)
+        bout, blse, _ = brute_fwd(q, k, v, mask, bq, bk, scale)
+        _close(out, bout, TOL, "out %s" % (dt,))
+        _close(lse, blse, TOL, "lse %s" % (dt,))
+
+
+def _sdpa(q, k, v, full, scale):
+    return torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.as_tensor(full), scale=float(np.float32(scale))).numpy()
+
+
+def sdpa_dense(orc):
+    B, H, S, D, bq, bk = 2, 2, 32, 8, 8, 4
+    q, k, v = (_rand((B, H, S, D), s) for s in (11, 12, 13))
+    mask = torch.ones(B, H, S // bq, S // bk, dtype=torch.uint8)
+    out, _ = orc.fwd(q, k, v, mask, bq, bk, 0.3)
+    want = _sdpa(q, k, v, np.ones((B, H, S, S), dtype=bool), 0.3)
+    _close(out, want, TOL, "dense")
+
+
+def sdpa_block_causal(orc):
+    B, H, S, D, b = 1, 3, 48, 8, 8
+    q, k, v = (_rand((B, H, S, D), s) for s in (21, 22, 23))
+    n = S // b
+    mask = torch.tril(torch.ones(n, n, dtype=torch.uint8)).expand(B, H, n, n).contiguous()
+    out, _ = orc.fwd(q, k, v, mask, b, b, 0.4)
+    want = _sdpa(q, k, v, expand_mask(mask, b, b), 0.4)
+    _close(out, want, TOL, "block causal")
+
+
+def block_diagonal(orc):
+    B, H, S, D, b = 1, 2, 32, 4, 8
+    q, k, v = (_rand((B, H, S, D), s) for s in (31, 32, 33))
+    n = S // b
+    mask = torch.eye(n, dtype=torch.uint8).expand(B, H, n, n).contiguous()
+    out, _ = orc.fwd(q, k, v, mask, b, b, 0.5)
+    for i in range(n):
+        sl = slice(i * b, (i + 1) * b)
+        want = _sdpa(q[:, :, sl], k[:, :, sl], v[:, :, sl], np.ones((B, H, b, b), bool), 0.5)
+        _close(out[:, :, sl], want, TOL, "block %d" % i)
+
+
+def probs_sum(orc):
+    B, H, S, D, bq, bk = 2, 2, 16, 4, 4, 2
+    q, k, v = (_rand((B, H, S, D), s) for s in (41, 42, 43))
+    mask = _mask(B, H, S // bq, S // bk, 0.5, 44, empty_rows=[(1, 1, 2)])
+    P = orc.probs(q, k, v, mask, bq, bk, 0.8)
+    full = expand_mask(mask, bq, bk)
+    assert np.all(P >= 0.0)
+    assert np.all(P[~full] == 0.0)
+    sums = P.sum(-1)
+    nonempty = full.any(-1)
+    assert np.all(np.abs(sums[nonempty] - 1.0) <= 1e-14), float(np.max(np.abs(sums[nonempty] - 1)))
+    assert np.all(sums[~nonempty] == 0.0)
+    # and the probabilities are the brute force's
+    _, _, bp = brute_fwd(q, k, v, mask, bq, bk, 0.8)
+    _close(P, bp, TOL, "P")
+
+
+def constant_v(orc):
+    B, H, S, D, bq, bk = 1, 2, 16, 6, 4, 4
+    q, k = _rand((B, H, S, D), 51), _rand((B, H, S, D), 52)
+    v = torch.full((B, H, S, D), 2.75, dtype=torch.float64)
+    mask = _mask(B, H, S // bq, S // bk, 0.5, 53, empty_rows=[(0, 1, 0)])
+    out, _ = orc.fwd(q, k, v, mask, bq, bk, 1.1)
+    nonempty = expand_mask(mask, bq, bk).any(-1)
+    assert np.all(np.abs(out[nonempty] - 2.75) <= 1e-13)
+    assert np.all(out[~nonempty] == 0.0)
+
+
+def zero_query(orc):
+    B, H, S, D, bq, bk = 1, 2, 24, 5, 6, 3
+    k, v = _rand((B, H, S, D), 61), _rand((B, H, S, D), 62)
+    mask = _mask(B, H, S // bq, S // bk, 0.5, 63, empty_rows=[(0, 0, 3)])
+    full = expand_mask(mask, bq, bk)
+    vv = v.numpy()
+    cnt = full.sum(-1)
+    want_out = np.where(cnt[..., None] > 0,
+                        np.einsum("bhij,bhjd->bhid", full.astype(np.float64), vv)
+                        / np.maximum(cnt, 1)[..., None], 0.0)
+    want_lse = np.where(cnt > 0, np.log(np.maximum(cnt, 1)), -np.inf)
+    # Q == 0 with a nonzero scale, and a random Q with scale == 0
+    for q, scale in ((torch.zeros(B, H, S, D, dtype=torch.float64), 0.9),
+                     (_rand((B, H, S, D), 64), 0.0)):
+        out, lse = orc.fwd(q, k, v, mask, bq, bk, scale)
+        _close(out, want_out, 1e-13, "out")
+        _close(lse, want_lse, 1e-13, "lse")
+
+
+def empty_rows(orc):
+    B, H, S, D, bq, bk = 1, 2, 16, 4, 4, 4
+    q, k, v = (_rand((B, H, S, D), s) for s in (71, 72, 73))
+    mask = torch.ones(B, H, S // bq, S // bk, dtype=torch.uint8)
+    mask[0, 1, 2, :] = 0
+    mask[0, 0, 0, :] = 0
+    out, lse = orc.fwd(q, k, v, mask, bq, bk, 0.5)
+    for (h, i) in ((1, 2), (0, 0)):
+        rows = slice(i * bq, (i + 1) * bq)
+        assert np.all(out[0, h, rows] == 0.0)
+        assert np.all(np.isneginf(lse[0, h, rows]))
+    assert np.all(np.isfinite(lse[0, 0, bq:]))
+
+
+def linearity(orc):
+    B, H, S, D, bq, bk = 1, 1, 16, 4, 4, 2
+    q, k, v1, v2 = (_rand((B, H, S, D), s) for s in (81, 82, 83, 84))
+    mask = _mask(B, H, S // bq, S // bk, 0.6, 85)
+    a, b = 1.5, -0.25
+    o1, _ = orc.fwd(q, k, v1, mask, bq, bk, 0.6)
+    o2, _ = orc.fwd(q, k, v2, mask, bq, bk, 0.6)
+    o3, _ = orc.fwd(q, k, a * v1 + b * v2, mask, bq, bk, 0.6)
+    _close(o3, a * o1 + b * o2, 1e-12, "linearity")
+
+
+def key_permutation(orc):
+    B, H, S, D, bq, bk = 1, 2, 16, 4, 4, 4
+    q, k, v = (_rand((B, H, S, D), s) for s in (91, 92, 93))
+    mask = _mask(B, H, S // bq, S // bk, 0.6, 94)
+    out, lse = orc.fwd(q, k, v, mask, bq, bk, 0.7)
+    g = torch.Generator().manual_seed(95)
+    perm = torch.arange(S)
+    for kj in range(S // bk):  # shuffle keys inside every key block
+        idx = torch.randperm(bk, generator=g) + kj * bk
+        perm[kj * bk:(kj + 1) * bk] = idx
+    out2, lse2 = orc.fwd(q, k[:, :, perm], v[:, :, perm], mask, bq, bk, 0.7)
+    _close(out2, out, 1e-12, "out")
+    _close(lse2, lse, 1e-12, "lse")
+
+
+def shift(orc):
+    B, H, S, D, bq, bk = 1, 2, 16, 4, 4, 4
+    q, k, v = (_rand((B, H, S, D), s) for s in (101, 102, 103))
+    mask = _mask(B, H, S // bq, S // bk, 0.7, 104)
+    scale = 0.5
+    out, lse = orc.fwd(q, k, v, mask, bq, bk, scale)
+    for mag in (1.0, 5000.0):  # 5000 pushes |score| past the fp64 exp range (~709)
+        c = mag * _rand((D,), 105)
+        out2, lse2 = orc.fwd(q, k + c, v, mask, bq, bk, scale)
+        _close(out2, out, 1e-9, "out shift %g" % mag)
+        qc = scale * np.einsum("bhsd,d->bhs", q.numpy(), c.numpy())
+        want = np.where(np.isfinite(lse), lse + qc, lse)
+        _close(lse2, want, 1e-9, "lse shift %g" % mag)
+
+
+def rows_match_full(orc):
+    B, H, S, D, bq, bk = 2, 2, 16, 8, 4, 8
+    q, k, v = (_rand((B, H, S, D), s) for s in (111, 112, 113))
+    mask = _mask(B, H, S // bq, S // bk, 0.5, 114, empty_rows=[(1, 0, 1)])
+    out, lse = orc.fwd(q, k, v, mask, bq, bk, 0.45)
+    rows = np.array([0, 5, 17, 33, 40, 63], dtype=np.int64)
+    ro, rl = orc.fwd_rows(q, k, v, mask, bq, bk, 0.45, rows)
+    assert np.array_equal(ro, out.reshape(-1, D)[rows])
+    assert np.array_equal(rl, lse.reshape(-1)[rows])
+
+
+def bf16_widening(orc):
+    B, H, S, D, bq, bk = 1, 2, 16, 8, 4, 4
+    q, k, v = (_rand((B, H, S, D), s, torch.bfloat16) for s in (121, 122, 123))
+    mask = _mask(B, H, S // bq, S // bk, 0.6, 124)
+    o1, l1 = orc.fwd(q, k, v, mask, bq, bk, 0.3)
+    o2, l2 = orc.fwd(q.double(), k.double(), v.double(), mask, bq, bk, 0.3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def compact_brute(orc):
+    for (shape, p, seed) in (((1, 2, 4, 4), 0.5, 0), ((2, 3, 5, 70), 0.3, 1),
+                             ((1, 1, 3, 129), 0.02, 2), ((2, 2, 4, 8), 0.0, 3),
+                             ((1, 2, 3, 64), 1.0, 4)):
+        g = torch.Generator().manual_seed(seed)
+        m = (torch.rand(*shape, generator=g) < p).to(torch.uint8)
+        rp, ci = orc.compact(m)
+        brp, bci = brute_compact(m)
+        assert np.array_equal(rp, brp) and np.array_equal(ci, bci)
+        assert rp[-1] == int(m.sum())
+        for r in range(len(rp) - 1):  # strictly ascending within each row
+            seg = ci[rp[r]:rp[r + 1]]
+            assert np.all(np.diff(seg) > 0)
+        rebuilt = np.zeros((len(rp) - 1, shape[-1]), dtype=np.uint8)
+        for r in range(len(rp) - 1):
+            rebuilt[r, ci[rp[r]:rp[r + 1]]] = 1
+        assert np.array_equal(rebuilt.reshape(shape), m.numpy())
+
+
+ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
+       constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
+       bf16_widening, compact_brute]
+
+
+def run_all(orc):
+    """Run every check; return the names of those that failed (any exception)."""
+    failed = []
+    for fn in ALL:
+        try:
+            fn(orc)
+        except Exception:  # noqa: BLE001 -- a crash or wrong value both count
+            failed.append(fn.__name__)
+    return failed
+
+
+if __name__ == "__main__":  # used by the mutant runner: python oracle_checks.py <lib.so>
+    import ctypes
+    import sys
+    sys.path.insert(0, os.path.dirname(HERE))
+    import oracle
+    oracle._lib = oracle.configure(ctypes.CDLL(sys.argv[1]))
+    print(json.dumps(run_all(oracle)))

@@ -1,0 +1,89 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one of them.  Each mutant is compiled from a patched copy of
+oracle/oracle.c into a temporary directory and checked in a child process, so a
+mutant that crashes counts as caught without taking the test run down."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
+
+# name -> list of (original text, replacement); every original must occur in oracle.c
+MUTANTS = {
+    "drop_scale": [("const double sj = p->scale * dot;", "const double sj = dot;")],
+    "query_block_uses_block_k": [("const int64_t qi = s / p->block_q;",
+                                  "const int64_t qi = s / p->block_k;")],
+    "no_max_subtraction": [("sbuf[t] = exp(sbuf[t] - m);", "sbuf[t] = exp(sbuf[t]);"),
+                           ("*lse_out = m + log(l);", "*lse_out = log(l);")],
+    "lse_drops_max": [("*lse_out = m + log(l);", "*lse_out = log(l);")],
+    "key_block_short_by_one": [("for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                                "            const int64_t kbase",
+                                "for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k - 1; ++j) {\n"
+                                "            const int64_t kbase"),
+                               ("for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                                "            const int64_t vbase",
+                                "for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k - 1; ++j) {\n"
+                                "            const int64_t vbase")],
+    "v_row_is_query_row": [("const int64_t vbase = (bh * p->S + j) * D;",
+                            "const int64_t vbase = (bh * p->S + s) * D;")],
+    "empty_row_lse_zero": [("*lse_out = -INFINITY;\n        return;", "*lse_out = 0.0;\n        return;")],
+    "dot_uses_k_twice": [("dot += widen(p->q, p->dtype, qbase + d) * widen(p->k, p->dtype, kbase + d);",
+                          "dot += widen(p->k, p->dtype, qbase + d) * widen(p->k, p->dtype, kbase + d);")],
+    "no_normalisation": [("out_row[d] = acc[d] / l;", "out_row[d] = acc[d];")],
+    "k_ignores_head": [("const int64_t kbase = (bh * p->S + j) * D;\n            double dot = 0.0;\n"
+                        "            for (int64_t d = 0; d < D; ++d)\n                dot += widen(p->q",
+                        "const int64_t kbase = (j) * D;\n            double dot = 0.0;\n"
+                        "            for (int64_t d = 0; d < D; ++d)\n                dot += widen(p->q")],
+    "mask_transposed": [("if (!mrow[kj]) continue;\n        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                         "            const int64_t kbase",
+                         "if (kj >= p->n_q || qi >= p->n_k || !p->mask[(bh * p->n_q + kj) * p->n_k + qi]) continue;\n"
+                         "        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                         "            const int64_t kbase"),
+                        ("if (!mrow[kj]) continue;\n        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                         "            const int64_t vbase",
+                         "if (kj >= p->n_q || qi >= p->n_k || !p->mask[(bh * p->n_q + kj) * p->n_k + qi]) continue;\n"
+                         "        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                         "            const int64_t vbase")],
+    "bf16_wrong_shift": [("((uint32_t)((const uint16_t*)base)[idx]) << 16;",
+                          "((uint32_t)((const uint16_t*)base)[idx]) << 15;")],
+    "compact_skips_last_column": [("for (int64_t kj = 0; kj < n_k; ++kj)\n            if (mask[r * n_k + kj])",
+                                   "for (int64_t kj = 0; kj < n_k - 1; ++kj)\n            if (mask[r * n_k + kj])")],
+}
+
+
+def _build(tmp_path, name, patches):
+    src = open(SRC).read()
+    for old, new in patches:
+        assert old in src, "patch for %s no longer applies: %r" % (name, old[:60])
+        src = src.replace(old, new)
+    c = tmp_path / ("%s.c" % name)
+    c.write_text(src)
+    so = tmp_path / ("lib%s.so" % name)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"],
+                   check=True)
+    return so
+
+
+def _run_checks(so):
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_checks.py"), str(so)],
+                       capture_output=True, text=True, env=env, cwd=HERE, timeout=300)
+    if r.returncode != 0:
+        return ["<crashed rc=%d>" % r.returncode]
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = _build(tmp_path, "clean", [])
+    assert _run_checks(so) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    so = _build(tmp_path, name, MUTANTS[name])
+    failed = _run_checks(so)
+    assert failed, "mutant %s passed every pin" % name
