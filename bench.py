@@ -1,0 +1,201 @@
+"""Benchmark of the block-sparse flash-attention forward on one MI355X.
+
+One step = one bsattn_fwd call (mask compaction + fused attention kernel) over the
+workload's resident inputs.  Prints ONE JSON line on stdout:
+  value      effective TFLOP/s = 4*D*(active score elements) / (time per step)
+  roofline   the attention kernel alone: its average duration over K launches
+             timed with HIP events on the stream it runs on, achieved TFLOP/s
+             against the bf16 dense MFMA peak, and (when a counter summary for
+             the current kernel source exists under profiles/) HBM traffic
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd effective TFLOP/s (active blocks) + % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_F32_TFLOPS = 157.3     # fp32 MFMA/vector dense
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/attn_bf16.hip",
+                  "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
+                  "block_sparse_flash_mask_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per attention-kernel launch from a committed counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, mask, budget_s):
+    """Time the fp64 oracle on a bounded, evenly spaced sample of query rows."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    total = w.B * w.H * w.S
+    cnt = mask.ne(0).sum(-1).reshape(-1).numpy()  # active blocks per mask row
+    flops_row = lambda rows: float(sum(4 * w.D * int(cnt[r // w.block_q]) * w.block_k
+                                       for r in rows))
+    calib = np.arange(0, total, max(1, total // 256), dtype=np.int64)[:256]
+    t0 = time.perf_counter()
+    oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, calib)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / len(calib)
+    n = int(min(total, max(len(calib), budget_s / max(per_row, 1e-9))))
+    stride = max(1, total // n)
+    rows = np.arange(0, total, stride, dtype=np.int64)[:n]
+    t0 = time.perf_counter()
+    oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, rows)
+    t = time.perf_counter() - t0
+    fl = flops_row(rows)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d query rows (every %dth), each over its full key list; %.1f s"
+                      % (len(rows), total, stride, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_bf16")
+    ap.add_argument("--config", default=None, help="tile config tq,tk,waves,stages (default: autotune)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the block-sparse forward runs on a single "
+              "MI355X (no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_flash_mask_amd as bs
+    import workloads as W
+
+    if not os.path.exists(bs.LIB_PATH):
+        from block_sparse_flash_mask_amd import build
+        build.build()
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs" % w.name)
+    q, k, v, mask = W.make_inputs(w)
+    qd, kd, vd, md = q.to(dev), k.to(dev), v.to(dev), mask.to(dev)
+    nnz = int(mask.ne(0).sum())
+    flops = 4.0 * w.D * nnz * w.block_q * w.block_k
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(bs.workspace_size(w.B, w.H, w.S, w.block_q, w.block_k), dtype=torch.uint8,
+                     device=dev)
+
+    if args.config:
+        cfg = tuple(int(x) for x in args.config.split(","))
+        tune_rows = []
+    else:
+        log("bench: autotuning tile configs (untimed)")
+        best, tune_rows = bs.autotune(qd, kd, vd, md, w.block_q, w.block_k, w.scale,
+                                      warmup=3, iters=10)
+        cfg = best.as_tuple()
+        for r in tune_rows:
+            log("  tune id=%d cfg=%s t_mean=%.4e t_std=%.2e" % (r.id, r.config, r.t_mean_s,
+                                                              r.t_std_s))
+
+    def step():
+        bs.fwd(qd, kd, vd, md, w.block_q, w.block_k, w.scale, out=out, lse=lse, workspace=ws,
+               config=cfg)
+
+    stream = torch.cuda.current_stream()
+    log("bench: warmup %d, timed %d steps, config %s" % (args.warmup, args.steps, cfg))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log("bench: %.4f ms/step (events), %.4f ms/step (wall)" % (ms_step, wall * 1e3 / args.steps))
+
+    # The dominant kernel alone: attention on a precomputed compaction, K launches
+    # bracketed by HIP events on the launch stream.
+    rp, ci = bs.compact_mask(md)
+    for _ in range(3):
+        bs.fwd_compacted(qd, kd, vd, rp, ci, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                         config=cfg)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.steps):
+        bs.fwd_compacted(qd, kd, vd, rp, ci, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                         config=cfg)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = a0.elapsed_time(a1) / args.steps
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    traffic = traffic_from_profiles(w.name)
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic,
+                "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+                "kernel_ms": ms_attn}
+    if traffic:
+        roofline["hbm_gbs"] = traffic / (ms_attn * 1e-3) / 1e9
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_k": w.block_k, "mask": w.mask_kind,
+                   "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
+                   "tile_config": list(cfg), "flops_per_step": flops},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, mask, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

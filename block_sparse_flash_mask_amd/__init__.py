@@ -1,0 +1,307 @@
+"""Block-sparse flash-attention forward for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libbsattn.so (C ABI in include/bsattn.h).  Every step of
+the computation runs in the library's HIP kernels; this module only checks
+tensor properties, allocates outputs and workspace through torch, and passes raw
+device pointers and torch's current HIP stream.  If libbsattn.so is missing the
+calls raise: there is no fallback path.
+
+    out, lse = fwd(q, k, v, block_mask, block_q, block_k, scale)
+
+q, k, v: [B, H, S, D] CUDA (HIP) tensors, bf16 or fp32, contiguous.
+block_mask: [B, H, S/block_q, S/block_k] uint8 or bool on the same device.
+Returns out (dtype of q, [B, H, S, D]) and lse (fp32, [B, H, S]).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+
+BSATTN_F32, BSATTN_BF16 = 0, 1
+STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
+          3: "BSATTN_ERR_UNSUPPORTED", 4: "BSATTN_ERR_ALIGN", 5: "BSATTN_ERR_WORKSPACE",
+          6: "BSATTN_ERR_SCALE", 7: "BSATTN_ERR_ALIAS", 8: "BSATTN_ERR_HIP"}
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [("tile_q", ctypes.c_int), ("tile_k", ctypes.c_int),
+                ("waves", ctypes.c_int), ("stages", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.tile_q, self.tile_k, self.waves, self.stages)
+
+    def __repr__(self):
+        return "TileConfig(tile_q=%d, tile_k=%d, waves=%d, stages=%d)" % self.as_tuple()
+
+
+class TuneResult(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("cfg", TileConfig), ("t_mean_s", ctypes.c_double),
+                ("t_std_s", ctypes.c_double), ("t_min_s", ctypes.c_double)]
+
+
+_lib = None
+
+
+def library():
+    """Load libbsattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libbsattn.so is not built (%s); run "
+                           "`python -m block_sparse_flash_mask_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    cfgp = ctypes.POINTER(TileConfig)
+    i32p = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "bsattn_version": ([], i32),
+        "bsattn_status_string": ([i32], ctypes.c_char_p),
+        "bsattn_last_hip_error": ([], i32),
+        "bsattn_compact_workspace_size": ([i32, i32, i32, i32, szp], i32),
+        "bsattn_compact_mask": ([p, i32, i32, i32, i32, p, p, p, sz, p], i32),
+        "bsattn_workspace_size": ([i32, i32, i32, i32, i32, szp], i32),
+        "bsattn_fwd": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz, p], i32),
+        "bsattn_fwd_config": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
+                               cfgp, p], i32),
+        "bsattn_fwd_compacted": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
+                                  cfgp, p], i32),
+        "bsattn_list_configs": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
+        "bsattn_autotune": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
+                             i32, i32, cfgp, ctypes.POINTER(TuneResult), i32, i32p,
+                             ctypes.c_char_p, p], i32),
+        "bsattn_load_tune_cache": ([ctypes.c_char_p], i32),
+        "bsattn_clear_tune_cache": ([], None),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        lib = library()
+        msg = lib.bsattn_status_string(rc).decode()
+        if rc == 8:
+            msg += " (hipError %d)" % lib.bsattn_last_hip_error()
+        raise BsattnError(rc, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BSATTN_BF16
+    if t.dtype == torch.float32:
+        return BSATTN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _cfg(config):
+    if config is None:
+        return None
+    if isinstance(config, TileConfig):
+        return ctypes.byref(config)
+    return ctypes.byref(TileConfig(*config))
+
+
+def default_scale(D):
+    """1/sqrt(D) rounded to fp32."""
+    return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous [B, H, S, D]" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be 4-D [B, H, S, D]" % name)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have one shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one dtype")
+    return tuple(q.shape)
+
+
+def _mask_u8(block_mask):
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dtype != torch.uint8:
+        raise TypeError("block_mask must be uint8 or bool")
+    if not block_mask.is_contiguous():
+        raise ValueError("block_mask must be contiguous")
+    return block_mask
+
+
+def workspace_size(B, H, S, block_q, block_k):
+    n = ctypes.c_size_t(0)
+    _check(library().bsattn_workspace_size(B, H, S, block_q, block_k, ctypes.byref(n)))
+    return n.value
+
+
+def compact_workspace_size(B, H, n_q, n_k):
+    n = ctypes.c_size_t(0)
+    _check(library().bsattn_compact_workspace_size(B, H, n_q, n_k, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small: need %d bytes" % nbytes)
+    return workspace
+
+
+def fwd(q, k, v, block_mask, block_q, block_k, scale=None, *, out=None, lse=None,
+        workspace=None, config=None, stream=None):
+    """Block-sparse attention forward; returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    block_mask = _mask_u8(block_mask)
+    if tuple(block_mask.shape) != (B, H, S // block_q, S // block_k):
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ws = _workspace(workspace_size(B, H, S, block_q, block_k), q.device, workspace)
+    lib = library()
+    rc = lib.bsattn_fwd_config(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(out), _ptr(lse),
+                               B, H, S, D, block_q, block_k, float(scale), _dtype_code(q),
+                               _ptr(ws), ws.numel() * ws.element_size(), _cfg(config),
+                               _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def compact_mask(block_mask, *, row_ptr=None, col_idx=None, workspace=None, stream=None):
+    """CSR lists of active key blocks per mask row.  Returns (row_ptr [R+1],
+    col_idx [R*n_k] int32, of which the first row_ptr[-1] entries are valid)."""
+    block_mask = _mask_u8(block_mask)
+    if block_mask.dim() != 4:
+        raise ValueError("block_mask must be [B, H, n_q, n_k]")
+    B, H, n_q, n_k = block_mask.shape
+    R = B * H * n_q
+    dev = block_mask.device
+    if row_ptr is None:
+        row_ptr = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(R * n_k, 1), dtype=torch.int32, device=dev)
+    ws = _workspace(compact_workspace_size(B, H, n_q, n_k), dev, workspace)
+    rc = library().bsattn_compact_mask(_ptr(block_mask), B, H, n_q, n_k, _ptr(row_ptr),
+                                       _ptr(col_idx), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream))
+    _check(rc)
+    return row_ptr, col_idx
+
+
+def fwd_compacted(q, k, v, row_ptr, col_idx, block_q, block_k, scale=None, *, out=None,
+                  lse=None, config=None, stream=None):
+    """The attention kernel alone on lists from compact_mask()."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if row_ptr.numel() != B * H * (S // block_q) + 1:
+        raise ValueError("row_ptr has the wrong length")
+    rc = library().bsattn_fwd_compacted(_ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
+                                        _ptr(out), _ptr(lse), B, H, S, D, block_q, block_k,
+                                        float(scale), _dtype_code(q), _cfg(config),
+                                        _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def list_configs(dtype, D, block_q, block_k):
+    """Tile configs built for this shape, in the library's preference order."""
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    n = ctypes.c_int(0)
+    lib = library()
+    _check(lib.bsattn_list_configs(code, D, block_q, block_k, None, 0, ctypes.byref(n)))
+    arr = (TileConfig * max(n.value, 1))()
+    _check(lib.bsattn_list_configs(code, D, block_q, block_k, arr, n.value, ctypes.byref(n)))
+    return [arr[i] for i in range(n.value)]
+
+
+@dataclass
+class TuneRow:
+    id: int
+    config: tuple
+    t_mean_s: float
+    t_std_s: float
+    t_min_s: float
+
+
+def autotune(q, k, v, block_mask, block_q, block_k, scale=None, *, warmup=3, iters=10,
+             cache_path=None, stream=None):
+    """Time every built tile config on these inputs; returns (best TileConfig,
+    [TuneRow sorted by t_mean]).  The winner is cached in-process for bsattn_fwd
+    (and merged into cache_path if given)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    block_mask = _mask_u8(block_mask)
+    if scale is None:
+        scale = default_scale(D)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ws = _workspace(workspace_size(B, H, S, block_q, block_k), q.device, None)
+    cap = 64
+    res = (TuneResult * cap)()
+    n = ctypes.c_int(0)
+    best = TileConfig()
+    path = cache_path.encode() if cache_path else None
+    rc = library().bsattn_autotune(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(out),
+                                   _ptr(lse), B, H, S, D, block_q, block_k, float(scale),
+                                   _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(),
+                                   warmup, iters, ctypes.byref(best), res, cap, ctypes.byref(n),
+                                   path, _stream(stream))
+    _check(rc)
+    rows = [TuneRow(res[i].id, res[i].cfg.as_tuple(), res[i].t_mean_s, res[i].t_std_s,
+                    res[i].t_min_s) for i in range(min(n.value, cap))]
+    return best, rows
+
+
+def load_tune_cache(path):
+    _check(library().bsattn_load_tune_cache(path.encode()))
+
+
+def clear_tune_cache():
+    library().bsattn_clear_tune_cache()
+
+
+def version():
+    v = library().bsattn_version()
+    return (v >> 16, (v >> 8) & 0xFF, v & 0xFF)

@@ -1,0 +1,504 @@
+// api.cpp -- the C ABI of libbsattn.so (declared in include/bsattn.h): argument
+// checks, workspace layout, tile-config choice, launches, and the autotuner.
+//
+// Every check runs on the host before the first HIP call, so a bad argument never
+// reaches the device.  Kernels are launched on the caller's stream and nothing is
+// allocated on the forward path.
+#include <algorithm>
+#include <cerrno>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "bsattn.h"
+#include "kernels.h"
+
+using namespace bsattn;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip = (int)e;
+    return BSATTN_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Compaction workspace: per-row counts, then per-row lists padded to n_k.
+size_t compact_ws_bytes(int64_t R, int64_t n_k) {
+    return align_up((size_t)R * 4) + align_up((size_t)(R * n_k) * 4);
+}
+
+int check_grid(int B, int H, int n_q, int n_k) {
+    if (B <= 0 || H <= 0 || n_q <= 0 || n_k <= 0) return BSATTN_ERR_SHAPE;
+    const int64_t R = (int64_t)B * H * n_q;
+    if (R * n_k >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;  // list entries are int32
+    if (R >= ((int64_t)1 << 31) / 2) return BSATTN_ERR_SHAPE;
+    return BSATTN_OK;
+}
+
+bool block_ok(int b) { return b == 64 || b == 128; }
+
+int check_fwd_shape(int B, int H, int S, int D, int block_q, int block_k, int dtype) {
+    if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block_q <= 0 || block_k <= 0)
+        return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    if (dtype != BSATTN_F32 && dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return BSATTN_ERR_UNSUPPORTED;
+    if (!block_ok(block_q) || !block_ok(block_k)) return BSATTN_ERR_UNSUPPORTED;
+    const int rc = check_grid(B, H, S / block_q, S / block_k);
+    if (rc) return rc;
+    if ((int64_t)B * H * S * D >= ((int64_t)1 << 40)) return BSATTN_ERR_SHAPE;
+    return BSATTN_OK;
+}
+
+// Checks shared by every forward entry point that takes q/k/v/out/lse.
+// Order: NULL pointers, then shapes, then alignment, scale and aliasing (the
+// alias test needs valid sizes).
+int check_fwd_buffers(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, int B, int H, int S, int D, int block_q, int block_k,
+                      int dtype, float scale) {
+    if (!q || !k || !v || !out || !lse) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
+    if (rc) return rc;
+    if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||
+        !is_aligned(lse, 4))
+        return BSATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return BSATTN_ERR_SCALE;
+    const size_t esz = dtype == BSATTN_F32 ? 4 : 2;
+    const size_t nt = (size_t)B * H * S * D * esz;
+    const size_t nl = (size_t)B * H * S * 4;
+    if (overlap(out, nt, q, nt) || overlap(out, nt, k, nt) || overlap(out, nt, v, nt) ||
+        overlap(lse, nl, q, nt) || overlap(lse, nl, k, nt) || overlap(lse, nl, v, nt) ||
+        overlap(lse, nl, out, nt))
+        return BSATTN_ERR_ALIAS;
+    return BSATTN_OK;
+}
+
+const Variant* variants(int dtype, int* n) {
+    return dtype == BSATTN_BF16 ? bf16_variants(n) : f32_variants(n);
+}
+
+bool legal(const Variant& v, int dtype, int D, int block_q, int block_k) {
+    return v.dtype == dtype && v.D == D && block_q % v.tile_q == 0 && block_k % v.tile_k == 0;
+}
+
+bool matches(const Variant& v, const bsattn_tile_config& c) {
+    return (!c.tile_q || c.tile_q == v.tile_q) && (!c.tile_k || c.tile_k == v.tile_k) &&
+           (!c.waves || c.waves == v.waves) && (!c.stages || c.stages == v.stages);
+}
+
+bool is_auto(const bsattn_tile_config* c) {
+    return !c || (!c->tile_q && !c->tile_k && !c->waves && !c->stages);
+}
+
+const Variant* find(int dtype, int D, int block_q, int block_k, const bsattn_tile_config& c) {
+    int n = 0;
+    const Variant* t = variants(dtype, &n);
+    for (int i = 0; i < n; ++i)
+        if (legal(t[i], dtype, D, block_q, block_k) && matches(t[i], c)) return &t[i];
+    return nullptr;
+}
+
+// ---- tuning cache -------------------------------------------------------------
+typedef std::tuple<int, int, int, int, int, int64_t> TuneKey;  // dtype, D, bq, bk, S, B*H
+
+struct TuneEntry {
+    bsattn_tile_config cfg;
+    double t_mean_s;
+};
+
+std::mutex g_tune_mu;
+std::map<TuneKey, TuneEntry> g_tune;
+
+bool tune_lookup(const TuneKey& key, bsattn_tile_config* out) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = g_tune.find(key);
+    if (it == g_tune.end()) return false;
+    *out = it->second.cfg;
+    return true;
+}
+
+bool json_number(const std::string& obj, const char* name, double* out) {
+    const std::string pat = std::string("\"") + name + "\"";
+    size_t p = obj.find(pat);
+    if (p == std::string::npos) return false;
+    p = obj.find(':', p + pat.size());
+    if (p == std::string::npos) return false;
+    const char* s = obj.c_str() + p + 1;
+    char* end = nullptr;
+    errno = 0;
+    const double v = std::strtod(s, &end);
+    if (end == s || errno) return false;
+    *out = v;
+    return true;
+}
+
+// Parse the entries of a cache file written by write_cache(); returns false if
+// the file cannot be opened.
+bool read_cache(const char* path, std::map<TuneKey, TuneEntry>* into) {
+    FILE* f = std::fopen(path, "rb");
+    if (!f) return false;
+    std::string text;
+    char buf[4096];
+    size_t n;
+    while ((n = std::fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, n);
+    std::fclose(f);
+    size_t p = text.find("\"entries\"");
+    if (p == std::string::npos) return true;
+    while ((p = text.find('{', p + 1)) != std::string::npos) {
+        const size_t e = text.find('}', p);
+        if (e == std::string::npos) break;
+        const std::string obj = text.substr(p, e - p + 1);
+        double dt, D, bq, bk, S, BH, tq, tk, w, st, tm = 0.0;
+        if (json_number(obj, "dtype", &dt) && json_number(obj, "D", &D) &&
+            json_number(obj, "block_q", &bq) && json_number(obj, "block_k", &bk) &&
+            json_number(obj, "S", &S) && json_number(obj, "BH", &BH) &&
+            json_number(obj, "tile_q", &tq) && json_number(obj, "tile_k", &tk) &&
+            json_number(obj, "waves", &w) && json_number(obj, "stages", &st)) {
+            json_number(obj, "t_mean_s", &tm);
+            TuneEntry te;
+            te.cfg = bsattn_tile_config{(int)tq, (int)tk, (int)w, (int)st};
+            te.t_mean_s = tm;
+            (*into)[TuneKey((int)dt, (int)D, (int)bq, (int)bk, (int)S, (int64_t)BH)] = te;
+        }
+        p = e;
+    }
+    return true;
+}
+
+bool write_cache(const char* path, const std::map<TuneKey, TuneEntry>& m) {
+    const std::string tmp = std::string(path) + ".tmp";
+    FILE* f = std::fopen(tmp.c_str(), "wb");
+    if (!f) return false;
+    std::fprintf(f, "{\"bsattn_tune_cache\": 1, \"entries\": [\n");
+    size_t i = 0;
+    for (const auto& kv : m) {
+        const TuneKey& k = kv.first;
+        const TuneEntry& e = kv.second;
+        std::fprintf(f,
+                     "  {\"dtype\": %d, \"D\": %d, \"block_q\": %d, \"block_k\": %d, \"S\": %d, "
+                     "\"BH\": %lld, \"tile_q\": %d, \"tile_k\": %d, \"waves\": %d, \"stages\": %d, "
+                     "\"t_mean_s\": %.6e}%s\n",
+                     std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k),
+                     std::get<4>(k), (long long)std::get<5>(k), e.cfg.tile_q, e.cfg.tile_k,
+                     e.cfg.waves, e.cfg.stages, e.t_mean_s, (++i < m.size()) ? "," : "");
+    }
+    std::fprintf(f, "]}\n");
+    const bool ok = std::fclose(f) == 0;
+    return ok && std::rename(tmp.c_str(), path) == 0;
+}
+
+bool env_config(bsattn_tile_config* c, bool* bad) {
+    *bad = false;
+    const char* s = std::getenv("BSATTN_CONFIG");
+    if (!s || !*s) return false;
+    int v[4] = {0, 0, 0, 0};
+    if (std::sscanf(s, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) != 4) {
+        *bad = true;
+        return false;
+    }
+    *c = bsattn_tile_config{v[0], v[1], v[2], v[3]};
+    return true;
+}
+
+// Choose the variant for a call: explicit config, else BSATTN_CONFIG, else the
+// tuning cache, else the first legal entry of the variant table (its order is
+// the built-in preference).
+const Variant* choose(int dtype, int D, int S, int64_t BH, int block_q, int block_k,
+                      const bsattn_tile_config* cfg) {
+    if (!is_auto(cfg)) return find(dtype, D, block_q, block_k, *cfg);
+    bsattn_tile_config c{0, 0, 0, 0};
+    bool bad = false;
+    if (env_config(&c, &bad)) return find(dtype, D, block_q, block_k, c);
+    if (bad) return nullptr;
+    if (tune_lookup(TuneKey(dtype, D, block_q, block_k, S, BH), &c)) {
+        const Variant* v = find(dtype, D, block_q, block_k, c);
+        if (v) return v;
+    }
+    return find(dtype, D, block_q, block_k, bsattn_tile_config{0, 0, 0, 0});
+}
+
+FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float* lse, int H,
+                  int S, int block_q, int block_k, float scale, const Variant& var) {
+    FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.H = H;
+    a.S = S;
+    a.n_q = S / block_q;
+    a.n_k = S / block_k;
+    a.block_q = block_q;
+    a.block_k = block_k;
+    a.sub_per_row = block_q / var.tile_q;
+    const bool neg = std::signbit(scale) && scale != 0.0f;
+    a.c = std::fabs(scale) * kLog2e;
+    a.qsign = neg ? 0x80008000u : 0u;
+    a.qsign32 = neg ? 0x80000000u : 0u;
+    return a;
+}
+
+int run_attention(const FwdArgs& a, const Variant& var, int64_t R, hipStream_t stream) {
+    const int64_t grid = R * a.sub_per_row;
+    if (grid <= 0 || grid >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    const hipError_t e = var.launch(a, (unsigned)grid, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsattn_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* bsattn_status_string(int status) {
+    switch (status) {
+        case BSATTN_OK: return "BSATTN_OK: success";
+        case BSATTN_ERR_NULL: return "BSATTN_ERR_NULL: a required pointer is NULL";
+        case BSATTN_ERR_SHAPE:
+            return "BSATTN_ERR_SHAPE: a size is <= 0, S is not divisible by a block size, "
+                   "or an index would overflow";
+        case BSATTN_ERR_UNSUPPORTED:
+            return "BSATTN_ERR_UNSUPPORTED: head dim, dtype, block size or tile config not built";
+        case BSATTN_ERR_ALIGN:
+            return "BSATTN_ERR_ALIGN: q/k/v/out must be 16-byte and lse 4-byte aligned";
+        case BSATTN_ERR_WORKSPACE: return "BSATTN_ERR_WORKSPACE: workspace missing or too small";
+        case BSATTN_ERR_SCALE: return "BSATTN_ERR_SCALE: scale is not finite";
+        case BSATTN_ERR_ALIAS: return "BSATTN_ERR_ALIAS: an output overlaps an input or the other output";
+        case BSATTN_ERR_HIP: return "BSATTN_ERR_HIP: a HIP runtime call failed";
+        default: return "BSATTN: unknown status";
+    }
+}
+
+int bsattn_last_hip_error(void) { return g_last_hip; }
+
+int bsattn_compact_workspace_size(int B, int H, int n_q, int n_k, size_t* bytes) {
+    if (!bytes) return BSATTN_ERR_NULL;
+    const int rc = check_grid(B, H, n_q, n_k);
+    if (rc) return rc;
+    *bytes = compact_ws_bytes((int64_t)B * H * n_q, n_k);
+    return BSATTN_OK;
+}
+
+int bsattn_compact_mask(const uint8_t* block_mask, int B, int H, int n_q, int n_k,
+                        int32_t* row_ptr, int32_t* col_idx, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (!block_mask || !row_ptr || !col_idx) return BSATTN_ERR_NULL;
+    int rc = check_grid(B, H, n_q, n_k);
+    if (rc) return rc;
+    const int64_t R = (int64_t)B * H * n_q;
+    if (!workspace || workspace_bytes < compact_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(row_ptr, 4) || !is_aligned(col_idx, 4) || !is_aligned(workspace, 4))
+        return BSATTN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* counts = (int32_t*)workspace;
+    int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
+    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_compact_scan(counts, R, row_ptr, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_compact_pack(counts, lists, R, n_k, row_ptr, col_idx, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes) {
+    if (!bytes) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    const int rc = check_grid(B, H, S / block_q, S / block_k);
+    if (rc) return rc;
+    *bytes = compact_ws_bytes((int64_t)B * H * (S / block_q), S / block_k);
+    return BSATTN_OK;
+}
+
+int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                      void* out, float* lse, int B, int H, int S, int D, int block_q,
+                      int block_k, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, const bsattn_tile_config* cfg, void* stream) {
+    if (!block_mask) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const int64_t R = (int64_t)B * H * n_q;
+    if (!workspace || workspace_bytes < compact_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
+    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* counts = (int32_t*)workspace;
+    int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
+    const hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    if (e != hipSuccess) return hip_fail(e);
+
+    FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
+    a.counts = counts;
+    a.list = lists;
+    a.ell_stride = n_k;
+    return run_attention(a, *var, R, s);
+}
+
+int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+               void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+               float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return bsattn_fwd_config(q, k, v, block_mask, out, lse, B, H, S, D, block_q, block_k, scale,
+                             dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,
+                         const int32_t* col_idx, void* out, float* lse, int B, int H, int S,
+                         int D, int block_q, int block_k, float scale, int dtype,
+                         const bsattn_tile_config* cfg, void* stream) {
+    if (!row_ptr || !col_idx) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    if (!is_aligned(row_ptr, 4) || !is_aligned(col_idx, 4)) return BSATTN_ERR_ALIGN;
+    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)B * H * (S / block_q);
+    FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
+    a.row_ptr = row_ptr;
+    a.list = col_idx;
+    a.ell_stride = 0;
+    return run_attention(a, *var, R, (hipStream_t)stream);
+}
+
+int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
+                        int cap, int* n) {
+    if (!n) return BSATTN_ERR_NULL;
+    if (dtype != BSATTN_F32 && dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    int nv = 0;
+    const Variant* t = variants(dtype, &nv);
+    int cnt = 0;
+    for (int i = 0; i < nv; ++i) {
+        if (!legal(t[i], dtype, D, block_q, block_k)) continue;
+        if (cfgs && cnt < cap)
+            cfgs[cnt] = bsattn_tile_config{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
+        ++cnt;
+    }
+    *n = cnt;
+    return BSATTN_OK;
+}
+
+int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                    void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes, int warmup,
+                    int iters, bsattn_tile_config* best, bsattn_tune_result* results, int cap,
+                    int* n_results, const char* cache_path, void* stream) {
+    if (!best || !block_mask) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    const int64_t R = (int64_t)B * H * (S / block_q);
+    if (!workspace || workspace_bytes < compact_ws_bytes(R, S / block_k)) return BSATTN_ERR_WORKSPACE;
+    if (warmup < 0 || iters < 1) return BSATTN_ERR_SHAPE;
+
+    int nv = 0;
+    const Variant* t = variants(dtype, &nv);
+    std::vector<bsattn_tune_result> res;
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<hipEvent_t> ev((size_t)iters + 1);
+    for (auto& e : ev) {
+        const hipError_t he = hipEventCreate(&e);
+        if (he != hipSuccess) return hip_fail(he);
+    }
+    int status = BSATTN_OK;
+    for (int i = 0; i < nv && status == BSATTN_OK; ++i) {
+        if (!legal(t[i], dtype, D, block_q, block_k)) continue;
+        const bsattn_tile_config c{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
+        for (int w = 0; w < warmup && status == BSATTN_OK; ++w)
+            status = bsattn_fwd_config(q, k, v, block_mask, out, lse, B, H, S, D, block_q, block_k,
+                                       scale, dtype, workspace, workspace_bytes, &c, stream);
+        hipError_t he = hipEventRecord(ev[0], s);
+        if (he != hipSuccess) { status = hip_fail(he); break; }
+        for (int it = 0; it < iters && status == BSATTN_OK; ++it) {
+            status = bsattn_fwd_config(q, k, v, block_mask, out, lse, B, H, S, D, block_q, block_k,
+                                       scale, dtype, workspace, workspace_bytes, &c, stream);
+            he = hipEventRecord(ev[(size_t)it + 1], s);
+            if (he != hipSuccess) status = hip_fail(he);
+        }
+        if (status != BSATTN_OK) break;
+        he = hipEventSynchronize(ev[(size_t)iters]);
+        if (he != hipSuccess) { status = hip_fail(he); break; }
+        double sum = 0.0, sum2 = 0.0, mn = 1e300;
+        for (int it = 0; it < iters; ++it) {
+            float ms = 0.f;
+            he = hipEventElapsedTime(&ms, ev[(size_t)it], ev[(size_t)it + 1]);
+            if (he != hipSuccess) { status = hip_fail(he); break; }
+            const double sec = ms * 1e-3;
+            sum += sec;
+            sum2 += sec * sec;
+            mn = std::min(mn, sec);
+        }
+        if (status != BSATTN_OK) break;
+        const double mean = sum / iters;
+        const double var = std::max(0.0, sum2 / iters - mean * mean);
+        bsattn_tune_result r;
+        r.id = i;
+        r.cfg = c;
+        r.t_mean_s = mean;
+        r.t_std_s = std::sqrt(var);
+        r.t_min_s = mn;
+        res.push_back(r);
+    }
+    for (auto& e : ev) hipEventDestroy(e);
+    if (status != BSATTN_OK) return status;
+    if (res.empty()) return BSATTN_ERR_UNSUPPORTED;
+    std::stable_sort(res.begin(), res.end(), [](const bsattn_tune_result& x,
+                                                 const bsattn_tune_result& y) {
+        return x.t_mean_s < y.t_mean_s;
+    });
+    *best = res[0].cfg;
+    if (n_results) *n_results = (int)res.size();
+    if (results)
+        for (int i = 0; i < cap && i < (int)res.size(); ++i) results[i] = res[(size_t)i];
+    const TuneKey key(dtype, D, block_q, block_k, S, (int64_t)B * H);
+    {
+        std::lock_guard<std::mutex> lk(g_tune_mu);
+        g_tune[key] = TuneEntry{res[0].cfg, res[0].t_mean_s};
+        if (cache_path) {
+            std::map<TuneKey, TuneEntry> merged;
+            read_cache(cache_path, &merged);
+            merged[key] = g_tune[key];
+            if (!write_cache(cache_path, merged)) return BSATTN_ERR_NULL;
+        }
+    }
+    return BSATTN_OK;
+}
+
+int bsattn_load_tune_cache(const char* cache_path) {
+    if (!cache_path) return BSATTN_ERR_NULL;
+    std::map<TuneKey, TuneEntry> m;
+    if (!read_cache(cache_path, &m)) return BSATTN_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    for (const auto& kv : m) g_tune[kv.first] = kv.second;
+    return BSATTN_OK;
+}
+
+void bsattn_clear_tune_cache(void) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune.clear();
+}
+
+}  // extern "C"

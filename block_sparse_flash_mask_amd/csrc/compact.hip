@@ -1,0 +1,131 @@
+// compact.hip -- block-mask compaction kernels for gfx950.
+//
+// The forward pass visits only active (query block, key block) pairs.  These
+// kernels turn the uint8 block mask [B][H][n_q][n_k] into per-mask-row lists of
+// active key blocks, in ascending kj order:
+//   rows_kernel   one wave per mask row: a ballot over 64 mask bytes at a time
+//                 and a per-lane prefix count (mbcnt) place each active kj; the
+//                 row's count and its list (padded to n_k entries) are written.
+//   scan_kernel   one workgroup: exclusive scan of the row counts -> row_ptr.
+//   pack_kernel   one wave per row: copy each padded list to its CSR slot.
+// All integer, so the result is bit-exact and deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace bsattn {
+
+constexpr int kRowsPerBlock = 4;  // one wave per mask row, 4 waves per workgroup
+
+__global__ __launch_bounds__(256) void rows_kernel(const uint8_t* __restrict__ mask, int64_t R,
+                                                   int n_k, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ lists) {
+    const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (r >= R) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const uint8_t* mrow = mask + r * n_k;
+    int32_t* lrow = lists + r * n_k;
+    int base = 0;
+    for (int s0 = 0; s0 < n_k; s0 += kWave) {
+        const int kj = s0 + lane;
+        const bool active = kj < n_k && mrow[kj] != 0;
+        const uint64_t bal = __ballot(active);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (active) lrow[base + below] = kj;
+        base += __popcll(bal);
+    }
+    if (lane == 0) counts[r] = base;
+}
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanPerThread = 4;
+
+// Inclusive scan across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
+                                                            int64_t R,
+                                                            int32_t* __restrict__ row_ptr) {
+    __shared__ int wave_tot[kScanThreads / kWave];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) {
+        row_ptr[0] = 0;
+        carry_s = 0;
+    }
+    __syncthreads();
+    constexpr int64_t kTile = (int64_t)kScanThreads * kScanPerThread;
+    for (int64_t t0 = 0; t0 < R; t0 += kTile) {
+        const int64_t i0 = t0 + (int64_t)tid * kScanPerThread;
+        int v[kScanPerThread];
+        int run = 0;
+#pragma unroll
+        for (int j = 0; j < kScanPerThread; ++j) {
+            v[j] = (i0 + j < R) ? counts[i0 + j] : 0;
+            run += v[j];
+            v[j] = run;  // inclusive within the thread
+        }
+        const int incl = wave_inclusive_scan(run);
+        if (lane == 63) wave_tot[wave] = incl;
+        __syncthreads();
+        if (wave == 0) {
+            int wt = lane < kScanThreads / kWave ? wave_tot[lane] : 0;
+            wt = wave_inclusive_scan(wt);
+            if (lane < kScanThreads / kWave) wave_tot[lane] = wt;  // inclusive over waves
+        }
+        __syncthreads();
+        const int carry = carry_s;
+        const int before = carry + (wave > 0 ? wave_tot[wave - 1] : 0) + (incl - run);
+#pragma unroll
+        for (int j = 0; j < kScanPerThread; ++j)
+            if (i0 + j < R) row_ptr[i0 + j + 1] = before + v[j];
+        __syncthreads();
+        if (tid == 0) carry_s = carry + wave_tot[kScanThreads / kWave - 1];
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ lists, int64_t R,
+                                                   int n_k, const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ col_idx) {
+    const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (r >= R) return;
+    const int lane = threadIdx.x & 63;
+    const int cnt = counts[r];
+    const int32_t* src = lists + r * n_k;
+    int32_t* dst = col_idx + row_ptr[r];
+    for (int i = lane; i < cnt; i += kWave) dst[i] = src[i];
+}
+
+hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t* counts,
+                               int32_t* lists, hipStream_t stream) {
+    const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, R, n_k,
+                       counts, lists);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_scan(const int32_t* counts, int64_t R, int32_t* row_ptr,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, R, row_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int64_t R, int n_k,
+                               const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream) {
+    const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, counts, lists, R,
+                       n_k, row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+}  // namespace bsattn

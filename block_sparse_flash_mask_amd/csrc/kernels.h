@@ -1,0 +1,34 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to libbsattn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace bsattn {
+
+// Mask compaction (compact.hip).
+hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t* counts,
+                               int32_t* lists, hipStream_t stream);
+hipError_t launch_compact_scan(const int32_t* counts, int64_t R, int32_t* row_ptr,
+                               hipStream_t stream);
+hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int64_t R, int n_k,
+                               const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
+// One compiled attention variant.
+struct Variant {
+    int dtype;   // 0 = fp32, 1 = bf16
+    int D;
+    int tile_q;
+    int tile_k;
+    int waves;
+    int stages;
+    hipError_t (*launch)(const FwdArgs& a, unsigned grid, hipStream_t stream);
+};
+
+// Tables of the built variants (attn_bf16.hip, attn_f32.hip).
+const Variant* bf16_variants(int* n);
+const Variant* f32_variants(int* n);
+
+}  // namespace bsattn

@@ -1,0 +1,174 @@
+/*
+ * bsattn.h -- C ABI of the block-sparse flash-attention forward library for
+ * AMD Instinct MI355X (gfx950), libbsattn.so.
+ *
+ * The operation.  For every batch b, head h and query row r:
+ *   out[b,h,r,:] = sum_j softmax_j(scale * q[b,h,r,:] . k[b,h,j,:]) * v[b,h,j,:]
+ *   lse[b,h,r]   = log sum_j exp(scale * q[b,h,r,:] . k[b,h,j,:])      (natural log)
+ * where j runs only over keys whose key block is active for the query block of r:
+ * block_mask[b,h,r/block_q,j/block_k] != 0.  All other scores count as -inf.  A
+ * row with no active key block gets out = 0 and lse = -inf.
+ * Source: "Writing Pallas Kernels for JAX" (rajatpandit.com), section "Writing the
+ * Kernel Logic: Load, Compute, Store" (scaled scores, mask to -inf, softmax, times
+ * V); "Pallas-Triton kernels and kernel auto-tuning" (robertdyro.com), section
+ * "Flash Attention" (the tiled method computes the operator exactly, never
+ * building the score matrix).
+ *
+ * Conventions shared by every entry point.
+ *  - Every array argument is a DEVICE pointer owned by the caller.  Nothing is
+ *    allocated on the call path of bsattn_compact_mask, bsattn_fwd,
+ *    bsattn_fwd_config or bsattn_fwd_compacted; the caller passes a workspace.
+ *  - Layouts: q, k, v, out are [B][H][S][D], contiguous, D fastest, all of one
+ *    element type (fp32 or bf16 as IEEE bits); lse is float [B][H][S];
+ *    block_mask is uint8 [B][H][S/block_q][S/block_k], any nonzero byte = active.
+ *  - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; results are valid once the stream has synchronised.
+ *  - Every argument check runs on the host before any device work.  A failed
+ *    check returns a nonzero bsattn_status and touches nothing.  A failed HIP
+ *    call returns BSATTN_ERR_HIP and bsattn_last_hip_error() gives its code.
+ *    No exception crosses this boundary and nothing aborts.
+ *  - Calls on different streams may run concurrently if they use different
+ *    workspaces and outputs.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BSATTN_F32 = 0, BSATTN_BF16 = 1 } bsattn_dtype;
+
+typedef enum {
+    BSATTN_OK = 0,
+    BSATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    BSATTN_ERR_SHAPE = 2,       /* a size <= 0, S not divisible by a block size,
+                                   or an index would overflow int32 */
+    BSATTN_ERR_UNSUPPORTED = 3, /* D, dtype, block size or tile config not built */
+    BSATTN_ERR_ALIGN = 4,       /* q/k/v/out not 16-byte or lse not 4-byte aligned */
+    BSATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    BSATTN_ERR_SCALE = 6,       /* scale is NaN or infinite */
+    BSATTN_ERR_ALIAS = 7,       /* out or lse overlaps q, k or v (or each other) */
+    BSATTN_ERR_HIP = 8          /* a HIP runtime call failed */
+} bsattn_status;
+
+/* Kernel tiling of the attention kernel (the autotuner's search space).
+ *   tile_q  query rows per workgroup: 64 or 128, must divide block_q;
+ *   tile_k  keys per inner step: 32, 64 or 128, must divide block_k;
+ *   waves   wavefronts per workgroup (64 lanes each); with 32 query rows per
+ *           wave this is tile_q / 32;
+ *   stages  K/V tiles resident in LDS: 1 (load, barrier, compute) or 2 (the
+ *           next tile is written while the current one is consumed).
+ * A zero field means "choose automatically".  The kernel tiling never changes
+ * the result beyond fp32 rounding order: block_q and block_k (the mask
+ * granularity) do. */
+typedef struct {
+    int tile_q;
+    int tile_k;
+    int waves;
+    int stages;
+} bsattn_tile_config;
+
+/* One timed variant, in the column layout of the tuning table in
+ * "Pallas-Triton kernels and kernel auto-tuning", section "Auto-tuning". */
+typedef struct {
+    int id;
+    bsattn_tile_config cfg;
+    double t_mean_s;
+    double t_std_s;
+    double t_min_s;
+} bsattn_tune_result;
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int bsattn_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* bsattn_status_string(int status);
+
+/* The hipError_t of the last failed HIP call in this thread (0 if none). */
+int bsattn_last_hip_error(void);
+
+/* Workspace bytes needed by bsattn_compact_mask for a mask of B*H*n_q rows of
+ * n_k blocks.  Returns BSATTN_ERR_SHAPE / BSATTN_ERR_NULL on bad arguments. */
+int bsattn_compact_workspace_size(int B, int H, int n_q, int n_k, size_t* bytes);
+
+/* Mask compaction (the first step of the forward): the per-query-block lists of
+ * active key blocks, in CSR form.  For each mask row in (b, h, qi) row-major
+ * order the active kj are listed in ascending order:
+ *   row_ptr[0] = 0, row_ptr[i+1] = row_ptr[i] + (active blocks of row i),
+ *   col_idx[row_ptr[i] .. row_ptr[i+1]) = those kj.
+ * row_ptr has B*H*n_q + 1 entries; col_idx must have room for B*H*n_q*n_k
+ * entries (only the first row_ptr[B*H*n_q] are written).  The result is unique
+ * and bit-exact.  The mask pages describe the block-skipping idea only loosely
+ * ("Writing Pallas Kernels for JAX", section "Writing the Kernel Logic": the mask
+ * tile is read once per chunk); the list form is this library's. */
+int bsattn_compact_mask(const uint8_t* block_mask, int B, int H, int n_q, int n_k,
+                        int32_t* row_ptr, int32_t* col_idx, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by bsattn_fwd / bsattn_fwd_config. */
+int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes);
+
+/* The forward pass: mask compaction, then the fused attention kernel (S = scale
+ * Q K^T per active tile pair, an online softmax with running row max and row sum,
+ * O += P V), writing out (same element type as q) and lse.
+ *   D        64 or 128;   block_q, block_k   64 or 128;   S % block_q == 0 and
+ *            S % block_k == 0;   scale  any finite fp32 (negative and 0 allowed);
+ *   dtype    BSATTN_BF16 (fp32 accumulation, bf16 out) or BSATTN_F32.
+ * The tile config comes from the environment (BSATTN_CONFIG="tq,tk,waves,stages"),
+ * else from the autotuner's cache for this shape, else a built-in default. */
+int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+               void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+               float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As bsattn_fwd with an explicit tile config (cfg == NULL or all-zero = auto). */
+int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                      void* out, float* lse, int B, int H, int S, int D, int block_q,
+                      int block_k, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, const bsattn_tile_config* cfg, void* stream);
+
+/* The attention kernel alone, on lists already built by bsattn_compact_mask
+ * (row_ptr, col_idx as that call wrote them, for the same mask).  This is the
+ * second step of bsattn_fwd, exposed so callers can reuse one compaction across
+ * calls and time the kernel by itself.  cfg as in bsattn_fwd_config. */
+int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,
+                         const int32_t* col_idx, void* out, float* lse, int B, int H, int S,
+                         int D, int block_q, int block_k, float scale, int dtype,
+                         const bsattn_tile_config* cfg, void* stream);
+
+/* Number of tile configs built for (dtype, D, block_q, block_k), and the configs
+ * themselves (up to cap are written to cfgs; cfgs may be NULL to count). */
+int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
+                        int cap, int* n);
+
+/* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
+ * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
+ * point, keep the fastest).  Times bsattn_fwd_config for every built config of
+ * this shape on the caller's buffers (warmup runs, then iters timed runs each,
+ * with HIP events on stream), writes the fastest to *best, records it in the
+ * in-process cache used by bsattn_fwd for this shape, and, if cache_path is not
+ * NULL, merges it into that JSON file.  results (may be NULL) receives up to cap
+ * rows sorted by t_mean; *n_results gets the number of configs timed.  out and
+ * lse are overwritten.  This call synchronises the stream and may take seconds. */
+int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                    void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes, int warmup,
+                    int iters, bsattn_tile_config* best, bsattn_tune_result* results, int cap,
+                    int* n_results, const char* cache_path, void* stream);
+
+/* Load tuned configs from a JSON file written by bsattn_autotune into the
+ * in-process cache.  Returns BSATTN_OK, or BSATTN_ERR_NULL if the file cannot be
+ * read. */
+int bsattn_load_tune_cache(const char* cache_path);
+
+/* Clear the in-process tuning cache. */
+void bsattn_clear_tune_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

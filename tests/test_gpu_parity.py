@@ -1,0 +1,141 @@
+"""GPU forward vs the fp64 CPU oracle on identical seeded inputs.
+
+Small shapes are compared element by element over the whole output; the five
+workloads run at full size in the default launch configuration and are compared
+on a seeded sample of rows the oracle computes one by one (plus properties that
+hold for every row)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import bs, compare, dkey, ensure_built, rand_mask, rand_qkv, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(q, k, v, mask, bq, bk, scale, config=None, what=""):
+    ensure_built()
+    say("fwd", what, tuple(q.shape), q.dtype, bq, bk, scale, config)
+    out, lse = bs.fwd(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), bq, bk, scale, config=config)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, mask, bq, bk, scale)
+    return compare(out, lse, ro, rl, dkey(q), what)
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_workload_sampled_rows(name):
+    w = W.WORKLOADS[name]
+    ensure_built()
+    q, k, v, mask = W.make_inputs(w)
+    say("workload", name, tuple(q.shape), int(mask.sum()))
+    out, lse = bs.fwd(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), w.block_q, w.block_k, w.scale)
+    torch.cuda.synchronize()
+    # properties of every row: finite, no NaN, |out| bounded by max |v|
+    o = out.float()
+    assert torch.isfinite(o).all()
+    assert torch.isfinite(lse).all()  # no workload has an empty mask row
+    assert float(o.abs().max()) <= float(v.float().abs().max()) + 1e-2
+    rows = W.sample_rows(w.B, w.H, w.S, w.block_q, 64, mask=mask)
+    ro, rl = oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, rows)
+    go = out.reshape(-1, w.D)[torch.as_tensor(rows, device=out.device)]
+    gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
+    stats = compare(go, gl, ro, rl, w.dtype, name)
+    say("  stats", stats)
+    if name == "tiny_f32":  # small enough for the whole output
+        _run_full(q, k, v, mask, w.block_q, w.block_k, w.scale, what=name)
+
+
+SHAPES = [
+    # B, H, S, D, bq, bk, dtype, p
+    (1, 2, 256, 64, 64, 64, torch.float32, 0.5),
+    (1, 2, 384, 128, 128, 128, torch.bfloat16, 0.6),
+    (2, 1, 320, 64, 64, 64, torch.bfloat16, 0.5),     # n_q = n_k = 5
+    (1, 3, 512, 128, 64, 128, torch.bfloat16, 0.5),   # block_q != block_k
+    (1, 2, 512, 64, 128, 64, torch.bfloat16, 0.5),
+    (1, 1, 1024, 128, 128, 128, torch.bfloat16, 1.0),  # dense, 8 key blocks per row
+    (2, 2, 256, 128, 64, 64, torch.float32, 0.4),
+    (1, 2, 384, 64, 128, 64, torch.float32, 0.5),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(x) for x in s[:6]) + str(s[6])[-4:])
+def test_full_output_default_config(shape):
+    B, H, S, D, bq, bk, dt, p = shape
+    q, k, v = rand_qkv(B, H, S, D, dt, seed=S + D)
+    mask = rand_mask(B, H, S // bq, S // bk, p, seed=7, diag=True, empty_rows=[(0, 0, 1)])
+    _run_full(q, k, v, mask, bq, bk, 1.0 / np.sqrt(D), what=str(shape))
+
+
+def _configs(dtype, D, bq, bk):
+    ensure_built()
+    return [c.as_tuple() for c in bs.list_configs(dtype, D, bq, bk)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("blocks", [(128, 128), (64, 64), (64, 128)])
+def test_every_config(dtype, D, blocks):
+    bq, bk = blocks
+    B, H, S = 1, 2, 512
+    q, k, v = rand_qkv(B, H, S, D, dtype, seed=D + bq)
+    mask = rand_mask(B, H, S // bq, S // bk, 0.5, seed=bk, empty_rows=[(0, 1, 0)])
+    ro, rl = oracle.fwd(q, k, v, mask, bq, bk, 0.1)
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    cfgs = _configs(dtype, D, bq, bk)
+    assert cfgs
+    for cfg in cfgs:
+        say("config", cfg, D, blocks, dtype)
+        out, lse = bs.fwd(qd, kd, vd, md, bq, bk, 0.1, config=cfg)
+        torch.cuda.synchronize()
+        compare(out, lse, ro, rl, dkey(q), str(cfg))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_edge_cases(dtype):
+    B, H, S, D, b = 2, 2, 256, 64, 64
+    q, k, v = rand_qkv(B, H, S, D, dtype, seed=3)
+    n = S // b
+    # all-empty mask: zeros and -inf everywhere
+    _run_full(q, k, v, torch.zeros(B, H, n, n, dtype=torch.uint8), b, b, 0.125, what="empty")
+    # one active block per row, a different block per head
+    m = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    for h in range(H):
+        for i in range(n):
+            m[:, h, i, (i + h) % n] = 1
+    _run_full(q, k, v, m, b, b, 0.125, what="single block")
+    # negative and zero scale
+    mask = rand_mask(B, H, n, n, 0.5, seed=11, empty_rows=[(1, 1, 3)])
+    _run_full(q, k, v, mask, b, b, -0.3, what="negative scale")
+    _run_full(q, k, v, mask, b, b, 0.0, what="zero scale")
+    # large score magnitudes: a shared offset on every key (checks max subtraction)
+    c = 4.0 * torch.randn(D, generator=torch.Generator().manual_seed(5))
+    k2 = (k.float() + c).to(dtype)
+    _run_full(q, k2, v, mask, b, b, 0.125, what="shifted keys")
+
+
+def test_compacted_matches_fwd():
+    ensure_built()
+    B, H, S, D, b = 1, 4, 512, 128, 128
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=21)
+    mask = rand_mask(B, H, S // b, S // b, 0.5, seed=22)
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    o1, l1 = bs.fwd(qd, kd, vd, md, b, b, 0.09)
+    rp, ci = bs.compact_mask(md)
+    o2, l2 = bs.fwd_compacted(qd, kd, vd, rp, ci, b, b, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic():
+    ensure_built()
+    w = W.WORKLOADS["sparse_bf16"]
+    B, H, S = 1, 4, 4096
+    q, k, v = rand_qkv(B, H, S, 128, torch.bfloat16, seed=31)
+    mask = W.mask_window_global_random(B, H, S // 128, S // 128, seed=7)
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    o1, l1 = bs.fwd(qd, kd, vd, md, 128, 128, w.scale)
+    o2, l2 = bs.fwd(qd, kd, vd, md, 128, 128, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
