@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--config", default=None, help="tile config tq,tk,waves,stages (default: autotune)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times (to scale HBM "
+                         "byte counters against a kernel of known traffic)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -103,6 +106,16 @@ def main():
 
     import block_sparse_flash_mask_amd as bs
     import workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
 
     if not os.path.exists(bs.LIB_PATH):
         from block_sparse_flash_mask_amd import build

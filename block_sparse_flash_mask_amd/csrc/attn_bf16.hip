@@ -7,38 +7,48 @@
 // per-tile softmax of that page's listing, the softmax here runs over the whole
 // row with a running row max and running row sum, so the result is the exact
 // operator ("Pallas-Triton kernels and kernel auto-tuning", section "Flash
-// Attention").  Inactive key blocks are not visited at all.
+// Attention").  Inactive key blocks are never visited.
 //
 // Work decomposition.  One workgroup owns tile_q = 32*WAVES query rows of one mask
 // row (b, h, qi); wave w owns 32 of them.  It walks that mask row's list of active
-// key blocks in steps of TK keys.  Per step:
-//   S^T[key][q] = K Q^T   v_mfma_f32_32x32x16_bf16, A = K (from LDS), B = Q^T
-//                         (held in VGPRs for the whole kernel).  Each lane holds
-//                         one query column and 16 keys per 32x32 tile, so the row
-//                         max is a lane-local max plus one exchange with lane^32.
-//   online softmax        m' = max(m, c*rowmax S), alpha = 2^(m - m'),
-//                         P = 2^(c*S - m'), l = alpha*l + rowsum P, O *= alpha,
-//                         with c = |scale| * log2(e) (a negative scale flips the
-//                         sign of Q, which is exact in bf16).
-//   O^T[d][q] += V^T P^T  v_mfma_f32_32x32x16_bf16, A = V^T (from LDS), B = P^T
-//                         straight from the S^T registers converted to bf16.
-// The K rows are fed to the first MFMA in a bit-swapped order (kperm) chosen so
-// that the keys each lane holds after it are exactly the keys the second MFMA
-// wants in that lane: P never moves between lanes.
+// key blocks in steps of TK keys.  Per step and wave:
+//   S^T[key][q] = K Q^T   v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T held
+//                         in VGPRs for the whole kernel.  Each lane owns one query
+//                         column, so the row max is lane-local plus one exchange
+//                         with lane^32.
+//   online softmax        base 2 with c = |scale|*log2(e) (a negative scale flips
+//                         the sign of Q, exact in bf16).  The reference max m only
+//                         moves when the tile max exceeds it by more than 8 (2^8
+//                         headroom): then O and l are rescaled by 2^(m-m').  Any
+//                         reference <= the true max gives the same exact result,
+//                         so most steps skip the rescale.
+//   O^T[d][q] += V^T P^T  v_mfma_f32_32x32x16_bf16; A = V^T read from LDS with
+//                         the transposing ds_read_b64_tr_b16, B = P^T straight from
+//                         the S^T registers converted to bf16.
+// K rows enter the first MFMA in a bit-swapped order (kperm) so that the keys a
+// lane holds after it are exactly the keys the second MFMA wants in that lane.
 //
-// LDS.  K tile [TK][D] row-major, V tile transposed [D][TK]; both XOR-swizzled at
-// 16-byte granularity so the MFMA operand reads (8 rows x 16 B per LDS cycle) and
-// the writes hit distinct banks.  STAGES = 2 keeps two K/V tiles: the next tile is
-// fetched into VGPRs before the current tile's MFMAs and written to the other LDS
-// buffer after them, one barrier per step.  STAGES = 1 uses one buffer and two
-// barriers per step.
+// Memory path.  K and V tiles go HBM -> LDS by direct DMA (global_load_lds, 16 B
+// per lane), no VGPR staging.  Both are stored in LDS in the order the MFMA
+// operand reads consume them:
+//   K: one 1 KiB block per (32-key tile mt, 16-deep k-step ks); lane l's 16 bytes
+//      at l*16 are K[32mt + kperm(l%32)][16ks + 8(l/32) .. +7];
+//   V: one 512 B block per (mt, 16-key half e, 4-key quarter r, 32-wide d tile md);
+//      lane l's 8 bytes at l*8 are what the 16x4 transpose of its 16-lane group
+//      needs: V[32mt + 16e + 8h + 4r + L/4][32md + 16g + 4(L%4) .. +3] with
+//      L = l%16, g = (l/16)%2, h = l/32.
+// Every LDS read is lane-linear (conflict free) at a per-lane base plus a
+// compile-time offset.  Two stages live in distinct LDS arrays: the next step's
+// DMA is issued into the other array right after the per-step barrier and
+// overlaps the current step's MFMAs.
 #include "common.h"
 #include "kernels.h"
 
 namespace bsattn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#define BSATTN_LDS __attribute__((address_space(3)))
 
 // Row order of K fed to the S^T MFMA: swap bits 2 and 3 of the 5-bit row index.
 // After the MFMA, register i of lane (half h) holds key 16*(i/8) + 8*h + i%8 of
@@ -46,35 +56,64 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // which is the B-operand layout of two 16-key steps of the P V MFMA.
 __device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// 16-byte chunk swizzle of a K row: rows read together by 8 lanes (0..3, 8..11 or
-// 4..7, 12..15 of each 16) get distinct chunks.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
+template <int D, int TK>
+struct TileGeom {
+    static constexpr int KS = D / 16;               // 16-deep k-steps of S^T
+    static constexpr int MT = TK / 32;              // 32-key tiles
+    static constexpr int MD = D / 32;               // 32-wide d tiles of O^T
+    static constexpr int KBLK = MT * KS;            // 1 KiB K blocks per tile
+    static constexpr int VBLK = MT * 2 * 2 * MD;    // 512 B V blocks per tile
+    static constexpr int BYTES = TK * D * 2;        // one K (or V) tile
+    static_assert(KBLK * 1024 == BYTES, "K layout covers the tile");
+    static_assert(VBLK * 512 == BYTES, "V layout covers the tile");
+};
 
-// 16-byte chunk swizzle of a V^T row (one head-dim index d): consecutive d and
-// d 8 apart (the write pattern) get distinct chunks.
-template <int TK>
-__device__ __forceinline__ int swz_v(int d) {
-    return (d ^ (d >> 3)) & (TK / 8 - 1);
-}
+// Per-lane global element offsets (relative to the tile's first key) of the DMA
+// instructions a wave issues for one tile.
+template <int D, int WAVES, int TK>
+struct DmaPlan {
+    typedef TileGeom<D, TK> G;
+    static constexpr int NK = G::KBLK / WAVES;      // K DMA instructions per wave
+    static constexpr int NV = G::VBLK / 2 / WAVES;  // V DMA instructions (2 blocks each)
+    static_assert(G::KBLK % WAVES == 0 && (G::VBLK / 2) % WAVES == 0, "even DMA split");
+    int koff[NK];
+    int voff[NV];
 
-template <int D, int WAVES, int TK, int STAGES>
-__global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(FwdArgs a) {
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int blk = wave + i * WAVES;  // = mt*KS + ks
+            const int mt = blk / G::KS, ks = blk % G::KS;
+            const int row = 32 * mt + kperm(lane & 31);
+            koff[i] = row * D + 16 * ks + 8 * (lane >> 5);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            // one DMA instruction fills V blocks 2j (lanes 0..31) and 2j+1 (32..63);
+            // block index tb = ((mt*2 + e)*2 + r)*MD + md, md even for 2j.
+            const int j = wave + i * WAVES;
+            const int tb = 2 * j + (lane >> 5);
+            const int md = tb % G::MD, r = (tb / G::MD) % 2, e = (tb / G::MD / 2) % 2,
+                      mt = tb / G::MD / 4;
+            const int u = 2 * (lane & 31);  // first of the two 8-byte units of this lane
+            const int L = u & 15, g = (u >> 4) & 1, h = u >> 5;
+            const int row = 32 * mt + 16 * e + 8 * h + 4 * r + (L >> 2);
+            voff[i] = row * D + 32 * md + 16 * g + 4 * (L & 3);
+        }
+    }
+};
+
+template <int D, int WAVES, int TK, int OCC>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_bf16_kernel(FwdArgs a) {
+    typedef TileGeom<D, TK> G;
+    typedef DmaPlan<D, WAVES, TK> P;
     constexpr int TQ = 32 * WAVES;
-    constexpr int NT = 64 * WAVES;
-    constexpr int KS = D / 16;   // 16-deep k-steps of the S^T MFMA
-    constexpr int MT = TK / 32;  // 32-key tiles of S^T
-    constexpr int MD = D / 32;   // 32-wide d tiles of O^T
-    constexpr int KROW = D * 2;  // bytes of one K row in LDS
-    constexpr int VROW = TK * 2; // bytes of one V^T row in LDS
-    constexpr int KTILE = TK * KROW;
-    constexpr int VTILE = D * VROW;
-    constexpr int KCH = TK * D / 8;  // 16-byte chunks in a K tile
-    constexpr int KCH_T = KCH / NT;
-    static_assert(KCH % NT == 0, "K tile must split evenly over the workgroup");
-    constexpr int VGRP = (TK / 4) * (D / 8);  // (4 keys x 8 d) groups of a V tile
-    constexpr int VGRP_T = (VGRP + NT - 1) / NT;
+    constexpr int KS = G::KS, MT = G::MT, MD = G::MD;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * (KTILE + VTILE)];
+    __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t v1s[G::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -108,8 +147,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(FwdArgs a) {
         }
     }
 
-    u32x4 kreg[KCH_T];
-    u32x4 vreg[VGRP_T][4];
+    P plan;
+    plan.init(wave, lane);
 
     auto step_key0 = [&](int t) -> int {
         const int blk_i = t / tpb;
@@ -117,140 +156,99 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(FwdArgs a) {
         return kj * a.block_k + (t - blk_i * tpb) * TK;
     };
 
-    // HBM -> VGPR: K rows as 16-byte chunks; V as 4 keys x 8 d per group.
-    auto load_step = [&](int key0) {
+    // HBM -> LDS DMA of step t's K and V tiles into one stage.
+    auto issue = [&](int t, uint8_t* ks_, uint8_t* vs_) {
+        const int key0 = step_key0(t);
         const uint16_t* kt = kg + (size_t)key0 * D;
-#pragma unroll
-        for (int i = 0; i < KCH_T; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            kreg[i] = *(const u32x4*)(kt + row * D + cc * 8);
-        }
         const uint16_t* vt = vg + (size_t)key0 * D;
 #pragma unroll
-        for (int i = 0; i < VGRP_T; ++i) {
-            const int g = tid + i * NT;
-            if (VGRP % NT == 0 || g < VGRP) {
-                const int dc = g % (D / 8), kq = g / (D / 8);
+        for (int i = 0; i < P::NK; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(kt + plan.koff[i]),
+                                             (BSATTN_LDS void*)(ks_ + (wave + i * WAVES) * 1024),
+                                             16, 0, 0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    vreg[i][u] = *(const u32x4*)(vt + (size_t)(4 * kq + u) * D + dc * 8);
-            }
-        }
+        for (int i = 0; i < P::NV; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(vt + plan.voff[i]),
+                                             (BSATTN_LDS void*)(vs_ + (wave + i * WAVES) * 1024),
+                                             16, 0, 0);
     };
 
-    // VGPR -> LDS buffer st: K as is (swizzled), V transposed to [d][key].
-    auto store_step = [&](int st) {
-        uint8_t* ks_ = smem + st * (KTILE + VTILE);
-        uint8_t* vs_ = ks_ + KTILE;
-#pragma unroll
-        for (int i = 0; i < KCH_T; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            *(u32x4*)(ks_ + row * KROW + ((cc ^ swz_k(row)) << 4)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VGRP_T; ++i) {
-            const int g = tid + i * NT;
-            if (VGRP % NT == 0 || g < VGRP) {
-                const int dc = g % (D / 8), kq = g / (D / 8);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int w = j >> 1;
-                    uint32_t e0, e1, e2, e3;
-                    if (j & 1) {
-                        e0 = vreg[i][0][w] >> 16; e1 = vreg[i][1][w] >> 16;
-                        e2 = vreg[i][2][w] >> 16; e3 = vreg[i][3][w] >> 16;
-                    } else {
-                        e0 = vreg[i][0][w] & 0xffffu; e1 = vreg[i][1][w] & 0xffffu;
-                        e2 = vreg[i][2][w] & 0xffffu; e3 = vreg[i][3][w] & 0xffffu;
-                    }
-                    const int d = 8 * dc + j;
-                    u32x2 pk;
-                    pk[0] = e0 | (e1 << 16);
-                    pk[1] = e2 | (e3 << 16);
-                    *(u32x2*)(vs_ + d * VROW + (((kq >> 1) ^ swz_v<TK>(d)) << 4) + ((kq & 1) << 3)) = pk;
-                }
-            }
-        }
-    };
-
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    float m_run = -INFINITY;  // reference max (base-2, scaled units)
+    float l_run = 0.f;        // this lane's partial row sum
     f32x16 oacc[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
 
-    if (n_steps > 0) {
-        load_step(step_key0(0));
-        store_step(0);
-        __syncthreads();
-        for (int t = 0; t < n_steps; ++t) {
-            const int st = (STAGES == 2) ? (t & 1) : 0;
-            const bool more = t + 1 < n_steps;
-            if (more) load_step(step_key0(t + 1));
-            const uint8_t* ks_ = smem + st * (KTILE + VTILE);
-            const uint8_t* vs_ = ks_ + KTILE;
-
-            // S^T = K Q^T
-            f32x16 sacc[MT];
+    auto compute = [&](const uint8_t* ks_, const uint8_t* vs_) {
+        // S^T = K Q^T
+        f32x16 sacc[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+        for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int row = 32 * mt + kperm(l32);
-                    const bf16x8 kf =
-                        *(const bf16x8*)(ks_ + row * KROW + (((2 * ks + h) ^ swz_k(row)) << 4));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-                }
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 kf = *(const bf16x8*)(ks_ + (mt * KS + ks) * 1024 + lane * 16);
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
             }
 
-            // online softmax (base 2)
-            float mx = sacc[0][0];
+        // online softmax with a lazily moved reference max
+        float mx = sacc[0][0];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[mt][i]);
-            mx = __builtin_fmaxf(mx, xor32(mx));
-            const float m_new = __builtin_fmaxf(m_run, mx * a.c);
+            for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[mt][i]);
+        mx = __builtin_fmaxf(mx, xor32(mx)) * a.c;
+        if (__ballot(mx > m_run + 8.0f) != 0) {
+            const float m_new = __builtin_fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);
-            float psum = 0.f;
-            bf16x8 pb[MT][2];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_new));
-                    psum += p;
-                    pb[mt][i >> 3][i & 7] = (__bf16)p;
-                }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
             for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+            m_run = m_new;
+        }
+        bf16x8 pb[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_run));
+                l_run += p;
+                pb[mt][i >> 3][i & 7] = (__bf16)p;
+            }
 
-            // O^T += V^T P^T
+        // O^T += V^T P^T
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int e = 0; e < 2; ++e)
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
-                    for (int md = 0; md < MD; ++md) {
-                        const int d = 32 * md + l32;
-                        const bf16x8 vf = *(const bf16x8*)(vs_ + d * VROW +
-                                                           (((4 * mt + 2 * e + h) ^ swz_v<TK>(d)) << 4));
-                        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mt][e], oacc[md], 0, 0, 0);
-                    }
+                for (int md = 0; md < MD; ++md) {
+                    const uint8_t* vb = vs_ + (((mt * 2 + e) * 2) * MD + md) * 512 + lane * 8;
+                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb));
+                    const bf16x4 v1 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb + MD * 512));
+                    const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mt][e], oacc[md], 0, 0, 0);
+                }
+    };
 
-            if (STAGES == 2) {
-                if (more) store_step(st ^ 1);
+    // Two-stage pipeline over distinct LDS arrays (unrolled by two so each body
+    // names its arrays statically).  Before computing step t: wait for this
+    // wave's DMA of step t, barrier (all waves' DMA landed and all waves are done
+    // with step t-1), then start step t+1's DMA into the array step t-1 used.
+    if (n_steps > 0) {
+        issue(0, k0s, v0s);
+        for (int t = 0; t < n_steps; t += 2) {
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+            __syncthreads();
+            if (t + 1 < n_steps) issue(t + 1, k1s, v1s);
+            compute(k0s, v0s);
+            if (t + 1 < n_steps) {
+                __builtin_amdgcn_s_waitcnt(0x3f70);
                 __syncthreads();
-            } else {
-                __syncthreads();
-                if (more) store_step(0);
-                __syncthreads();
+                if (t + 2 < n_steps) issue(t + 2, k0s, v0s);
+                compute(k1s, v1s);
             }
         }
     }
@@ -265,7 +263,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int d0 = 32 * md + 8 * g4 + 4 * h;
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
             bf16x4 o;
 #pragma unroll
             for (int u = 0; u < 4; ++u) o[u] = (__bf16)(oacc[md][4 * g4 + u] * inv);
@@ -274,26 +271,21 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(FwdArgs a) {
     if (h == 0) a.lse[(size_t)bh * a.S + q_row] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, int W, int TK, int ST>
+template <int D, int W, int TK, int OCC>
 static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, ST>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-#define BSATTN_BF16_VARIANT(D, W, TK, ST) {1, D, 32 * W, TK, W, ST, &launch_bf16<D, W, TK, ST>}
+#define BSATTN_BF16_VARIANT(D, W, TK) {1, D, 32 * W, TK, W, 2, &launch_bf16<D, W, TK, 2>}
 
 static const Variant kBf16Variants[] = {
-    BSATTN_BF16_VARIANT(128, 4, 64, 2),  BSATTN_BF16_VARIANT(128, 4, 32, 2),
-    BSATTN_BF16_VARIANT(128, 4, 128, 2), BSATTN_BF16_VARIANT(128, 4, 64, 1),
-    BSATTN_BF16_VARIANT(128, 4, 32, 1),  BSATTN_BF16_VARIANT(128, 4, 128, 1),
-    BSATTN_BF16_VARIANT(128, 2, 64, 2),  BSATTN_BF16_VARIANT(128, 2, 32, 2),
-    BSATTN_BF16_VARIANT(128, 2, 64, 1),  BSATTN_BF16_VARIANT(128, 2, 32, 1),
-    BSATTN_BF16_VARIANT(64, 4, 64, 2),   BSATTN_BF16_VARIANT(64, 4, 32, 2),
-    BSATTN_BF16_VARIANT(64, 4, 128, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1),
-    BSATTN_BF16_VARIANT(64, 4, 32, 1),   BSATTN_BF16_VARIANT(64, 4, 128, 1),
-    BSATTN_BF16_VARIANT(64, 2, 64, 2),   BSATTN_BF16_VARIANT(64, 2, 32, 2),
-    BSATTN_BF16_VARIANT(64, 2, 128, 2),  BSATTN_BF16_VARIANT(64, 2, 64, 1),
-    BSATTN_BF16_VARIANT(64, 2, 32, 1),   BSATTN_BF16_VARIANT(64, 2, 128, 1),
+    BSATTN_BF16_VARIANT(128, 4, 64), BSATTN_BF16_VARIANT(128, 4, 32),
+    BSATTN_BF16_VARIANT(128, 4, 128), BSATTN_BF16_VARIANT(128, 2, 64),
+    BSATTN_BF16_VARIANT(128, 2, 32), BSATTN_BF16_VARIANT(128, 2, 128),
+    BSATTN_BF16_VARIANT(64, 4, 64), BSATTN_BF16_VARIANT(64, 4, 128),
+    BSATTN_BF16_VARIANT(64, 2, 64), BSATTN_BF16_VARIANT(64, 2, 32),
+    BSATTN_BF16_VARIANT(64, 2, 128),
 };
 
 const Variant* bf16_variants(int* n) {

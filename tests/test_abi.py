@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments with the documented status before any device
+work.  Pointers here are fake addresses: every call below must fail a host-side
+check, so none of them is ever dereferenced or reaches a kernel."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_flash_mask_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, SCALE, ALIAS, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bs.LIB_PATH):
+        from block_sparse_flash_mask_amd import build
+        build.build()
+    return bs.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsattn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in bs.STATUS.items():
+        s = lib.bsattn_status_string(code).decode()
+        assert s.startswith(name), (code, s)
+    assert lib.bsattn_status_string(99).decode().startswith("BSATTN")
+
+
+def test_version(lib):
+    assert bs.version() >= (0, 1, 0)
+
+
+def test_workspace_sizes(lib):
+    # counts (R int32) + lists (R*n_k int32), each rounded up to 256 bytes
+    R, nk = 4 * 16 * 16, 16
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert bs.workspace_size(4, 16, 2048, 128, 128) == rnd(R * 4) + rnd(R * nk * 4)
+    assert bs.compact_workspace_size(1, 2, 3, 5) == rnd(6 * 4) + rnd(30 * 4)
+    n = ctypes.c_size_t()
+    assert lib.bsattn_workspace_size(1, 1, 100, 64, 64, ctypes.byref(n)) == SHAPE
+    assert lib.bsattn_workspace_size(0, 1, 128, 64, 64, ctypes.byref(n)) == SHAPE
+    assert lib.bsattn_workspace_size(1, 1, 128, 64, 64, None) == NULL
+    assert lib.bsattn_compact_workspace_size(1, 1, 1 << 16, 1 << 16, ctypes.byref(n)) == SHAPE
+
+
+def test_list_configs(lib):
+    import torch
+    c = bs.list_configs(torch.bfloat16, 128, 128, 128)
+    assert c and all(t.tile_q in (64, 128) and t.tile_k in (32, 64, 128) for t in c)
+    assert all(t.waves * 32 == t.tile_q and t.stages in (1, 2) for t in c)
+    assert all(t.tile_q <= 64 for t in bs.list_configs(torch.bfloat16, 64, 64, 128))
+    assert all(t.tile_k <= 64 for t in bs.list_configs(torch.float32, 64, 64, 64))
+    n = ctypes.c_int()
+    assert lib.bsattn_list_configs(7, 64, 64, 64, None, 0, ctypes.byref(n)) == UNSUP
+
+
+A = 1 << 20  # fake, 16-byte-aligned, far-apart device addresses
+
+
+def _fwd(lib, q=1 * A, k=3 * A, v=5 * A, mask=7 * A, out=9 * A, lse=11 * A, B=1, H=1, S=256,
+         D=64, bq=64, bk=64, scale=0.125, dtype=1, ws=13 * A, wsb=1 << 20, cfg=None):
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    c = ctypes.byref(bs.TileConfig(*cfg)) if cfg else None
+    return lib.bsattn_fwd_config(p(q), p(k), p(v), p(mask), p(out), p(lse), B, H, S, D, bq, bk,
+                                 scale, dtype, p(ws), wsb, c, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(mask=0), NULL),
+    (dict(out=0), NULL), (dict(lse=0), NULL),
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(S=250), SHAPE), (dict(S=0), SHAPE),
+    (dict(D=96), UNSUP), (dict(D=256), UNSUP), (dict(dtype=5), UNSUP), (dict(bq=32, S=256), UNSUP),
+    (dict(bk=256), UNSUP),
+    (dict(q=A + 8), ALIGN), (dict(out=9 * A + 4), ALIGN), (dict(lse=11 * A + 2), ALIGN),
+    (dict(scale=math.nan), SCALE), (dict(scale=math.inf), SCALE), (dict(scale=-math.inf), SCALE),
+    (dict(out=1 * A + 1024), ALIAS), (dict(lse=5 * A + 64), ALIAS), (dict(lse=9 * A), ALIAS),
+    (dict(ws=0), WS), (dict(wsb=16), WS),
+    (dict(cfg=(256, 64, 8, 2)), UNSUP), (dict(cfg=(128, 64, 4, 2), bq=64), UNSUP),
+    (dict(cfg=(64, 48, 2, 1)), UNSUP),
+])
+def test_fwd_argument_checks(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def test_env_config_parse_error(lib, monkeypatch):
+    monkeypatch.setenv("BSATTN_CONFIG", "not-a-config")
+    assert _fwd(lib) == UNSUP
+    monkeypatch.setenv("BSATTN_CONFIG", "256,64,8,2")
+    assert _fwd(lib) == UNSUP
+
+
+def test_compact_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.bsattn_compact_mask
+    assert f(None, 1, 1, 4, 4, p(A), p(2 * A), p(3 * A), 1 << 20, None) == NULL
+    assert f(p(A), 0, 1, 4, 4, p(2 * A), p(3 * A), p(4 * A), 1 << 20, None) == SHAPE
+    assert f(p(A), 1, 1, 4, 4, p(2 * A), p(3 * A), p(4 * A), 8, None) == WS
+    assert f(p(A), 1, 1, 4, 4, p(2 * A + 2), p(3 * A), p(4 * A), 1 << 20, None) == ALIGN
+
+
+def test_compacted_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.bsattn_fwd_compacted
+    args = [p(A), p(3 * A), p(5 * A), p(7 * A), p(8 * A), p(9 * A), p(11 * A), 1, 1, 256, 64,
+            64, 64, 0.1, 1, None, None]
+    bad = list(args)
+    bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(args)
+    bad[9] = 100
+    assert f(*bad) == SHAPE
+
+
+def test_autotune_argument_checks(lib):
+    p = ctypes.c_void_p
+    best = bs.TileConfig()
+    n = ctypes.c_int()
+    f = lib.bsattn_autotune
+    base = [p(A), p(3 * A), p(5 * A), p(7 * A), p(9 * A), p(11 * A), 1, 1, 256, 64, 64, 64, 0.1,
+            1, p(13 * A), 1 << 20, 1, 1, ctypes.byref(best), None, 0, ctypes.byref(n), None, None]
+    bad = list(base)
+    bad[18] = None
+    assert f(*bad) == NULL
+    bad = list(base)
+    bad[17] = 0  # iters
+    assert f(*bad) == SHAPE
+    bad = list(base)
+    bad[15] = 4
+    assert f(*bad) == WS
+
+
+def test_tune_cache_roundtrip(lib, tmp_path):
+    path = tmp_path / "tune.json"
+    path.write_text('{"bsattn_tune_cache": 1, "entries": [\n'
+                    '  {"dtype": 1, "D": 128, "block_q": 128, "block_k": 128, "S": 2048, '
+                    '"BH": 64, "tile_q": 128, "tile_k": 32, "waves": 4, "stages": 1, '
+                    '"t_mean_s": 1.0e-04}\n]}\n')
+    assert lib.bsattn_load_tune_cache(str(path).encode()) == OK
+    assert lib.bsattn_load_tune_cache(str(tmp_path / "missing.json").encode()) == NULL
+    lib.bsattn_clear_tune_cache()
