@@ -251,6 +251,8 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
     a.block_q = block_q;
     a.block_k = block_k;
     a.sub_per_row = block_q / var.tile_q;
+    a.steps_log2 = 0;
+    while ((var.tile_k << a.steps_log2) < block_k) ++a.steps_log2;
     const bool neg = std::signbit(scale) && scale != 0.0f;
     a.c = std::fabs(scale) * kLog2e;
     a.qsign = neg ? 0x80008000u : 0u;

@@ -128,8 +128,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     const int qi = r - bh * a.n_q;
     int beg, cnt;
     row_list(a, r, beg, cnt);
-    const int tpb = a.block_k / TK;  // kernel steps per key block
-    const int n_steps = cnt * tpb;
+    const int sh = a.steps_log2;  // kernel steps per key block = 1 << sh
+    const int n_steps = cnt << sh;
     const int q_row = qi * a.block_q + sub * TQ + wave * 32 + l32;
     const size_t head = (size_t)bh * a.S * D;
     const uint16_t* __restrict__ kg = (const uint16_t*)a.k + head;
@@ -150,15 +150,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     P plan;
     plan.init(wave, lane);
 
-    auto step_key0 = [&](int t) -> int {
-        const int blk_i = t / tpb;
-        const int kj = list_entry(a, beg + blk_i);
-        return kj * a.block_k + (t - blk_i * tpb) * TK;
+    // List entries are fetched one step before they are needed, so the DMA issue
+    // never waits on a global load: `pre` holds the entry of the next issue.
+    auto entry_ptr = [&](int t) -> const int32_t* {
+        const int i = t >> sh;
+        return a.list + beg + (i < cnt ? i : cnt - 1);
     };
+    int pre = cnt > 0 ? *entry_ptr(0) : 0;
 
-    // HBM -> LDS DMA of step t's K and V tiles into one stage.
+    // HBM -> LDS DMA of step t's K and V tiles into one stage; prefetch the list
+    // entry of step t+1.
     auto issue = [&](int t, uint8_t* ks_, uint8_t* vs_) {
-        const int key0 = step_key0(t);
+        int kj = wave_uniform(pre);
+        kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
+        const int key0 = kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
+        pre = *entry_ptr(t + 1);
         const uint16_t* kt = kg + (size_t)key0 * D;
         const uint16_t* vt = vg + (size_t)key0 * D;
 #pragma unroll
@@ -193,12 +199,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             }
 
         // online softmax with a lazily moved reference max
-        float mx = sacc[0][0];
+        float tmp[16 * MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[mt][i]);
-        mx = __builtin_fmaxf(mx, xor32(mx)) * a.c;
+            for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = sacc[mt][i];
+        const float mx = max_halves(tree_max<16 * MT>(tmp)) * a.c;
         if (__ballot(mx > m_run + 8.0f) != 0) {
             const float m_new = __builtin_fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);
@@ -213,9 +219,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_run));
-                l_run += p;
+                tmp[16 * mt + i] = p;
                 pb[mt][i >> 3][i & 7] = (__bf16)p;
             }
+        l_run += tree_sum<16 * MT>(tmp);
 
         // O^T += V^T P^T
 #pragma unroll
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     }
 
     // Epilogue: O / l in bf16 (round to nearest even), lse = ln2 * (m + log2 l).
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = sum_halves(l_run);
     const bool any = n_steps > 0;
     const float inv = any ? 1.0f / l_tot : 0.0f;
     uint16_t* og = (uint16_t*)a.out + head + (size_t)q_row * D;

@@ -32,6 +32,7 @@ struct FwdArgs {
     int H, S, n_q, n_k;
     int block_q, block_k;
     int sub_per_row;   // block_q / tile_q: workgroups per mask row
+    int steps_log2;    // log2(block_k / tile_k): kernel steps per key block
     float c;           // |scale| * log2(e)
     uint32_t qsign;    // 0x80008000 flips the sign of two packed bf16 (scale < 0)
     uint32_t qsign32;  // 0x80000000 flips an fp32 sign (scale < 0)
@@ -41,6 +42,36 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(x[lane], x[lane ^ 32]) and x[lane] + x[lane ^ 32] with one v_permlane32_swap:
+// it returns (own, partner) in the low half-wave and (partner, own) in the high one.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Pairwise (tree) max / sum of N register values: log2(N) dependent levels
+// instead of a serial chain.
+template <int N>
+__device__ __forceinline__ float tree_max(float* v) {
+#pragma unroll
+    for (int w = N / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = __builtin_fmaxf(v[i], v[i + w]);
+    return v[0];
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(float* v) {
+#pragma unroll
+    for (int w = N / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+    return v[0];
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
