@@ -45,6 +45,16 @@ size_t compact_ws_bytes(int64_t R, int64_t n_k) {
     return align_up((size_t)R * 4) + align_up((size_t)(R * n_k) * 4);
 }
 
+// Slots per XCD for nwg workgroups.
+int64_t xcd_chunk(int64_t nwg) { return (nwg + 7) / 8; }
+
+// Forward workspace: the compaction workspace, then the dispatch order for up to
+// block_q / 64 workgroups per mask row.
+size_t fwd_ws_bytes(int64_t R, int64_t n_k, int block_q) {
+    const int64_t nwg_max = R * (block_q / 64 > 0 ? block_q / 64 : 1);
+    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(nwg_max)) * 4);
+}
+
 int check_grid(int B, int H, int n_q, int n_k) {
     if (B <= 0 || H <= 0 || n_q <= 0 || n_k <= 0) return BSATTN_ERR_SHAPE;
     const int64_t R = (int64_t)B * H * n_q;
@@ -260,9 +270,9 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
     return a;
 }
 
-int run_attention(const FwdArgs& a, const Variant& var, int64_t R, hipStream_t stream) {
-    const int64_t grid = R * a.sub_per_row;
-    if (grid <= 0 || grid >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+int run_attention(const FwdArgs& a, const Variant& var, hipStream_t stream) {
+    const int64_t grid = 8 * (int64_t)a.chunk;
+    if (a.nwg <= 0 || grid >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
     const hipError_t e = var.launch(a, (unsigned)grid, stream);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
@@ -331,7 +341,7 @@ int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t*
     if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
     const int rc = check_grid(B, H, S / block_q, S / block_k);
     if (rc) return rc;
-    *bytes = compact_ws_bytes((int64_t)B * H * (S / block_q), S / block_k);
+    *bytes = fwd_ws_bytes((int64_t)B * H * (S / block_q), S / block_k, block_q);
     return BSATTN_OK;
 }
 
@@ -344,7 +354,7 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
     if (rc) return rc;
     const int n_q = S / block_q, n_k = S / block_k;
     const int64_t R = (int64_t)B * H * n_q;
-    if (!workspace || workspace_bytes < compact_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < fwd_ws_bytes(R, n_k, block_q)) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
     const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
     if (!var) return BSATTN_ERR_UNSUPPORTED;
@@ -352,14 +362,22 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
     hipStream_t s = (hipStream_t)stream;
     int32_t* counts = (int32_t*)workspace;
     int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
-    const hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
+    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
     if (e != hipSuccess) return hip_fail(e);
 
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
     a.counts = counts;
     a.list = lists;
     a.ell_stride = n_k;
-    return run_attention(a, *var, R, s);
+    a.nwg = (int)(R * a.sub_per_row);
+    a.chunk = (int)xcd_chunk(a.nwg);
+    if (a.chunk <= kMaxOrderChunk) {
+        e = launch_compact_order(counts, a.nwg, a.sub_per_row, a.chunk, order, s);
+        if (e != hipSuccess) return hip_fail(e);
+        a.order = order;
+    }
+    return run_attention(a, *var, s);
 }
 
 int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
@@ -384,7 +402,9 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
     a.row_ptr = row_ptr;
     a.list = col_idx;
     a.ell_stride = 0;
-    return run_attention(a, *var, R, (hipStream_t)stream);
+    a.nwg = (int)(R * a.sub_per_row);
+    a.chunk = (int)xcd_chunk(a.nwg);
+    return run_attention(a, *var, (hipStream_t)stream);
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
@@ -413,7 +433,8 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
     const int64_t R = (int64_t)B * H * (S / block_q);
-    if (!workspace || workspace_bytes < compact_ws_bytes(R, S / block_k)) return BSATTN_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k, block_q))
+        return BSATTN_ERR_WORKSPACE;
     if (warmup < 0 || iters < 1) return BSATTN_ERR_SHAPE;
 
     int nv = 0;

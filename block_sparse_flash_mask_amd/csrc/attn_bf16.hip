@@ -121,7 +121,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    const int wg = blockIdx.x;
+    const int wg = block_work(a);
+    if (wg < 0) return;
     const int r = wg / a.sub_per_row;
     const int sub = wg - r * a.sub_per_row;
     const int bh = r / a.n_q;

@@ -31,6 +31,11 @@ struct FwdArgs {
     float* lse;
     int H, S, n_q, n_k;
     int block_q, block_k;
+    // Dispatch: blockIdx b runs slot (b % 8) * chunk + b / 8 of `order` (or the
+    // slot itself when order is NULL); slots >= nwg or marked -1 do nothing.
+    const int32_t* order;
+    int nwg;           // workgroups with work: (mask rows) * sub_per_row
+    int chunk;         // slots per XCD
     int sub_per_row;   // block_q / tile_q: workgroups per mask row
     int steps_log2;    // log2(block_k / tile_k): kernel steps per key block
     float c;           // |scale| * log2(e)
@@ -80,6 +85,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int list_entry(const FwdArgs& a, int i) {
     const int kj = wave_uniform(a.list[i]);
     return kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
+}
+
+// The workgroup index this block runs, or -1 (uniform across the block).
+__device__ __forceinline__ int block_work(const FwdArgs& a) {
+    const int b = blockIdx.x;
+    const int slot = (b & 7) * a.chunk + (b >> 3);
+    int w = slot < 8 * a.chunk ? (a.order ? a.order[slot] : slot) : -1;
+    if (w >= a.nwg) w = -1;
+    return wave_uniform(w);
 }
 
 // Resolve the key-block list of mask row r (wave-uniform results).

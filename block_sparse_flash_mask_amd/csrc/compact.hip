@@ -106,6 +106,46 @@ __global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ c
     for (int i = lane; i < cnt; i += kWave) dst[i] = src[i];
 }
 
+// Dispatch order of the attention workgroups.  Workgroups go to the 8 XCDs of
+// the chip round-robin by blockIdx, so blockIdx b runs on XCD b % 8 and is the
+// (b / 8)-th workgroup that XCD receives.  Workgroup indices w = r*sub + s
+// (mask row r, sub-tile s) are cut into 8 contiguous chunks of `chunk`, one per
+// XCD, so neighbouring query tiles of a head share that XCD's L2.  Inside a
+// chunk the order is longest first (count of active key blocks, descending; ties
+// by w) so the longest rows start first and the chunk finishes evenly.
+// order[x*chunk + k] = w, or -1 for padding slots.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxChunk = 4096;
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
+                                                              int64_t nwg, int sub, int chunk,
+                                                              int32_t* __restrict__ order) {
+    __shared__ int c[kOrderMaxChunk];
+    const int x = blockIdx.x;
+    const int64_t w0 = (int64_t)x * chunk;
+    const int g = (int)(w0 >= nwg ? 0 : (nwg - w0 < chunk ? nwg - w0 : chunk));
+    for (int i = threadIdx.x; i < g; i += kOrderThreads) c[i] = counts[(w0 + i) / sub];
+    for (int i = g + threadIdx.x; i < chunk; i += kOrderThreads) order[w0 + i] = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < g; i += kOrderThreads) {
+        const int ci = c[i];
+        int pos = 0;
+        for (int j = 0; j < g; ++j) {
+            const int cj = c[j];
+            pos += (cj > ci) | ((cj == ci) & (j < i));
+        }
+        order[w0 + pos] = (int32_t)(w0 + i);
+    }
+}
+
+hipError_t launch_compact_order(const int32_t* counts, int64_t nwg, int sub, int chunk,
+                                int32_t* order, hipStream_t stream) {
+    if (chunk > kOrderMaxChunk) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, nwg, sub,
+                       chunk, order);
+    return hipGetLastError();
+}
+
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t* counts,
                                int32_t* lists, hipStream_t stream) {
     const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;

@@ -50,10 +50,13 @@ def test_version(lib):
 
 
 def test_workspace_sizes(lib):
-    # counts (R int32) + lists (R*n_k int32), each rounded up to 256 bytes
+    # counts (R int32) + lists (R*n_k int32) + dispatch order (8 slots per XCD chunk of
+    # up to block_q/64 workgroups per mask row), each rounded up to 256 bytes
     R, nk = 4 * 16 * 16, 16
     rnd = lambda x: (x + 255) // 256 * 256
-    assert bs.workspace_size(4, 16, 2048, 128, 128) == rnd(R * 4) + rnd(R * nk * 4)
+    nwg_max = R * 2
+    order = 8 * ((nwg_max + 7) // 8) * 4
+    assert bs.workspace_size(4, 16, 2048, 128, 128) == rnd(R * 4) + rnd(R * nk * 4) + rnd(order)
     assert bs.compact_workspace_size(1, 2, 3, 5) == rnd(6 * 4) + rnd(30 * 4)
     n = ctypes.c_size_t()
     assert lib.bsattn_workspace_size(1, 1, 100, 64, 64, ctypes.byref(n)) == SHAPE
