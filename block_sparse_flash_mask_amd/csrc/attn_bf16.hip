@@ -41,6 +41,12 @@
 // compile-time offset.  Two stages live in distinct LDS arrays: the next step's
 // DMA is issued into the other array right after the per-step barrier and
 // overlaps the current step's MFMAs.
+#include <type_traits>
+
+#ifndef BSATTN_SCHED_GROUPS
+#define BSATTN_SCHED_GROUPS 0
+#endif
+
 #include "common.h"
 #include "kernels.h"
 
@@ -68,52 +74,58 @@ struct TileGeom {
     static_assert(VBLK * 512 == BYTES, "V layout covers the tile");
 };
 
-// Per-lane global element offsets (relative to the tile's first key) of the DMA
-// instructions a wave issues for one tile.
+// Global element offsets (relative to the tile's first key) of the DMA
+// instructions a wave issues for one tile: a per-lane part shared by all of the
+// wave's K (or V) instructions plus a wave-uniform part per instruction, so the
+// address is a scalar base plus one 32-bit VGPR offset.
 template <int D, int WAVES, int TK>
 struct DmaPlan {
     typedef TileGeom<D, TK> G;
     static constexpr int NK = G::KBLK / WAVES;      // K DMA instructions per wave
     static constexpr int NV = G::VBLK / 2 / WAVES;  // V DMA instructions (2 blocks each)
     static_assert(G::KBLK % WAVES == 0 && (G::VBLK / 2) % WAVES == 0, "even DMA split");
-    int koff[NK];
-    int voff[NV];
+    static_assert(G::MD % 2 == 0, "V blocks pair along d");
+    int k_lane;  // kperm(l%32) * D + 8 * (l/32)
+    int v_lane;  // see v_uniform
 
-    __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int blk = wave + i * WAVES;  // = mt*KS + ks
-            const int mt = blk / G::KS, ks = blk % G::KS;
-            const int row = 32 * mt + kperm(lane & 31);
-            koff[i] = row * D + 16 * ks + 8 * (lane >> 5);
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            // one DMA instruction fills V blocks 2j (lanes 0..31) and 2j+1 (32..63);
-            // block index tb = ((mt*2 + e)*2 + r)*MD + md, md even for 2j.
-            const int j = wave + i * WAVES;
-            const int tb = 2 * j + (lane >> 5);
-            const int md = tb % G::MD, r = (tb / G::MD) % 2, e = (tb / G::MD / 2) % 2,
-                      mt = tb / G::MD / 4;
-            const int u = 2 * (lane & 31);  // first of the two 8-byte units of this lane
-            const int L = u & 15, g = (u >> 4) & 1, h = u >> 5;
-            const int row = 32 * mt + 16 * e + 8 * h + 4 * r + (L >> 2);
-            voff[i] = row * D + 32 * md + 16 * g + 4 * (L & 3);
-        }
+    __device__ __forceinline__ void init(int lane) {
+        k_lane = kperm(lane & 31) * D + 8 * (lane >> 5);
+        // One V DMA instruction fills blocks 2j (lanes 0..31) and 2j+1 (32..63),
+        // block index tb = ((mt*2 + e)*2 + r)*MD + md; lane l writes the 8-byte
+        // units u = 2(l%32), u+1 of its block, which hold
+        // V[32mt + 16e + 8(u/32) + 4r + (u%16)/4][32md + 16((u/16)%2) + 4(u%4) ..].
+        const int u = 2 * (lane & 31);
+        const int L = u & 15, g = (u >> 4) & 1, hh = u >> 5;
+        v_lane = (8 * hh + (L >> 2)) * D + 32 * (lane >> 5) + 16 * g + 4 * (L & 3);
+    }
+    // K instruction i of wave w: block blk = w + i*WAVES = mt*KS + ks.
+    __device__ __forceinline__ static int k_uniform(int w, int i) {
+        const int blk = w + i * WAVES;
+        return 32 * (blk / G::KS) * D + 16 * (blk % G::KS);
+    }
+    // V instruction i of wave w: block pair j = w + i*WAVES, first block tb = 2j.
+    __device__ __forceinline__ static int v_uniform(int w, int i) {
+        const int tb = 2 * (w + i * WAVES);
+        const int md = tb % G::MD, r = (tb / G::MD) % 2, e = (tb / G::MD / 2) % 2,
+                  mt = tb / G::MD / 4;
+        return (32 * mt + 16 * e + 4 * r) * D + 32 * md;
     }
 };
 
-template <int D, int WAVES, int TK, int OCC>
+template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_bf16_kernel(FwdArgs a) {
     typedef TileGeom<D, TK> G;
     typedef DmaPlan<D, WAVES, TK> P;
-    constexpr int TQ = 32 * WAVES;
+    constexpr int TQ = 32 * NQ * WAVES;  // query rows per workgroup
     constexpr int KS = G::KS, MT = G::MT, MD = G::MD;
 
+    static_assert(ST == 2 || (ST == 3 && !PIPE), "three stages use the plain schedule");
     __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t v0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t k1s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t v1s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k2s[ST > 2 ? G::BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t v2s[ST > 2 ? G::BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -131,169 +143,326 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     row_list(a, r, beg, cnt);
     const int sh = a.steps_log2;  // kernel steps per key block = 1 << sh
     const int n_steps = cnt << sh;
-    const int q_row = qi * a.block_q + sub * TQ + wave * 32 + l32;
+    // This lane's query row in each of the wave's NQ 32-row tiles.
+    const int q_row0 = qi * a.block_q + sub * TQ + wave * 32 * NQ + l32;
     const size_t head = (size_t)bh * a.S * D;
     const uint16_t* __restrict__ kg = (const uint16_t*)a.k + head;
     const uint16_t* __restrict__ vg = (const uint16_t*)a.v + head;
 
     // Q^T fragments: lane (h, q) holds Q[q][16*ks + 8*h .. +7] for every ks.
-    bf16x8 qf[KS];
-    {
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)q_row * D);
+    bf16x8 qf[NQ][KS];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)(q_row0 + 32 * n) * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 t = qp[2 * ks + h];
             t ^= a.qsign;
-            qf[ks] = __builtin_bit_cast(bf16x8, t);
+            qf[n][ks] = __builtin_bit_cast(bf16x8, t);
         }
     }
 
     P plan;
-    plan.init(wave, lane);
+    plan.init(lane);
+    const int wave_s = wave_uniform(wave);
 
-    // List entries are fetched one step before they are needed, so the DMA issue
-    // never waits on a global load: `pre` holds the entry of the next issue.
-    auto entry_ptr = [&](int t) -> const int32_t* {
+    // Key-block list entries are fetched ahead of use so a DMA issue never waits
+    // on a global load.
+    auto entry = [&](int t) -> int {
         const int i = t >> sh;
-        return a.list + beg + (i < cnt ? i : cnt - 1);
+        return a.list[beg + (i < cnt ? i : cnt - 1)];
     };
-    int pre = cnt > 0 ? *entry_ptr(0) : 0;
-
-    // HBM -> LDS DMA of step t's K and V tiles into one stage; prefetch the list
-    // entry of step t+1.
-    auto issue = [&](int t, uint8_t* ks_, uint8_t* vs_) {
-        int kj = wave_uniform(pre);
+    auto key0_of = [&](int kj_raw, int t) -> int {
+        int kj = wave_uniform(kj_raw);
         kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
-        const int key0 = kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
-        pre = *entry_ptr(t + 1);
+        return kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
+    };
+
+    // HBM -> LDS DMA of one K tile or one V tile (keys key0 .. key0+TK-1).
+    auto issue_k = [&](int key0, uint8_t* kbuf) {
         const uint16_t* kt = kg + (size_t)key0 * D;
-        const uint16_t* vt = vg + (size_t)key0 * D;
 #pragma unroll
         for (int i = 0; i < P::NK; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(kt + plan.koff[i]),
-                                             (BSATTN_LDS void*)(ks_ + (wave + i * WAVES) * 1024),
+            __builtin_amdgcn_global_load_lds((const void*)(kt + P::k_uniform(wave_s, i) + plan.k_lane),
+                                             (BSATTN_LDS void*)(kbuf + (wave_s + i * WAVES) * 1024),
                                              16, 0, 0);
+    };
+    auto issue_v = [&](int key0, uint8_t* vbuf) {
+        const uint16_t* vt = vg + (size_t)key0 * D;
 #pragma unroll
         for (int i = 0; i < P::NV; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(vt + plan.voff[i]),
-                                             (BSATTN_LDS void*)(vs_ + (wave + i * WAVES) * 1024),
+            __builtin_amdgcn_global_load_lds((const void*)(vt + P::v_uniform(wave_s, i) + plan.v_lane),
+                                             (BSATTN_LDS void*)(vbuf + (wave_s + i * WAVES) * 1024),
                                              16, 0, 0);
     };
 
-    float m_run = -INFINITY;  // reference max (base-2, scaled units)
-    float l_run = 0.f;        // this lane's partial row sum
-    f32x16 oacc[MD];
+    float m_run[NQ];  // reference max per query tile (base-2, scaled units)
+    float l_run[NQ];  // this lane's partial row sums
+    f32x16 oacc[NQ][MD];
 #pragma unroll
-    for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+    for (int n = 0; n < NQ; ++n) {
+        m_run[n] = -INFINITY;
+        l_run[n] = 0.f;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) oacc[n][md] = f32x16{};
+    }
 
-    auto compute = [&](const uint8_t* ks_, const uint8_t* vs_) {
-        // S^T = K Q^T
-        f32x16 sacc[MT];
+    // VALU instructions placed between consecutive S MFMAs of the next tile: the
+    // softmax costs ~3.5 VALU instructions per score element (fma, exp, half a
+    // cvt, the sum tree), 16 elements per lane per 32-key tile and query tile,
+    // spread over the NQ*KS MFMAs of that tile.
+    constexpr int SCHED_VALU = 56 / KS;
+    struct SAcc { f32x16 v[NQ][MT]; };
+    struct PTile { bf16x8 v[NQ][MT][2]; };
+
+    // S^T = K Q^T for the K tile in kbuf; each K fragment read from LDS feeds the
+    // NQ query tiles.
+    auto qk = [&](const uint8_t* kbuf) -> SAcc {
+        SAcc s;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+        for (int n = 0; n < NQ; ++n)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) s.v[n][mt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 kf = *(const bf16x8*)(ks_ + (mt * KS + ks) * 1024 + lane * 16);
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+                const bf16x8 kf = *(const bf16x8*)(kbuf + (mt * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+                for (int n = 0; n < NQ; ++n)
+                    s.v[n][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[n][ks], s.v[n][mt], 0, 0, 0);
             }
+        return s;
+    };
 
-        // online softmax with a lazily moved reference max
-        float tmp[16 * MT];
+    // Row max of S and the lazy move of the reference max (rescaling O and l).
+    auto update_max = [&](const SAcc& s) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int n = 0; n < NQ; ++n) {
+            float tmp[16 * MT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = sacc[mt][i];
-        const float mx = max_halves(tree_max<16 * MT>(tmp)) * a.c;
-        if (__ballot(mx > m_run + 8.0f) != 0) {
-            const float m_new = __builtin_fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
-            l_run *= alpha;
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
-            m_run = m_new;
+                for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = s.v[n][mt][i];
+            const float mx = max_halves(tree_max<16 * MT>(tmp)) * a.c;
+            if (__ballot(mx > m_run[n] + 8.0f) != 0) {
+                const float m_new = __builtin_fmaxf(m_run[n], mx);
+                const float alpha = fast_exp2(m_run[n] - m_new);
+                l_run[n] *= alpha;
+#pragma unroll
+                for (int md = 0; md < MD; ++md) oacc[n][md] *= alpha;
+                m_run[n] = m_new;
+            }
         }
-        bf16x8 pb[MT][2];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_run));
-                tmp[16 * mt + i] = p;
-                pb[mt][i >> 3][i & 7] = (__bf16)p;
-            }
-        l_run += tree_sum<16 * MT>(tmp);
+    };
 
-        // O^T += V^T P^T
+    // P = 2^(c S - m) in bf16, and its row sums into l.
+    auto exps = [&](const SAcc& s) -> PTile {
+        PTile p;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            float tmp[16 * MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_run[n]));
+                    tmp[16 * mt + i] = e;
+                    p.v[n][mt][i >> 3][i & 7] = (__bf16)e;
+                }
+            l_run[n] += tree_sum<16 * MT>(tmp);
+        }
+        return p;
+    };
+
+    // O^T += V^T P^T for the V tile in vbuf; each V fragment feeds NQ MFMAs.
+    auto pv = [&](const PTile& p, const uint8_t* vbuf) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int md = 0; md < MD; ++md) {
-                    const uint8_t* vb = vs_ + (((mt * 2 + e) * 2) * MD + md) * 512 + lane * 8;
+                    const uint8_t* vb = vbuf + (((mt * 2 + e) * 2) * MD + md) * 512 + lane * 8;
                     const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb));
                     const bf16x4 v1 =
                         __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb + MD * 512));
                     const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mt][e], oacc[md], 0, 0, 0);
+#pragma unroll
+                    for (int n = 0; n < NQ; ++n)
+                        oacc[n][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p.v[n][mt][e], oacc[n][md], 0, 0, 0);
                 }
     };
 
-    // Two-stage pipeline over distinct LDS arrays (unrolled by two so each body
-    // names its arrays statically).  Before computing step t: wait for this
-    // wave's DMA of step t, barrier (all waves' DMA landed and all waves are done
-    // with step t-1), then start step t+1's DMA into the array step t-1 used.
-    if (n_steps > 0) {
-        issue(0, k0s, v0s);
-        for (int t = 0; t < n_steps; t += 2) {
-            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-            __syncthreads();
-            if (t + 1 < n_steps) issue(t + 1, k1s, v1s);
-            compute(k0s, v0s);
-            if (t + 1 < n_steps) {
-                __builtin_amdgcn_s_waitcnt(0x3f70);
-                __syncthreads();
-                if (t + 2 < n_steps) issue(t + 2, k0s, v0s);
-                compute(k1s, v1s);
+    // Software pipeline.  K runs one step ahead of V: step t's body computes the
+    // softmax of S(t) on the VALU while the matrix cores compute S(t+1) = K(t+1)
+    // Q^T, then O += P(t) V(t).  Step s's K tile lives in k{s%2}s and its V tile
+    // in v{s%2}s (distinct LDS arrays, named statically by unrolling by two).  At
+    // the top of step t: wait for this wave's DMA (K(t+1), V(t), issued one step
+    // earlier), barrier (everyone's DMA landed; everyone finished reading K(t)
+    // and V(t-1)), then start the DMA of K(t+2) and V(t+1) into those buffers.
+    auto body = [&](auto has_next, int t, int& kv_next, int& pre, SAcc& s, uint8_t* kfree,
+                    uint8_t* vfree, const uint8_t* knext, const uint8_t* vcur) {
+        constexpr bool NEXT = decltype(has_next)::value;
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+        __syncthreads();
+        const int k2 = key0_of(pre, t + 2);
+        pre = entry(t + 3);
+        if (t + 2 < n_steps) issue_k(k2, kfree);
+        if (t + 1 < n_steps) issue_v(kv_next, vfree);
+        kv_next = k2;
+        update_max(s);
+        SAcc s_next;
+        if constexpr (NEXT) s_next = qk(knext);
+        const PTile p = exps(s);
+        pv(p, vcur);
+        if constexpr (NEXT) {
+            s = s_next;
+#if BSATTN_SCHED_GROUPS
+            // Interleave the next tile's S MFMAs with this tile's exponentials
+            // (independent work), then the P V MFMAs with their V reads.
+#pragma unroll
+            for (int i = 0; i < KS * MT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);             // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, NQ * SCHED_VALU, 0);  // VALU
             }
+#pragma unroll
+            for (int i = 0; i < 2 * MT * MD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
+            }
+#endif
+        }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // Plain schedule: K and V of step t share a stage, ST stages in flight.  The
+    // body of step t waits until only the DMA of later steps is outstanding,
+    // barriers (everyone's step-t data landed; everyone is done with step t-1's
+    // stage), then loads the list entry two issues ahead and starts the DMA of
+    // step t+ST-1 into the stage step t-1 used, then runs S, softmax, P V.
+    // vmcnt counts in issue order: list-entry load, then the step's DMA, so
+    // waiting for "at most NDMA outstanding" (ST = 3) retires step t's DMA and
+    // the entry load issued before step t+1's DMA.
+    constexpr int NDMA = P::NK + P::NV;
+    auto plain = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur,
+                     const uint8_t* vcur) {
+        if (ST == 3 && t + 1 < n_steps)
+            __builtin_amdgcn_s_waitcnt(0x3f70 | (NDMA & 15) | ((NDMA >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+        __syncthreads();
+        if (t + ST - 1 < n_steps) {
+            const int kn = key0_of(pre, t + ST - 1);
+            pre = entry(t + ST);
+            issue_k(kn, kfill);
+            issue_v(kn, vfill);
+        }
+        const SAcc s = qk(kcur);
+        update_max(s);
+        const PTile p = exps(s);
+        pv(p, vcur);
+    };
+
+    if (n_steps > 0 && PIPE) {
+        const int k0 = key0_of(entry(0), 0);
+        const int k1 = key0_of(entry(1), 1);
+        int pre = entry(2);
+        issue_k(k0, k0s);
+        issue_v(k0, v0s);
+        if (n_steps > 1) issue_k(k1, k1s);
+        int kv_next = k1;
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        __syncthreads();
+        SAcc s = qk(k0s);
+        int t = 0;
+        for (; t + 2 < n_steps; t += 2) {
+            body(yes{}, t, kv_next, pre, s, k0s, v1s, k1s, v0s);
+            body(yes{}, t + 1, kv_next, pre, s, k1s, v0s, k0s, v1s);
+        }
+        if (t + 1 < n_steps) {
+            body(yes{}, t, kv_next, pre, s, k0s, v1s, k1s, v0s);
+            body(no{}, t + 1, kv_next, pre, s, k1s, v0s, k0s, v1s);
+        } else {
+            body(no{}, t, kv_next, pre, s, k0s, v1s, k1s, v0s);
+        }
+    } else if (n_steps > 0 && ST == 2) {
+        const int k0 = key0_of(entry(0), 0);
+        int pre = entry(1);
+        issue_k(k0, k0s);
+        issue_v(k0, v0s);
+        for (int t = 0; t < n_steps; t += 2) {
+            plain(t, pre, k1s, v1s, k0s, v0s);
+            if (t + 1 < n_steps) plain(t + 1, pre, k0s, v0s, k1s, v1s);
+        }
+    } else if (n_steps > 0) {
+        const int k0 = key0_of(entry(0), 0);
+        const int k1 = key0_of(entry(1), 1);
+        int pre = entry(2);
+        issue_k(k0, k0s);
+        issue_v(k0, v0s);
+        if (n_steps > 1) {
+            issue_k(k1, k1s);
+            issue_v(k1, v1s);
+        }
+        for (int t = 0; t < n_steps; t += 3) {
+            plain(t, pre, k2s, v2s, k0s, v0s);
+            if (t + 1 < n_steps) plain(t + 1, pre, k0s, v0s, k1s, v1s);
+            if (t + 2 < n_steps) plain(t + 2, pre, k1s, v1s, k2s, v2s);
         }
     }
 
     // Epilogue: O / l in bf16 (round to nearest even), lse = ln2 * (m + log2 l).
-    const float l_tot = sum_halves(l_run);
     const bool any = n_steps > 0;
-    const float inv = any ? 1.0f / l_tot : 0.0f;
-    uint16_t* og = (uint16_t*)a.out + head + (size_t)q_row * D;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+    for (int n = 0; n < NQ; ++n) {
+        const int q_row = q_row0 + 32 * n;
+        const float l_tot = sum_halves(l_run[n]);
+        const float inv = any ? 1.0f / l_tot : 0.0f;
+        uint16_t* og = (uint16_t*)a.out + head + (size_t)q_row * D;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * md + 8 * g4 + 4 * h;
-            bf16x4 o;
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[u] = (__bf16)(oacc[md][4 * g4 + u] * inv);
-            *(bf16x4*)(og + d0) = o;
-        }
-    if (h == 0) a.lse[(size_t)bh * a.S + q_row] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * md + 8 * g4 + 4 * h;
+                bf16x4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[u] = (__bf16)(oacc[n][md][4 * g4 + u] * inv);
+                *(bf16x4*)(og + d0) = o;
+            }
+        if (h == 0)
+            a.lse[(size_t)bh * a.S + q_row] = any ? (m_run[n] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
 }
 
-template <int D, int W, int TK, int OCC>
+template <int D, int W, int TK, int NQ, int PIPE, int ST, int OCC>
 static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, NQ, PIPE, ST, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-#define BSATTN_BF16_VARIANT(D, W, TK) {1, D, 32 * W, TK, W, 2, &launch_bf16<D, W, TK, 2>}
+// {dtype, D, tile_q, tile_k, waves, stages, launcher}.  The table order is the
+// built-in preference when no tuning result exists.  NQ = 2 (64 query rows per
+// wave, each K/V fragment read from LDS feeding two MFMAs) runs one wave per
+// SIMD; NQ = 1 runs two or three.  PIPE = 1 overlaps the next tile's S MFMAs
+// with this tile's softmax inside a wave (two stages); PIPE = 0 runs the steps
+// in order with ST K/V stages resident in LDS.
+#define BSATTN_BF16_VARIANT(D, W, TK, NQ, PIPE, ST, OCC) \
+    {1, D, 32 * NQ * W, TK, W, ST, &launch_bf16<D, W, TK, NQ, PIPE, ST, OCC>}
 
 static const Variant kBf16Variants[] = {
-    BSATTN_BF16_VARIANT(128, 4, 64), BSATTN_BF16_VARIANT(128, 4, 32),
-    BSATTN_BF16_VARIANT(128, 4, 128), BSATTN_BF16_VARIANT(128, 2, 64),
-    BSATTN_BF16_VARIANT(128, 2, 32), BSATTN_BF16_VARIANT(128, 2, 128),
-    BSATTN_BF16_VARIANT(64, 4, 64), BSATTN_BF16_VARIANT(64, 4, 128),
-    BSATTN_BF16_VARIANT(64, 2, 64), BSATTN_BF16_VARIANT(64, 2, 32),
-    BSATTN_BF16_VARIANT(64, 2, 128),
+    BSATTN_BF16_VARIANT(128, 4, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 4, 64, 1, 1, 2, 2),
+    BSATTN_BF16_VARIANT(128, 4, 32, 1, 1, 2, 2), BSATTN_BF16_VARIANT(128, 4, 64, 1, 0, 3, 1),
+    BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 2, 1), BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 3, 1),
+    BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 2, 64, 1, 1, 2, 2),
+    BSATTN_BF16_VARIANT(128, 1, 32, 2, 0, 3, 1),
+    BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 1, 2, 2),
+    BSATTN_BF16_VARIANT(64, 4, 32, 1, 1, 2, 2),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
+    BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),
+    BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 2, 32, 1, 1, 2, 2),
+    BSATTN_BF16_VARIANT(64, 1, 64, 2, 0, 2, 1),
 };
 
 const Variant* bf16_variants(int* n) {
