@@ -45,14 +45,18 @@ size_t compact_ws_bytes(int64_t R, int64_t n_k) {
     return align_up((size_t)R * 4) + align_up((size_t)(R * n_k) * 4);
 }
 
-// Slots per XCD for nwg workgroups.
-int64_t xcd_chunk(int64_t nwg) { return (nwg + 7) / 8; }
+// Slots per XCD for nwg workgroups (a multiple of sub, the workgroups per row).
+int64_t xcd_chunk(int64_t nwg, int sub = 1) {
+    const int64_t c = (nwg + 7) / 8;
+    return (c + sub - 1) / sub * sub;
+}
+
 
 // Forward workspace: the compaction workspace, then the dispatch order for up to
 // block_q / 64 workgroups per mask row.
 size_t fwd_ws_bytes(int64_t R, int64_t n_k, int block_q) {
     const int64_t nwg_max = R * (block_q / 64 > 0 ? block_q / 64 : 1);
-    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(nwg_max)) * 4);
+    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(nwg_max, 2)) * 4);
 }
 
 int check_grid(int B, int H, int n_q, int n_k) {
@@ -363,17 +367,17 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
     int32_t* counts = (int32_t*)workspace;
     int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
     int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
-    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
-    if (e != hipSuccess) return hip_fail(e);
 
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
     a.counts = counts;
     a.list = lists;
     a.ell_stride = n_k;
     a.nwg = (int)(R * a.sub_per_row);
-    a.chunk = (int)xcd_chunk(a.nwg);
-    if (a.chunk <= kMaxOrderChunk) {
-        e = launch_compact_order(counts, a.nwg, a.sub_per_row, a.chunk, order, s);
+    a.chunk = (int)xcd_chunk(a.nwg, a.sub_per_row);
+    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (a.chunk / a.sub_per_row <= kMaxOrderRows) {
+        e = launch_compact_order(counts, R, n_k, a.sub_per_row, a.chunk, order, s);
         if (e != hipSuccess) return hip_fail(e);
         a.order = order;
     }

@@ -108,41 +108,95 @@ __global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ c
 
 // Dispatch order of the attention workgroups.  Workgroups go to the 8 XCDs of
 // the chip round-robin by blockIdx, so blockIdx b runs on XCD b % 8 and is the
-// (b / 8)-th workgroup that XCD receives.  Workgroup indices w = r*sub + s
-// (mask row r, sub-tile s) are cut into 8 contiguous chunks of `chunk`, one per
-// XCD, so neighbouring query tiles of a head share that XCD's L2.  Inside a
-// chunk the order is longest first (count of active key blocks, descending; ties
-// by w) so the longest rows start first and the chunk finishes evenly.
-// order[x*chunk + k] = w, or -1 for padding slots.
+// (b / 8)-th workgroup that XCD receives.  Work units w = r*sub + s (mask row r,
+// sub-tile s) are cut into 8 contiguous chunks of `chunk` (a multiple of sub),
+// one per XCD, so neighbouring query tiles of a head share that XCD's L2.  Inside
+// a chunk the rows go longest first: a counting sort on the active-block count
+// (histogram in LDS, exclusive scan, scatter); units of one row stay adjacent.
+// Rows with equal counts land in arbitrary order, which cannot change any result
+// (each row is computed independently).  order[x*chunk + j] = w, or -1 for padding.
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderMaxChunk = 4096;
+constexpr int kOrderMaxBins = 4096;
+constexpr int kOrderMaxRowsPerThread = 4;  // chunk rows <= 4096
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
-                                                              int64_t nwg, int sub, int chunk,
-                                                              int32_t* __restrict__ order) {
-    __shared__ int c[kOrderMaxChunk];
-    const int x = blockIdx.x;
-    const int64_t w0 = (int64_t)x * chunk;
-    const int g = (int)(w0 >= nwg ? 0 : (nwg - w0 < chunk ? nwg - w0 : chunk));
-    for (int i = threadIdx.x; i < g; i += kOrderThreads) c[i] = counts[(w0 + i) / sub];
-    for (int i = g + threadIdx.x; i < chunk; i += kOrderThreads) order[w0 + i] = -1;
-    __syncthreads();
-    for (int i = threadIdx.x; i < g; i += kOrderThreads) {
-        const int ci = c[i];
-        int pos = 0;
-        for (int j = 0; j < g; ++j) {
-            const int cj = c[j];
-            pos += (cj > ci) | ((cj == ci) & (j < i));
-        }
-        order[w0 + pos] = (int32_t)(w0 + i);
+__device__ __forceinline__ int order_wave_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
+    return x;
 }
 
-hipError_t launch_compact_order(const int32_t* counts, int64_t nwg, int sub, int chunk,
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
+                                                              int64_t R, int sub, int chunk,
+                                                              int nbins,
+                                                              int32_t* __restrict__ order) {
+    __shared__ int hist[kOrderMaxBins];
+    __shared__ int wave_tot[kOrderThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int x = blockIdx.x;
+    const int64_t w0 = (int64_t)x * chunk;
+    const int64_t nwg = R * sub;
+    const int g = (int)(w0 >= nwg ? 0 : (nwg - w0 < chunk ? nwg - w0 : chunk));
+    const int64_t r0 = w0 / sub;
+    const int nr = g / sub;
+    for (int b = tid; b < nbins; b += kOrderThreads) hist[b] = 0;
+    __syncthreads();
+    // bin = (nbins - 1) - min(count, nbins - 1): ascending bin = descending count
+    int bin[kOrderMaxRowsPerThread];
+#pragma unroll
+    for (int j = 0; j < kOrderMaxRowsPerThread; ++j) {
+        const int k = tid + j * kOrderThreads;
+        bin[j] = -1;
+        if (k < nr) {
+            const int c = counts[r0 + k];
+            bin[j] = nbins - 1 - (c < nbins - 1 ? c : nbins - 1);
+            atomicAdd(&hist[bin[j]], 1);
+        }
+    }
+    __syncthreads();
+    // exclusive scan of hist: each thread owns a run of consecutive bins
+    const int per = (nbins + kOrderThreads - 1) / kOrderThreads;
+    const int b0 = tid * per;
+    int run = 0;
+    for (int b = b0; b < b0 + per && b < nbins; ++b) run += hist[b];
+    const int incl = order_wave_scan(run);
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int t = lane < kOrderThreads / kWave ? wave_tot[lane] : 0;
+        t = order_wave_scan(t);
+        if (lane < kOrderThreads / kWave) wave_tot[lane] = t;
+    }
+    __syncthreads();
+    int pre = (wave > 0 ? wave_tot[wave - 1] : 0) + incl - run;
+    for (int b = b0; b < b0 + per && b < nbins; ++b) {
+        const int h = hist[b];
+        hist[b] = pre;
+        pre += h;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kOrderMaxRowsPerThread; ++j) {
+        const int k = tid + j * kOrderThreads;
+        if (bin[j] >= 0) {
+            const int pos = atomicAdd(&hist[bin[j]], 1);
+            for (int s = 0; s < sub; ++s)
+                order[w0 + (int64_t)pos * sub + s] = (int32_t)(w0 + (int64_t)k * sub + s);
+        }
+    }
+    for (int i = g + tid; i < chunk; i += kOrderThreads) order[w0 + i] = -1;
+}
+
+hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_k, int sub, int chunk,
                                 int32_t* order, hipStream_t stream) {
-    if (chunk > kOrderMaxChunk) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, nwg, sub,
-                       chunk, order);
+    if (sub <= 0 || chunk % sub != 0 || chunk / sub > kOrderThreads * kOrderMaxRowsPerThread)
+        return hipErrorInvalidValue;
+    const int nbins = n_k + 1 < kOrderMaxBins ? n_k + 1 : kOrderMaxBins;
+    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, sub, chunk,
+                       nbins, order);
     return hipGetLastError();
 }
 

@@ -58,10 +58,11 @@ typedef enum {
 /* Kernel tiling of the attention kernel (the autotuner's search space).
  *   tile_q  query rows per workgroup: 64 or 128, must divide block_q;
  *   tile_k  keys per inner step: 32, 64 or 128, must divide block_k;
- *   waves   wavefronts per workgroup (64 lanes each); with 32 query rows per
- *           wave this is tile_q / 32;
- *   stages  K/V tiles resident in LDS: 1 (load, barrier, compute) or 2 (the
- *           next tile is written while the current one is consumed).
+ *   waves   wavefronts per workgroup (64 lanes each); a wave owns 32 or 64
+ *           query rows, so waves is tile_q / 32 or tile_q / 64;
+ *   stages  K/V tiles resident in LDS: 1 (load, barrier, compute), 2 or 3
+ *           (later tiles are written while the current one is consumed).
+ * bsattn_list_configs gives the combinations that are built.
  * A zero field means "choose automatically".  The kernel tiling never changes
  * the result beyond fp32 rounding order: block_q and block_k (the mask
  * granularity) do. */

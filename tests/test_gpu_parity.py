@@ -139,3 +139,4 @@ def test_deterministic():
     o2, l2 = bs.fwd(qd, kd, vd, md, 128, 128, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
