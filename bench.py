@@ -1,9 +1,11 @@
 """Benchmark of the block-sparse flash-attention forward on one MI355X.
 
-One step = one bsattn_fwd call (mask compaction + fused attention kernel) over the
-workload's resident inputs.  Prints ONE JSON line on stdout:
+One step = one bsattn_fwd call (the plan: mask compaction and dispatch order, then
+the fused attention kernel) over the workload's resident inputs.  Prints ONE JSON
+line on stdout:
   value      effective TFLOP/s = 4*D*(active score elements) / (time per step)
-  roofline   the attention kernel alone: its average duration over K launches
+  roofline   the attention kernel alone (bsattn_fwd_planned: the step's launch on
+             a plan made once): its average duration over K launches
              timed with HIP events on the stream it runs on, achieved TFLOP/s
              against the bf16 dense MFMA peak, and (when a counter summary for
              the current kernel source exists under profiles/) HBM traffic
@@ -165,18 +167,19 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log("bench: %.4f ms/step (events), %.4f ms/step (wall)" % (ms_step, wall * 1e3 / args.steps))
 
-    # The dominant kernel alone: attention on a precomputed compaction, K launches
-    # bracketed by HIP events on the launch stream.
-    rp, ci = bs.compact_mask(md)
+    # The dominant kernel alone: the attention launch of the step (same plan, same
+    # tile config, same grid) on a plan made once, K launches bracketed by HIP
+    # events on the launch stream.
+    plan_ws = bs.plan(md, w.S, w.block_q, w.block_k)
     for _ in range(3):
-        bs.fwd_compacted(qd, kd, vd, rp, ci, w.block_q, w.block_k, w.scale, out=out, lse=lse,
-                         config=cfg)
+        bs.fwd_planned(qd, kd, vd, plan_ws, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                       config=cfg)
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(stream)
     for _ in range(args.steps):
-        bs.fwd_compacted(qd, kd, vd, rp, ci, w.block_q, w.block_k, w.scale, out=out, lse=lse,
-                         config=cfg)
+        bs.fwd_planned(qd, kd, vd, plan_ws, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                       config=cfg)
     a1.record(stream)
     torch.cuda.synchronize()
     ms_attn = a0.elapsed_time(a1) / args.steps

@@ -78,6 +78,9 @@ def library():
         "bsattn_fwd": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz, p], i32),
         "bsattn_fwd_config": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
                                cfgp, p], i32),
+        "bsattn_plan": ([p, i32, i32, i32, i32, i32, p, sz, p], i32),
+        "bsattn_fwd_planned": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
+                                cfgp, p], i32),
         "bsattn_fwd_compacted": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
                                   cfgp, p], i32),
         "bsattn_list_configs": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
@@ -201,6 +204,42 @@ def fwd(q, k, v, block_mask, block_q, block_k, scale=None, *, out=None, lse=None
                                B, H, S, D, block_q, block_k, float(scale), _dtype_code(q),
                                _ptr(ws), ws.numel() * ws.element_size(), _cfg(config),
                                _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def plan(block_mask, S, block_q, block_k, *, workspace=None, stream=None):
+    """The mask-dependent step of fwd() on its own: per-row key-block lists and
+    the dispatch order, written into a workspace tensor (returned).  The plan
+    depends only on the mask and (B, H, S, block_q, block_k): one plan serves
+    every fwd_planned() call that shares the mask."""
+    block_mask = _mask_u8(block_mask)
+    if block_mask.dim() != 4:
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    B, H, n_q, n_k = block_mask.shape
+    if (n_q * block_q, n_k * block_k) != (S, S):
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    ws = _workspace(workspace_size(B, H, S, block_q, block_k), block_mask.device, workspace)
+    rc = library().bsattn_plan(_ptr(block_mask), B, H, S, block_q, block_k, _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return ws
+
+
+def fwd_planned(q, k, v, plan_ws, block_q, block_k, scale=None, *, out=None, lse=None,
+                config=None, stream=None):
+    """The attention kernel alone on a plan from plan(); returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    rc = library().bsattn_fwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S,
+                                      D, block_q, block_k, float(scale), _dtype_code(q),
+                                      _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(),
+                                      _cfg(config), _stream(stream))
     _check(rc)
     return out, lse
 

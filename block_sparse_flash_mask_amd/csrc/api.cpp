@@ -45,18 +45,13 @@ size_t compact_ws_bytes(int64_t R, int64_t n_k) {
     return align_up((size_t)R * 4) + align_up((size_t)(R * n_k) * 4);
 }
 
-// Slots per XCD for nwg workgroups (a multiple of sub, the workgroups per row).
-int64_t xcd_chunk(int64_t nwg, int sub = 1) {
-    const int64_t c = (nwg + 7) / 8;
-    return (c + sub - 1) / sub * sub;
-}
+// Mask rows per XCD chunk.
+int64_t xcd_chunk(int64_t R) { return (R + 7) / 8; }
 
-
-// Forward workspace: the compaction workspace, then the dispatch order for up to
-// block_q / 64 workgroups per mask row.
-size_t fwd_ws_bytes(int64_t R, int64_t n_k, int block_q) {
-    const int64_t nwg_max = R * (block_q / 64 > 0 ? block_q / 64 : 1);
-    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(nwg_max, 2)) * 4);
+// Forward workspace (the plan): the compaction workspace (per-row counts and
+// padded lists), then the dispatch order, 8 * xcd_chunk(R) row slots.
+size_t fwd_ws_bytes(int64_t R, int64_t n_k) {
+    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(R)) * 4);
 }
 
 int check_grid(int B, int H, int n_q, int n_k) {
@@ -101,6 +96,19 @@ int check_fwd_buffers(const void* q, const void* k, const void* v, const void* o
     if (overlap(out, nt, q, nt) || overlap(out, nt, k, nt) || overlap(out, nt, v, nt) ||
         overlap(lse, nl, q, nt) || overlap(lse, nl, k, nt) || overlap(lse, nl, v, nt) ||
         overlap(lse, nl, out, nt))
+        return BSATTN_ERR_ALIAS;
+    return BSATTN_OK;
+}
+
+// The plan region of a forward workspace (ws_used bytes) must not overlap q, k,
+// v, out or lse.  Run after check_fwd_buffers (sizes are valid then).
+int check_ws_alias(const void* ws, size_t ws_used, const void* q, const void* k, const void* v,
+                   const void* out, const float* lse, int B, int H, int S, int D, int dtype) {
+    const size_t esz = dtype == BSATTN_F32 ? 4 : 2;
+    const size_t nt = (size_t)B * H * S * D * esz;
+    const size_t nl = (size_t)B * H * S * 4;
+    if (overlap(ws, ws_used, q, nt) || overlap(ws, ws_used, k, nt) || overlap(ws, ws_used, v, nt) ||
+        overlap(ws, ws_used, out, nt) || overlap(ws, ws_used, lse, nl))
         return BSATTN_ERR_ALIAS;
     return BSATTN_OK;
 }
@@ -265,6 +273,8 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
     a.block_q = block_q;
     a.block_k = block_k;
     a.sub_per_row = block_q / var.tile_q;
+    a.sub_log2 = 0;
+    while ((1 << a.sub_log2) < a.sub_per_row) ++a.sub_log2;
     a.steps_log2 = 0;
     while ((var.tile_k << a.steps_log2) < block_k) ++a.steps_log2;
     const bool neg = std::signbit(scale) && scale != 0.0f;
@@ -275,8 +285,9 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
 }
 
 int run_attention(const FwdArgs& a, const Variant& var, hipStream_t stream) {
-    const int64_t grid = 8 * (int64_t)a.chunk;
-    if (a.nwg <= 0 || grid >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    const int64_t grid = 8 * (int64_t)a.chunk * a.sub_per_row;
+    if (a.nrows <= 0 || (1 << a.sub_log2) != a.sub_per_row || grid >= ((int64_t)1 << 31))
+        return BSATTN_ERR_SHAPE;
     const hipError_t e = var.launch(a, (unsigned)grid, stream);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
@@ -345,8 +356,56 @@ int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t*
     if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
     const int rc = check_grid(B, H, S / block_q, S / block_k);
     if (rc) return rc;
-    *bytes = fwd_ws_bytes((int64_t)B * H * (S / block_q), S / block_k, block_q);
+    *bytes = fwd_ws_bytes((int64_t)B * H * (S / block_q), S / block_k);
     return BSATTN_OK;
+}
+
+int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int block_k,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_mask || !workspace) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    if (!block_ok(block_q) || !block_ok(block_k)) return BSATTN_ERR_UNSUPPORTED;
+    const int n_q = S / block_q, n_k = S / block_k;
+    int rc = check_grid(B, H, n_q, n_k);
+    if (rc) return rc;
+    const int64_t R = (int64_t)B * H * n_q;
+    if (workspace_bytes < fwd_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* counts = (int32_t*)workspace;
+    int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
+    int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
+    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_compact_order(counts, R, n_k, xcd_chunk(R), order, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_fwd_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int H, int S, int D, int block_q, int block_k, float scale, int dtype,
+                       const void* workspace, size_t workspace_bytes,
+                       const bsattn_tile_config* cfg, void* stream) {
+    if (!workspace) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const int64_t R = (int64_t)B * H * n_q;
+    if (workspace_bytes < fwd_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
+    if (check_ws_alias(workspace, fwd_ws_bytes(R, n_k), q, k, v, out, lse, B, H, S, D, dtype))
+        return BSATTN_ERR_ALIAS;
+    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+    FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
+    a.counts = (const int32_t*)workspace;
+    a.list = (const int32_t*)((const char*)workspace + align_up((size_t)R * 4));
+    a.ell_stride = n_k;
+    a.order = (const int32_t*)((const char*)workspace + compact_ws_bytes(R, n_k));
+    a.nrows = (int)R;
+    a.chunk = (int)xcd_chunk(R);
+    return run_attention(a, *var, (hipStream_t)stream);
 }
 
 int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t* block_mask,
@@ -356,32 +415,19 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
     if (!block_mask) return BSATTN_ERR_NULL;
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
-    const int n_q = S / block_q, n_k = S / block_k;
-    const int64_t R = (int64_t)B * H * n_q;
-    if (!workspace || workspace_bytes < fwd_ws_bytes(R, n_k, block_q)) return BSATTN_ERR_WORKSPACE;
+    const int64_t R = (int64_t)B * H * (S / block_q);
+    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k)) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
-    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
-    if (!var) return BSATTN_ERR_UNSUPPORTED;
-
-    hipStream_t s = (hipStream_t)stream;
-    int32_t* counts = (int32_t*)workspace;
-    int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
-    int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
-
-    FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
-    a.counts = counts;
-    a.list = lists;
-    a.ell_stride = n_k;
-    a.nwg = (int)(R * a.sub_per_row);
-    a.chunk = (int)xcd_chunk(a.nwg, a.sub_per_row);
-    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
-    if (e != hipSuccess) return hip_fail(e);
-    if (a.chunk / a.sub_per_row <= kMaxOrderRows) {
-        e = launch_compact_order(counts, R, n_k, a.sub_per_row, a.chunk, order, s);
-        if (e != hipSuccess) return hip_fail(e);
-        a.order = order;
-    }
-    return run_attention(a, *var, s);
+    if (check_ws_alias(workspace, fwd_ws_bytes(R, S / block_k), q, k, v, out, lse, B, H, S, D,
+                       dtype))
+        return BSATTN_ERR_ALIAS;
+    // Resolve the tile config before any device work, so an unsupported one
+    // fails with nothing enqueued.
+    if (!choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg)) return BSATTN_ERR_UNSUPPORTED;
+    int st = bsattn_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return bsattn_fwd_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, dtype,
+                              workspace, workspace_bytes, cfg, stream);
 }
 
 int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
@@ -406,8 +452,8 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
     a.row_ptr = row_ptr;
     a.list = col_idx;
     a.ell_stride = 0;
-    a.nwg = (int)(R * a.sub_per_row);
-    a.chunk = (int)xcd_chunk(a.nwg);
+    a.nrows = (int)R;
+    a.chunk = (int)xcd_chunk(R);
     return run_attention(a, *var, (hipStream_t)stream);
 }
 
@@ -437,7 +483,7 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
     const int64_t R = (int64_t)B * H * (S / block_q);
-    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k, block_q))
+    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k))
         return BSATTN_ERR_WORKSPACE;
     if (warmup < 0 || iters < 1) return BSATTN_ERR_SHAPE;
 

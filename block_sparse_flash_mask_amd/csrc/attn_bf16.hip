@@ -133,10 +133,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    const int wg = block_work(a);
-    if (wg < 0) return;
-    const int r = wg / a.sub_per_row;
-    const int sub = wg - r * a.sub_per_row;
+    int r, sub;
+    block_work(a, r, sub);
+    if (r < 0) return;
     const int bh = r / a.n_q;
     const int qi = r - bh * a.n_q;
     int beg, cnt;

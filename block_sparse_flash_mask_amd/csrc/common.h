@@ -31,12 +31,17 @@ struct FwdArgs {
     float* lse;
     int H, S, n_q, n_k;
     int block_q, block_k;
-    // Dispatch: blockIdx b runs slot (b % 8) * chunk + b / 8 of `order` (or the
-    // slot itself when order is NULL); slots >= nwg or marked -1 do nothing.
+    // Dispatch.  Mask rows are cut into 8 chunks of `chunk` rows, one per XCD
+    // (blockIdx b runs on XCD b % 8).  Block b takes position j = b / 8 of its
+    // XCD's queue: row slot (b % 8) * chunk + j / sub_per_row, sub-tile
+    // j % sub_per_row, so the sub-tiles of one row run side by side.  A slot is a
+    // mask row itself, or order[slot] when order is not NULL; a row outside
+    // [0, nrows) does nothing.
     const int32_t* order;
-    int nwg;           // workgroups with work: (mask rows) * sub_per_row
-    int chunk;         // slots per XCD
-    int sub_per_row;   // block_q / tile_q: workgroups per mask row
+    int nrows;         // mask rows: B * H * n_q
+    int chunk;         // row slots per XCD
+    int sub_per_row;   // block_q / tile_q: workgroups per mask row (a power of 2)
+    int sub_log2;      // log2(sub_per_row)
     int steps_log2;    // log2(block_k / tile_k): kernel steps per key block
     float c;           // |scale| * log2(e)
     uint32_t qsign;    // 0x80008000 flips the sign of two packed bf16 (scale < 0)
@@ -87,13 +92,20 @@ __device__ __forceinline__ int list_entry(const FwdArgs& a, int i) {
     return kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
 }
 
-// The workgroup index this block runs, or -1 (uniform across the block).
-__device__ __forceinline__ int block_work(const FwdArgs& a) {
+// The mask row and sub-tile this block runs; row = -1 for a block with no work
+// (uniform across the block).
+__device__ __forceinline__ void block_work(const FwdArgs& a, int& row, int& sub) {
     const int b = blockIdx.x;
-    const int slot = (b & 7) * a.chunk + (b >> 3);
-    int w = slot < 8 * a.chunk ? (a.order ? a.order[slot] : slot) : -1;
-    if (w >= a.nwg) w = -1;
-    return wave_uniform(w);
+    const int j = b >> 3;
+    const int jr = j >> a.sub_log2;
+    int r = -1;
+    if (jr < a.chunk) {
+        const int slot = (b & 7) * a.chunk + jr;
+        r = a.order ? a.order[slot] : slot;
+    }
+    if (r < 0 || r >= a.nrows) r = -1;
+    row = wave_uniform(r);
+    sub = wave_uniform(j & (a.sub_per_row - 1));
 }
 
 // Resolve the key-block list of mask row r (wave-uniform results).
@@ -105,6 +117,8 @@ __device__ __forceinline__ void row_list(const FwdArgs& a, int r, int& beg, int&
         beg = a.row_ptr[r];
         cnt = a.row_ptr[r + 1] - beg;
     }
+    // A row lists each key block at most once: a larger count is malformed input.
+    cnt = cnt < 0 ? 0 : (cnt > a.n_k ? a.n_k : cnt);
     beg = wave_uniform(beg);
     cnt = wave_uniform(cnt);
 }

@@ -108,16 +108,15 @@ __global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ c
 
 // Dispatch order of the attention workgroups.  Workgroups go to the 8 XCDs of
 // the chip round-robin by blockIdx, so blockIdx b runs on XCD b % 8 and is the
-// (b / 8)-th workgroup that XCD receives.  Work units w = r*sub + s (mask row r,
-// sub-tile s) are cut into 8 contiguous chunks of `chunk` (a multiple of sub),
-// one per XCD, so neighbouring query tiles of a head share that XCD's L2.  Inside
-// a chunk the rows go longest first: a counting sort on the active-block count
-// (histogram in LDS, exclusive scan, scatter); units of one row stay adjacent.
-// Rows with equal counts land in arbitrary order, which cannot change any result
-// (each row is computed independently).  order[x*chunk + j] = w, or -1 for padding.
+// (b / 8)-th workgroup that XCD receives.  Mask rows are cut into 8 contiguous
+// chunks of `chunk` rows, one per XCD, so neighbouring query tiles of a head share
+// that XCD's L2; inside a chunk the rows go longest first.  One workgroup per
+// chunk runs a counting sort on the active-block count: a histogram in LDS, an
+// exclusive scan of it, then a scatter.  Rows with equal counts land in arbitrary
+// order, which cannot change any result (each row is computed on its own).
+// order[x * chunk + j] = mask row, or -1 for padding past the last row.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxBins = 4096;
-constexpr int kOrderMaxRowsPerThread = 4;  // chunk rows <= 4096
 
 __device__ __forceinline__ int order_wave_scan(int x) {
     const int lane = threadIdx.x & 63;
@@ -129,35 +128,27 @@ __device__ __forceinline__ int order_wave_scan(int x) {
     return x;
 }
 
+// Bin of a row with c active blocks: ascending bin = descending count.
+__device__ __forceinline__ int order_bin(int c, int nbins) {
+    c = c < 0 ? 0 : (c > nbins - 1 ? nbins - 1 : c);
+    return nbins - 1 - c;
+}
+
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
-                                                              int64_t R, int sub, int chunk,
+                                                              int64_t R, int64_t chunk,
                                                               int nbins,
                                                               int32_t* __restrict__ order) {
     __shared__ int hist[kOrderMaxBins];
     __shared__ int wave_tot[kOrderThreads / kWave];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int x = blockIdx.x;
-    const int64_t w0 = (int64_t)x * chunk;
-    const int64_t nwg = R * sub;
-    const int g = (int)(w0 >= nwg ? 0 : (nwg - w0 < chunk ? nwg - w0 : chunk));
-    const int64_t r0 = w0 / sub;
-    const int nr = g / sub;
+    const int64_t r0 = (int64_t)blockIdx.x * chunk;
+    const int64_t nr = r0 >= R ? 0 : (R - r0 < chunk ? R - r0 : chunk);
     for (int b = tid; b < nbins; b += kOrderThreads) hist[b] = 0;
     __syncthreads();
-    // bin = (nbins - 1) - min(count, nbins - 1): ascending bin = descending count
-    int bin[kOrderMaxRowsPerThread];
-#pragma unroll
-    for (int j = 0; j < kOrderMaxRowsPerThread; ++j) {
-        const int k = tid + j * kOrderThreads;
-        bin[j] = -1;
-        if (k < nr) {
-            const int c = counts[r0 + k];
-            bin[j] = nbins - 1 - (c < nbins - 1 ? c : nbins - 1);
-            atomicAdd(&hist[bin[j]], 1);
-        }
-    }
+    for (int64_t k = tid; k < nr; k += kOrderThreads)
+        atomicAdd(&hist[order_bin(counts[r0 + k], nbins)], 1);
     __syncthreads();
-    // exclusive scan of hist: each thread owns a run of consecutive bins
+    // Exclusive scan of hist: each thread owns a run of consecutive bins.
     const int per = (nbins + kOrderThreads - 1) / kOrderThreads;
     const int b0 = tid * per;
     int run = 0;
@@ -178,24 +169,18 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
         pre += h;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kOrderMaxRowsPerThread; ++j) {
-        const int k = tid + j * kOrderThreads;
-        if (bin[j] >= 0) {
-            const int pos = atomicAdd(&hist[bin[j]], 1);
-            for (int s = 0; s < sub; ++s)
-                order[w0 + (int64_t)pos * sub + s] = (int32_t)(w0 + (int64_t)k * sub + s);
-        }
+    for (int64_t k = tid; k < nr; k += kOrderThreads) {
+        const int pos = atomicAdd(&hist[order_bin(counts[r0 + k], nbins)], 1);
+        order[r0 + pos] = (int32_t)(r0 + k);
     }
-    for (int i = g + tid; i < chunk; i += kOrderThreads) order[w0 + i] = -1;
+    for (int64_t i = nr + tid; i < chunk; i += kOrderThreads) order[r0 + i] = -1;
 }
 
-hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_k, int sub, int chunk,
+hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_k, int64_t chunk,
                                 int32_t* order, hipStream_t stream) {
-    if (sub <= 0 || chunk % sub != 0 || chunk / sub > kOrderThreads * kOrderMaxRowsPerThread)
-        return hipErrorInvalidValue;
+    if (R <= 0 || chunk <= 0 || 8 * chunk < R) return hipErrorInvalidValue;
     const int nbins = n_k + 1 < kOrderMaxBins ? n_k + 1 : kOrderMaxBins;
-    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, sub, chunk,
+    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, chunk,
                        nbins, order);
     return hipGetLastError();
 }

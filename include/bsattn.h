@@ -16,8 +16,9 @@
  *
  * Conventions shared by every entry point.
  *  - Every array argument is a DEVICE pointer owned by the caller.  Nothing is
- *    allocated on the call path of bsattn_compact_mask, bsattn_fwd,
- *    bsattn_fwd_config or bsattn_fwd_compacted; the caller passes a workspace.
+ *    allocated on the call path of bsattn_compact_mask, bsattn_plan, bsattn_fwd,
+ *    bsattn_fwd_config, bsattn_fwd_planned or bsattn_fwd_compacted; the caller
+ *    passes a workspace.
  *  - Layouts: q, k, v, out are [B][H][S][D], contiguous, D fastest, all of one
  *    element type (fp32 or bf16 as IEEE bits); lse is float [B][H][S];
  *    block_mask is uint8 [B][H][S/block_q][S/block_k], any nonzero byte = active.
@@ -51,7 +52,8 @@ typedef enum {
     BSATTN_ERR_ALIGN = 4,       /* q/k/v/out not 16-byte or lse not 4-byte aligned */
     BSATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     BSATTN_ERR_SCALE = 6,       /* scale is NaN or infinite */
-    BSATTN_ERR_ALIAS = 7,       /* out or lse overlaps q, k or v (or each other) */
+    BSATTN_ERR_ALIAS = 7,       /* out or lse overlaps q, k or v (or each other), or
+                                   a forward workspace overlaps any of them */
     BSATTN_ERR_HIP = 8          /* a HIP runtime call failed */
 } bsattn_status;
 
@@ -110,7 +112,8 @@ int bsattn_compact_mask(const uint8_t* block_mask, int B, int H, int n_q, int n_
                         int32_t* row_ptr, int32_t* col_idx, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-/* Workspace bytes needed by bsattn_fwd / bsattn_fwd_config. */
+/* Workspace bytes needed by bsattn_fwd, bsattn_fwd_config, bsattn_plan and
+ * bsattn_fwd_planned (the same figure for all four). */
 int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes);
 
 /* The forward pass: mask compaction, then the fused attention kernel (S = scale
@@ -125,16 +128,54 @@ int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block
                void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* As bsattn_fwd with an explicit tile config (cfg == NULL or all-zero = auto). */
+/* As bsattn_fwd with an explicit tile config (cfg == NULL or all-zero = auto).
+ * It is exactly bsattn_plan followed by bsattn_fwd_planned on one workspace. */
 int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t* block_mask,
                       void* out, float* lse, int B, int H, int S, int D, int block_q,
                       int block_k, float scale, int dtype, void* workspace,
                       size_t workspace_bytes, const bsattn_tile_config* cfg, void* stream);
 
+/* The plan: the mask-dependent first step of bsattn_fwd, on its own.  Writes
+ * into workspace, for every mask row in (b, h, qi) row-major order, the number of
+ * active key blocks and their kj in ascending order (a list padded to n_k
+ * entries), then the order in which the attention kernel dispatches its
+ * workgroups: rows cut into 8 contiguous chunks (one per XCD of the chip), each
+ * chunk longest row first.  With R = B*H*(S/block_q), n_k = S/block_k and
+ * A(x) = x rounded up to a multiple of 256, the plan is three int32 arrays:
+ *   counts[R]              at byte 0;
+ *   lists[R][n_k]          at byte A(4R), row i's kj in lists[i][0 .. counts[i]);
+ *   order[8 * ceil(R/8)]   at byte A(4R) + A(4 R n_k): chunk x is
+ *                          order[x*ceil(R/8) ..], its rows by descending count,
+ *                          then -1 past the last row.
+ * The plan depends only on block_mask and (B, H, S,
+ * block_q, block_k), never on q/k/v, D, dtype, scale or the tile config, so one
+ * plan serves every call that shares the mask (the block mask is fixed ahead of
+ * the kernel: "Writing Pallas Kernels for JAX", section "Writing the Kernel
+ * Logic").  workspace_bytes >= bsattn_workspace_size(B, H, S, block_q, block_k);
+ * the workspace is owned by the caller and must stay alive and unmodified until
+ * the last bsattn_fwd_planned that reads it has completed on its stream. */
+int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int block_k,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The attention kernel alone, on a plan written by bsattn_plan for the same
+ * mask and shape (B, H, S, block_q, block_k); any tile config may run on any
+ * plan.  workspace is only read.  A workspace that holds no such plan gives
+ * undefined values in out and lse but no access outside q, k, v, out, lse and
+ * the workspace's first bsattn_workspace_size bytes (counts and entries are
+ * clamped to the shape).  Arguments and checks otherwise as bsattn_fwd_config,
+ * plus BSATTN_ERR_ALIAS when the plan region overlaps q, k, v, out or lse. */
+int bsattn_fwd_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int H, int S, int D, int block_q, int block_k, float scale, int dtype,
+                       const void* workspace, size_t workspace_bytes,
+                       const bsattn_tile_config* cfg, void* stream);
+
 /* The attention kernel alone, on lists already built by bsattn_compact_mask
  * (row_ptr, col_idx as that call wrote them, for the same mask).  This is the
- * second step of bsattn_fwd, exposed so callers can reuse one compaction across
- * calls and time the kernel by itself.  cfg as in bsattn_fwd_config. */
+ * attention step of bsattn_fwd reading CSR lists instead of a plan, for callers
+ * that keep the mask in CSR form; workgroups go in mask-row order (no
+ * longest-first dispatch).  row_ptr must be a valid CSR of B*H*(S/block_q) rows
+ * over col_idx: per-row counts are clamped to [0, S/block_k] and entries into
+ * [0, S/block_k), but row_ptr values are trusted.  cfg as in bsattn_fwd_config. */
 int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,
                          const int32_t* col_idx, void* out, float* lse, int B, int H, int S,
                          int D, int block_q, int block_k, float scale, int dtype,

@@ -50,13 +50,13 @@ def test_version(lib):
 
 
 def test_workspace_sizes(lib):
-    # counts (R int32) + lists (R*n_k int32) + dispatch order (8 slots per XCD chunk of
-    # up to block_q/64 workgroups per mask row), each rounded up to 256 bytes
-    R, nk = 4 * 16 * 16, 16
+    # counts (R int32) + lists (R*n_k int32) + dispatch order (8 chunks of ceil(R/8)
+    # mask rows, int32), each rounded up to 256 bytes
     rnd = lambda x: (x + 255) // 256 * 256
-    nwg_max = R * 2
-    order = 8 * ((nwg_max + 7) // 8) * 4
-    assert bs.workspace_size(4, 16, 2048, 128, 128) == rnd(R * 4) + rnd(R * nk * 4) + rnd(order)
+    for B, H, S, bq, bk in ((4, 16, 2048, 128, 128), (1, 3, 640, 64, 128), (1, 1, 64, 64, 64)):
+        R, nk = B * H * (S // bq), S // bk
+        order = 8 * ((R + 7) // 8) * 4
+        assert bs.workspace_size(B, H, S, bq, bk) == rnd(R * 4) + rnd(R * nk * 4) + rnd(order)
     assert bs.compact_workspace_size(1, 2, 3, 5) == rnd(6 * 4) + rnd(30 * 4)
     n = ctypes.c_size_t()
     assert lib.bsattn_workspace_size(1, 1, 100, 64, 64, ctypes.byref(n)) == SHAPE
@@ -96,7 +96,7 @@ def _fwd(lib, q=1 * A, k=3 * A, v=5 * A, mask=7 * A, out=9 * A, lse=11 * A, B=1,
     (dict(q=A + 8), ALIGN), (dict(out=9 * A + 4), ALIGN), (dict(lse=11 * A + 2), ALIGN),
     (dict(scale=math.nan), SCALE), (dict(scale=math.inf), SCALE), (dict(scale=-math.inf), SCALE),
     (dict(out=1 * A + 1024), ALIAS), (dict(lse=5 * A + 64), ALIAS), (dict(lse=9 * A), ALIAS),
-    (dict(ws=0), WS), (dict(wsb=16), WS),
+    (dict(ws=0), WS), (dict(wsb=16), WS), (dict(ws=9 * A + 256), ALIAS), (dict(ws=3 * A), ALIAS),
     (dict(cfg=(256, 64, 8, 2)), UNSUP), (dict(cfg=(128, 64, 4, 2), bq=64), UNSUP),
     (dict(cfg=(64, 48, 2, 1)), UNSUP),
 ])
@@ -118,6 +118,42 @@ def test_compact_argument_checks(lib):
     assert f(p(A), 0, 1, 4, 4, p(2 * A), p(3 * A), p(4 * A), 1 << 20, None) == SHAPE
     assert f(p(A), 1, 1, 4, 4, p(2 * A), p(3 * A), p(4 * A), 8, None) == WS
     assert f(p(A), 1, 1, 4, 4, p(2 * A + 2), p(3 * A), p(4 * A), 1 << 20, None) == ALIGN
+
+
+def test_plan_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.bsattn_plan
+    ok = [p(A), 1, 2, 512, 128, 64, p(3 * A), 1 << 20, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    assert call(0, None) == NULL and call(6, None) == NULL
+    assert call(1, 0) == SHAPE and call(3, 500) == SHAPE and call(3, -512) == SHAPE
+    assert call(4, 32) == UNSUP and call(5, 256) == UNSUP
+    assert call(7, 64) == WS
+    assert call(6, p(3 * A + 2)) == ALIGN
+
+
+def test_planned_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.bsattn_fwd_planned
+    ok = [p(A), p(3 * A), p(5 * A), p(9 * A), p(11 * A), 1, 1, 256, 64, 64, 64, 0.1, 1,
+          p(13 * A), 1 << 20, None, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    assert call(13, None) == NULL and call(0, None) == NULL and call(3, None) == NULL
+    assert call(7, 100) == SHAPE and call(8, 96) == UNSUP
+    assert call(14, 16) == WS
+    assert call(13, p(13 * A + 2)) == ALIGN
+    assert call(13, p(9 * A + 512)) == ALIAS and call(13, p(11 * A)) == ALIAS
+    assert call(3, p(1 * A)) == ALIAS
+    assert call(11, math.nan) == SCALE
+    assert call(15, ctypes.byref(bs.TileConfig(256, 64, 8, 2))) == UNSUP
 
 
 def test_compacted_argument_checks(lib):

@@ -55,3 +55,58 @@ def test_compact_nonbinary_bytes():
     m = torch.randint(0, 256, (1, 2, 6, 100), generator=g, dtype=torch.uint8)
     m[m < 128] = 0
     _check(m)
+
+
+def _rnd(x):
+    return (x + 255) // 256 * 256
+
+
+def _check_plan(mask, block_q=128, block_k=128):
+    """bsattn_plan's three arrays: counts and lists equal the oracle's compaction
+    bit for bit; each XCD chunk of the order holds exactly its own rows, by
+    non-increasing count, then -1 padding."""
+    ensure_built()
+    B, H, n_q, n_k = mask.shape
+    S = n_q * block_q
+    assert n_k * block_k == S
+    say("plan", tuple(mask.shape), int(mask.sum()))
+    ws = bs.plan(mask.cuda(), S, block_q, block_k)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy().view(np.int32)
+    R = B * H * n_q
+    counts = w[:R]
+    lists = w[_rnd(4 * R) // 4:][:R * n_k].reshape(R, n_k)
+    chunk = (R + 7) // 8
+    order = w[(_rnd(4 * R) + _rnd(4 * R * n_k)) // 4:][:8 * chunk]
+    orp, oci = oracle.compact(mask)
+    assert np.array_equal(counts, np.diff(orp))
+    for i in range(R):
+        assert np.array_equal(lists[i, :counts[i]], oci[orp[i]:orp[i + 1]]), i
+    for x in range(8):
+        r0, r1 = min(x * chunk, R), min((x + 1) * chunk, R)
+        got = order[x * chunk:(x + 1) * chunk]
+        nr = r1 - r0
+        assert np.array_equal(np.sort(got[:nr]), np.arange(r0, r1)), x
+        assert np.all(got[nr:] == -1), x
+        c = counts[got[:nr]]
+        assert np.all(c[:-1] >= c[1:]), x
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_plan_workloads(name):
+    w = W.WORKLOADS[name]
+    _check_plan(W.make_mask(w), w.block_q, w.block_k)
+
+
+@pytest.mark.parametrize("shape,p,seed", [
+    ((1, 1, 1, 1), 1.0, 0),        # one row: seven empty chunks
+    ((1, 1, 5, 5), 0.5, 1),        # fewer rows than XCDs
+    ((2, 3, 7, 7), 0.3, 2),        # R = 42, a ragged last chunk
+    ((1, 2, 40, 40), 0.0, 3),      # all empty
+    ((1, 4, 64, 64), 1.0, 4),      # all full: every count ties
+    ((3, 5, 33, 33), 0.2, 5),
+])
+def test_plan_random(shape, p, seed):
+    g = torch.Generator().manual_seed(seed)
+    m = (torch.rand(*shape, generator=g) < p).to(torch.uint8)
+    _check_plan(m)

@@ -128,6 +128,29 @@ def test_compacted_matches_fwd():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 64)])
+def test_planned_matches_fwd(dtype, D):
+    """One plan, every built tile config: bsattn_fwd_planned equals bsattn_fwd_config
+    bit for bit, and the plan stays valid for new q/k/v of the same mask."""
+    ensure_built()
+    B, H, S, b = 2, 3, 640, 128
+    mask = rand_mask(B, H, S // b, S // b, 0.4, seed=41, empty_rows=[(1, 2, 0)])
+    md = mask.cuda()
+    ws = bs.plan(md, S, b, b)
+    for seed in (42, 43):
+        q, k, v = rand_qkv(B, H, S, D, dtype, seed=seed)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        for cfg in bs.list_configs(dtype, D, b, b):
+            say("planned", dtype, D, seed, cfg)
+            o1, l1 = bs.fwd(qd, kd, vd, md, b, b, 0.11, config=cfg)
+            o2, l2 = bs.fwd_planned(qd, kd, vd, ws, b, b, 0.11, config=cfg)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), cfg
+        orf, lrf = oracle.fwd(q, k, v, mask, b, b, 0.11)
+        compare(o2, l2, orf, lrf, dkey(q), what="planned")
+
+
 def test_deterministic():
     ensure_built()
     w = W.WORKLOADS["sparse_bf16"]
