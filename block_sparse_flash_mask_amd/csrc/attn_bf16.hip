@@ -47,70 +47,11 @@
 #define BSATTN_SCHED_GROUPS 0
 #endif
 
+#include "bf16_layout.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace bsattn {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#define BSATTN_LDS __attribute__((address_space(3)))
-
-// Row order of K fed to the S^T MFMA: swap bits 2 and 3 of the 5-bit row index.
-// After the MFMA, register i of lane (half h) holds key 16*(i/8) + 8*h + i%8 of
-// the 32-key tile: keys 8h..8h+7 in registers 0..7 and 16+8h..16+8h+7 in 8..15,
-// which is the B-operand layout of two 16-key steps of the P V MFMA.
-__device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-template <int D, int TK>
-struct TileGeom {
-    static constexpr int KS = D / 16;               // 16-deep k-steps of S^T
-    static constexpr int MT = TK / 32;              // 32-key tiles
-    static constexpr int MD = D / 32;               // 32-wide d tiles of O^T
-    static constexpr int KBLK = MT * KS;            // 1 KiB K blocks per tile
-    static constexpr int VBLK = MT * 2 * 2 * MD;    // 512 B V blocks per tile
-    static constexpr int BYTES = TK * D * 2;        // one K (or V) tile
-    static_assert(KBLK * 1024 == BYTES, "K layout covers the tile");
-    static_assert(VBLK * 512 == BYTES, "V layout covers the tile");
-};
-
-// Global element offsets (relative to the tile's first key) of the DMA
-// instructions a wave issues for one tile: a per-lane part shared by all of the
-// wave's K (or V) instructions plus a wave-uniform part per instruction, so the
-// address is a scalar base plus one 32-bit VGPR offset.
-template <int D, int WAVES, int TK>
-struct DmaPlan {
-    typedef TileGeom<D, TK> G;
-    static constexpr int NK = G::KBLK / WAVES;      // K DMA instructions per wave
-    static constexpr int NV = G::VBLK / 2 / WAVES;  // V DMA instructions (2 blocks each)
-    static_assert(G::KBLK % WAVES == 0 && (G::VBLK / 2) % WAVES == 0, "even DMA split");
-    static_assert(G::MD % 2 == 0, "V blocks pair along d");
-    int k_lane;  // kperm(l%32) * D + 8 * (l/32)
-    int v_lane;  // see v_uniform
-
-    __device__ __forceinline__ void init(int lane) {
-        k_lane = kperm(lane & 31) * D + 8 * (lane >> 5);
-        // One V DMA instruction fills blocks 2j (lanes 0..31) and 2j+1 (32..63),
-        // block index tb = ((mt*2 + e)*2 + r)*MD + md; lane l writes the 8-byte
-        // units u = 2(l%32), u+1 of its block, which hold
-        // V[32mt + 16e + 8(u/32) + 4r + (u%16)/4][32md + 16((u/16)%2) + 4(u%4) ..].
-        const int u = 2 * (lane & 31);
-        const int L = u & 15, g = (u >> 4) & 1, hh = u >> 5;
-        v_lane = (8 * hh + (L >> 2)) * D + 32 * (lane >> 5) + 16 * g + 4 * (L & 3);
-    }
-    // K instruction i of wave w: block blk = w + i*WAVES = mt*KS + ks.
-    __device__ __forceinline__ static int k_uniform(int w, int i) {
-        const int blk = w + i * WAVES;
-        return 32 * (blk / G::KS) * D + 16 * (blk % G::KS);
-    }
-    // V instruction i of wave w: block pair j = w + i*WAVES, first block tb = 2j.
-    __device__ __forceinline__ static int v_uniform(int w, int i) {
-        const int tb = 2 * (w + i * WAVES);
-        const int md = tb % G::MD, r = (tb / G::MD) % 2, e = (tb / G::MD / 2) % 2,
-                  mt = tb / G::MD / 4;
-        return (32 * mt + 16 * e + 4 * r) * D + 32 * md;
-    }
-};
 
 template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_bf16_kernel(FwdArgs a) {
@@ -243,9 +184,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = s.v[n][mt][i];
-            const float mx = max_halves(tree_max<16 * MT>(tmp)) * a.c;
+            const float mx = max_halves_nan(max_tree3<16 * MT>(tmp)) * a.c;
             if (__ballot(mx > m_run[n] + 8.0f) != 0) {
-                const float m_new = __builtin_fmaxf(m_run[n], mx);
+                const float m_new = fmax_nan(m_run[n], mx);
                 const float alpha = fast_exp2(m_run[n] - m_new);
                 l_run[n] *= alpha;
 #pragma unroll
@@ -452,11 +393,13 @@ static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t strea
     {1, D, 32 * NQ * W, TK, W, ST, &launch_bf16<D, W, TK, NQ, PIPE, ST, OCC>}
 
 static const Variant kBf16Variants[] = {
+    {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
     BSATTN_BF16_VARIANT(128, 4, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 4, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(128, 4, 32, 1, 1, 2, 2), BSATTN_BF16_VARIANT(128, 4, 64, 1, 0, 3, 1),
     BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 2, 1), BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 3, 1),
     BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 2, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(128, 1, 32, 2, 0, 3, 1),
+    {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
     BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 4, 32, 1, 1, 2, 2),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
     BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),

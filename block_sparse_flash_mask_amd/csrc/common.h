@@ -53,27 +53,49 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-// max(x[lane], x[lane ^ 32]) and x[lane] + x[lane ^ 32] with one v_permlane32_swap:
-// it returns (own, partner) in the low half-wave and (partner, own) in the high one.
-__device__ __forceinline__ float max_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// x[lane] + x[lane ^ 32] with one v_permlane32_swap: it returns (own, partner)
+// in the low half-wave and (partner, own) in the high one.
 __device__ __forceinline__ float sum_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Pairwise (tree) max / sum of N register values: log2(N) dependent levels
-// instead of a serial chain.
-template <int N>
-__device__ __forceinline__ float tree_max(float* v) {
-#pragma unroll
-    for (int w = N / 2; w >= 1; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) v[i] = __builtin_fmaxf(v[i], v[i + w]);
-    return v[0];
+// NaN-propagating maximum: v_maximum3_f32 on gfx950, with none of the
+// canonicalising moves that an IEEE-mode fmaxf needs in front of v_max_f32.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max(x[lane], x[lane ^ 32]) with fmax_nan.
+__device__ __forceinline__ float max_halves_nan(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+// Maximum of N register values as a tree of three-input maxima (one
+// v_maximum3_f32 per node; ceil(log3 N) dependent levels).
+template <int N>
+__device__ __forceinline__ float max_tree3(const float* v) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else if constexpr (N == 2) {
+        return fmax_nan(v[0], v[1]);
+    } else {
+        constexpr int M = (N + 2) / 3;
+        float w[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (3 * i + 2 < N)
+                w[i] = fmax_nan(fmax_nan(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+            else if (3 * i + 1 < N)
+                w[i] = fmax_nan(v[3 * i], v[3 * i + 1]);
+            else
+                w[i] = v[3 * i];
+        }
+        return max_tree3<M>(w);
+    }
+}
+
+// Pairwise (tree) sum of N register values: log2(N) dependent levels instead
+// of a serial chain.
 template <int N>
 __device__ __forceinline__ float tree_sum(float* v) {
 #pragma unroll

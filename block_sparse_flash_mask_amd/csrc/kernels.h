@@ -31,6 +31,10 @@ struct Variant {
     hipError_t (*launch)(const FwdArgs& a, unsigned grid, hipStream_t stream);
 };
 
+// The two-group bf16 kernel (attn_bf16_pp.hip): 8 waves, 128 query rows, 32-key tiles.
+template <int D>
+hipError_t launch_bf16_pp(const FwdArgs& a, unsigned grid, hipStream_t stream);
+
 // Tables of the built variants (attn_bf16.hip, attn_f32.hip).
 const Variant* bf16_variants(int* n);
 const Variant* f32_variants(int* n);

@@ -61,7 +61,9 @@ typedef enum {
  *   tile_q  query rows per workgroup: 64 or 128, must divide block_q;
  *   tile_k  keys per inner step: 32, 64 or 128, must divide block_k;
  *   waves   wavefronts per workgroup (64 lanes each); a wave owns 32 or 64
- *           query rows, so waves is tile_q / 32 or tile_q / 64;
+ *           query rows, so waves is tile_q / 32 or tile_q / 64, or 8 with
+ *           tile_q 128 for the two-group schedule (two 4-wave groups on the
+ *           same rows, each taking every other key tile, merged at the end);
  *   stages  K/V tiles resident in LDS: 1 (load, barrier, compute), 2 or 3
  *           (later tiles are written while the current one is consumed).
  * bsattn_list_configs gives the combinations that are built.
