@@ -27,7 +27,10 @@ METRIC = "block-sparse attn fwd effective TFLOP/s (active blocks) + % bf16 MFMA 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
 PEAK_F32_TFLOPS = 157.3     # fp32 MFMA/vector dense
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/attn_bf16.hip",
+KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
+                  "block_sparse_flash_mask_amd/csrc/attn_bf16.hip",
+                  "block_sparse_flash_mask_amd/csrc/attn_bf16_pp.hip",
+                  "block_sparse_flash_mask_amd/csrc/bf16_layout.h",
                   "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
                   "block_sparse_flash_mask_amd/csrc/common.h"]
 
@@ -44,15 +47,17 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload):
+def traffic_from_profiles(workload, cfg):
     """HBM bytes per attention-kernel launch from a committed counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel source with this tile config; else None."""
     path = os.path.join(ROOT, "profiles", "attn_traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if list(rec.get("config", [])) != list(cfg):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -186,10 +191,11 @@ def main():
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     achieved = flops / (ms_attn * 1e-3) / 1e12
-    traffic = traffic_from_profiles(w.name)
+    traffic = traffic_from_profiles(w.name, cfg)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": traffic,
-                "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+                "kernel": ("attn_bf16_pp_kernel" if cfg[2] == 8 else "attn_bf16_kernel") if bf16
+                          else "attn_f32_kernel",
                 "kernel_ms": ms_attn}
     if traffic:
         roofline["hbm_gbs"] = traffic / (ms_attn * 1e-3) / 1e9

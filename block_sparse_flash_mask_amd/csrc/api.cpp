@@ -378,7 +378,7 @@ int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int
     int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
     hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = launch_compact_order(counts, R, n_k, xcd_chunk(R), order, s);
+    e = launch_compact_order(counts, R, n_q, n_k, xcd_chunk(R), order, s);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }

@@ -109,12 +109,16 @@ __global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ c
 // Dispatch order of the attention workgroups.  Workgroups go to the 8 XCDs of
 // the chip round-robin by blockIdx, so blockIdx b runs on XCD b % 8 and is the
 // (b / 8)-th workgroup that XCD receives.  Mask rows are cut into 8 contiguous
-// chunks of `chunk` rows, one per XCD, so neighbouring query tiles of a head share
-// that XCD's L2; inside a chunk the rows go longest first.  One workgroup per
-// chunk runs a counting sort on the active-block count: a histogram in LDS, an
-// exclusive scan of it, then a scatter.  Rows with equal counts land in arbitrary
-// order, which cannot change any result (each row is computed on its own).
-// order[x * chunk + j] = mask row, or -1 for padding past the last row.
+// chunks of `chunk` rows, one per XCD, so the query tiles of a head share that
+// XCD's L2.  Inside a chunk the rows go head by head, in (b, h) order, and within
+// a head longest first: the workgroups in flight on an XCD then read the K and V
+// of one or two heads (which stay in its L2), and the short rows come last, which
+// evens out the finishing times.  One workgroup per chunk runs a counting sort on
+// the key (local head, -count): a histogram in LDS, an exclusive scan of it, then
+// a scatter.  If a chunk would need more bins than the histogram holds, the key
+// is -count alone (longest first over the whole chunk).  Rows with equal keys land
+// in arbitrary order, which cannot change any result (each row is computed on its
+// own).  order[x * chunk + j] = mask row, or -1 for padding past the last row.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxBins = 4096;
 
@@ -128,25 +132,30 @@ __device__ __forceinline__ int order_wave_scan(int x) {
     return x;
 }
 
-// Bin of a row with c active blocks: ascending bin = descending count.
-__device__ __forceinline__ int order_bin(int c, int nbins) {
-    c = c < 0 ? 0 : (c > nbins - 1 ? nbins - 1 : c);
-    return nbins - 1 - c;
+// Sort key of a row with c active blocks out of nk1 - 1; hl is its head's index
+// within the chunk (0 when the chunk is sorted by count alone).
+__device__ __forceinline__ int order_bin(int c, int hl, int nk1) {
+    c = c < 0 ? 0 : (c > nk1 - 1 ? nk1 - 1 : c);
+    return hl * nk1 + (nk1 - 1 - c);
 }
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
-                                                              int64_t R, int64_t chunk,
-                                                              int nbins,
+                                                              int64_t R, int64_t chunk, int n_q,
+                                                              int nk1, int by_head, int nbins,
                                                               int32_t* __restrict__ order) {
     __shared__ int hist[kOrderMaxBins];
     __shared__ int wave_tot[kOrderThreads / kWave];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t r0 = (int64_t)blockIdx.x * chunk;
     const int64_t nr = r0 >= R ? 0 : (R - r0 < chunk ? R - r0 : chunk);
+    const int64_t h0 = r0 / n_q;
+    auto key = [&](int64_t k) {
+        const int hl = by_head ? (int)((r0 + k) / n_q - h0) : 0;
+        return order_bin(counts[r0 + k], hl, nk1);
+    };
     for (int b = tid; b < nbins; b += kOrderThreads) hist[b] = 0;
     __syncthreads();
-    for (int64_t k = tid; k < nr; k += kOrderThreads)
-        atomicAdd(&hist[order_bin(counts[r0 + k], nbins)], 1);
+    for (int64_t k = tid; k < nr; k += kOrderThreads) atomicAdd(&hist[key(k)], 1);
     __syncthreads();
     // Exclusive scan of hist: each thread owns a run of consecutive bins.
     const int per = (nbins + kOrderThreads - 1) / kOrderThreads;
@@ -170,18 +179,27 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
     __syncthreads();
     for (int64_t k = tid; k < nr; k += kOrderThreads) {
-        const int pos = atomicAdd(&hist[order_bin(counts[r0 + k], nbins)], 1);
+        const int pos = atomicAdd(&hist[key(k)], 1);
         order[r0 + pos] = (int32_t)(r0 + k);
     }
     for (int64_t i = nr + tid; i < chunk; i += kOrderThreads) order[r0 + i] = -1;
 }
 
-hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_k, int64_t chunk,
+hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n_k, int64_t chunk,
                                 int32_t* order, hipStream_t stream) {
-    if (R <= 0 || chunk <= 0 || 8 * chunk < R) return hipErrorInvalidValue;
-    const int nbins = n_k + 1 < kOrderMaxBins ? n_k + 1 : kOrderMaxBins;
-    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, chunk,
-                       nbins, order);
+    if (R <= 0 || n_q <= 0 || n_k <= 0 || chunk <= 0 || 8 * chunk < R) return hipErrorInvalidValue;
+    // A chunk of `chunk` consecutive rows touches at most this many heads.
+    const int64_t heads = (chunk + n_q - 1) / n_q + 1;
+    int nk1 = n_k + 1, by_head = 0, nbins;
+    if (heads * nk1 <= kOrderMaxBins) {
+        by_head = 1;
+        nbins = (int)(heads * nk1);
+    } else {
+        nk1 = nk1 < kOrderMaxBins ? nk1 : kOrderMaxBins;
+        nbins = nk1;
+    }
+    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, chunk, n_q,
+                       nk1, by_head, nbins, order);
     return hipGetLastError();
 }
 

@@ -13,9 +13,9 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t*
                                int32_t* lists, hipStream_t stream);
 hipError_t launch_compact_scan(const int32_t* counts, int64_t R, int32_t* row_ptr,
                                hipStream_t stream);
-// Longest-first dispatch order of mask rows per XCD chunk of `chunk` rows
-// (8 * chunk >= R); order has 8 * chunk entries.
-hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_k, int64_t chunk,
+// Dispatch order of mask rows per XCD chunk of `chunk` rows (8 * chunk >= R):
+// head by head, longest row first within a head; order has 8 * chunk entries.
+hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n_k, int64_t chunk,
                                 int32_t* order, hipStream_t stream);
 hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int64_t R, int n_k,
                                const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);

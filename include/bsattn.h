@@ -142,12 +142,13 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
  * active key blocks and their kj in ascending order (a list padded to n_k
  * entries), then the order in which the attention kernel dispatches its
  * workgroups: rows cut into 8 contiguous chunks (one per XCD of the chip), each
- * chunk longest row first.  With R = B*H*(S/block_q), n_k = S/block_k and
+ * chunk head by head in (b, h) order and each head's rows longest first (or,
+ * when a chunk spans more than 4096 head x count bins, longest first overall).  With R = B*H*(S/block_q), n_k = S/block_k and
  * A(x) = x rounded up to a multiple of 256, the plan is three int32 arrays:
  *   counts[R]              at byte 0;
  *   lists[R][n_k]          at byte A(4R), row i's kj in lists[i][0 .. counts[i]);
  *   order[8 * ceil(R/8)]   at byte A(4R) + A(4 R n_k): chunk x is
- *                          order[x*ceil(R/8) ..], its rows by descending count,
+ *                          order[x*ceil(R/8) ..], its rows in the order above,
  *                          then -1 past the last row.
  * The plan depends only on block_mask and (B, H, S,
  * block_q, block_k), never on q/k/v, D, dtype, scale or the tile config, so one

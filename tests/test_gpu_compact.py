@@ -63,8 +63,9 @@ def _rnd(x):
 
 def _check_plan(mask, block_q=128, block_k=128):
     """bsattn_plan's three arrays: counts and lists equal the oracle's compaction
-    bit for bit; each XCD chunk of the order holds exactly its own rows, by
-    non-increasing count, then -1 padding."""
+    bit for bit; each XCD chunk of the order holds exactly its own rows, then -1
+    padding, head by head with each head's rows by non-increasing count (or by
+    non-increasing count alone when a chunk spans too many head x count bins)."""
     ensure_built()
     B, H, n_q, n_k = mask.shape
     S = n_q * block_q
@@ -88,8 +89,16 @@ def _check_plan(mask, block_q=128, block_k=128):
         nr = r1 - r0
         assert np.array_equal(np.sort(got[:nr]), np.arange(r0, r1)), x
         assert np.all(got[nr:] == -1), x
-        c = counts[got[:nr]]
-        assert np.all(c[:-1] >= c[1:]), x
+        rows = got[:nr]
+        c = counts[rows]
+        by_head = ((chunk + n_q - 1) // n_q + 1) * (n_k + 1) <= 4096
+        if by_head:
+            hd = rows // n_q
+            assert np.all(hd[:-1] <= hd[1:]), x
+            same = hd[:-1] == hd[1:]
+            assert np.all(c[:-1][same] >= c[1:][same]), x
+        else:
+            assert np.all(c[:-1] >= c[1:]), x
 
 
 @pytest.mark.parametrize("name", W.ORDER)
@@ -110,3 +119,10 @@ def test_plan_random(shape, p, seed):
     g = torch.Generator().manual_seed(seed)
     m = (torch.rand(*shape, generator=g) < p).to(torch.uint8)
     _check_plan(m)
+
+
+def test_plan_order_without_heads():
+    """A chunk spanning 65 heads x 65 counts (> 4096 bins) is sorted by count alone."""
+    g = torch.Generator().manual_seed(6)
+    m = (torch.rand(4, 128, 128, 64, generator=g) < 0.1).to(torch.uint8)
+    _check_plan(m, 64, 128)
