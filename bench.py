@@ -57,9 +57,8 @@ def traffic_from_profiles(workload, cfg):
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    if list(rec.get("config", [])) != list(cfg):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    entry = rec.get("by_config", {}).get(",".join(str(x) for x in cfg))
+    return entry.get("hbm_bytes_per_launch") if entry else None
 
 
 def cpu_baseline(w, q, k, v, mask, budget_s):
