@@ -75,7 +75,7 @@ def _configs(dtype, D, bq, bk):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("blocks", [(128, 128), (64, 64), (64, 128)])
+@pytest.mark.parametrize("blocks", [(128, 128), (64, 64), (64, 128), (128, 64)])
 def test_every_config(dtype, D, blocks):
     bq, bk = blocks
     B, H, S = 1, 2, 512
@@ -113,6 +113,30 @@ def test_edge_cases(dtype):
     c = 4.0 * torch.randn(D, generator=torch.Generator().manual_seed(5))
     k2 = (k.float() + c).to(dtype)
     _run_full(q, k2, v, mask, b, b, 0.125, what="shifted keys")
+
+
+@pytest.mark.parametrize("bk", [128, 64])
+def test_long_rows_every_config(bk):
+    """Rows with more than 64 active key blocks (kernels that hold the row's list
+    64 entries at a time must reload it): block-causal, S = 16384, every config,
+    on sampled rows from the first and the last query blocks."""
+    ensure_built()
+    B, H, S, D, bq = 1, 1, 16384, 128, 128
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=51)
+    n_q, n_k = S // bq, S // bk
+    qi = torch.arange(n_q)[:, None]
+    kj = torch.arange(n_k)[None, :]
+    mask = (kj * bk < (qi + 1) * bq).to(torch.uint8).expand(B, H, n_q, n_k).contiguous()
+    assert int(mask[0, 0, -1].sum()) > 64
+    rows = np.concatenate([np.arange(0, 256, 37), np.arange(S - 1024, S, 61), [S - 1]]).astype(np.int64)
+    ro, rl = oracle.fwd_rows(q, k, v, mask, bq, bk, 0.088, rows)
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    idx = torch.as_tensor(rows, device="cuda")
+    for cfg in bs.list_configs(torch.bfloat16, D, bq, bk):
+        say("long rows", bk, cfg)
+        out, lse = bs.fwd(qd, kd, vd, md, bq, bk, 0.088, config=cfg)
+        torch.cuda.synchronize()
+        compare(out.reshape(-1, D)[idx], lse.reshape(-1)[idx], ro, rl, "bf16", "long rows %s" % (cfg,))
 
 
 def test_compacted_matches_fwd():
