@@ -48,11 +48,29 @@ size_t compact_ws_bytes(int64_t R, int64_t n_k) {
 // Mask rows per XCD chunk.
 int64_t xcd_chunk(int64_t R) { return (R + 7) / 8; }
 
-// Forward workspace (the plan): the compaction workspace (per-row counts and
-// padded lists), then the dispatch order, 8 * xcd_chunk(R) row slots.
-size_t fwd_ws_bytes(int64_t R, int64_t n_k) {
-    return compact_ws_bytes(R, n_k) + align_up((size_t)(8 * xcd_chunk(R)) * 4);
+// Forward workspace (the plan): per-row counts, padded lists, the dispatch
+// order of the R rows (8 * xcd_chunk(R) slots) and that of the P pairs of
+// adjacent rows (8 * xcd_chunk(P) slots), each region 256-byte aligned.
+struct PlanLayout {
+    int64_t R, P;           // mask rows; pairs of rows (2j, 2j+1) of a head
+    int64_t chunk, pchunk;  // rows / pairs per XCD chunk
+    size_t lists, order, porder, bytes;
+};
+
+PlanLayout plan_layout(int64_t BH, int n_q, int n_k) {
+    PlanLayout L;
+    L.R = BH * n_q;
+    L.P = BH * ((n_q + 1) / 2);
+    L.chunk = xcd_chunk(L.R);
+    L.pchunk = xcd_chunk(L.P);
+    L.lists = align_up((size_t)L.R * 4);
+    L.order = L.lists + align_up((size_t)(L.R * n_k) * 4);
+    L.porder = L.order + align_up((size_t)(8 * L.chunk) * 4);
+    L.bytes = L.porder + align_up((size_t)(8 * L.pchunk) * 4);
+    return L;
 }
+
+size_t fwd_ws_bytes(int64_t BH, int n_q, int n_k) { return plan_layout(BH, n_q, n_k).bytes; }
 
 int check_grid(int B, int H, int n_q, int n_k) {
     if (B <= 0 || H <= 0 || n_q <= 0 || n_k <= 0) return BSATTN_ERR_SHAPE;
@@ -117,8 +135,12 @@ const Variant* variants(int dtype, int* n) {
     return dtype == BSATTN_BF16 ? bf16_variants(n) : f32_variants(n);
 }
 
+// Row-pair variants: two 128-row mask rows per workgroup.
+bool is_pair(const Variant& v) { return v.tile_q == 256; }
+
 bool legal(const Variant& v, int dtype, int D, int block_q, int block_k) {
-    return v.dtype == dtype && v.D == D && block_q % v.tile_q == 0 && block_k % v.tile_k == 0;
+    const bool rows_ok = is_pair(v) ? block_q == 128 : block_q % v.tile_q == 0;
+    return v.dtype == dtype && v.D == D && rows_ok && block_k % v.tile_k == 0;
 }
 
 bool matches(const Variant& v, const bsattn_tile_config& c) {
@@ -272,7 +294,7 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
     a.n_k = S / block_k;
     a.block_q = block_q;
     a.block_k = block_k;
-    a.sub_per_row = block_q / var.tile_q;
+    a.sub_per_row = is_pair(var) ? 1 : block_q / var.tile_q;
     a.sub_log2 = 0;
     while ((1 << a.sub_log2) < a.sub_per_row) ++a.sub_log2;
     a.steps_log2 = 0;
@@ -356,7 +378,7 @@ int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t*
     if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
     const int rc = check_grid(B, H, S / block_q, S / block_k);
     if (rc) return rc;
-    *bytes = fwd_ws_bytes((int64_t)B * H * (S / block_q), S / block_k);
+    *bytes = fwd_ws_bytes((int64_t)B * H, S / block_q, S / block_k);
     return BSATTN_OK;
 }
 
@@ -369,16 +391,16 @@ int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int
     const int n_q = S / block_q, n_k = S / block_k;
     int rc = check_grid(B, H, n_q, n_k);
     if (rc) return rc;
-    const int64_t R = (int64_t)B * H * n_q;
-    if (workspace_bytes < fwd_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    int32_t* counts = (int32_t*)workspace;
-    int32_t* lists = (int32_t*)((char*)workspace + align_up((size_t)R * 4));
-    int32_t* order = (int32_t*)((char*)workspace + compact_ws_bytes(R, n_k));
-    hipError_t e = launch_compact_rows(block_mask, R, n_k, counts, lists, s);
+    char* ws = (char*)workspace;
+    int32_t* counts = (int32_t*)ws;
+    hipError_t e = launch_compact_rows(block_mask, L.R, n_k, counts, (int32_t*)(ws + L.lists), s);
     if (e != hipSuccess) return hip_fail(e);
-    e = launch_compact_order(counts, R, n_q, n_k, xcd_chunk(R), order, s);
+    e = launch_compact_order(counts, L.R, n_q, n_k, L.chunk, (int32_t*)(ws + L.order), L.pchunk,
+                             (int32_t*)(ws + L.porder), s);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }
@@ -391,20 +413,28 @@ int bsattn_fwd_planned(const void* q, const void* k, const void* v, void* out, f
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
     const int n_q = S / block_q, n_k = S / block_k;
-    const int64_t R = (int64_t)B * H * n_q;
-    if (workspace_bytes < fwd_ws_bytes(R, n_k)) return BSATTN_ERR_WORKSPACE;
+    const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
-    if (check_ws_alias(workspace, fwd_ws_bytes(R, n_k), q, k, v, out, lse, B, H, S, D, dtype))
+    if (check_ws_alias(workspace, L.bytes, q, k, v, out, lse, B, H, S, D, dtype))
         return BSATTN_ERR_ALIAS;
     const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
     if (!var) return BSATTN_ERR_UNSUPPORTED;
+    if (is_pair(*var) && n_k > kPairMaxBlocks) return BSATTN_ERR_UNSUPPORTED;
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
-    a.counts = (const int32_t*)workspace;
-    a.list = (const int32_t*)((const char*)workspace + align_up((size_t)R * 4));
+    const char* ws = (const char*)workspace;
+    a.counts = (const int32_t*)ws;
+    a.list = (const int32_t*)(ws + L.lists);
     a.ell_stride = n_k;
-    a.order = (const int32_t*)((const char*)workspace + compact_ws_bytes(R, n_k));
-    a.nrows = (int)R;
-    a.chunk = (int)xcd_chunk(R);
+    if (is_pair(*var)) {
+        a.order = (const int32_t*)(ws + L.porder);
+        a.nrows = (int)L.P;
+        a.chunk = (int)L.pchunk;
+    } else {
+        a.order = (const int32_t*)(ws + L.order);
+        a.nrows = (int)L.R;
+        a.chunk = (int)L.chunk;
+    }
     return run_attention(a, *var, (hipStream_t)stream);
 }
 
@@ -415,15 +445,15 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
     if (!block_mask) return BSATTN_ERR_NULL;
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
-    const int64_t R = (int64_t)B * H * (S / block_q);
-    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k)) return BSATTN_ERR_WORKSPACE;
+    const size_t need = fwd_ws_bytes((int64_t)B * H, S / block_q, S / block_k);
+    if (!workspace || workspace_bytes < need) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
-    if (check_ws_alias(workspace, fwd_ws_bytes(R, S / block_k), q, k, v, out, lse, B, H, S, D,
-                       dtype))
+    if (check_ws_alias(workspace, need, q, k, v, out, lse, B, H, S, D, dtype))
         return BSATTN_ERR_ALIAS;
     // Resolve the tile config before any device work, so an unsupported one
     // fails with nothing enqueued.
-    if (!choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg)) return BSATTN_ERR_UNSUPPORTED;
+    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
+    if (!var || (is_pair(*var) && S / block_k > kPairMaxBlocks)) return BSATTN_ERR_UNSUPPORTED;
     int st = bsattn_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
     if (st) return st;
     return bsattn_fwd_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, dtype,
@@ -447,13 +477,14 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
     if (!is_aligned(row_ptr, 4) || !is_aligned(col_idx, 4)) return BSATTN_ERR_ALIGN;
     const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
     if (!var) return BSATTN_ERR_UNSUPPORTED;
-    const int64_t R = (int64_t)B * H * (S / block_q);
+    if (is_pair(*var) && S / block_k > kPairMaxBlocks) return BSATTN_ERR_UNSUPPORTED;
+    const PlanLayout L = plan_layout((int64_t)B * H, S / block_q, S / block_k);
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
     a.row_ptr = row_ptr;
     a.list = col_idx;
     a.ell_stride = 0;
-    a.nrows = (int)R;
-    a.chunk = (int)xcd_chunk(R);
+    a.nrows = (int)(is_pair(*var) ? L.P : L.R);
+    a.chunk = (int)xcd_chunk(a.nrows);
     return run_attention(a, *var, (hipStream_t)stream);
 }
 
@@ -482,8 +513,7 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     if (!best || !block_mask) return BSATTN_ERR_NULL;
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
     if (rc) return rc;
-    const int64_t R = (int64_t)B * H * (S / block_q);
-    if (!workspace || workspace_bytes < fwd_ws_bytes(R, S / block_k))
+    if (!workspace || workspace_bytes < fwd_ws_bytes((int64_t)B * H, S / block_q, S / block_k))
         return BSATTN_ERR_WORKSPACE;
     if (warmup < 0 || iters < 1) return BSATTN_ERR_SHAPE;
 
@@ -499,6 +529,7 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     int status = BSATTN_OK;
     for (int i = 0; i < nv && status == BSATTN_OK; ++i) {
         if (!legal(t[i], dtype, D, block_q, block_k)) continue;
+        if (is_pair(t[i]) && S / block_k > kPairMaxBlocks) continue;
         const bsattn_tile_config c{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
         for (int w = 0; w < warmup && status == BSATTN_OK; ++w)
             status = bsattn_fwd_config(q, k, v, block_mask, out, lse, B, H, S, D, block_q, block_k,

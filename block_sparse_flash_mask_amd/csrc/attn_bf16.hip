@@ -53,12 +53,13 @@
 
 namespace bsattn {
 
-template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC>
+template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_bf16_kernel(FwdArgs a) {
     typedef TileGeom<D, TK> G;
     typedef DmaPlan<D, WAVES, TK> P;
-    constexpr int TQ = 32 * NQ * WAVES;  // query rows per workgroup
+    constexpr int TQ = 32 * NQ * WAVES;  // query rows per workgroup (both rows of a pair)
     constexpr int KS = G::KS, MT = G::MT, MD = G::MD;
+    static_assert(!PAIR || (WAVES == 8 && NQ == 1 && !PIPE), "row pairs: two 4-wave groups");
 
     static_assert(ST == 2 || (ST == 3 && !PIPE), "three stages use the plain schedule");
     __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
@@ -77,14 +78,77 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     int r, sub;
     block_work(a, r, sub);
     if (r < 0) return;
-    const int bh = r / a.n_q;
-    const int qi = r - bh * a.n_q;
-    int beg, cnt;
-    row_list(a, r, beg, cnt);
     const int sh = a.steps_log2;  // kernel steps per key block = 1 << sh
+    int bh, qi, beg = 0, cnt;
+    bool row_ok = true;  // this wave's query rows exist (false: second row of a pair past n_q)
+    int q_row0;          // this lane's query row in each of the wave's NQ 32-row tiles
+    // Row pairs: the workgroup runs over the union of the two rows' key-block lists,
+    // built here in LDS as (kj | member bits << 30); group g = wave / 4 owns row 2j + g
+    // and computes only the blocks of its own row.
+    __shared__ uint32_t pair_bits[PAIR ? 2 * (kPairMaxBlocks / 32) : 1];
+    __shared__ uint32_t pair_list[PAIR ? kPairMaxBlocks : 1];
+    __shared__ int pair_cnt[1];
+    const int grp = PAIR ? wave >> 2 : 0;
+    if constexpr (PAIR) {
+        if (a.n_k > kPairMaxBlocks) return;  // the host rejects such shapes first
+        const int hq = (a.n_q + 1) >> 1;
+        bh = r / hq;
+        const int j = r - bh * hq;
+        qi = 2 * j + grp;
+        row_ok = qi < a.n_q;
+        const int ra = bh * a.n_q + 2 * j;
+        const bool has_b = 2 * j + 1 < a.n_q;
+        const int nw = (a.n_k + 31) >> 5;
+        for (int w = tid; w < 2 * nw; w += WAVES * 64) pair_bits[(w / nw) * (kPairMaxBlocks / 32) + w % nw] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            if (side == 1 && !has_b) break;
+            int b0, c0;
+            row_list(a, ra + side, b0, c0);
+            for (int i = tid; i < c0; i += WAVES * 64) {
+                int kj = a.list[b0 + i];
+                kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
+                atomicOr(&pair_bits[side * (kPairMaxBlocks / 32) + (kj >> 5)], 1u << (kj & 31));
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // Compact the union bitmap: lane l takes word l of each 64-word chunk.
+            int base = 0;
+            for (int w0 = 0; w0 < nw; w0 += 64) {
+                const int w = w0 + lane;
+                const uint32_t ba = w < nw ? pair_bits[w] : 0u;
+                const uint32_t bb = w < nw ? pair_bits[(kPairMaxBlocks / 32) + w] : 0u;
+                uint32_t u = ba | bb;
+                const int c = __popc(u);
+                int incl = c;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += y;
+                }
+                int pos = base + incl - c;
+                while (u) {
+                    const int bit = __builtin_ctz(u);
+                    u &= u - 1;
+                    const uint32_t m = 1u << bit;
+                    pair_list[pos++] = (uint32_t)(w * 32 + bit) | ((ba & m) ? 1u << 30 : 0u) | ((bb & m) ? 1u << 31 : 0u);
+                }
+                base += __shfl(incl, 63, 64);
+            }
+            if (lane == 0) pair_cnt[0] = base;
+        }
+        __syncthreads();
+        cnt = wave_uniform(pair_cnt[0]);
+        q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
+    } else {
+        bh = r / a.n_q;
+        qi = r - bh * a.n_q;
+        row_list(a, r, beg, cnt);
+        q_row0 = qi * a.block_q + sub * TQ + wave * 32 * NQ + l32;
+    }
     const int n_steps = cnt << sh;
-    // This lane's query row in each of the wave's NQ 32-row tiles.
-    const int q_row0 = qi * a.block_q + sub * TQ + wave * 32 * NQ + l32;
     const size_t head = (size_t)bh * a.S * D;
     const uint16_t* __restrict__ kg = (const uint16_t*)a.k + head;
     const uint16_t* __restrict__ vg = (const uint16_t*)a.v + head;
@@ -93,7 +157,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     bf16x8 qf[NQ][KS];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)(q_row0 + 32 * n) * D);
+        // (a missing second row of a pair reads its partner's rows, never used)
+        const int qr = row_ok ? q_row0 + 32 * n : q_row0 - a.block_q;
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)qr * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 t = qp[2 * ks + h];
@@ -110,10 +176,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // on a global load.
     auto entry = [&](int t) -> int {
         const int i = t >> sh;
-        return a.list[beg + (i < cnt ? i : cnt - 1)];
+        if constexpr (PAIR)
+            return (int)pair_list[i < cnt ? i : cnt - 1];
+        else
+            return a.list[beg + (i < cnt ? i : cnt - 1)];
+    };
+    // Does this wave's row own the key block of step t (always, unless paired)?
+    auto mine = [&](int t) -> bool {
+        if constexpr (PAIR)
+            return (pair_list[wave_uniform(t >> sh)] >> (30 + grp)) & 1u;
+        else
+            return true;
     };
     auto key0_of = [&](int kj_raw, int t) -> int {
         int kj = wave_uniform(kj_raw);
+        if constexpr (PAIR) kj &= 0x3fffffff;
         kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
         return kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
     };
@@ -300,10 +377,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             issue_k(kn, kfill);
             issue_v(kn, vfill);
         }
-        const SAcc s = qk(kcur);
-        update_max(s);
-        const PTile p = exps(s);
-        pv(p, vcur);
+        if (mine(t)) {
+            const SAcc s = qk(kcur);
+            update_max(s);
+            const PTile p = exps(s);
+            pv(p, vcur);
+        }
     };
 
     if (n_steps > 0 && PIPE) {
@@ -355,9 +434,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     }
 
     // Epilogue: O / l in bf16 (round to nearest even), lse = ln2 * (m + log2 l).
-    const bool any = n_steps > 0;
+    // A row that saw no key block (m never left -inf) gets 0 and -inf.
+    if (!row_ok) return;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
+        const bool any = PAIR ? m_run[n] != -INFINITY : n_steps > 0;
         const int q_row = q_row0 + 32 * n;
         const float l_tot = sum_halves(l_run[n]);
         const float inv = any ? 1.0f / l_tot : 0.0f;
@@ -377,34 +458,41 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     }
 }
 
-template <int D, int W, int TK, int NQ, int PIPE, int ST, int OCC>
+template <int D, int W, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR = 0>
 static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, NQ, PIPE, ST, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, NQ, PIPE, ST, OCC, PAIR>), dim3(grid), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 // {dtype, D, tile_q, tile_k, waves, stages, launcher}.  The table order is the
-// built-in preference when no tuning result exists.  NQ = 2 (64 query rows per
+// built-in preference when no tuning result exists (the two-group and row-pair
+// kernels come last: they win only on particular shapes and masks).  NQ = 2 (64 query rows per
 // wave, each K/V fragment read from LDS feeding two MFMAs) runs one wave per
 // SIMD; NQ = 1 runs two or three.  PIPE = 1 overlaps the next tile's S MFMAs
 // with this tile's softmax inside a wave (two stages); PIPE = 0 runs the steps
 // in order with ST K/V stages resident in LDS.
 #define BSATTN_BF16_VARIANT(D, W, TK, NQ, PIPE, ST, OCC) \
     {1, D, 32 * NQ * W, TK, W, ST, &launch_bf16<D, W, TK, NQ, PIPE, ST, OCC>}
+// Row pairs: 8 waves, two adjacent 128-row mask rows of a head per workgroup
+// (tile_q 256), sharing every K/V tile of the union of their block lists.
+#define BSATTN_BF16_PAIR(D, TK, ST, OCC) \
+    {1, D, 256, TK, 8, ST, &launch_bf16<D, 8, TK, 1, 0, ST, OCC, 1>}
 
 static const Variant kBf16Variants[] = {
-    {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
     BSATTN_BF16_VARIANT(128, 4, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 4, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(128, 4, 32, 1, 1, 2, 2), BSATTN_BF16_VARIANT(128, 4, 64, 1, 0, 3, 1),
     BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 2, 1), BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 3, 1),
     BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 2, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(128, 1, 32, 2, 0, 3, 1),
-    {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
+    {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
+    BSATTN_BF16_PAIR(128, 32, 3, 2), BSATTN_BF16_PAIR(128, 64, 3, 2),
     BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 4, 32, 1, 1, 2, 2),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
     BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),
     BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 2, 32, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 1, 64, 2, 0, 2, 1),
+    {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
+    BSATTN_BF16_PAIR(64, 64, 3, 2), BSATTN_BF16_PAIR(64, 128, 2, 2),
 };
 
 const Variant* bf16_variants(int* n) {

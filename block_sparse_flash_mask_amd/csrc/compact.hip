@@ -139,25 +139,48 @@ __device__ __forceinline__ int order_bin(int c, int hl, int nk1) {
     return hl * nk1 + (nk1 - 1 - c);
 }
 
+// One sort job: `items` entries (mask rows, or pairs of adjacent mask rows of a
+// head) dealt to 8 XCD chunks of `chunk`, each sorted by (head, -count).
+struct OrderJob {
+    int64_t items;
+    int64_t chunk;
+    int per_head;   // items per (b, h): n_q rows, or ceil(n_q / 2) pairs
+    int pairs;      // 1: item p is rows (b, h, 2j) and (b, h, 2j + 1)
+    int by_head;
+    int nk1;
+    int nbins;
+    int32_t* order;
+};
+
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
-                                                              int64_t R, int64_t chunk, int n_q,
-                                                              int nk1, int by_head, int nbins,
-                                                              int32_t* __restrict__ order) {
+                                                              int n_q, OrderJob rows_job,
+                                                              OrderJob pairs_job) {
     __shared__ int hist[kOrderMaxBins];
     __shared__ int wave_tot[kOrderThreads / kWave];
+    const OrderJob& job = blockIdx.x < 8 ? rows_job : pairs_job;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * chunk;
-    const int64_t nr = r0 >= R ? 0 : (R - r0 < chunk ? R - r0 : chunk);
-    const int64_t h0 = r0 / n_q;
-    auto key = [&](int64_t k) {
-        const int hl = by_head ? (int)((r0 + k) / n_q - h0) : 0;
-        return order_bin(counts[r0 + k], hl, nk1);
+    const int64_t r0 = (int64_t)(blockIdx.x & 7) * job.chunk;
+    const int64_t nr = r0 >= job.items ? 0 : (job.items - r0 < job.chunk ? job.items - r0 : job.chunk);
+    const int64_t h0 = r0 / job.per_head;
+    auto count_of = [&](int64_t i) -> int {
+        if (!job.pairs) return counts[i];
+        const int64_t bh = i / job.per_head;
+        const int j = (int)(i - bh * job.per_head);
+        const int64_t ra = bh * n_q + 2 * j;
+        const int ca = counts[ra];
+        const int cb = 2 * j + 1 < n_q ? counts[ra + 1] : 0;
+        return ca > cb ? ca : cb;
     };
-    for (int b = tid; b < nbins; b += kOrderThreads) hist[b] = 0;
+    auto key = [&](int64_t k) {
+        const int hl = job.by_head ? (int)((r0 + k) / job.per_head - h0) : 0;
+        return order_bin(count_of(r0 + k), hl, job.nk1);
+    };
+    for (int b = tid; b < job.nbins; b += kOrderThreads) hist[b] = 0;
     __syncthreads();
     for (int64_t k = tid; k < nr; k += kOrderThreads) atomicAdd(&hist[key(k)], 1);
     __syncthreads();
     // Exclusive scan of hist: each thread owns a run of consecutive bins.
+    const int nbins = job.nbins;
     const int per = (nbins + kOrderThreads - 1) / kOrderThreads;
     const int b0 = tid * per;
     int run = 0;
@@ -180,26 +203,43 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     __syncthreads();
     for (int64_t k = tid; k < nr; k += kOrderThreads) {
         const int pos = atomicAdd(&hist[key(k)], 1);
-        order[r0 + pos] = (int32_t)(r0 + k);
+        job.order[r0 + pos] = (int32_t)(r0 + k);
     }
-    for (int64_t i = nr + tid; i < chunk; i += kOrderThreads) order[r0 + i] = -1;
+    for (int64_t i = nr + tid; i < job.chunk; i += kOrderThreads) job.order[r0 + i] = -1;
+}
+
+static OrderJob make_job(int64_t items, int64_t chunk, int per_head, int pairs, int n_k,
+                         int32_t* order) {
+    OrderJob j;
+    j.items = items;
+    j.chunk = chunk;
+    j.per_head = per_head;
+    j.pairs = pairs;
+    j.order = order;
+    // A chunk of `chunk` consecutive items touches at most this many heads.
+    const int64_t heads = (chunk + per_head - 1) / per_head + 1;
+    j.nk1 = n_k + 1;
+    if (heads * j.nk1 <= kOrderMaxBins) {
+        j.by_head = 1;
+        j.nbins = (int)(heads * j.nk1);
+    } else {
+        j.by_head = 0;
+        j.nk1 = j.nk1 < kOrderMaxBins ? j.nk1 : kOrderMaxBins;
+        j.nbins = j.nk1;
+    }
+    return j;
 }
 
 hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n_k, int64_t chunk,
-                                int32_t* order, hipStream_t stream) {
+                                int32_t* order, int64_t pchunk, int32_t* porder,
+                                hipStream_t stream) {
     if (R <= 0 || n_q <= 0 || n_k <= 0 || chunk <= 0 || 8 * chunk < R) return hipErrorInvalidValue;
-    // A chunk of `chunk` consecutive rows touches at most this many heads.
-    const int64_t heads = (chunk + n_q - 1) / n_q + 1;
-    int nk1 = n_k + 1, by_head = 0, nbins;
-    if (heads * nk1 <= kOrderMaxBins) {
-        by_head = 1;
-        nbins = (int)(heads * nk1);
-    } else {
-        nk1 = nk1 < kOrderMaxBins ? nk1 : kOrderMaxBins;
-        nbins = nk1;
-    }
-    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(kOrderThreads), 0, stream, counts, R, chunk, n_q,
-                       nk1, by_head, nbins, order);
+    const int hq = (n_q + 1) / 2;
+    const int64_t P = R / n_q * hq;
+    if (pchunk <= 0 || 8 * pchunk < P) return hipErrorInvalidValue;
+    const OrderJob rj = make_job(R, chunk, n_q, 0, n_k, order);
+    const OrderJob pj = make_job(P, pchunk, hq, 1, n_k, porder);
+    hipLaunchKernelGGL(order_kernel, dim3(16), dim3(kOrderThreads), 0, stream, counts, n_q, rj, pj);
     return hipGetLastError();
 }
 

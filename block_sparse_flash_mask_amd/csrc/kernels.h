@@ -13,12 +13,19 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t*
                                int32_t* lists, hipStream_t stream);
 hipError_t launch_compact_scan(const int32_t* counts, int64_t R, int32_t* row_ptr,
                                hipStream_t stream);
-// Dispatch order of mask rows per XCD chunk of `chunk` rows (8 * chunk >= R):
-// head by head, longest row first within a head; order has 8 * chunk entries.
+// Dispatch orders per XCD chunk (head by head, longest first within a head):
+// of the R mask rows in chunks of `chunk` (order: 8 * chunk entries), and of the
+// B*H*ceil(n_q/2) pairs of adjacent rows (rows 2j, 2j+1 of a head, keyed by the
+// longer of the two) in chunks of `pchunk` (porder: 8 * pchunk entries).
 hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n_k, int64_t chunk,
-                                int32_t* order, hipStream_t stream);
+                                int32_t* order, int64_t pchunk, int32_t* porder,
+                                hipStream_t stream);
 hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int64_t R, int n_k,
                                const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
+// Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block
+// lists in LDS, so they take masks of at most this many key blocks per row.
+constexpr int kPairMaxBlocks = 2048;
 
 // One compiled attention variant.
 struct Variant {

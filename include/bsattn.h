@@ -58,7 +58,11 @@ typedef enum {
 } bsattn_status;
 
 /* Kernel tiling of the attention kernel (the autotuner's search space).
- *   tile_q  query rows per workgroup: 64 or 128, must divide block_q;
+ *   tile_q  query rows per workgroup: 64 or 128, must divide block_q; or 256
+ *           with block_q 128: a workgroup takes two adjacent mask rows of a head
+ *           (query blocks 2j and 2j+1), loads each K/V tile of the union of
+ *           their block lists once for both, and each row computes only its own
+ *           blocks (at most 2048 key blocks per row);
  *   tile_k  keys per inner step: 32, 64 or 128, must divide block_k;
  *   waves   wavefronts per workgroup (64 lanes each); a wave owns 32 or 64
  *           query rows, so waves is tile_q / 32 or tile_q / 64, or 8 with
@@ -149,7 +153,12 @@ int bsattn_fwd_config(const void* q, const void* k, const void* v, const uint8_t
  *   lists[R][n_k]          at byte A(4R), row i's kj in lists[i][0 .. counts[i]);
  *   order[8 * ceil(R/8)]   at byte A(4R) + A(4 R n_k): chunk x is
  *                          order[x*ceil(R/8) ..], its rows in the order above,
- *                          then -1 past the last row.
+ *                          then -1 past the last row;
+ *   porder[8 * ceil(P/8)]  at byte A(4R) + A(4 R n_k) + A(4 * 8 ceil(R/8)): the
+ *                          same for the P = B*H*ceil(S/block_q / 2) pairs of
+ *                          query blocks (2j, 2j+1) of a head, pair index
+ *                          (b*H + h)*ceil(S/block_q / 2) + j, keyed by the
+ *                          longer list of the two (used by tile_q 256).
  * The plan depends only on block_mask and (B, H, S,
  * block_q, block_k), never on q/k/v, D, dtype, scale or the tile config, so one
  * plan serves every call that shares the mask (the block mask is fixed ahead of

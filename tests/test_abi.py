@@ -50,13 +50,17 @@ def test_version(lib):
 
 
 def test_workspace_sizes(lib):
-    # counts (R int32) + lists (R*n_k int32) + dispatch order (8 chunks of ceil(R/8)
-    # mask rows, int32), each rounded up to 256 bytes
+    # counts (R int32) + lists (R*n_k int32) + dispatch order of the rows (8 chunks
+    # of ceil(R/8), int32) + that of the row pairs (8 chunks of ceil(P/8)), each
+    # rounded up to 256 bytes
     rnd = lambda x: (x + 255) // 256 * 256
     for B, H, S, bq, bk in ((4, 16, 2048, 128, 128), (1, 3, 640, 64, 128), (1, 1, 64, 64, 64)):
         R, nk = B * H * (S // bq), S // bk
+        P = B * H * ((S // bq + 1) // 2)
         order = 8 * ((R + 7) // 8) * 4
-        assert bs.workspace_size(B, H, S, bq, bk) == rnd(R * 4) + rnd(R * nk * 4) + rnd(order)
+        porder = 8 * ((P + 7) // 8) * 4
+        assert bs.workspace_size(B, H, S, bq, bk) == (rnd(R * 4) + rnd(R * nk * 4) + rnd(order)
+                                                      + rnd(porder))
     assert bs.compact_workspace_size(1, 2, 3, 5) == rnd(6 * 4) + rnd(30 * 4)
     n = ctypes.c_size_t()
     assert lib.bsattn_workspace_size(1, 1, 100, 64, 64, ctypes.byref(n)) == SHAPE
@@ -68,9 +72,11 @@ def test_workspace_sizes(lib):
 def test_list_configs(lib):
     import torch
     c = bs.list_configs(torch.bfloat16, 128, 128, 128)
-    assert c and all(t.tile_q in (64, 128) and t.tile_k in (32, 64, 128) for t in c)
+    assert c and all(t.tile_q in (64, 128, 256) and t.tile_k in (32, 64, 128) for t in c)
     # a wave owns 32 or 64 query rows; the 8-wave two-group kernel has two waves per 32 rows
     assert all(t.tile_q in (16 * t.waves, 32 * t.waves, 64 * t.waves) and t.stages in (1, 2, 3) for t in c)
+    assert any(t.tile_q == 256 for t in c)  # row pairs, block_q 128 only
+    assert not any(t.tile_q == 256 for t in bs.list_configs(torch.bfloat16, 128, 64, 128))
     assert all(t.tile_q <= 64 for t in bs.list_configs(torch.bfloat16, 64, 64, 128))
     assert all(t.tile_k <= 64 for t in bs.list_configs(torch.float32, 64, 64, 64))
     n = ctypes.c_int()

@@ -79,8 +79,31 @@ def _check_plan(mask, block_q=128, block_k=128):
     lists = w[_rnd(4 * R) // 4:][:R * n_k].reshape(R, n_k)
     chunk = (R + 7) // 8
     order = w[(_rnd(4 * R) + _rnd(4 * R * n_k)) // 4:][:8 * chunk]
+    hq = (n_q + 1) // 2
+    P = B * H * hq
+    pchunk = (P + 7) // 8
+    porder = w[(_rnd(4 * R) + _rnd(4 * R * n_k) + _rnd(4 * 8 * chunk)) // 4:][:8 * pchunk]
     orp, oci = oracle.compact(mask)
     assert np.array_equal(counts, np.diff(orp))
+    # pair order: each chunk holds its own pairs, by head, then by the longer list
+    cnt_r = np.diff(orp)
+    for x in range(8):
+        p0, p1 = min(x * pchunk, P), min((x + 1) * pchunk, P)
+        got = porder[x * pchunk:(x + 1) * pchunk]
+        npr = p1 - p0
+        assert np.array_equal(np.sort(got[:npr]), np.arange(p0, p1)), ("pairs", x)
+        assert np.all(got[npr:] == -1), ("pairs", x)
+        pr = got[:npr]
+        bh, j = pr // hq, pr % hq
+        ra = bh * n_q + 2 * j
+        cb = np.where(2 * j + 1 < n_q, cnt_r[np.minimum(ra + 1, R - 1)], 0)
+        c = np.maximum(cnt_r[ra], cb)
+        if ((pchunk + hq - 1) // hq + 1) * (n_k + 1) <= 4096:
+            assert np.all(bh[:-1] <= bh[1:]), ("pairs", x)
+            same = bh[:-1] == bh[1:]
+            assert np.all(c[:-1][same] >= c[1:][same]), ("pairs", x)
+        else:
+            assert np.all(c[:-1] >= c[1:]), ("pairs", x)
     for i in range(R):
         assert np.array_equal(lists[i, :counts[i]], oci[orp[i]:orp[i + 1]]), i
     for x in range(8):

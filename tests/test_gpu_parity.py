@@ -139,6 +139,36 @@ def test_long_rows_every_config(bk):
         compare(out.reshape(-1, D)[idx], lse.reshape(-1)[idx], ro, rl, "bf16", "long rows %s" % (cfg,))
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_row_pair_edge_cases(D):
+    """Row-pair configs (tile_q 256): both rows of a pair empty, one empty, an odd
+    number of query blocks (last pair has one row), lists that differ, every
+    pair config; whole output against the oracle, and fwd_compacted agrees."""
+    ensure_built()
+    B, H, S, b = 1, 2, 640, 128
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=61)
+    n = S // b
+    mask = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    mask[0, 0, 2, :] = 1          # pair 0 of head 0: both rows empty; pair 1: row 3 empty
+    mask[0, 0, 4, 1] = 1          # pair 2: one row (n_q odd), one block
+    g = torch.Generator().manual_seed(62)
+    mask[0, 1] = (torch.rand(n, n, generator=g) < 0.4).to(torch.uint8)
+    mask[0, 1, 1] = 0
+    mask[0, 1, 1, 4] = 1          # rows 0/1 of head 1: very different lists
+    ro, rl = oracle.fwd(q, k, v, mask, b, b, 0.1)
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    rp, ci = bs.compact_mask(md)
+    cfgs = [c for c in bs.list_configs(torch.bfloat16, D, b, b) if c.tile_q == 256]
+    assert cfgs
+    for cfg in cfgs:
+        say("row pairs", D, cfg)
+        out, lse = bs.fwd(qd, kd, vd, md, b, b, 0.1, config=cfg)
+        o2, l2 = bs.fwd_compacted(qd, kd, vd, rp, ci, b, b, 0.1, config=cfg)
+        torch.cuda.synchronize()
+        compare(out, lse, ro, rl, "bf16", "pairs %s" % (cfg,))
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 def test_compacted_matches_fwd():
     ensure_built()
     B, H, S, D, b = 1, 4, 512, 128, 128
