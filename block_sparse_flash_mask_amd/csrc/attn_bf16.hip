@@ -79,7 +79,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     block_work(a, r, sub);
     if (r < 0) return;
     const int sh = a.steps_log2;  // kernel steps per key block = 1 << sh
-    int bh, qi, beg = 0, cnt;
+    int bh, qi, qi0, beg = 0, cnt;
     bool row_ok = true;  // this wave's query rows exist (false: second row of a pair past n_q)
     int q_row0;          // this lane's query row in each of the wave's NQ 32-row tiles
     // Row pairs: the workgroup runs over the union of the two rows' key-block lists,
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         bh = r / hq;
         const int j = r - bh * hq;
         qi = 2 * j + grp;
+        qi0 = 2 * j;
         row_ok = qi < a.n_q;
         const int ra = bh * a.n_q + 2 * j;
         const bool has_b = 2 * j + 1 < a.n_q;
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     } else {
         bh = r / a.n_q;
         qi = r - bh * a.n_q;
+        qi0 = qi;
         row_list(a, r, beg, cnt);
         q_row0 = qi * a.block_q + sub * TQ + wave * 32 * NQ + l32;
     }
@@ -157,8 +159,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     bf16x8 qf[NQ][KS];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-        // (a missing second row of a pair reads its partner's rows, never used)
-        const int qr = row_ok ? q_row0 + 32 * n : q_row0 - a.block_q;
+        // (a missing row of a row group reads the group's first row, which
+        // always exists; those values are never used)
+        const int qr = row_ok ? q_row0 + 32 * n : q_row0 - (qi - qi0) * a.block_q;
         const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)qr * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -486,6 +489,7 @@ static const Variant kBf16Variants[] = {
     BSATTN_BF16_VARIANT(128, 1, 32, 2, 0, 3, 1),
     {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
     BSATTN_BF16_PAIR(128, 32, 3, 2), BSATTN_BF16_PAIR(128, 64, 3, 2),
+    BSATTN_BF16_PAIR(128, 64, 2, 2), BSATTN_BF16_PAIR(128, 128, 2, 2),
     BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 4, 32, 1, 1, 2, 2),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
     BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),
