@@ -92,6 +92,8 @@ int check_fwd_shape(int B, int H, int S, int D, int block_q, int block_k, int dt
     const int rc = check_grid(B, H, S / block_q, S / block_k);
     if (rc) return rc;
     if ((int64_t)B * H * S * D >= ((int64_t)1 << 40)) return BSATTN_ERR_SHAPE;
+    // One head of K or V is read through a buffer descriptor with a 32-bit range.
+    if ((int64_t)S * D * 4 >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
     return BSATTN_OK;
 }
 

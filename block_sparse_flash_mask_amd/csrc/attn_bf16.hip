@@ -28,8 +28,8 @@
 // K rows enter the first MFMA in a bit-swapped order (kperm) so that the keys a
 // lane holds after it are exactly the keys the second MFMA wants in that lane.
 //
-// Memory path.  K and V tiles go HBM -> LDS by direct DMA (global_load_lds, 16 B
-// per lane), no VGPR staging.  Both are stored in LDS in the order the MFMA
+// Memory path.  K and V tiles go HBM -> LDS by direct DMA (buffer loads with the
+// LDS flag, 16 B per lane), no VGPR staging.  Both are stored in LDS in the order the MFMA
 // operand reads consume them:
 //   K: one 1 KiB block per (32-key tile mt, 16-deep k-step ks); lane l's 16 bytes
 //      at l*16 are K[32mt + kperm(l%32)][16ks + 8(l/32) .. +7];
@@ -198,22 +198,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         return kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
     };
 
-    // HBM -> LDS DMA of one K tile or one V tile (keys key0 .. key0+TK-1).
+    // HBM -> LDS DMA of one K tile or one V tile (keys key0 .. key0+TK-1), as raw
+    // buffer loads over this head's K (or V): the per-lane byte offset is fixed,
+    // the uniform part goes in the scalar offset (no per-step VALU address math).
+    const int nrec = a.S * D * 2;
+    const int k_voff = plan.k_lane * 2, v_voff = plan.v_lane * 2;
     auto issue_k = [&](int key0, uint8_t* kbuf) {
-        const uint16_t* kt = kg + (size_t)key0 * D;
 #pragma unroll
         for (int i = 0; i < P::NK; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(kt + P::k_uniform(wave_s, i) + plan.k_lane),
-                                             (BSATTN_LDS void*)(kbuf + (wave_s + i * WAVES) * 1024),
-                                             16, 0, 0);
+            dma16(kg, nrec, (BSATTN_LDS void*)(kbuf + (wave_s + i * WAVES) * 1024), k_voff,
+                  (key0 * D + P::k_uniform(wave_s, i)) * 2);
     };
     auto issue_v = [&](int key0, uint8_t* vbuf) {
-        const uint16_t* vt = vg + (size_t)key0 * D;
 #pragma unroll
         for (int i = 0; i < P::NV; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(vt + P::v_uniform(wave_s, i) + plan.v_lane),
-                                             (BSATTN_LDS void*)(vbuf + (wave_s + i * WAVES) * 1024),
-                                             16, 0, 0);
+            dma16(vg, nrec, (BSATTN_LDS void*)(vbuf + (wave_s + i * WAVES) * 1024), v_voff,
+                  (key0 * D + P::v_uniform(wave_s, i)) * 2);
     };
 
     float m_run[NQ];  // reference max per query tile (base-2, scaled units)

@@ -47,7 +47,9 @@ typedef enum {
     BSATTN_OK = 0,
     BSATTN_ERR_NULL = 1,        /* a required pointer is NULL */
     BSATTN_ERR_SHAPE = 2,       /* a size <= 0, S not divisible by a block size,
-                                   or an index would overflow int32 */
+                                   an index would overflow int32, B*H*S*D >= 2^40,
+                                   or S*D*4 >= 2^31 (one head is read through a
+                                   buffer with a 32-bit byte range) */
     BSATTN_ERR_UNSUPPORTED = 3, /* D, dtype, block size or tile config not built */
     BSATTN_ERR_ALIGN = 4,       /* q/k/v/out not 16-byte or lse not 4-byte aligned */
     BSATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */

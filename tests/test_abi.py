@@ -111,6 +111,15 @@ def test_fwd_argument_checks(lib, kw, code):
     assert _fwd(lib, **kw) == code
 
 
+def test_fwd_head_size_limit(lib):
+    """One head of K/V is read through a buffer with a 32-bit byte range, so S*D*4
+    must stay below 2^31 (the sizes just under pass the shape checks and then fail
+    on the fake, overlapping pointers)."""
+    kw = dict(D=128, bq=128, bk=128)
+    assert _fwd(lib, S=(1 << 22) - 128, **kw) not in (OK, SHAPE)
+    assert _fwd(lib, S=1 << 22, **kw) == SHAPE
+
+
 def test_env_config_parse_error(lib, monkeypatch):
     monkeypatch.setenv("BSATTN_CONFIG", "not-a-config")
     assert _fwd(lib) == UNSUP
