@@ -193,7 +193,7 @@ def main():
     traffic = traffic_from_profiles(w.name, cfg)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": traffic,
-                "kernel": ("attn_bf16_pp_kernel" if cfg[2] == 8 else "attn_bf16_kernel") if bf16
+                "kernel": ("attn_bf16_pp_kernel" if cfg[0] == 128 and cfg[2] == 8 else "attn_bf16_kernel") if bf16
                           else "attn_f32_kernel",
                 "kernel_ms": ms_attn}
     if traffic:

@@ -399,10 +399,9 @@ int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     int32_t* counts = (int32_t*)ws;
-    hipError_t e = launch_compact_rows(block_mask, L.R, n_k, counts, (int32_t*)(ws + L.lists), s);
-    if (e != hipSuccess) return hip_fail(e);
-    e = launch_compact_order(counts, L.R, n_q, n_k, L.chunk, (int32_t*)(ws + L.order), L.pchunk,
-                             (int32_t*)(ws + L.porder), s);
+    const hipError_t e = launch_plan(block_mask, L.R, n_q, n_k, counts, (int32_t*)(ws + L.lists),
+                                     L.chunk, (int32_t*)(ws + L.order), L.pchunk,
+                                     (int32_t*)(ws + L.porder), s);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }

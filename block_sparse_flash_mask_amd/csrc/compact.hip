@@ -152,32 +152,16 @@ struct OrderJob {
     int32_t* order;
 };
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
-                                                              int n_q, OrderJob rows_job,
-                                                              OrderJob pairs_job) {
-    __shared__ int hist[kOrderMaxBins];
-    __shared__ int wave_tot[kOrderThreads / kWave];
-    const OrderJob& job = blockIdx.x < 8 ? rows_job : pairs_job;
+// Counting sort of chunk x of a job (one workgroup of kOrderThreads): a
+// histogram of the keys in LDS, an exclusive scan of it, then a scatter.
+// key_of(k) is the sort key of item r0 + k (it may be called twice per item).
+template <class KeyOf>
+__device__ void sort_chunk(const OrderJob& job, int64_t r0, int64_t nr, KeyOf key_of, int* hist,
+                           int* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t r0 = (int64_t)(blockIdx.x & 7) * job.chunk;
-    const int64_t nr = r0 >= job.items ? 0 : (job.items - r0 < job.chunk ? job.items - r0 : job.chunk);
-    const int64_t h0 = r0 / job.per_head;
-    auto count_of = [&](int64_t i) -> int {
-        if (!job.pairs) return counts[i];
-        const int64_t bh = i / job.per_head;
-        const int j = (int)(i - bh * job.per_head);
-        const int64_t ra = bh * n_q + 2 * j;
-        const int ca = counts[ra];
-        const int cb = 2 * j + 1 < n_q ? counts[ra + 1] : 0;
-        return ca > cb ? ca : cb;
-    };
-    auto key = [&](int64_t k) {
-        const int hl = job.by_head ? (int)((r0 + k) / job.per_head - h0) : 0;
-        return order_bin(count_of(r0 + k), hl, job.nk1);
-    };
     for (int b = tid; b < job.nbins; b += kOrderThreads) hist[b] = 0;
     __syncthreads();
-    for (int64_t k = tid; k < nr; k += kOrderThreads) atomicAdd(&hist[key(k)], 1);
+    for (int64_t k = tid; k < nr; k += kOrderThreads) atomicAdd(&hist[key_of(k)], 1);
     __syncthreads();
     // Exclusive scan of hist: each thread owns a run of consecutive bins.
     const int nbins = job.nbins;
@@ -202,10 +186,110 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     }
     __syncthreads();
     for (int64_t k = tid; k < nr; k += kOrderThreads) {
-        const int pos = atomicAdd(&hist[key(k)], 1);
+        const int pos = atomicAdd(&hist[key_of(k)], 1);
         job.order[r0 + pos] = (int32_t)(r0 + k);
     }
     for (int64_t i = nr + tid; i < job.chunk; i += kOrderThreads) job.order[r0 + i] = -1;
+}
+
+// Rows (or pairs) r0 .. r0 + nr - 1 of chunk x of a job.
+__device__ __forceinline__ void chunk_range(const OrderJob& job, int x, int64_t& r0, int64_t& nr) {
+    r0 = (int64_t)x * job.chunk;
+    nr = r0 >= job.items ? 0 : (job.items - r0 < job.chunk ? job.items - r0 : job.chunk);
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
+                                                              int n_q, OrderJob rows_job,
+                                                              OrderJob pairs_job) {
+    __shared__ int hist[kOrderMaxBins];
+    __shared__ int wave_tot[kOrderThreads / kWave];
+    const OrderJob& job = blockIdx.x < 8 ? rows_job : pairs_job;
+    int64_t r0, nr;
+    chunk_range(job, blockIdx.x & 7, r0, nr);
+    const int64_t h0 = r0 / job.per_head;
+    auto count_of = [&](int64_t i) -> int {
+        if (!job.pairs) return counts[i];
+        const int64_t bh = i / job.per_head;
+        const int j = (int)(i - bh * job.per_head);
+        const int64_t ra = bh * n_q + 2 * j;
+        const int ca = counts[ra];
+        const int cb = 2 * j + 1 < n_q ? counts[ra + 1] : 0;
+        return ca > cb ? ca : cb;
+    };
+    auto key = [&](int64_t k) {
+        const int hl = job.by_head ? (int)((r0 + k) / job.per_head - h0) : 0;
+        return order_bin(count_of(r0 + k), hl, job.nk1);
+    };
+    sort_chunk(job, r0, nr, key, hist, wave_tot);
+}
+
+// Active blocks of one mask row, counted by a whole wave (wave-uniform result).
+__device__ __forceinline__ int mask_row_count(const uint8_t* __restrict__ mrow, int n_k, int lane) {
+    int c = 0;
+    for (int s0 = 0; s0 < n_k; s0 += kWave) {
+        const int kj = s0 + lane;
+        c += __popcll(__ballot(kj < n_k && mrow[kj] != 0));
+    }
+    return c;
+}
+
+// The whole plan in one launch, for masks small enough that 16 workgroups can
+// count their chunks' rows straight from the mask in about the time the row
+// lists take.  Workgroups 0-15 run the two sorts (rows, pairs), counting the
+// active blocks of their own rows from the mask into an LDS key cache; the
+// others are rows_kernel with 16 mask rows (one per wave) each.
+constexpr int kPlanMaxChunk = 8192;
+constexpr int64_t kPlanMaxMaskBytes = (int64_t)4 << 20;
+
+__global__ __launch_bounds__(kOrderThreads) void plan_kernel(const uint8_t* __restrict__ mask,
+                                                             int64_t R, int n_q, int n_k,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ lists,
+                                                             OrderJob rows_job, OrderJob pairs_job) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (blockIdx.x >= 16) {
+        const int64_t r = (int64_t)(blockIdx.x - 16) * (kOrderThreads / kWave) + wave;
+        if (r >= R) return;  // wave-uniform
+        const uint8_t* mrow = mask + r * n_k;
+        int32_t* lrow = lists + r * n_k;
+        int base = 0;
+        for (int s0 = 0; s0 < n_k; s0 += kWave) {
+            const int kj = s0 + lane;
+            const bool active = kj < n_k && mrow[kj] != 0;
+            const uint64_t bal = __ballot(active);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+            if (active) lrow[base + below] = kj;
+            base += __popcll(bal);
+        }
+        if (lane == 0) counts[r] = base;
+        return;
+    }
+    __shared__ int hist[kOrderMaxBins];
+    __shared__ int wave_tot[kOrderThreads / kWave];
+    __shared__ int keys[kPlanMaxChunk];
+    const OrderJob& job = blockIdx.x < 8 ? rows_job : pairs_job;
+    int64_t r0, nr;
+    chunk_range(job, blockIdx.x & 7, r0, nr);
+    const int64_t h0 = r0 / job.per_head;
+    for (int64_t k = wave; k < nr; k += kOrderThreads / kWave) {
+        const int64_t i = r0 + k;
+        int c;
+        if (!job.pairs) {
+            c = mask_row_count(mask + i * n_k, n_k, lane);
+        } else {
+            const int64_t bh = i / job.per_head;
+            const int j = (int)(i - bh * job.per_head);
+            const int64_t ra = bh * n_q + 2 * j;
+            const int ca = mask_row_count(mask + ra * n_k, n_k, lane);
+            const int cb = 2 * j + 1 < n_q ? mask_row_count(mask + (ra + 1) * n_k, n_k, lane) : 0;
+            c = ca > cb ? ca : cb;
+        }
+        const int hl = job.by_head ? (int)(i / job.per_head - h0) : 0;
+        if (lane == 0) keys[k] = order_bin(c, hl, job.nk1);
+    }
+    __syncthreads();
+    sort_chunk(job, r0, nr, [&](int64_t k) { return keys[k]; }, hist, wave_tot);
 }
 
 static OrderJob make_job(int64_t items, int64_t chunk, int per_head, int pairs, int n_k,
@@ -240,6 +324,26 @@ hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n
     const OrderJob rj = make_job(R, chunk, n_q, 0, n_k, order);
     const OrderJob pj = make_job(P, pchunk, hq, 1, n_k, porder);
     hipLaunchKernelGGL(order_kernel, dim3(16), dim3(kOrderThreads), 0, stream, counts, n_q, rj, pj);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const uint8_t* mask, int64_t R, int n_q, int n_k, int32_t* counts,
+                       int32_t* lists, int64_t chunk, int32_t* order, int64_t pchunk,
+                       int32_t* porder, hipStream_t stream) {
+    if (R <= 0 || n_q <= 0 || n_k <= 0 || chunk <= 0 || 8 * chunk < R) return hipErrorInvalidValue;
+    const int hq = (n_q + 1) / 2;
+    const int64_t P = R / n_q * hq;
+    if (pchunk <= 0 || 8 * pchunk < P) return hipErrorInvalidValue;
+    if (R * n_k > kPlanMaxMaskBytes || chunk > kPlanMaxChunk || pchunk > kPlanMaxChunk) {
+        hipError_t e = launch_compact_rows(mask, R, n_k, counts, lists, stream);
+        if (e != hipSuccess) return e;
+        return launch_compact_order(counts, R, n_q, n_k, chunk, order, pchunk, porder, stream);
+    }
+    const OrderJob rj = make_job(R, chunk, n_q, 0, n_k, order);
+    const OrderJob pj = make_job(P, pchunk, hq, 1, n_k, porder);
+    const int64_t row_blocks = (R + kOrderThreads / kWave - 1) / (kOrderThreads / kWave);
+    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(16 + row_blocks)), dim3(kOrderThreads), 0, stream,
+                       mask, R, n_q, n_k, counts, lists, rj, pj);
     return hipGetLastError();
 }
 

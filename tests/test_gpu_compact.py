@@ -137,6 +137,8 @@ def test_plan_workloads(name):
     ((1, 2, 40, 40), 0.0, 3),      # all empty
     ((1, 4, 64, 64), 1.0, 4),      # all full: every count ties
     ((3, 5, 33, 33), 0.2, 5),
+    # a mask over 4 MiB: the row lists and the orders come from two launches
+    ((1, 8, 1024, 1024), 0.02, 8),
 ])
 def test_plan_random(shape, p, seed):
     g = torch.Generator().manual_seed(seed)
@@ -148,4 +150,11 @@ def test_plan_order_without_heads():
     """A chunk spanning 65 heads x 65 counts (> 4096 bins) is sorted by count alone."""
     g = torch.Generator().manual_seed(6)
     m = (torch.rand(4, 128, 128, 64, generator=g) < 0.1).to(torch.uint8)
+    _check_plan(m, 64, 128)
+
+
+def test_plan_large_chunks():
+    """More than 8192 rows per XCD chunk (131072 rows): the two-launch plan."""
+    g = torch.Generator().manual_seed(10)
+    m = (torch.rand(4, 128, 256, 128, generator=g) < 0.05).to(torch.uint8)
     _check_plan(m, 64, 128)
