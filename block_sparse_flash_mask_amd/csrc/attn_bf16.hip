@@ -471,7 +471,9 @@ static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t strea
 // built-in preference when no tuning result exists (the two-group and row-pair
 // kernels come last: they win only on particular shapes and masks).  NQ = 2 (64 query rows per
 // wave, each K/V fragment read from LDS feeding two MFMAs) runs one wave per
-// SIMD; NQ = 1 runs two or three.  PIPE = 1 overlaps the next tile's S MFMAs
+// SIMD; NQ = 1 runs two to five (OCC): with D = 64 the softmax is as much VALU
+// work as with D = 128 against half the MFMA work, and four or five waves per
+// SIMD hide it better than two.  PIPE = 1 overlaps the next tile's S MFMAs
 // with this tile's softmax inside a wave (two stages); PIPE = 0 runs the steps
 // in order with ST K/V stages resident in LDS.
 #define BSATTN_BF16_VARIANT(D, W, TK, NQ, PIPE, ST, OCC) \
@@ -490,13 +492,13 @@ static const Variant kBf16Variants[] = {
     {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
     BSATTN_BF16_PAIR(128, 32, 3, 2), BSATTN_BF16_PAIR(128, 64, 3, 2),
     BSATTN_BF16_PAIR(128, 64, 2, 2), BSATTN_BF16_PAIR(128, 128, 2, 2),
-    BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 1, 2, 2),
-    BSATTN_BF16_VARIANT(64, 4, 32, 1, 1, 2, 2),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
+    BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 2, 4),  BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 3, 3),
+    BSATTN_BF16_VARIANT(64, 4, 32, 1, 0, 2, 5),  BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 2, 2),
     BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),
     BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 2, 32, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 1, 64, 2, 0, 2, 1),
     {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
-    BSATTN_BF16_PAIR(64, 64, 3, 2), BSATTN_BF16_PAIR(64, 128, 2, 2),
+    BSATTN_BF16_PAIR(64, 64, 3, 4), BSATTN_BF16_PAIR(64, 64, 2, 4), BSATTN_BF16_PAIR(64, 128, 2, 2),
 };
 
 const Variant* bf16_variants(int* n) {

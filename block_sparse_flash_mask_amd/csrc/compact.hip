@@ -223,26 +223,42 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
     sort_chunk(job, r0, nr, key, hist, wave_tot);
 }
 
-// Active blocks of one mask row, counted by a whole wave (wave-uniform result).
-__device__ __forceinline__ int mask_row_count(const uint8_t* __restrict__ mrow, int n_k, int lane) {
+// Nonzero bytes of a 32-bit word: bit 7 of each byte of
+// ((x & 0x7f..) + 0x7f..) | x is set iff that byte is nonzero (no carry crosses
+// a byte).
+__device__ __forceinline__ int nonzero_bytes(uint32_t x) {
+    return __popc((((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u);
+}
+
+// Active blocks of one mask row, counted by one thread: 16-byte loads when the
+// rows are 16-byte aligned (vec = 16), 4-byte loads when 4-byte aligned
+// (vec = 4), else bytes.  The loads of a row are independent, so they overlap.
+__device__ __forceinline__ int mask_row_count(const uint8_t* __restrict__ mrow, int n_k, int vec) {
     int c = 0;
-    for (int s0 = 0; s0 < n_k; s0 += kWave) {
-        const int kj = s0 + lane;
-        c += __popcll(__ballot(kj < n_k && mrow[kj] != 0));
+    if (vec == 16) {
+        for (int b = 0; b < n_k; b += 16) {
+            const uint4 v = *(const uint4*)(mrow + b);
+            c += nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
+        }
+    } else if (vec == 4) {
+        for (int b = 0; b < n_k; b += 4) c += nonzero_bytes(*(const uint32_t*)(mrow + b));
+    } else {
+        for (int b = 0; b < n_k; ++b) c += mrow[b] != 0;
     }
     return c;
 }
 
 // The whole plan in one launch, for masks small enough that 16 workgroups can
 // count their chunks' rows straight from the mask in about the time the row
-// lists take.  Workgroups 0-15 run the two sorts (rows, pairs), counting the
-// active blocks of their own rows from the mask into an LDS key cache; the
-// others are rows_kernel with 16 mask rows (one per wave) each.
+// lists take.  Workgroups 0-15 run the two sorts (rows, pairs), each thread
+// counting the active blocks of one row (or both rows of one pair) of its
+// chunk from the mask into an LDS key cache; the others are rows_kernel with
+// 16 mask rows (one per wave) each.
 constexpr int kPlanMaxChunk = 8192;
 constexpr int64_t kPlanMaxMaskBytes = (int64_t)4 << 20;
 
 __global__ __launch_bounds__(kOrderThreads) void plan_kernel(const uint8_t* __restrict__ mask,
-                                                             int64_t R, int n_q, int n_k,
+                                                             int64_t R, int n_q, int n_k, int vec,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ lists,
                                                              OrderJob rows_job, OrderJob pairs_job) {
@@ -272,21 +288,21 @@ __global__ __launch_bounds__(kOrderThreads) void plan_kernel(const uint8_t* __re
     int64_t r0, nr;
     chunk_range(job, blockIdx.x & 7, r0, nr);
     const int64_t h0 = r0 / job.per_head;
-    for (int64_t k = wave; k < nr; k += kOrderThreads / kWave) {
+    for (int64_t k = tid; k < nr; k += kOrderThreads) {
         const int64_t i = r0 + k;
         int c;
         if (!job.pairs) {
-            c = mask_row_count(mask + i * n_k, n_k, lane);
+            c = mask_row_count(mask + i * n_k, n_k, vec);
         } else {
             const int64_t bh = i / job.per_head;
             const int j = (int)(i - bh * job.per_head);
             const int64_t ra = bh * n_q + 2 * j;
-            const int ca = mask_row_count(mask + ra * n_k, n_k, lane);
-            const int cb = 2 * j + 1 < n_q ? mask_row_count(mask + (ra + 1) * n_k, n_k, lane) : 0;
+            const int ca = mask_row_count(mask + ra * n_k, n_k, vec);
+            const int cb = 2 * j + 1 < n_q ? mask_row_count(mask + (ra + 1) * n_k, n_k, vec) : 0;
             c = ca > cb ? ca : cb;
         }
         const int hl = job.by_head ? (int)(i / job.per_head - h0) : 0;
-        if (lane == 0) keys[k] = order_bin(c, hl, job.nk1);
+        keys[k] = order_bin(c, hl, job.nk1);
     }
     __syncthreads();
     sort_chunk(job, r0, nr, [&](int64_t k) { return keys[k]; }, hist, wave_tot);
@@ -342,8 +358,10 @@ hipError_t launch_plan(const uint8_t* mask, int64_t R, int n_q, int n_k, int32_t
     const OrderJob rj = make_job(R, chunk, n_q, 0, n_k, order);
     const OrderJob pj = make_job(P, pchunk, hq, 1, n_k, porder);
     const int64_t row_blocks = (R + kOrderThreads / kWave - 1) / (kOrderThreads / kWave);
+    const uintptr_t mbase = (uintptr_t)mask;
+    const int vec = (mbase % 16 == 0 && n_k % 16 == 0) ? 16 : (mbase % 4 == 0 && n_k % 4 == 0) ? 4 : 1;
     hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(16 + row_blocks)), dim3(kOrderThreads), 0, stream,
-                       mask, R, n_q, n_k, counts, lists, rj, pj);
+                       mask, R, n_q, n_k, vec, counts, lists, rj, pj);
     return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ def _rnd(x):
     return (x + 255) // 256 * 256
 
 
-def _check_plan(mask, block_q=128, block_k=128):
+def _check_plan(mask, block_q=128, block_k=128, mask_dev=None):
     """bsattn_plan's three arrays: counts and lists equal the oracle's compaction
     bit for bit; each XCD chunk of the order holds exactly its own rows, then -1
     padding, head by head with each head's rows by non-increasing count (or by
@@ -71,7 +71,7 @@ def _check_plan(mask, block_q=128, block_k=128):
     S = n_q * block_q
     assert n_k * block_k == S
     say("plan", tuple(mask.shape), int(mask.sum()))
-    ws = bs.plan(mask.cuda(), S, block_q, block_k)
+    ws = bs.plan(mask.cuda() if mask_dev is None else mask_dev, S, block_q, block_k)
     torch.cuda.synchronize()
     w = ws.cpu().numpy().view(np.int32)
     R = B * H * n_q
@@ -137,6 +137,7 @@ def test_plan_workloads(name):
     ((1, 2, 40, 40), 0.0, 3),      # all empty
     ((1, 4, 64, 64), 1.0, 4),      # all full: every count ties
     ((3, 5, 33, 33), 0.2, 5),
+    ((2, 3, 20, 20), 0.4, 11),     # rows of 20 bytes: 4-byte mask loads
     # a mask over 4 MiB: the row lists and the orders come from two launches
     ((1, 8, 1024, 1024), 0.02, 8),
 ])
@@ -158,3 +159,14 @@ def test_plan_large_chunks():
     g = torch.Generator().manual_seed(10)
     m = (torch.rand(4, 128, 256, 128, generator=g) < 0.05).to(torch.uint8)
     _check_plan(m, 64, 128)
+
+
+def test_plan_unaligned_mask():
+    """A mask tensor starting at an odd address: the counts are read byte by byte."""
+    g = torch.Generator().manual_seed(12)
+    m = (torch.rand(2, 3, 32, 32, generator=g) < 0.3).to(torch.uint8)
+    big = torch.zeros(m.numel() + 1, dtype=torch.uint8, device="cuda")
+    view = big[1:].view(m.shape)
+    view.copy_(m.cuda())
+    assert view.data_ptr() % 2 == 1
+    _check_plan(m, mask_dev=view)
