@@ -254,8 +254,12 @@ __device__ __forceinline__ int mask_row_count(const uint8_t* __restrict__ mrow, 
 // counting the active blocks of one row (or both rows of one pair) of its
 // chunk from the mask into an LDS key cache; the others are rows_kernel with
 // 16 mask rows (one per wave) each.
+// Limits of the single launch: the mask size, and the row length (a thread reads
+// a whole row; longer rows than one or two cache lines per thread thrash the L1
+// when a wave reads 64 rows at once, and the two launches are faster).
 constexpr int kPlanMaxChunk = 8192;
 constexpr int64_t kPlanMaxMaskBytes = (int64_t)4 << 20;
+constexpr int kPlanMaxRowBytes = 128;
 
 __global__ __launch_bounds__(kOrderThreads) void plan_kernel(const uint8_t* __restrict__ mask,
                                                              int64_t R, int n_q, int n_k, int vec,
@@ -350,7 +354,8 @@ hipError_t launch_plan(const uint8_t* mask, int64_t R, int n_q, int n_k, int32_t
     const int hq = (n_q + 1) / 2;
     const int64_t P = R / n_q * hq;
     if (pchunk <= 0 || 8 * pchunk < P) return hipErrorInvalidValue;
-    if (R * n_k > kPlanMaxMaskBytes || chunk > kPlanMaxChunk || pchunk > kPlanMaxChunk) {
+    if (R * n_k > kPlanMaxMaskBytes || n_k > kPlanMaxRowBytes || chunk > kPlanMaxChunk ||
+        pchunk > kPlanMaxChunk) {
         hipError_t e = launch_compact_rows(mask, R, n_k, counts, lists, stream);
         if (e != hipSuccess) return e;
         return launch_compact_order(counts, R, n_q, n_k, chunk, order, pchunk, porder, stream);

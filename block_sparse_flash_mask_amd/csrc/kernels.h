@@ -21,8 +21,8 @@ hipError_t launch_compact_order(const int32_t* counts, int64_t R, int n_q, int n
                                 int32_t* order, int64_t pchunk, int32_t* porder,
                                 hipStream_t stream);
 // The plan of a forward pass (row counts and lists as launch_compact_rows, both
-// dispatch orders as launch_compact_order): one launch for masks of at most a
-// few MiB, else those two launches.
+// dispatch orders as launch_compact_order): one launch for masks of at most
+// 4 MiB with rows of at most 128 blocks, else those two launches.
 hipError_t launch_plan(const uint8_t* mask, int64_t R, int n_q, int n_k, int32_t* counts,
                        int32_t* lists, int64_t chunk, int32_t* order, int64_t pchunk,
                        int32_t* porder, hipStream_t stream);
