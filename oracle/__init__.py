@@ -59,6 +59,12 @@ def configure(lib):
     lib.oracle_fwd_rows.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32,
                                     p, i64, p, p, i32]
     lib.oracle_fwd_rows.restype = i32
+    lib.oracle_fwd_elem.argtypes = [p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                    f32, p, p, i32]
+    lib.oracle_fwd_elem.restype = i32
+    lib.oracle_fwd_rows_elem.argtypes = [p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64,
+                                         i64, f32, p, i64, p, p, i32]
+    lib.oracle_fwd_rows_elem.restype = i32
     lib.oracle_probs.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p]
     lib.oracle_probs.restype = i32
     lib.oracle_compact.argtypes = [p, i64, i64, p, p]
@@ -154,6 +160,72 @@ def fwd_rows(q, k, v, mask, block_q, block_k, scale, rows, nthreads=0):
                              rows.ctypes.data, n, out.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc:
         raise ValueError("oracle_fwd_rows failed with code %d" % rc)
+    return out, lse
+
+
+def _elem_args(states, pidx, pbits, B, H, n_q, n_k, block_q, block_k):
+    """Raw block states (uint8, 0 empty / 1 full / else partial), tile index per
+    block (int32) and bit tiles (uint32 [n_tiles, block_q, block_k / 32])."""
+    try:
+        import torch
+        conv = lambda x: x.contiguous().numpy() if isinstance(x, torch.Tensor) else x
+    except ImportError:  # pragma: no cover
+        conv = lambda x: x
+    st = np.ascontiguousarray(conv(states), dtype=np.uint8)
+    pi = np.ascontiguousarray(conv(pidx), dtype=np.int32)
+    pb = np.ascontiguousarray(conv(pbits))
+    if pb.dtype != np.uint32:
+        pb = pb.astype(np.int64).astype(np.uint32)
+    if st.shape != (B, H, n_q, n_k) or pi.shape != (B, H, n_q, n_k):
+        raise ValueError("states / pidx must be [B, H, S/block_q, S/block_k]")
+    if pb.ndim != 3 or pb.shape[1:] != (block_q, block_k // 32):
+        raise ValueError("pbits must be [n_tiles, block_q, block_k / 32]")
+    if pb.shape[0] == 0:
+        pb = np.zeros((1, block_q, block_k // 32), dtype=np.uint32)
+        return st, pi, pb, 0
+    return st, pi, pb, pb.shape[0]
+
+
+def fwd_elem(q, k, v, states, pidx, pbits, block_q, block_k, scale, nthreads=0):
+    """Full forward with an element-level mask (block states + bit tiles; see the
+    header of oracle.c).  Returns (out float64 [B,H,S,D], lse float64 [B,H,S])."""
+    lib = _load()
+    qa, dt = _as_raw(q)
+    ka, _ = _as_raw(k)
+    va, _ = _as_raw(v)
+    B, H, S, D = qa.shape
+    st, pi, pb, nt = _elem_args(states, pidx, pbits, B, H, S // block_q, S // block_k,
+                                block_q, block_k)
+    out = np.empty((B, H, S, D), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    rc = lib.oracle_fwd_elem(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, st.ctypes.data,
+                             pi.ctypes.data, pb.ctypes.data, nt, B, H, S, D, block_q, block_k,
+                             float(np.float32(scale)), out.ctypes.data, lse.ctypes.data,
+                             int(nthreads))
+    if rc:
+        raise ValueError("oracle_fwd_elem failed with code %d" % rc)
+    return out, lse
+
+
+def fwd_rows_elem(q, k, v, states, pidx, pbits, block_q, block_k, scale, rows, nthreads=0):
+    """Selected rows (flat (b*H + h)*S + s) of fwd_elem: (out [n, D], lse [n])."""
+    lib = _load()
+    qa, dt = _as_raw(q)
+    ka, _ = _as_raw(k)
+    va, _ = _as_raw(v)
+    B, H, S, D = qa.shape
+    st, pi, pb, nt = _elem_args(states, pidx, pbits, B, H, S // block_q, S // block_k,
+                                block_q, block_k)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    out = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_fwd_rows_elem(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                                  st.ctypes.data, pi.ctypes.data, pb.ctypes.data, nt, B, H, S, D,
+                                  block_q, block_k, float(np.float32(scale)), rows.ctypes.data, n,
+                                  out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_fwd_rows_elem failed with code %d" % rc)
     return out, lse
 
 

@@ -39,6 +39,17 @@
  * Compaction (the block-list form of the mask): for each mask row in (b, h, qi)
  * row-major order, the ascending list of kj with mask != 0; row_ptr[0] = 0 and
  * row_ptr[r+1] = row_ptr[r] + count of row r.
+ *
+ * Element-level masks (the *_elem entry points).  The mask the pages load per
+ * (query block, key block) is an element tile: "Writing Pallas Kernels for JAX",
+ * section "Writing the Kernel Logic: Load, Compute, Store", keeps a score where
+ * the mask tile is set and pushes it to -inf elsewhere.  Reading: a block of the
+ * block mask is empty (0: every element masked), full (1: every element kept) or
+ * partial (any other value: element (i, j) of the block is kept iff bit j % 32 of
+ * word j / 32 of row i of bit tile pidx[block] is set, the tiles being
+ * pbits[n_tiles][block_q][block_k / 32]).  Everything else is as above, with the
+ * kept elements in place of the active keys; a row with no kept element has
+ * out = 0 and lse = -inf.
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,6 +70,10 @@ typedef struct {
     int64_t B, H, S, D;
     int64_t block_q, block_k, n_q, n_k;
     double scale;
+    /* element-level masks: NULL pidx means the block mask alone decides */
+    const int32_t* pidx;
+    const uint32_t* pbits;
+    int64_t n_tiles;
 } problem;
 
 /* Exact widening of one element to double.  bf16 is the top 16 bits of an fp32. */
@@ -79,7 +94,24 @@ static int check(const problem* p) {
     if (p->block_q <= 0 || p->block_k <= 0) return 2;
     if (p->S % p->block_q != 0 || p->S % p->block_k != 0) return 2;
     if (p->dtype < ORC_F32 || p->dtype > ORC_F64) return 3;
+    if (p->pidx) {
+        if (!p->pbits || p->n_tiles < 0 || p->block_k % 32 != 0) return 4;
+        /* every partial block must name an existing tile */
+        const int64_t nb = p->B * p->H * p->n_q * p->n_k;
+        for (int64_t i = 0; i < nb; ++i)
+            if (p->mask[i] > 1 && (p->pidx[i] < 0 || p->pidx[i] >= p->n_tiles)) return 4;
+    }
     return 0;
+}
+
+/* Is key j kept for query s?  blk is the mask value of (s's query block, j's key
+ * block), bi that block's flat index. */
+static int kept(const problem* p, uint8_t blk, int64_t bi, int64_t s, int64_t j) {
+    if (blk == 0) return 0;
+    if (!p->pidx || blk == 1) return 1;
+    const int64_t i = s % p->block_q, c = j % p->block_k;
+    const uint32_t w = p->pbits[((int64_t)p->pidx[bi] * p->block_q + i) * (p->block_k / 32) + c / 32];
+    return (int)((w >> (c % 32)) & 1u);
 }
 
 /* One query row: bh = b*H + h, s = query position.  sbuf holds S doubles,
@@ -91,12 +123,15 @@ static void oracle_row(const problem* p, int64_t bh, int64_t s, double* out_row,
     const uint8_t* mrow = p->mask + (bh * p->n_q + qi) * p->n_k;
     const int64_t qbase = (bh * p->S + s) * D;
 
+    const int64_t brow = (bh * p->n_q + qi) * p->n_k;
+
     /* pass 1: scores of the active keys, ascending, and their max */
     int64_t n = 0;
     double m = -INFINITY;
     for (int64_t kj = 0; kj < p->n_k; ++kj) {
         if (!mrow[kj]) continue;
         for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;
             const int64_t kbase = (bh * p->S + j) * D;
             double dot = 0.0;
             for (int64_t d = 0; d < D; ++d)
@@ -123,6 +158,7 @@ static void oracle_row(const problem* p, int64_t bh, int64_t s, double* out_row,
     for (int64_t kj = 0; kj < p->n_k; ++kj) {
         if (!mrow[kj]) continue;
         for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;
             const int64_t vbase = (bh * p->S + j) * D;
             const double e = sbuf[t++];
             for (int64_t d = 0; d < D; ++d) acc[d] += e * widen(p->v, p->dtype, vbase + d);
@@ -150,20 +186,22 @@ static problem make_problem(const void* q, const void* k, const void* v, int dty
     p.n_q = block_q > 0 ? S / block_q : 0;
     p.n_k = block_k > 0 ? S / block_k : 0;
     p.scale = (double)scale;
+    p.pidx = NULL;
+    p.pbits = NULL;
+    p.n_tiles = 0;
     return p;
 }
 
 /* Full forward: out is double[B][H][S][D], lse is double[B][H][S].
  * Returns 0 on success, nonzero on a bad argument (nothing written). */
-int oracle_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
-               int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
-               float scale, double* out, double* lse, int nthreads) {
-    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+static int run_fwd(const problem* pp, double* out, double* lse, int nthreads) {
+    const problem p = *pp;
+    const int64_t S = p.S, D = p.D;
     int rc = check(&p);
     if (rc) return rc;
     if (!out || !lse) return 1;
     set_threads(nthreads);
-    const int64_t rows = B * H * S;
+    const int64_t rows = p.B * p.H * S;
     int failed = 0;
 #pragma omp parallel
     {
@@ -183,18 +221,38 @@ int oracle_fwd(const void* q, const void* k, const void* v, int dtype, const uin
     return failed ? 9 : 0;
 }
 
+int oracle_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+               int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+               float scale, double* out, double* lse, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    return run_fwd(&p, out, lse, nthreads);
+}
+
+/* Element-level masks: mask holds block states (0 empty, 1 full, else partial),
+ * pidx[B][H][n_q][n_k] the bit tile of each partial block, pbits the tiles. */
+int oracle_fwd_elem(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+                    const int32_t* pidx, const uint32_t* pbits, int64_t n_tiles, int64_t B,
+                    int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k, float scale,
+                    double* out, double* lse, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    if (!pidx) return 1;
+    p.pidx = pidx;
+    p.pbits = pbits;
+    p.n_tiles = n_tiles;
+    return run_fwd(&p, out, lse, nthreads);
+}
+
 /* Selected rows only: rows[i] is a flat row index (b*H + h)*S + s.
  * out_rows is double[n_rows][D], lse_rows is double[n_rows]. */
-int oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
-                    int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
-                    float scale, const int64_t* rows, int64_t n_rows, double* out_rows,
+static int run_rows(const problem* pp, const int64_t* rows, int64_t n_rows, double* out_rows,
                     double* lse_rows, int nthreads) {
-    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    const problem p = *pp;
+    const int64_t S = p.S, D = p.D;
     int rc = check(&p);
     if (rc) return rc;
     if (!rows || !out_rows || !lse_rows) return 1;
     for (int64_t i = 0; i < n_rows; ++i)
-        if (rows[i] < 0 || rows[i] >= B * H * S) return 2;
+        if (rows[i] < 0 || rows[i] >= p.B * p.H * S) return 2;
     set_threads(nthreads);
     int failed = 0;
 #pragma omp parallel
@@ -213,6 +271,27 @@ int oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype, cons
         free(acc);
     }
     return failed ? 9 : 0;
+}
+
+int oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+                    int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+                    float scale, const int64_t* rows, int64_t n_rows, double* out_rows,
+                    double* lse_rows, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    return run_rows(&p, rows, n_rows, out_rows, lse_rows, nthreads);
+}
+
+int oracle_fwd_rows_elem(const void* q, const void* k, const void* v, int dtype,
+                         const uint8_t* mask, const int32_t* pidx, const uint32_t* pbits,
+                         int64_t n_tiles, int64_t B, int64_t H, int64_t S, int64_t D,
+                         int64_t block_q, int64_t block_k, float scale, const int64_t* rows,
+                         int64_t n_rows, double* out_rows, double* lse_rows, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    if (!pidx) return 1;
+    p.pidx = pidx;
+    p.pbits = pbits;
+    p.n_tiles = n_tiles;
+    return run_rows(&p, rows, n_rows, out_rows, lse_rows, nthreads);
 }
 
 /* Dense probability matrix P[b][h][s][j] (zero where masked), for tiny shapes:

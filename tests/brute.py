@@ -27,10 +27,38 @@ def expand_mask(mask, block_q, block_k):
     return np.repeat(np.repeat(m, block_q, axis=2), block_k, axis=3)  # [B,H,S,S]
 
 
+def expand_elem(states, pidx, pbits, block_q, block_k):
+    """Element mask [B,H,S,S] of block states (0 empty, 1 full, else partial) with
+    bit tiles pbits[n_tiles][block_q][block_k / 32] (bit c % 32 of word c / 32 of
+    row i keeps element (i, c) of a partial block using that tile)."""
+    st = np.asarray(widen(states), dtype=np.int64)
+    pi = np.asarray(widen(pidx), dtype=np.int64)
+    pb = np.ascontiguousarray(np.asarray(pbits).astype(np.uint32))
+    B, H, nq, nk = st.shape
+    if pb.shape[0]:
+        tiles = np.unpackbits(pb.view(np.uint8).reshape(pb.shape[0], block_q, -1), axis=-1,
+                              bitorder="little").astype(bool)
+    full = np.zeros((B, H, nq * block_q, nk * block_k), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                for j in range(nk):
+                    blk = full[b, h, i * block_q:(i + 1) * block_q, j * block_k:(j + 1) * block_k]
+                    if st[b, h, i, j] == 1:
+                        blk[:] = True
+                    elif st[b, h, i, j] > 1:
+                        blk[:] = tiles[pi[b, h, i, j]]
+    return full
+
+
 def brute_fwd(q, k, v, mask, block_q, block_k, scale):
+    return brute_fwd_full(q, k, v, expand_mask(mask, block_q, block_k), scale)
+
+
+def brute_fwd_full(q, k, v, full, scale):
+    """The same with an element mask full [B,H,S,S] (True = kept)."""
     q, k, v = widen(q), widen(k), widen(v)
     scale = float(np.float32(scale))
-    full = expand_mask(mask, block_q, block_k)
     s = scale * np.matmul(q, np.swapaxes(k, -1, -2))
     s = np.where(full, s, -np.inf)
     with np.errstate(invalid="ignore", divide="ignore"):

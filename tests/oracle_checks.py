@@ -23,6 +23,16 @@ What pins what:
   rows_match_full   the selected-rows entry point equals the full forward
   bf16_widening     bf16 inputs give the same result as their exact fp64 values
   compact_brute     CSR compaction equals np.nonzero per row
+Element-level masks (block states 0/1/partial + bit tiles):
+  elem_brute        dense literal -inf softmax over the expanded element mask
+  elem_tiles_all_set / elem_tiles_all_clear
+                    partial blocks whose tiles are all ones (zeros) equal the
+                    block-level oracle with those blocks active (inactive)
+  elem_token_causal torch SDPA with is_causal (fp64, CPU): block causal states
+                    with one lower-triangular tile on the diagonal blocks
+  elem_empty_row    a query row whose only active block is partial with that
+                    row's bits all clear gives out == 0, lse == -inf
+  elem_rows_match   the selected-rows entry point equals the full forward
 """
 import json
 import math
@@ -31,7 +41,7 @@ import os
 import numpy as np
 import torch
 
-from brute import brute_compact, brute_fwd, expand_mask
+from brute import brute_compact, brute_fwd, brute_fwd_full, expand_elem, expand_mask
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TOL = 1e-12
@@ -274,9 +284,106 @@ def compact_brute(orc):
         assert np.array_equal(rebuilt.reshape(shape), m.numpy())
 
 
+def _elem_case(B, H, S, bq, bk, n_tiles, seed, p=(0.3, 0.3, 0.4), density=0.5):
+    """Random block states (empty / full / partial with probabilities p) and
+    n_tiles random bit tiles of the given density."""
+    g = np.random.default_rng(seed)
+    st = g.choice(3, size=(B, H, S // bq, S // bk), p=p).astype(np.uint8)
+    st[st == 2] = g.choice([2, 7, 255], size=int((st == 2).sum()))  # any value > 1 is partial
+    pidx = g.integers(0, n_tiles, size=st.shape).astype(np.int32)
+    bits = (g.random((n_tiles, bq, bk)) < density)
+    pbits = np.packbits(bits, axis=-1, bitorder="little").view(np.uint32).reshape(n_tiles, bq, bk // 32)
+    return st, pidx, pbits
+
+
+ELEM_CASES = [
+    # B, H, S, D, block_q, block_k, n_tiles, seed, dtype, scale
+    (1, 2, 64, 8, 16, 32, 3, 31, torch.float64, 0.4),
+    (2, 1, 96, 4, 8, 32, 5, 32, torch.float32, -0.7),
+    (1, 1, 128, 16, 32, 64, 2, 33, torch.bfloat16, 0.25),
+]
+
+
+def elem_brute(orc):
+    for (B, H, S, D, bq, bk, nt, seed, dt, scale) in ELEM_CASES:
+        q = _rand((B, H, S, D), seed, dt)
+        k = _rand((B, H, S, D), seed + 100, dt)
+        v = _rand((B, H, S, D), seed + 200, dt)
+        st, pidx, pbits = _elem_case(B, H, S, bq, bk, nt, seed)
+        out, lse = orc.fwd_elem(q, k, v, st, pidx, pbits, bq, bk, scale)
+        bout, blse, _ = brute_fwd_full(q, k, v, expand_elem(st, pidx, pbits, bq, bk), scale)
+        _close(out, bout, TOL, "elem out %s" % (dt,))
+        _close(lse, blse, TOL, "elem lse %s" % (dt,))
+
+
+def _elem_vs_block(orc, fill):
+    B, H, S, D, bq, bk = 1, 2, 64, 8, 16, 32
+    q, k, v = (_rand((B, H, S, D), s) for s in (41, 42, 43))
+    st, pidx, pbits = _elem_case(B, H, S, bq, bk, 2, 44)
+    pbits[:] = np.uint32(0xFFFFFFFF) if fill else np.uint32(0)
+    out, lse = orc.fwd_elem(q, k, v, st, pidx, pbits, bq, bk, 0.5)
+    blk = (st != 0) if fill else (st == 1)
+    bout, blse = orc.fwd(q, k, v, blk.astype(np.uint8), bq, bk, 0.5)
+    _close(out, bout, 0.0, "elem vs block out")
+    _close(lse, blse, 0.0, "elem vs block lse")
+
+
+def elem_tiles_all_set(orc):
+    _elem_vs_block(orc, True)
+
+
+def elem_tiles_all_clear(orc):
+    _elem_vs_block(orc, False)
+
+
+def elem_token_causal(orc):
+    B, H, S, D, b = 1, 2, 96, 8, 32
+    q, k, v = (_rand((B, H, S, D), s) for s in (51, 52, 53))
+    n = S // b
+    st = (np.tril(np.ones((n, n), dtype=np.uint8)) + np.eye(n, dtype=np.uint8))  # 1 below, 2 on
+    st = np.broadcast_to(st, (B, H, n, n)).copy()
+    pidx = np.zeros((B, H, n, n), dtype=np.int32)
+    tri = np.tril(np.ones((b, b), dtype=bool))
+    pbits = np.packbits(tri, axis=-1, bitorder="little").view(np.uint32).reshape(1, b, b // 32)
+    out, lse = orc.fwd_elem(q, k, v, st, pidx, pbits, b, b, 0.3)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                            scale=float(np.float32(0.3))).numpy()
+    _close(out, want, TOL, "token causal")
+
+
+def elem_empty_row(orc):
+    B, H, S, D, bq, bk = 1, 1, 64, 4, 16, 32
+    q, k, v = (_rand((B, H, S, D), s) for s in (61, 62, 63))
+    st = np.zeros((B, H, S // bq, S // bk), dtype=np.uint8)
+    st[0, 0, 1, 1] = 2          # query block 1 sees only key block 1, through tile 0
+    st[0, 0, 2, :] = 1          # query block 2 sees everything
+    pidx = np.zeros(st.shape, dtype=np.int32)
+    bits = np.ones((1, bq, bk), dtype=bool)
+    bits[0, 5, :] = False       # query 16 + 5 keeps nothing
+    pbits = np.packbits(bits, axis=-1, bitorder="little").view(np.uint32).reshape(1, bq, bk // 32)
+    out, lse = orc.fwd_elem(q, k, v, st, pidx, pbits, bq, bk, 0.5)
+    assert np.all(out[0, 0, 21] == 0.0) and lse[0, 0, 21] == -np.inf
+    assert np.all(np.isfinite(lse[0, 0, 16:21])) and np.all(np.isfinite(lse[0, 0, 32:48]))
+    assert np.all(lse[0, 0, :16] == -np.inf) and np.all(out[0, 0, :16] == 0.0)
+
+
+def elem_rows_match(orc):
+    (B, H, S, D, bq, bk, nt, seed, dt, scale) = ELEM_CASES[1]
+    q = _rand((B, H, S, D), seed, dt)
+    k = _rand((B, H, S, D), seed + 100, dt)
+    v = _rand((B, H, S, D), seed + 200, dt)
+    st, pidx, pbits = _elem_case(B, H, S, bq, bk, nt, seed)
+    out, lse = orc.fwd_elem(q, k, v, st, pidx, pbits, bq, bk, scale)
+    rows = np.array([0, 5, 17, 95, 96 + 40, 2 * 96 - 1])
+    ro, rl = orc.fwd_rows_elem(q, k, v, st, pidx, pbits, bq, bk, scale, rows)
+    _close(ro, out.reshape(-1, D)[rows], 0.0, "rows out")
+    _close(rl, lse.reshape(-1)[rows], 0.0, "rows lse")
+
+
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
-       bf16_widening, compact_brute]
+       bf16_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
+       elem_token_causal, elem_empty_row, elem_rows_match]
 
 
 def run_all(orc):

@@ -21,12 +21,16 @@ MUTANTS = {
                            ("*lse_out = m + log(l);", "*lse_out = log(l);")],
     "lse_drops_max": [("*lse_out = m + log(l);", "*lse_out = log(l);")],
     "key_block_short_by_one": [("for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                                "            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;\n"
                                 "            const int64_t kbase",
                                 "for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k - 1; ++j) {\n"
+                                "            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;\n"
                                 "            const int64_t kbase"),
                                ("for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
+                                "            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;\n"
                                 "            const int64_t vbase",
                                 "for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k - 1; ++j) {\n"
+                                "            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;\n"
                                 "            const int64_t vbase")],
     "v_row_is_query_row": [("const int64_t vbase = (bh * p->S + j) * D;",
                             "const int64_t vbase = (bh * p->S + s) * D;")],
@@ -38,18 +42,20 @@ MUTANTS = {
                         "            for (int64_t d = 0; d < D; ++d)\n                dot += widen(p->q",
                         "const int64_t kbase = (j) * D;\n            double dot = 0.0;\n"
                         "            for (int64_t d = 0; d < D; ++d)\n                dot += widen(p->q")],
-    "mask_transposed": [("if (!mrow[kj]) continue;\n        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
-                         "            const int64_t kbase",
-                         "if (kj >= p->n_q || qi >= p->n_k || !p->mask[(bh * p->n_q + kj) * p->n_k + qi]) continue;\n"
-                         "        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
-                         "            const int64_t kbase"),
-                        ("if (!mrow[kj]) continue;\n        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
-                         "            const int64_t vbase",
-                         "if (kj >= p->n_q || qi >= p->n_k || !p->mask[(bh * p->n_q + kj) * p->n_k + qi]) continue;\n"
-                         "        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {\n"
-                         "            const int64_t vbase")],
+    # the block mask read transposed (mask[kj][qi] instead of mask[qi][kj])
+    "mask_transposed": [("const uint8_t* mrow = p->mask + (bh * p->n_q + qi) * p->n_k;",
+                         "uint8_t mrow_t[4096];\n"
+                         "    for (int64_t c = 0; c < p->n_k && c < 4096; ++c)\n"
+                         "        mrow_t[c] = (c < p->n_q && qi < p->n_k) ? p->mask[(bh * p->n_q + c) * p->n_k + qi] : 0;\n"
+                         "    const uint8_t* mrow = mrow_t;")],
     "bf16_wrong_shift": [("((uint32_t)((const uint16_t*)base)[idx]) << 16;",
                           "((uint32_t)((const uint16_t*)base)[idx]) << 15;")],
+    "elem_partial_ignores_bits": [("if (!p->pidx || blk == 1) return 1;", "return 1;")],
+    "elem_bit_order_reversed": [("return (int)((w >> (c % 32)) & 1u);", "return (int)((w >> (31 - c % 32)) & 1u);")],
+    "elem_tile_row_from_key": [("const int64_t i = s % p->block_q, c = j % p->block_k;",
+                                "const int64_t i = j % p->block_q, c = j % p->block_k;")],
+    "elem_tile_index_ignored": [("(int64_t)p->pidx[bi] * p->block_q", "(int64_t)0 * p->block_q")],
+    "elem_partial_as_empty": [("if (!p->pidx || blk == 1) return 1;", "if (!p->pidx || blk == 1) return 1;\n    if (blk > 1) return 0;")],
     "compact_skips_last_column": [("for (int64_t kj = 0; kj < n_k; ++kj)\n            if (mask[r * n_k + kj])",
                                    "for (int64_t kj = 0; kj < n_k - 1; ++kj)\n            if (mask[r * n_k + kj])")],
 }
