@@ -87,6 +87,12 @@ def library():
         "bsattn_autotune": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
                              i32, i32, cfgp, ctypes.POINTER(TuneResult), i32, i32p,
                              ctypes.c_char_p, p], i32),
+        "bsattn_plan_elem": ([p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
+        "bsattn_fwd_planned_elem": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p,
+                                     i32, p, sz, cfgp, p], i32),
+        "bsattn_fwd_elem": ([p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
+                             p, sz, cfgp, p], i32),
+        "bsattn_list_configs_elem": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
         "bsattn_load_tune_cache": ([ctypes.c_char_p], i32),
         "bsattn_clear_tune_cache": ([], None),
     }
@@ -283,6 +289,88 @@ def fwd_compacted(q, k, v, row_ptr, col_idx, block_q, block_k, scale=None, *, ou
                                         _stream(stream))
     _check(rc)
     return out, lse
+
+
+def _elem_tensors(block_states, partial_index, partial_bits):
+    """Check the element-mask tensors (see bsattn.h): uint8 states, int32 tile
+    index per block, int32/uint32 bit tiles [n_tiles, block_q, block_k / 32]."""
+    if block_states.dtype != torch.uint8 or not block_states.is_contiguous():
+        raise TypeError("block_states must be a contiguous uint8 tensor")
+    if partial_index.dtype != torch.int32 or not partial_index.is_contiguous():
+        raise TypeError("partial_index must be a contiguous int32 tensor")
+    if partial_bits.dtype not in (torch.int32, torch.uint32) or not partial_bits.is_contiguous():
+        raise TypeError("partial_bits must be a contiguous int32/uint32 tensor")
+    if block_states.shape != partial_index.shape or block_states.dim() != 4:
+        raise ValueError("block_states and partial_index must be [B, H, S/block_q, S/block_k]")
+    if partial_bits.dim() != 3:
+        raise ValueError("partial_bits must be [n_tiles, block_q, block_k / 32]")
+    return partial_bits.shape[0]
+
+
+def plan_elem(block_states, partial_index, partial_bits, S, block_q, block_k, *, workspace=None,
+              stream=None):
+    """Plan of an element-level mask (bsattn_plan_elem); returns the workspace."""
+    n_tiles = _elem_tensors(block_states, partial_index, partial_bits)
+    B, H, n_q, n_k = block_states.shape
+    if (n_q * block_q, n_k * block_k) != (S, S):
+        raise ValueError("block_states must be [B, H, S/block_q, S/block_k]")
+    ws = _workspace(workspace_size(B, H, S, block_q, block_k), block_states.device, workspace)
+    rc = library().bsattn_plan_elem(_ptr(block_states), _ptr(partial_index), n_tiles, B, H, S,
+                                    block_q, block_k, _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _check(rc)
+    return ws
+
+
+def fwd_planned_elem(q, k, v, partial_bits, plan_ws, block_q, block_k, scale=None, *, out=None,
+                     lse=None, config=None, stream=None):
+    """The attention kernel alone on a plan from plan_elem(); returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    rc = library().bsattn_fwd_planned_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H,
+                                           S, D, block_q, block_k, float(scale), _dtype_code(q),
+                                           _ptr(partial_bits), partial_bits.shape[0],
+                                           _ptr(plan_ws), plan_ws.numel() * plan_ws.element_size(),
+                                           _cfg(config), _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def fwd_elem(q, k, v, block_states, partial_index, partial_bits, block_q, block_k, scale=None, *,
+             out=None, lse=None, workspace=None, config=None, stream=None):
+    """Forward pass with an element-level mask (bsattn_fwd_elem); returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    n_tiles = _elem_tensors(block_states, partial_index, partial_bits)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ws = _workspace(workspace_size(B, H, S, block_q, block_k), q.device, workspace)
+    rc = library().bsattn_fwd_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(block_states),
+                                   _ptr(partial_index), _ptr(partial_bits), n_tiles, _ptr(out),
+                                   _ptr(lse), B, H, S, D, block_q, block_k, float(scale),
+                                   _dtype_code(q), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _cfg(config), _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def list_configs_elem(dtype, D, block_q, block_k):
+    """Tile configs built for element-level masks."""
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    n = ctypes.c_int(0)
+    lib = library()
+    _check(lib.bsattn_list_configs_elem(code, D, block_q, block_k, None, 0, ctypes.byref(n)))
+    arr = (TileConfig * max(n.value, 1))()
+    _check(lib.bsattn_list_configs_elem(code, D, block_q, block_k, arr, n.value, ctypes.byref(n)))
+    return [arr[i] for i in range(n.value)]
 
 
 def list_configs(dtype, D, block_q, block_k):

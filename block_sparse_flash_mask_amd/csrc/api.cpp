@@ -317,6 +317,31 @@ int run_attention(const FwdArgs& a, const Variant& var, hipStream_t stream) {
     return BSATTN_OK;
 }
 
+// ---- element-level masks ------------------------------------------------------
+
+// A partial block's tile index travels in bits 16..30 of its list entry (kj in
+// bits 0..15), so n_k <= 65536 and 1 <= n_tiles <= 32767.
+constexpr int kElemMaxTiles = 32767;
+
+int check_elem_shape(int B, int H, int S, int block_q, int block_k, int n_tiles) {
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    if (!block_ok(block_q) || !block_ok(block_k)) return BSATTN_ERR_UNSUPPORTED;
+    if (n_tiles < 1 || n_tiles > kElemMaxTiles || S / block_k > 65536) return BSATTN_ERR_SHAPE;
+    return check_grid(B, H, S / block_q, S / block_k);
+}
+
+const Variant* find_elem(int dtype, int D, int block_q, int block_k, const bsattn_tile_config* cfg) {
+    if (dtype != BSATTN_BF16) return nullptr;
+    int n = 0;
+    const Variant* t = bf16_elem_variants(&n);
+    const bsattn_tile_config any{0, 0, 0, 0};
+    const bsattn_tile_config& c = is_auto(cfg) ? any : *cfg;
+    for (int i = 0; i < n; ++i)
+        if (legal(t[i], dtype, D, block_q, block_k) && matches(t[i], c)) return &t[i];
+    return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -487,6 +512,108 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
     a.nrows = (int)(is_pair(*var) ? L.P : L.R);
     a.chunk = (int)xcd_chunk(a.nrows);
     return run_attention(a, *var, (hipStream_t)stream);
+}
+
+// ---- element-level masks ------------------------------------------------------
+
+int bsattn_plan_elem(const uint8_t* block_states, const int32_t* partial_index, int n_tiles, int B,
+                     int H, int S, int block_q, int block_k, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (!block_states || !partial_index || !workspace) return BSATTN_ERR_NULL;
+    const int rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4) || !is_aligned(partial_index, 4)) return BSATTN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    int32_t* counts = (int32_t*)ws;
+    hipError_t e = launch_compact_rows_elem(block_states, partial_index, n_tiles, L.R, n_k, counts,
+                                            (int32_t*)(ws + L.lists), s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_compact_order(counts, L.R, n_q, n_k, L.chunk, (int32_t*)(ws + L.order), L.pchunk,
+                             (int32_t*)(ws + L.porder), s);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_fwd_planned_elem(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                            int H, int S, int D, int block_q, int block_k, float scale, int dtype,
+                            const uint32_t* partial_bits, int n_tiles, const void* workspace,
+                            size_t workspace_bytes, const bsattn_tile_config* cfg, void* stream) {
+    if (!workspace || !partial_bits) return BSATTN_ERR_NULL;
+    int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4) || !is_aligned(partial_bits, 4)) return BSATTN_ERR_ALIGN;
+    if (check_ws_alias(workspace, L.bytes, q, k, v, out, lse, B, H, S, D, dtype))
+        return BSATTN_ERR_ALIAS;
+    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
+    const size_t nt = (size_t)B * H * S * D * (dtype == BSATTN_F32 ? 4 : 2);
+    if (overlap(partial_bits, nbits, out, nt) || overlap(partial_bits, nbits, lse, (size_t)B * H * S * 4) ||
+        overlap(partial_bits, nbits, workspace, L.bytes))
+        return BSATTN_ERR_ALIAS;
+    const Variant* var = find_elem(dtype, D, block_q, block_k, cfg);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+    FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
+    const char* ws = (const char*)workspace;
+    a.counts = (const int32_t*)ws;
+    a.list = (const int32_t*)(ws + L.lists);
+    a.ell_stride = n_k;
+    a.order = (const int32_t*)(ws + L.order);
+    a.nrows = (int)L.R;
+    a.chunk = (int)L.chunk;
+    a.pbits = partial_bits;
+    a.n_tiles = n_tiles;
+    return run_attention(a, *var, (hipStream_t)stream);
+}
+
+int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* block_states,
+                    const int32_t* partial_index, const uint32_t* partial_bits, int n_tiles, void* out,
+                    float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                    int dtype, void* workspace, size_t workspace_bytes,
+                    const bsattn_tile_config* cfg, void* stream) {
+    if (!block_states || !partial_index || !partial_bits) return BSATTN_ERR_NULL;
+    int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    const size_t need = fwd_ws_bytes((int64_t)B * H, S / block_q, S / block_k);
+    if (!workspace || workspace_bytes < need) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 4) || !is_aligned(partial_bits, 4) || !is_aligned(partial_index, 4))
+        return BSATTN_ERR_ALIGN;
+    if (check_ws_alias(workspace, need, q, k, v, out, lse, B, H, S, D, dtype)) return BSATTN_ERR_ALIAS;
+    // Resolve the tile config before any device work.
+    if (!find_elem(dtype, D, block_q, block_k, cfg)) return BSATTN_ERR_UNSUPPORTED;
+    rc = bsattn_plan_elem(block_states, partial_index, n_tiles, B, H, S, block_q, block_k, workspace,
+                          workspace_bytes, stream);
+    if (rc) return rc;
+    return bsattn_fwd_planned_elem(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, dtype,
+                                   partial_bits, n_tiles, workspace, workspace_bytes, cfg, stream);
+}
+
+int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
+                             int cap, int* n) {
+    if (!n) return BSATTN_ERR_NULL;
+    if (dtype != BSATTN_F32 && dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    int cnt = 0;
+    if (dtype == BSATTN_BF16) {
+        int nv = 0;
+        const Variant* t = bf16_elem_variants(&nv);
+        for (int i = 0; i < nv; ++i) {
+            if (!legal(t[i], dtype, D, block_q, block_k)) continue;
+            if (cfgs && cnt < cap)
+                cfgs[cnt] = bsattn_tile_config{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
+            ++cnt;
+        }
+    }
+    *n = cnt;
+    return BSATTN_OK;
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,

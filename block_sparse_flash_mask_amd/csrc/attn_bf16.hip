@@ -53,7 +53,7 @@
 
 namespace bsattn {
 
-template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR>
+template <int D, int WAVES, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR, int ELEM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_bf16_kernel(FwdArgs a) {
     typedef TileGeom<D, TK> G;
     typedef DmaPlan<D, WAVES, TK> P;
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     static_assert(!PAIR || (WAVES == 8 && NQ == 1 && !PIPE), "row pairs: two 4-wave groups");
 
     static_assert(ST == 2 || (ST == 3 && !PIPE), "three stages use the plain schedule");
+    static_assert(!ELEM || (!PIPE && !PAIR && NQ == 1), "element masks: plain schedule, one row");
     __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t v0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t k1s[G::BYTES];
@@ -194,6 +195,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     auto key0_of = [&](int kj_raw, int t) -> int {
         int kj = wave_uniform(kj_raw);
         if constexpr (PAIR) kj &= 0x3fffffff;
+        if constexpr (ELEM) kj &= 0xffff;  // element masks: tile + 1 in bits 16..30
         kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
         return kj * a.block_k + (t & ((1 << sh) - 1)) * TK;
     };
@@ -267,7 +269,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             const float mx = max_halves_nan(max_tree3<16 * MT>(tmp)) * a.c;
             if (__ballot(mx > m_run[n] + 8.0f) != 0) {
                 const float m_new = fmax_nan(m_run[n], mx);
-                const float alpha = fast_exp2(m_run[n] - m_new);
+                // (element masks: a row may still have no kept score, m = -inf;
+                // its l and O are zero, and 2^(-inf - -inf) would be NaN)
+                const float alpha =
+                    (ELEM && m_run[n] == -INFINITY) ? 0.f : fast_exp2(m_run[n] - m_new);
                 l_run[n] *= alpha;
 #pragma unroll
                 for (int md = 0; md < MD; ++md) oacc[n][md] *= alpha;
@@ -282,11 +287,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
             float tmp[16 * MT];
+            // (element masks: with no kept score yet every S is -inf; use m = 0)
+            const float m_use = (ELEM && m_run[n] == -INFINITY) ? 0.f : m_run[n];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_run[n]));
+                    const float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_use));
                     tmp[16 * mt + i] = e;
                     p.v[n][mt][i >> 3][i & 7] = (__bf16)e;
                 }
@@ -367,6 +374,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // waiting for "at most NDMA outstanding" (ST = 3) retires step t's DMA and
     // the entry load issued before step t+1's DMA.
     constexpr int NDMA = P::NK + P::NV;
+    // Element masks: the list entries of the steps in flight (e1 = this step, e2 =
+    // the next with three stages), and the kept-bit test applied to S.
+    int e1 = 0, e2 = 0;
+    auto apply_tile = [&](SAcc& s, int e, int t) {
+        int tile = (e >> 16) - 1;  // -1: full block
+        if (tile < 0) return;
+        tile = tile < a.n_tiles ? tile : a.n_tiles - 1;  // (a plan never holds more)
+        const int qr = q_row0 - qi * a.block_q;  // this lane's row inside the block
+        const int ko = (t & ((1 << sh) - 1)) * TK;
+        const int wpr = a.block_k >> 5;  // words per tile row
+        const uint32_t* wrow = a.pbits + ((size_t)tile * a.block_q + qr) * wpr + (ko >> 5);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            // register i holds key 16*(i/8) + 8h + i%8 of the 32-key tile mt
+            const uint32_t w = wrow[mt] >> (8 * h);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (!((w >> (16 * (i >> 3) + (i & 7))) & 1u)) s.v[0][mt][i] = -INFINITY;
+        }
+    };
     auto plain = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur,
                      const uint8_t* vcur) {
         if (ST == 3 && t + 1 < n_steps)
@@ -374,14 +401,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         else
             __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
         __syncthreads();
+        const int e_cur = e1;
+        if constexpr (ELEM && ST == 3) e1 = e2;
         if (t + ST - 1 < n_steps) {
             const int kn = key0_of(pre, t + ST - 1);
+            if constexpr (ELEM) (ST == 3 ? e2 : e1) = wave_uniform(pre);
             pre = entry(t + ST);
             issue_k(kn, kfill);
             issue_v(kn, vfill);
         }
         if (mine(t)) {
-            const SAcc s = qk(kcur);
+            SAcc s = qk(kcur);
+            if constexpr (ELEM) apply_tile(s, e_cur, t);
             update_max(s);
             const PTile p = exps(s);
             pv(p, vcur);
@@ -411,7 +442,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             body(no{}, t, kv_next, pre, s, k0s, v1s, k1s, v0s);
         }
     } else if (n_steps > 0 && ST == 2) {
-        const int k0 = key0_of(entry(0), 0);
+        e1 = wave_uniform(entry(0));
+        const int k0 = key0_of(e1, 0);
         int pre = entry(1);
         issue_k(k0, k0s);
         issue_v(k0, v0s);
@@ -420,8 +452,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             if (t + 1 < n_steps) plain(t + 1, pre, k0s, v0s, k1s, v1s);
         }
     } else if (n_steps > 0) {
-        const int k0 = key0_of(entry(0), 0);
-        const int k1 = key0_of(entry(1), 1);
+        e1 = wave_uniform(entry(0));
+        e2 = wave_uniform(entry(1));
+        const int k0 = key0_of(e1, 0);
+        const int k1 = key0_of(e2, 1);
         int pre = entry(2);
         issue_k(k0, k0s);
         issue_v(k0, v0s);
@@ -441,7 +475,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     if (!row_ok) return;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-        const bool any = PAIR ? m_run[n] != -INFINITY : n_steps > 0;
+        const bool any = (PAIR || ELEM) ? m_run[n] != -INFINITY : n_steps > 0;
         const int q_row = q_row0 + 32 * n;
         const float l_tot = sum_halves(l_run[n]);
         const float inv = any ? 1.0f / l_tot : 0.0f;
@@ -461,9 +495,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     }
 }
 
-template <int D, int W, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR = 0>
+template <int D, int W, int TK, int NQ, int PIPE, int ST, int OCC, int PAIR = 0, int ELEM = 0>
 static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, NQ, PIPE, ST, OCC, PAIR>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, TK, NQ, PIPE, ST, OCC, PAIR, ELEM>), dim3(grid), dim3(W * 64), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -500,6 +535,22 @@ static const Variant kBf16Variants[] = {
     {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
     BSATTN_BF16_PAIR(64, 64, 3, 4), BSATTN_BF16_PAIR(64, 64, 2, 4), BSATTN_BF16_PAIR(64, 128, 2, 2),
 };
+
+// Element-level masks (plain schedule, one 32-row query tile per wave, no row
+// pairs): the best block-mask configs of each D.
+#define BSATTN_BF16_ELEM(D, W, TK, ST, OCC) \
+    {1, D, 32 * W, TK, W, ST, &launch_bf16<D, W, TK, 1, 0, ST, OCC, 0, 1>}
+
+static const Variant kBf16ElemVariants[] = {
+    BSATTN_BF16_ELEM(128, 4, 32, 3, 3), BSATTN_BF16_ELEM(128, 4, 64, 2, 2), BSATTN_BF16_ELEM(128, 2, 32, 3, 3),
+    BSATTN_BF16_ELEM(64, 4, 64, 2, 4),  BSATTN_BF16_ELEM(64, 4, 32, 2, 5),  BSATTN_BF16_ELEM(64, 4, 128, 2, 2),
+    BSATTN_BF16_ELEM(64, 2, 64, 3, 2),
+};
+
+const Variant* bf16_elem_variants(int* n) {
+    *n = (int)(sizeof(kBf16ElemVariants) / sizeof(kBf16ElemVariants[0]));
+    return kBf16ElemVariants;
+}
 
 const Variant* bf16_variants(int* n) {
     *n = (int)(sizeof(kBf16Variants) / sizeof(kBf16Variants[0]));

@@ -43,6 +43,10 @@ struct FwdArgs {
     int sub_per_row;   // block_q / tile_q: workgroups per mask row (a power of 2)
     int sub_log2;      // log2(sub_per_row)
     int steps_log2;    // log2(block_k / tile_k): kernel steps per key block
+    // Element-level masks: bit tiles [n_tiles][block_q][block_k / 32]; the list
+    // entries then carry (tile + 1) << 16 for a partial block (0: full).
+    const uint32_t* pbits;
+    int n_tiles;
     float c;           // |scale| * log2(e)
     uint32_t qsign;    // 0x80008000 flips the sign of two packed bf16 (scale < 0)
     uint32_t qsign32;  // 0x80000000 flips an fp32 sign (scale < 0)

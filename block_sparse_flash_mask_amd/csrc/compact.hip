@@ -37,6 +37,42 @@ __global__ __launch_bounds__(256) void rows_kernel(const uint8_t* __restrict__ m
     if (lane == 0) counts[r] = base;
 }
 
+// Element-level masks: block states (0 empty, 1 full, else partial) and the bit
+// tile of each partial block.  Same lists as rows_kernel, with entries
+// kj | (tile + 1) << 16 (0 for a full block), the tile index clamped into
+// [0, n_tiles) so a malformed index can give wrong values but never an
+// out-of-bounds read.
+__global__ __launch_bounds__(256) void rows_elem_kernel(const uint8_t* __restrict__ states,
+                                                        const int32_t* __restrict__ pidx, int n_tiles,
+                                                        int64_t R, int n_k, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ lists) {
+    const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (r >= R) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const uint8_t* srow = states + r * n_k;
+    const int32_t* prow = pidx + r * n_k;
+    int32_t* lrow = lists + r * n_k;
+    int base = 0;
+    for (int s0 = 0; s0 < n_k; s0 += kWave) {
+        const int kj = s0 + lane;
+        const int st = kj < n_k ? srow[kj] : 0;
+        const bool active = st != 0;
+        const uint64_t bal = __ballot(active);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (active) {
+            int tile = 0;
+            if (st > 1) {
+                tile = prow[kj];
+                tile = (tile < 0 ? 0 : (tile >= n_tiles ? n_tiles - 1 : tile)) + 1;
+            }
+            lrow[base + below] = kj | (tile << 16);
+        }
+        base += __popcll(bal);
+    }
+    if (lane == 0) counts[r] = base;
+}
+
 constexpr int kScanThreads = 1024;
 constexpr int kScanPerThread = 4;
 
@@ -375,6 +411,14 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t*
     const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, R, n_k,
                        counts, lists);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_rows_elem(const uint8_t* states, const int32_t* pidx, int n_tiles, int64_t R,
+                                    int n_k, int32_t* counts, int32_t* lists, hipStream_t stream) {
+    const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(rows_elem_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, states, pidx, n_tiles,
+                       R, n_k, counts, lists);
     return hipGetLastError();
 }
 

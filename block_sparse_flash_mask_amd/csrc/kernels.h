@@ -11,6 +11,11 @@ namespace bsattn {
 // Mask compaction (compact.hip).
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t R, int n_k, int32_t* counts,
                                int32_t* lists, hipStream_t stream);
+// Element-level masks: row lists as launch_compact_rows from block states
+// (0 empty, else active), each entry kj | (tile + 1) << 16 for a partial block
+// (state > 1, tile = pidx clamped into [0, n_tiles)) or kj for a full one.
+hipError_t launch_compact_rows_elem(const uint8_t* states, const int32_t* pidx, int n_tiles, int64_t R,
+                                    int n_k, int32_t* counts, int32_t* lists, hipStream_t stream);
 hipError_t launch_compact_scan(const int32_t* counts, int64_t R, int32_t* row_ptr,
                                hipStream_t stream);
 // Dispatch orders per XCD chunk (head by head, longest first within a head):
@@ -50,6 +55,8 @@ hipError_t launch_bf16_pp(const FwdArgs& a, unsigned grid, hipStream_t stream);
 
 // Tables of the built variants (attn_bf16.hip, attn_f32.hip).
 const Variant* bf16_variants(int* n);
+// The bf16 variants built for element-level masks (plain schedule, no row pairs).
+const Variant* bf16_elem_variants(int* n);
 const Variant* f32_variants(int* n);
 
 }  // namespace bsattn

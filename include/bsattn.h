@@ -200,6 +200,58 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
                         int cap, int* n);
 
+/* ---- Element-level masks -------------------------------------------------------
+ * The mask of "Writing Pallas Kernels for JAX" (section "Writing the Kernel Logic:
+ * Load, Compute, Store") is an element tile per (query block, key block): a score
+ * is kept where the tile is set and is -inf elsewhere.  Here it is given as
+ *   block_states   uint8 [B][H][S/block_q][S/block_k]: 0 = empty block (every
+ *                  element masked, never visited), 1 = full block (every element
+ *                  kept), any other value = partial block;
+ *   partial_index  int32 [B][H][S/block_q][S/block_k]: for a partial block, the
+ *                  tile that holds its bits (read only where the state is > 1;
+ *                  an index outside [0, n_tiles) is clamped into it);
+ *   partial_bits   uint32 [n_tiles][block_q][block_k / 32]: element (i, j) of a
+ *                  partial block is kept iff bit j % 32 of word j / 32 of row i of
+ *                  its tile is set.  Tiles may be shared (e.g. one lower-triangular
+ *                  tile for every diagonal block of an exact token-causal mask).
+ * A query row with no kept element gets out = 0 and lse = -inf.  bf16 only
+ * (BSATTN_F32 gives BSATTN_ERR_UNSUPPORTED); 1 <= n_tiles <= 32767 and
+ * S / block_k <= 65536, else BSATTN_ERR_SHAPE.  The workspace is the same size
+ * as for bsattn_fwd (bsattn_workspace_size) and has the plan layout of
+ * bsattn_plan, except that a list entry of a partial block is kj | (tile + 1) << 16.
+ * Tile configs: bsattn_list_configs_elem (row-pair configs are not built for
+ * element masks). */
+
+/* Plan for an element-level mask: bsattn_plan's lists and dispatch orders over
+ * the non-empty blocks, each entry carrying its tile.  Arguments and ownership as
+ * bsattn_plan; BSATTN_ERR_NULL for a NULL block_states, partial_index or workspace,
+ * BSATTN_ERR_ALIGN if workspace or partial_index is not 4-byte aligned. */
+int bsattn_plan_elem(const uint8_t* block_states, const int32_t* partial_index, int n_tiles, int B,
+                     int H, int S, int block_q, int block_k, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* The attention kernel alone on a plan from bsattn_plan_elem (same mask, shape
+ * and n_tiles); partial_bits as above, only read, 4-byte aligned, not
+ * overlapping out, lse or the workspace (BSATTN_ERR_ALIAS).  Other arguments and
+ * checks as bsattn_fwd_planned; cfg selects among bsattn_list_configs_elem. */
+int bsattn_fwd_planned_elem(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                            int H, int S, int D, int block_q, int block_k, float scale, int dtype,
+                            const uint32_t* partial_bits, int n_tiles, const void* workspace,
+                            size_t workspace_bytes, const bsattn_tile_config* cfg, void* stream);
+
+/* The forward pass with an element-level mask: exactly bsattn_plan_elem followed
+ * by bsattn_fwd_planned_elem on one workspace. */
+int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* block_states,
+                    const int32_t* partial_index, const uint32_t* partial_bits, int n_tiles, void* out,
+                    float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                    int dtype, void* workspace, size_t workspace_bytes,
+                    const bsattn_tile_config* cfg, void* stream);
+
+/* Tile configs built for element-level masks (as bsattn_list_configs; zero for
+ * BSATTN_F32). */
+int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
+                             int cap, int* n);
+
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of

@@ -212,3 +212,73 @@ def test_tune_cache_roundtrip(lib, tmp_path):
     assert lib.bsattn_load_tune_cache(str(path).encode()) == OK
     assert lib.bsattn_load_tune_cache(str(tmp_path / "missing.json").encode()) == NULL
     lib.bsattn_clear_tune_cache()
+
+
+def test_elem_argument_checks(lib):
+    """Element-level masks: every call below fails a host check (fake pointers)."""
+    p = ctypes.c_void_p
+    f = lib.bsattn_fwd_elem
+    # q k v states pidx bits n_tiles out lse B H S D bq bk scale dtype ws wsb cfg stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), p(8 * A), p(15 * A), 2, p(9 * A), p(11 * A),
+          1, 1, 256, 64, 64, 64, 0.1, 1, p(13 * A), 16, None, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    assert call(3, None) == NULL and call(4, None) == NULL and call(5, None) == NULL
+    assert call(0, None) == NULL
+    assert call(6, 0) == SHAPE and call(6, 40000) == SHAPE and call(11, 100) == SHAPE
+    assert call(13, 32) == UNSUP and call(12, 96) == UNSUP
+    assert call(18, 16) == WS and call(17, None) == WS
+    ok[18] = 4096  # enough workspace: alignment, aliasing and the config decide
+    assert call(5, p(15 * A + 2)) == ALIGN and call(4, p(8 * A + 1)) == ALIGN
+    assert call(17, p(3 * A + 128)) == ALIAS and call(16, 0) == UNSUP
+
+    g = lib.bsattn_fwd_planned_elem
+    # q k v out lse B H S D bq bk scale dtype bits n_tiles ws wsb cfg stream
+    okp = [p(A), p(3 * A), p(5 * A), p(9 * A), p(11 * A), 1, 1, 256, 64, 64, 64, 0.1, 1,
+           p(15 * A), 2, p(13 * A), 16, None, None]
+
+    def callp(i, x):
+        a = list(okp)
+        a[i] = x
+        return g(*a)
+    assert callp(13, None) == NULL and callp(15, None) == NULL
+    assert callp(14, 0) == SHAPE
+    assert callp(16, 16) == WS
+    # with a large enough workspace (1 KiB here) the alignment and alias checks decide
+    okp[16] = 4096
+    assert callp(13, p(15 * A + 1)) == ALIGN
+    assert callp(13, p(9 * A + 64)) == ALIAS      # bit tiles overlap out
+    assert callp(13, p(11 * A + 8)) == ALIAS      # ... lse
+    assert callp(13, p(13 * A + 128)) == ALIAS    # ... the plan
+    assert callp(15, p(5 * A + 64)) == ALIAS      # the plan overlaps v
+    assert callp(12, 0) == UNSUP                  # fp32: no element-mask configs
+
+    h = lib.bsattn_plan_elem
+    # states pidx n_tiles B H S bq bk ws wsb stream
+    okh = [p(7 * A), p(8 * A), 2, 1, 1, 256, 64, 64, p(13 * A), 16, None]
+
+    def callh(i, x):
+        a = list(okh)
+        a[i] = x
+        return h(*a)
+    assert callh(0, None) == NULL and callh(1, None) == NULL and callh(8, None) == NULL
+    assert callh(2, 0) == SHAPE and callh(5, 250) == SHAPE
+    assert callh(6, 32) == UNSUP
+    assert callh(9, 16) == WS
+    okh[9] = 4096
+    assert callh(1, p(8 * A + 2)) == ALIGN and callh(8, p(13 * A + 2)) == ALIGN
+
+
+def test_elem_configs(lib):
+    n = ctypes.c_int(-1)
+    assert lib.bsattn_list_configs_elem(0, 64, 64, 64, None, 0, ctypes.byref(n)) == OK
+    assert n.value == 0  # fp32: none
+    for D in (64, 128):
+        cfgs = bs.list_configs_elem(__import__("torch").bfloat16, D, 128, 128)
+        assert len(cfgs) >= 3
+        assert bs.list_configs_elem(__import__("torch").bfloat16, D, 64, 64)  # tile_q 64 too
+        for c in cfgs:
+            assert c.tile_q in (64, 128) and c.waves in (2, 4) and c.stages in (2, 3)

@@ -68,3 +68,17 @@ def test_sample_rows_in_range():
     rows = W.sample_rows(w.B, w.H, w.S, w.block_q, 40, mask=W.make_mask(w))
     assert len(rows) >= 40 and rows.min() >= 0 and rows.max() < w.B * w.H * w.S
     assert len(np.unique(rows)) == len(rows)
+
+
+def test_token_causal_elem_workload():
+    """The element-level token-causal workload keeps exactly the lower triangle:
+    S (S + 1) / 2 elements per head, and its expanded mask is tril (checked on a
+    small copy of the same recipe)."""
+    from brute import expand_elem
+    w = W.ELEM_WORKLOADS["causal_elem_bf16"]
+    st, pidx, pbits = W.make_elem_mask(w)
+    assert W.kept_elements(st, pidx, pbits, w.block_q, w.block_k) == w.B * w.H * w.S * (w.S + 1) // 2
+    small = W.Workload("t", 1, 1, 512, 64, 128, 128, "bf16", "token_causal")
+    s2, p2, b2 = W.make_elem_mask(small)
+    full = expand_elem(s2.numpy(), p2.numpy(), b2.numpy().view(np.uint32), 128, 128)
+    assert np.array_equal(full[0, 0], np.tril(np.ones((512, 512), dtype=bool)))

@@ -17,6 +17,12 @@ for JAX", section "Designing the Block Specification"):
                                                            + every 16th key block + Bernoulli(0.01))
                                                            restricted to kj <= qi
 
+Element-level mask workload (block states + bit tiles, see bsattn.h):
+
+  causal_elem_bf16  B=2 H=32 S=8192 D=128 128x128 blocks  exact token-causal: blocks
+                    below the diagonal full, diagonal blocks partial through one shared
+                    lower-triangular tile (query i keeps keys j <= i)
+
 Recipe: Q, K, V ~ N(0, 1) drawn in that order from one torch CPU generator seeded 0,
 each of shape [B,H,S,D] in fp32, then rounded to bf16 (round-to-nearest-even) for
 the bf16 workloads.  Random mask extras come from a separate torch CPU generator
@@ -73,6 +79,11 @@ WORKLOADS = {
 }
 
 ORDER = ["tiny_f32", "dense_bf16", "causal_bf16", "sparse_bf16", "long_bf16"]
+
+ELEM_WORKLOADS = {
+    "causal_elem_bf16": Workload("causal_elem_bf16", 2, 32, 8192, 128, 128, 128, "bf16",
+                                 "token_causal"),
+}
 
 
 def make_qkv(B, H, S, D, dtype=torch.bfloat16, seed=0):
@@ -142,7 +153,43 @@ def make_mask(w: Workload):
         return mask_window_global_random(B, H, n_q, n_k, seed=w.mask_seed)
     if w.mask_kind == "causal_window_strided_random":
         return mask_causal_window_strided_random(B, H, n_q, n_k, seed=w.mask_seed)
+    if w.mask_kind == "token_causal":  # the non-empty blocks of the element mask
+        return mask_causal(B, H, n_q, n_k)
     raise ValueError(w.mask_kind)
+
+
+def pack_tiles(bits):
+    """Bool tiles [n, block_q, block_k] -> int32 words [n, block_q, block_k / 32],
+    bit c % 32 of word c / 32 = element c (little-endian bit order)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=bool))
+    n, bq, bk = b.shape
+    words = np.packbits(b, axis=-1, bitorder="little").view(np.uint32).reshape(n, bq, bk // 32)
+    return torch.from_numpy(words.view(np.int32).copy())
+
+
+def make_elem_mask(w: Workload):
+    """(block_states uint8, partial_index int32, partial_bits int32) of an
+    element-level workload."""
+    B, H, n_q, n_k = w.B, w.H, w.n_q, w.n_k
+    if w.mask_kind == "token_causal":
+        assert w.block_q == w.block_k
+        i, j = _grid(n_q, n_k)
+        states = ((j < i).to(torch.uint8) + 2 * (j == i).to(torch.uint8)).expand(B, H, n_q, n_k)
+        tri = np.tril(np.ones((w.block_q, w.block_k), dtype=bool))[None]
+        return (states.contiguous(), torch.zeros(B, H, n_q, n_k, dtype=torch.int32),
+                pack_tiles(tri))
+    raise ValueError(w.mask_kind)
+
+
+def kept_elements(states, partial_index, partial_bits, block_q, block_k) -> int:
+    """Number of kept (query, key) elements of an element-level mask."""
+    st = torch.as_tensor(states).to(torch.int64)
+    full = int((st == 1).sum().item()) * block_q * block_k
+    words = np.asarray(torch.as_tensor(partial_bits).numpy()).view(np.uint32)
+    per_tile = np.unpackbits(words.view(np.uint8).reshape(words.shape[0], -1), axis=-1).sum(-1)
+    pidx = torch.as_tensor(partial_index)[st > 1].numpy()
+    pidx = np.clip(pidx, 0, words.shape[0] - 1)
+    return full + int(per_tile[pidx].sum())
 
 
 def make_inputs(w: Workload, seed=0):
