@@ -11,6 +11,9 @@ line on stdout:
              the current kernel source exists under profiles/) HBM traffic
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
 
+Element-level mask workloads (--workload causal_elem_bf16) run bsattn_fwd_elem
+the same way, counting 4*D FLOPs per kept (query, key) element.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
@@ -89,6 +92,116 @@ def cpu_baseline(w, q, k, v, mask, budget_s):
                       % (len(rows), total, stride, t)}
 
 
+def cpu_baseline_elem(w, q, k, v, st, pidx, pbits, kept_per_row, budget_s):
+    """The oracle's element-mask forward on a bounded, evenly spaced row sample."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    total = w.B * w.H * w.S
+    calib = np.arange(0, total, max(1, total // 256), dtype=np.int64)[:256]
+    t0 = time.perf_counter()
+    oracle.fwd_rows_elem(q, k, v, st, pidx, pbits, w.block_q, w.block_k, w.scale, calib)
+    per_row = (time.perf_counter() - t0) / len(calib)
+    n = int(min(total, max(len(calib), budget_s / max(per_row, 1e-9))))
+    stride = max(1, total // n)
+    rows = np.arange(0, total, stride, dtype=np.int64)[:n]
+    t0 = time.perf_counter()
+    oracle.fwd_rows_elem(q, k, v, st, pidx, pbits, w.block_q, w.block_k, w.scale, rows)
+    t = time.perf_counter() - t0
+    fl = float(sum(4 * w.D * kept_per_row(int(r)) for r in rows))
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d query rows (every %dth), each over its kept keys; %.1f s"
+                      % (len(rows), total, stride, t)}
+
+
+def bench_elem(args, torch, bs, W):
+    """One step = bsattn_fwd_elem (element-level plan + attention)."""
+    w = W.ELEM_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs" % w.name)
+    q, k, v, _ = W.make_inputs(w)
+    st, pidx, pbits = W.make_elem_mask(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    sd, pd, bd = st.to(dev), pidx.to(dev), pbits.to(dev)
+    kept = W.kept_elements(st, pidx, pbits, w.block_q, w.block_k)
+    flops = 4.0 * w.D * kept
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(bs.workspace_size(w.B, w.H, w.S, w.block_q, w.block_k), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(cfg):
+        bs.fwd_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                    workspace=ws, config=cfg)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    if args.config:
+        cfg = tuple(int(x) for x in args.config.split(","))
+    else:
+        log("bench: timing the element-mask tile configs (untimed for the result)")
+        best = None
+        for c in bs.list_configs_elem(torch.bfloat16, w.D, w.block_q, w.block_k):
+            c = c.as_tuple()
+            for _ in range(3):
+                run(c)
+            t = timed(lambda: run(c), 10)
+            log("  tune cfg=%s t_mean=%.4e" % (c, t * 1e-3))
+            if best is None or t < best[0]:
+                best = (t, c)
+        cfg = best[1]
+    log("bench: warmup %d, timed %d steps, config %s" % (args.warmup, args.steps, cfg))
+    for _ in range(args.warmup):
+        run(cfg)
+    torch.cuda.synchronize()
+    ms_step = timed(lambda: run(cfg), args.steps)
+    plan_ws = bs.plan_elem(sd, pd, bd, w.S, w.block_q, w.block_k)
+    attn = lambda: bs.fwd_planned_elem(qd, kd, vd, bd, plan_ws, w.block_q, w.block_k, w.scale,
+                                       out=out, lse=lse, config=cfg)
+    for _ in range(3):
+        attn()
+    torch.cuda.synchronize()
+    ms_attn = timed(attn, args.steps)
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    traffic = traffic_from_profiles(w.name, cfg)
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "attn_bf16_kernel", "kernel_ms": ms_attn}
+    if traffic:
+        roofline["hbm_gbs"] = traffic / (ms_attn * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_k": w.block_k, "mask": w.mask_kind,
+                   "kept_elements": kept, "density": kept / (w.B * w.H * w.S * w.S),
+                   "tile_config": list(cfg), "flops_per_step": flops},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        assert w.mask_kind == "token_causal"
+        kept_row = lambda r: (r % w.S) + 1  # a token-causal row keeps its s + 1 first keys
+        res["cpu_baseline"] = cpu_baseline_elem(w, q, k, v, st, pidx, pbits, kept_row,
+                                                args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +239,9 @@ def main():
     if not os.path.exists(bs.LIB_PATH):
         from block_sparse_flash_mask_amd import build
         build.build()
+    if args.workload in W.ELEM_WORKLOADS:
+        bench_elem(args, torch, bs, W)
+        return
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
