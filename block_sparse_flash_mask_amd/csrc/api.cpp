@@ -560,14 +560,21 @@ int bsattn_fwd_planned_elem(const void* q, const void* k, const void* v, void* o
         return BSATTN_ERR_ALIAS;
     const Variant* var = find_elem(dtype, D, block_q, block_k, cfg);
     if (!var) return BSATTN_ERR_UNSUPPORTED;
+    if (is_pair(*var) && n_k > kPairMaxBlocks) return BSATTN_ERR_UNSUPPORTED;
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
     const char* ws = (const char*)workspace;
     a.counts = (const int32_t*)ws;
     a.list = (const int32_t*)(ws + L.lists);
     a.ell_stride = n_k;
-    a.order = (const int32_t*)(ws + L.order);
-    a.nrows = (int)L.R;
-    a.chunk = (int)L.chunk;
+    if (is_pair(*var)) {
+        a.order = (const int32_t*)(ws + L.porder);
+        a.nrows = (int)L.P;
+        a.chunk = (int)L.pchunk;
+    } else {
+        a.order = (const int32_t*)(ws + L.order);
+        a.nrows = (int)L.R;
+        a.chunk = (int)L.chunk;
+    }
     a.pbits = partial_bits;
     a.n_tiles = n_tiles;
     return run_attention(a, *var, (hipStream_t)stream);
@@ -589,7 +596,8 @@ int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* 
         return BSATTN_ERR_ALIGN;
     if (check_ws_alias(workspace, need, q, k, v, out, lse, B, H, S, D, dtype)) return BSATTN_ERR_ALIAS;
     // Resolve the tile config before any device work.
-    if (!find_elem(dtype, D, block_q, block_k, cfg)) return BSATTN_ERR_UNSUPPORTED;
+    const Variant* var = find_elem(dtype, D, block_q, block_k, cfg);
+    if (!var || (is_pair(*var) && S / block_k > kPairMaxBlocks)) return BSATTN_ERR_UNSUPPORTED;
     rc = bsattn_plan_elem(block_states, partial_index, n_tiles, B, H, S, block_q, block_k, workspace,
                           workspace_bytes, stream);
     if (rc) return rc;

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     static_assert(!PAIR || (WAVES == 8 && NQ == 1 && !PIPE), "row pairs: two 4-wave groups");
 
     static_assert(ST == 2 || (ST == 3 && !PIPE), "three stages use the plain schedule");
-    static_assert(!ELEM || (!PIPE && !PAIR && NQ == 1), "element masks: plain schedule, one row");
+    static_assert(!ELEM || (!PIPE && NQ == 1), "element masks: plain schedule, one 32-row tile per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t v0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t k1s[G::BYTES];
@@ -89,6 +89,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     __shared__ uint32_t pair_bits[PAIR ? 2 * (kPairMaxBlocks / 32) : 1];
     __shared__ uint32_t pair_list[PAIR ? kPairMaxBlocks : 1];
     __shared__ int pair_cnt[1];
+    // element masks on row pairs: tile + 1 of each key block of either row (0: full)
+    __shared__ uint16_t pair_tile[PAIR && ELEM ? 2 * kPairMaxBlocks : 1];
     const int grp = PAIR ? wave >> 2 : 0;
     if constexpr (PAIR) {
         if (a.n_k > kPairMaxBlocks) return;  // the host rejects such shapes first
@@ -110,8 +112,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             row_list(a, ra + side, b0, c0);
             for (int i = tid; i < c0; i += WAVES * 64) {
                 int kj = a.list[b0 + i];
+                int tile1 = 0;
+                if constexpr (ELEM) {
+                    tile1 = kj < 0 ? 0 : kj >> 16;
+                    kj &= 0xffff;
+                }
                 kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
                 atomicOr(&pair_bits[side * (kPairMaxBlocks / 32) + (kj >> 5)], 1u << (kj & 31));
+                if constexpr (ELEM) pair_tile[side * kPairMaxBlocks + kj] = (uint16_t)tile1;
             }
         }
         __syncthreads();
@@ -412,7 +420,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
         if (mine(t)) {
             SAcc s = qk(kcur);
-            if constexpr (ELEM) apply_tile(s, e_cur, t);
+            if constexpr (ELEM && PAIR)  // this group's own tile of the block
+                apply_tile(s, (int)pair_tile[grp * kPairMaxBlocks + (e_cur & 0xffff)] << 16, t);
+            else if constexpr (ELEM)
+                apply_tile(s, e_cur, t);
             update_max(s);
             const PTile p = exps(s);
             pv(p, vcur);
@@ -536,13 +547,18 @@ static const Variant kBf16Variants[] = {
     BSATTN_BF16_PAIR(64, 64, 3, 4), BSATTN_BF16_PAIR(64, 64, 2, 4), BSATTN_BF16_PAIR(64, 128, 2, 2),
 };
 
-// Element-level masks (plain schedule, one 32-row query tile per wave, no row
-// pairs): the best block-mask configs of each D.
+// Element-level masks (plain schedule, one 32-row query tile per wave): the best
+// block-mask configs of each D, row pairs included.
 #define BSATTN_BF16_ELEM(D, W, TK, ST, OCC) \
     {1, D, 32 * W, TK, W, ST, &launch_bf16<D, W, TK, 1, 0, ST, OCC, 0, 1>}
 
+#define BSATTN_BF16_ELEM_PAIR(D, TK, ST, OCC) \
+    {1, D, 256, TK, 8, ST, &launch_bf16<D, 8, TK, 1, 0, ST, OCC, 1, 1>}
+
 static const Variant kBf16ElemVariants[] = {
     BSATTN_BF16_ELEM(128, 4, 32, 3, 3), BSATTN_BF16_ELEM(128, 4, 64, 2, 2), BSATTN_BF16_ELEM(128, 2, 32, 3, 3),
+    BSATTN_BF16_ELEM_PAIR(128, 128, 2, 2), BSATTN_BF16_ELEM_PAIR(128, 64, 2, 2),
+    BSATTN_BF16_ELEM_PAIR(64, 64, 2, 4), BSATTN_BF16_ELEM_PAIR(64, 128, 2, 2),
     BSATTN_BF16_ELEM(64, 4, 64, 2, 4),  BSATTN_BF16_ELEM(64, 4, 32, 2, 5),  BSATTN_BF16_ELEM(64, 4, 128, 2, 2),
     BSATTN_BF16_ELEM(64, 2, 64, 3, 2),
 };

@@ -219,8 +219,8 @@ int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_
  * S / block_k <= 65536, else BSATTN_ERR_SHAPE.  The workspace is the same size
  * as for bsattn_fwd (bsattn_workspace_size) and has the plan layout of
  * bsattn_plan, except that a list entry of a partial block is kj | (tile + 1) << 16.
- * Tile configs: bsattn_list_configs_elem (row-pair configs are not built for
- * element masks). */
+ * Tile configs: bsattn_list_configs_elem (row-pair configs, tile_q 256, need
+ * block_q 128 and at most 2048 key blocks per row, as for block masks). */
 
 /* Plan for an element-level mask: bsattn_plan's lists and dispatch orders over
  * the non-empty blocks, each entry carrying its tile.  Arguments and ownership as

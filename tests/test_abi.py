@@ -281,4 +281,6 @@ def test_elem_configs(lib):
         assert len(cfgs) >= 3
         assert bs.list_configs_elem(__import__("torch").bfloat16, D, 64, 64)  # tile_q 64 too
         for c in cfgs:
-            assert c.tile_q in (64, 128) and c.waves in (2, 4) and c.stages in (2, 3)
+            assert (c.tile_q, c.waves) in ((64, 2), (128, 4), (256, 8)) and c.stages in (2, 3)
+        assert any(c.tile_q == 256 for c in cfgs)  # row pairs
+        assert not any(c.tile_q == 256 for c in bs.list_configs_elem(__import__("torch").bfloat16, D, 64, 64))
