@@ -65,6 +65,8 @@ def configure(lib):
     lib.oracle_fwd_rows_elem.argtypes = [p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64,
                                          i64, f32, p, i64, p, p, i32]
     lib.oracle_fwd_rows_elem.restype = i32
+    lib.oracle_ragged_dot.argtypes = [p, p, i32, p, i64, i64, i64, i64, p, i32]
+    lib.oracle_ragged_dot.restype = i32
     lib.oracle_probs.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p]
     lib.oracle_probs.restype = i32
     lib.oracle_compact.argtypes = [p, i64, i64, p, p]
@@ -227,6 +229,34 @@ def fwd_rows_elem(q, k, v, states, pidx, pbits, block_q, block_k, scale, rows, n
     if rc:
         raise ValueError("oracle_fwd_rows_elem failed with code %d" % rc)
     return out, lse
+
+
+def ragged_dot(lhs, rhs, group_sizes, nthreads=0):
+    """Ragged dot ("Pallas-Triton kernels and kernel auto-tuning", section "Ragged
+    Dot"): lhs [M, K], rhs [G, K, N], group_sizes [G] (int, >= 0, sum <= M).
+    Returns out float64 [M, N]; rows past the sum of the sizes are 0."""
+    lib = _load()
+    la, dt = _as_raw(lhs)
+    ra, dt2 = _as_raw(rhs)
+    if dt != dt2:
+        raise TypeError("lhs and rhs must share a dtype")
+    try:
+        import torch
+        if isinstance(group_sizes, torch.Tensor):
+            group_sizes = group_sizes.cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    gs = np.ascontiguousarray(np.asarray(group_sizes, dtype=np.int32))
+    M, K = la.shape
+    G, K2, N = ra.shape
+    if K2 != K or gs.shape != (G,):
+        raise ValueError("shapes: lhs [M,K], rhs [G,K,N], group_sizes [G]")
+    out = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_ragged_dot(la.ctypes.data, ra.ctypes.data, dt, gs.ctypes.data, G, M, K, N,
+                               out.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_ragged_dot failed with code %d" % rc)
+    return out
 
 
 def probs(q, k, v, mask, block_q, block_k, scale):

@@ -50,6 +50,15 @@
  * pbits[n_tiles][block_q][block_k / 32]).  Everything else is as above, with the
  * kept elements in place of the active keys; a row with no kept element has
  * out = 0 and lse = -inf.
+ *
+ * Ragged dot (oracle_ragged_dot): "Pallas-Triton kernels and kernel auto-tuning",
+ * section "Ragged Dot (Group Matrix Multiplication)": the right-hand side is a
+ * stack of G expert matrices rhs[g][K][N]; the rows of lhs[M][K] are assigned to
+ * the experts in order, group g taking the next group_sizes[g] rows, and output
+ * row i is lhs row i times the matrix of its group.  Readings: rows past the sum of
+ * the group sizes belong to no group and are 0; a negative size or a sum above M
+ * is a bad argument.  out[i][n] = sum over k ascending of lhs[i][k] * rhs[g][k][n],
+ * in fp64 from the exactly widened inputs.
  */
 #include <math.h>
 #include <stdint.h>
@@ -360,4 +369,36 @@ int oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* Ragged dot: out is double[M][N].  Returns 0 on success, nonzero on a bad
+ * argument (nothing written). */
+int oracle_ragged_dot(const void* lhs, const void* rhs, int dtype, const int32_t* group_sizes,
+                      int64_t G, int64_t M, int64_t K, int64_t N, double* out, int nthreads) {
+    if (!lhs || !rhs || !group_sizes || !out) return 1;
+    if (G <= 0 || M < 0 || K <= 0 || N <= 0) return 2;
+    if (dtype < ORC_F32 || dtype > ORC_F64) return 3;
+    int64_t total = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (group_sizes[g] < 0) return 2;
+        total += group_sizes[g];
+    }
+    if (total > M) return 2;
+    set_threads(nthreads);
+    int64_t start = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        const int64_t end = start + group_sizes[g];
+#pragma omp parallel for schedule(static)
+        for (int64_t i = start; i < end; ++i)
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += widen(lhs, dtype, i * K + k) * widen(rhs, dtype, (g * K + k) * N + n);
+                out[i * N + n] = acc;
+            }
+        start = end;
+    }
+    for (int64_t i = total; i < M; ++i)
+        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;
+    return 0;
 }

@@ -33,6 +33,13 @@ Element-level masks (block states 0/1/partial + bit tiles):
   elem_empty_row    a query row whose only active block is partial with that
                     row's bits all clear gives out == 0, lse == -inf
   elem_rows_match   the selected-rows entry point equals the full forward
+Ragged dot (expert matrices stacked on the right, rows assigned in order):
+  ragged_hand       a 4-row example worked out by hand (expert 1 empty, a tail row)
+  ragged_one_group  one group of all rows equals numpy matmul
+  ragged_permute    reordering the experts with their row blocks reorders the rows
+  ragged_linear     out(X, a W1 + b W2) == a out(X, W1) + b out(X, W2)
+  ragged_tail       rows past the sum of the sizes are 0; empty groups change nothing
+  ragged_bf16       bf16 inputs give the same result as their exact fp64 values
 """
 import json
 import math
@@ -380,10 +387,74 @@ def elem_rows_match(orc):
     _close(rl, lse.reshape(-1)[rows], 0.0, "rows lse")
 
 
+def ragged_hand(orc):
+    # lhs rows (0,1) (2,3) (4,5) (6,7); experts [[0,1],[2,3]], [[4,5],[6,7]],
+    # [[8,9],[10,11]]; sizes (1, 0, 2): row 0 uses expert 0: (0*0+1*2, 0*1+1*3) = (2, 3);
+    # rows 1, 2 use expert 2: (2*8+3*10, 2*9+3*11) = (46, 51), (4*8+5*10, 4*9+5*11) =
+    # (82, 91); row 3 belongs to no group: (0, 0).
+    lhs = np.arange(8, dtype=np.float64).reshape(4, 2)
+    rhs = np.arange(12, dtype=np.float64).reshape(3, 2, 2)
+    out = orc.ragged_dot(lhs, rhs, [1, 0, 2])
+    assert np.array_equal(out, np.array([[2, 3], [46, 51], [82, 91], [0, 0]], dtype=np.float64))
+
+
+def _ragged_inputs(M, K, N, G, seed, dt=torch.float64):
+    x = _rand((M, K), seed, dt)
+    w = _rand((G, K, N), seed + 1, dt)
+    return x, w
+
+
+def ragged_one_group(orc):
+    x, w = _ragged_inputs(7, 5, 3, 1, 71)
+    out = orc.ragged_dot(x, w, [7])
+    _close(out, x.numpy() @ w[0].numpy(), TOL, "one group")
+
+
+def ragged_permute(orc):
+    M, K, N = 9, 4, 3
+    x, w = _ragged_inputs(M, K, N, 3, 72)
+    sizes = [2, 4, 3]
+    out = orc.ragged_dot(x, w, sizes)
+    # experts in the order (2, 0, 1), the rows moved with them
+    xa = x.numpy()
+    blocks = [xa[0:2], xa[2:6], xa[6:9]]
+    xp = np.concatenate([blocks[2], blocks[0], blocks[1]])
+    wp = w.numpy()[[2, 0, 1]]
+    outp = orc.ragged_dot(xp, wp, [3, 2, 4])
+    _close(outp, np.concatenate([out[6:9], out[0:2], out[2:6]]), TOL, "permute")
+
+
+def ragged_linear(orc):
+    x, w1 = _ragged_inputs(10, 6, 4, 3, 73)
+    _, w2 = _ragged_inputs(10, 6, 4, 3, 74)
+    sizes = [3, 3, 4]
+    a, b = 0.75, -1.5
+    lhs = orc.ragged_dot(x, a * w1 + b * w2, sizes)
+    rhs = a * orc.ragged_dot(x, w1, sizes) + b * orc.ragged_dot(x, w2, sizes)
+    _close(lhs, rhs, 1e-13, "linear")
+
+
+def ragged_tail(orc):
+    x, w = _ragged_inputs(12, 5, 3, 4, 75)
+    out = orc.ragged_dot(x, w, [0, 5, 0, 4])
+    assert np.all(out[9:] == 0.0)
+    # the same rows through a 2-expert stack without the empty experts
+    out2 = orc.ragged_dot(x, w[torch.tensor([1, 3])].contiguous(), [5, 4])
+    _close(out, out2, 0.0, "empty groups")
+
+
+def ragged_bf16(orc):
+    x, w = _ragged_inputs(6, 8, 5, 2, 76, torch.bfloat16)
+    out = orc.ragged_dot(x, w, [2, 3])
+    ref = orc.ragged_dot(x.to(torch.float64), w.to(torch.float64), [2, 3])
+    _close(out, ref, 0.0, "bf16 widening")
+
+
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
        bf16_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
-       elem_token_causal, elem_empty_row, elem_rows_match]
+       elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_one_group,
+       ragged_permute, ragged_linear, ragged_tail, ragged_bf16]
 
 
 def run_all(orc):

@@ -56,6 +56,16 @@ MUTANTS = {
                                 "const int64_t i = j % p->block_q, c = j % p->block_k;")],
     "elem_tile_index_ignored": [("(int64_t)p->pidx[bi] * p->block_q", "(int64_t)0 * p->block_q")],
     "elem_partial_as_empty": [("if (!p->pidx || blk == 1) return 1;", "if (!p->pidx || blk == 1) return 1;\n    if (blk > 1) return 0;")],
+    "ragged_group_start_late": [("const int64_t end = start + group_sizes[g];",
+                                 "const int64_t end = start + group_sizes[g];\n        const int64_t start1 = start + (group_sizes[g] > 0);"),
+                                ("for (int64_t i = start; i < end; ++i)\n            for (int64_t n = 0; n < N; ++n) {",
+                                 "for (int64_t i = start1; i < end; ++i)\n            for (int64_t n = 0; n < N; ++n) {")],
+    "ragged_next_expert": [("widen(rhs, dtype, (g * K + k) * N + n)",
+                            "widen(rhs, dtype, (((g + 1) % G) * K + k) * N + n)")],
+    "ragged_rhs_transposed": [("widen(rhs, dtype, (g * K + k) * N + n)",
+                               "widen(rhs, dtype, (g * K + (n % K)) * N + (k % N))")],
+    "ragged_tail_not_zeroed": [("for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;",
+                                "for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 1.0;")],
     "compact_skips_last_column": [("for (int64_t kj = 0; kj < n_k; ++kj)\n            if (mask[r * n_k + kj])",
                                    "for (int64_t kj = 0; kj < n_k - 1; ++kj)\n            if (mask[r * n_k + kj])")],
 }
