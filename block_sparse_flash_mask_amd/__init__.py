@@ -93,6 +93,8 @@ def library():
         "bsattn_fwd_elem": ([p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
                              p, sz, cfgp, p], i32),
         "bsattn_list_configs_elem": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
+        "bsattn_ragged_dot_workspace_size": ([i32, i32, szp], i32),
+        "bsattn_ragged_dot": ([p, p, p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
         "bsattn_load_tune_cache": ([ctypes.c_char_p], i32),
         "bsattn_clear_tune_cache": ([], None),
     }
@@ -371,6 +373,33 @@ def list_configs_elem(dtype, D, block_q, block_k):
     arr = (TileConfig * max(n.value, 1))()
     _check(lib.bsattn_list_configs_elem(code, D, block_q, block_k, arr, n.value, ctypes.byref(n)))
     return [arr[i] for i in range(n.value)]
+
+
+def ragged_dot(lhs, rhs, group_sizes, *, out=None, out_dtype=None, workspace=None, stream=None):
+    """Ragged dot (bsattn_ragged_dot): lhs [M, K] bf16, rhs [G, K, N] bf16,
+    group_sizes [G] int32 on the device.  Returns out [M, N] (bf16, or out_dtype)."""
+    if lhs.dtype != torch.bfloat16 or rhs.dtype != torch.bfloat16:
+        raise TypeError("lhs and rhs must be bfloat16")
+    if lhs.dim() != 2 or rhs.dim() != 3 or rhs.shape[1] != lhs.shape[1]:
+        raise ValueError("shapes: lhs [M, K], rhs [G, K, N]")
+    if not (lhs.is_contiguous() and rhs.is_contiguous() and group_sizes.is_contiguous()):
+        raise ValueError("lhs, rhs and group_sizes must be contiguous")
+    if group_sizes.dtype != torch.int32 or group_sizes.shape != (rhs.shape[0],):
+        raise ValueError("group_sizes must be int32 [G]")
+    M, K = lhs.shape
+    G, _, N = rhs.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=lhs.device)
+    code = _dtype_code(out)
+    n = ctypes.c_size_t(0)
+    lib = library()
+    _check(lib.bsattn_ragged_dot_workspace_size(M, G, ctypes.byref(n)))
+    ws = _workspace(n.value, lhs.device, workspace)
+    rc = lib.bsattn_ragged_dot(_ptr(lhs), _ptr(rhs), _ptr(group_sizes), _ptr(out), M, K, N, G,
+                               _dtype_code(lhs), code, _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(rc)
+    return out
 
 
 def list_configs(dtype, D, block_q, block_k):

@@ -34,6 +34,14 @@ hipError_t launch_plan(const uint8_t* mask, int64_t R, int n_q, int n_k, int32_t
 hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int64_t R, int n_k,
                                const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
 
+// Ragged dot (ragged_dot.hip): the work-item bound of a plan (one item per
+// (128-row tile, group) pair that share rows), the workspace it needs, and the
+// launch (plan, zero tail, products) on stream.
+inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
+inline size_t ragged_ws_bytes(int64_t M, int64_t G) { return (size_t)ragged_max_items(M, G) * 16 + 16; }
+hipError_t launch_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
+                             int K, int N, int G, int out_f32, void* workspace, hipStream_t stream);
+
 // Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block
 // lists in LDS, so they take masks of at most this many key blocks per row.
 constexpr int kPairMaxBlocks = 2048;

@@ -1,0 +1,261 @@
+// ragged_dot.hip -- ragged dot (grouped matrix multiplication) for gfx950.
+//
+// What is computed: "Pallas-Triton kernels and kernel auto-tuning" (robertdyro.com),
+// section "Ragged Dot (Group Matrix Multiplication)": rhs is a stack of G expert
+// matrices [G][K][N]; the rows of lhs [M][K] are assigned to the experts in order,
+// group g taking the next group_sizes[g] rows, and output row i is lhs row i times
+// its group's matrix.  Rows past the sum of the sizes belong to no group and are
+// written as 0.  bf16 in, fp32 accumulation, bf16 or fp32 out.
+//
+// Plan (ragged_plan_kernel, one workgroup): the groups' row ranges (a scan of the
+// sizes, clamped into [0, M]) and the work items: one item per (128-row tile, group)
+// pair that share rows, in group order, each with the row range [lo, hi) it owns
+// (the compaction idea of the attention path: a tile visits only the groups that
+// touch it).  A tile that straddles a group boundary is visited once per group and
+// each visit stores only its own rows, so no two items write the same row.
+//
+// Kernel: one workgroup of 4 waves per (item, 128-column tile); wave w owns 32 rows.
+// C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on v_mfma_f32_32x32x16_bf16: the expert
+// tile W[g][k0..k0+63][n0..n0+127] goes HBM -> LDS by buffer loads with the LDS flag
+// in the transposed-read layout of bf16_layout.h (the V layout of the attention
+// kernel, row stride N), two stages; the A operand comes from ds_read_b64_tr_b16;
+// the B operand X^T is the wave's own rows of lhs, loaded straight into VGPRs one
+// step ahead.
+#include "bf16_layout.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace bsattn {
+
+constexpr int kRaggedTM = 128;     // rows per tile
+constexpr int kRaggedTN = 128;     // columns per tile
+constexpr int kRaggedTK = 64;      // k per step
+constexpr int kRaggedThreads = 1024;
+
+// Inclusive scan over the 1024 threads of the plan workgroup (wave scans, then a
+// scan of the wave totals).
+__device__ __forceinline__ int64_t block_scan(int64_t x, int64_t* wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int64_t t = lane < kRaggedThreads / 64 ? wave_tot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t y = __shfl_up(t, off, 64);
+            if (lane >= off) t += y;
+        }
+        if (lane < kRaggedThreads / 64) wave_tot[lane] = t;
+    }
+    __syncthreads();
+    const int64_t r = x + (wave > 0 ? wave_tot[wave - 1] : 0);
+    __syncthreads();
+    return r;
+}
+
+// items[i] = {row tile, group, lo, hi}; *n_items = their number.
+__global__ __launch_bounds__(kRaggedThreads) void ragged_plan_kernel(const int32_t* __restrict__ group_sizes,
+                                                                     int G, int M, int4* __restrict__ items,
+                                                                     int32_t* __restrict__ n_items) {
+    __shared__ int64_t wave_tot[kRaggedThreads / 64];
+    __shared__ int64_t carry[2];  // rows, items before this chunk
+    const int tid = threadIdx.x;
+    if (tid == 0) carry[0] = carry[1] = 0;
+    __syncthreads();
+    for (int g0 = 0; g0 < G; g0 += kRaggedThreads) {
+        const int g = g0 + tid;
+        const int64_t sz = g < G ? (group_sizes[g] > 0 ? group_sizes[g] : 0) : 0;
+        const int64_t rows_incl = block_scan(sz, wave_tot);
+        const int64_t r0 = carry[0];
+        int64_t start = r0 + rows_incl - sz, end = r0 + rows_incl;
+        start = start < M ? start : M;
+        end = end < M ? end : M;
+        const int64_t cnt = end > start ? (end - 1) / kRaggedTM - start / kRaggedTM + 1 : 0;
+        const int64_t items_incl = block_scan(cnt, wave_tot);
+        const int64_t pos = carry[1] + items_incl - cnt;
+        for (int64_t i = 0; i < cnt; ++i) {
+            const int64_t t = start / kRaggedTM + i;
+            const int64_t lo = start > t * kRaggedTM ? start : t * kRaggedTM;
+            const int64_t hi = end < (t + 1) * kRaggedTM ? end : (t + 1) * kRaggedTM;
+            items[pos + i] = make_int4((int)t, g, (int)lo, (int)hi);
+        }
+        __syncthreads();
+        if (tid == kRaggedThreads - 1) {
+            carry[0] = r0 + rows_incl;
+            carry[1] = carry[1] + items_incl;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) n_items[0] = (int32_t)carry[1];
+}
+
+// Rows [total, M) that no group owns are zero: a grid-stride fill run before the
+// products (it reads the sizes itself).
+template <int OUT_F32>
+__global__ __launch_bounds__(256) void ragged_tail_kernel(const int32_t* __restrict__ group_sizes, int G, int M,
+                                                          int N, void* __restrict__ out) {
+    __shared__ int64_t total_s;
+    if (threadIdx.x == 0) {
+        int64_t t = 0;
+        for (int g = 0; g < G; ++g) t += group_sizes[g] > 0 ? group_sizes[g] : 0;
+        total_s = t < M ? t : M;
+    }
+    __syncthreads();
+    const int64_t first = total_s * N, last = (int64_t)M * N;
+    for (int64_t i = first + (int64_t)blockIdx.x * 256 + threadIdx.x; i < last; i += (int64_t)gridDim.x * 256) {
+        if constexpr (OUT_F32)
+            ((float*)out)[i] = 0.f;
+        else
+            ((uint16_t*)out)[i] = 0;
+    }
+}
+
+template <int OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot_kernel(
+    const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
+    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N) {
+    typedef TileGeom<kRaggedTN, kRaggedTK> G;  // W^T tile: "D" = 128 columns, "keys" = 64 k
+    constexpr int KS = kRaggedTK / 16, MT = G::MT, MD = G::MD;
+    __shared__ __attribute__((aligned(1024))) uint8_t w0s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t w1s[G::BYTES];
+
+    const int n_tiles = N / kRaggedTN;
+    const int item = blockIdx.x / n_tiles;
+    const int nt = blockIdx.x - item * n_tiles;
+    if (item >= wave_uniform(n_items[0])) return;
+    const int4 it = items[item];
+    const int tile = wave_uniform(it.x), grp = wave_uniform(it.y);
+    const int lo = wave_uniform(it.z), hi = wave_uniform(it.w);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int wave_s = wave_uniform(wave);
+    const int n0 = nt * kRaggedTN;
+
+    // this lane's lhs row (rows outside [lo, hi) are computed on a valid row and
+    // never stored)
+    int m = tile * kRaggedTM + 32 * wave + l32;
+    const bool store = m >= lo && m < hi;
+    m = m < M ? m : M - 1;
+    const u32x4* xrow = (const u32x4*)(lhs + (size_t)m * K);
+
+    // W tile DMA: the V layout of bf16_layout.h with row stride N.  Lane offsets as
+    // DmaPlan<128, 4, 64>::init with D replaced by N for the row part.
+    const int u = 2 * (lane & 31);
+    const int L = u & 15, gg = (u >> 4) & 1, hh = u >> 5;
+    const int v_lane = (8 * hh + (L >> 2)) * N + 32 * (lane >> 5) + 16 * gg + 4 * (L & 3);
+    constexpr int NV = G::VBLK / 2 / 4;  // DMA instructions per wave per tile
+    const uint16_t* wg = rhs + (size_t)grp * K * N + n0;
+    const int nrec = (int)((size_t)K * N * 2 - (size_t)n0 * 2);  // bytes from wg to the expert's end
+    auto issue = [&](int k0, uint8_t* wbuf) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int tb = 2 * (wave_s + i * 4);
+            const int md = tb % MD, r = (tb / MD) % 2, e = (tb / MD / 2) % 2, mt = tb / MD / 4;
+            const int uni = (k0 + 32 * mt + 16 * e + 4 * r) * N + 32 * md;
+            dma16(wg, nrec, (BSATTN_LDS void*)(wbuf + (wave_s + i * 4) * 1024), v_lane * 2, uni * 2);
+        }
+    };
+
+    f32x16 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
+    bf16x8 xf[KS], xn[KS];
+    auto load_x = [&](int k0, bf16x8 (&dst)[KS]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, xrow[(k0 + 16 * ks) / 8 + h]);
+    };
+    auto step = [&](const uint8_t* wbuf) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const uint8_t* vb = wbuf + (((mt * 2 + e) * 2) * MD + md) * 512 + lane * 8;
+                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb));
+                    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb + MD * 512));
+                    const bf16x8 wf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[mt * 2 + e], acc[md], 0, 0, 0);
+                }
+    };
+
+    const int n_steps = K / kRaggedTK;
+    issue(0, w0s);
+    load_x(0, xf);
+    for (int t = 0; t < n_steps; t += 2) {
+        // even step: tile in w0s, next into w1s
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this step's W tile and X
+        __syncthreads();
+        if (t + 1 < n_steps) {
+            issue((t + 1) * kRaggedTK, w1s);
+            load_x((t + 1) * kRaggedTK, xn);
+        }
+        step(w0s);
+        if (t + 1 >= n_steps) break;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) xf[ks] = xn[ks];
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        __syncthreads();
+        if (t + 2 < n_steps) {
+            issue((t + 2) * kRaggedTK, w0s);
+            load_x((t + 2) * kRaggedTK, xn);
+        }
+        step(w1s);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) xf[ks] = xn[ks];
+    }
+
+    // C^T[n][m]: lane (h, m) holds n = 32 md + 8 g4 + 4 h + u for u = 0..3
+    if (!store) return;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int n = n0 + 32 * md + 8 * g4 + 4 * h;
+            if constexpr (OUT_F32) {
+                float4 o;
+                o.x = acc[md][4 * g4 + 0];
+                o.y = acc[md][4 * g4 + 1];
+                o.z = acc[md][4 * g4 + 2];
+                o.w = acc[md][4 * g4 + 3];
+                *(float4*)((float*)out + (size_t)m * N + n) = o;
+            } else {
+                bf16x4 o;
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu) o[uu] = (__bf16)acc[md][4 * g4 + uu];
+                *(bf16x4*)((uint16_t*)out + (size_t)m * N + n) = o;
+            }
+        }
+}
+
+hipError_t launch_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
+                             int K, int N, int G, int out_f32, void* workspace, hipStream_t stream) {
+    int4* items = (int4*)workspace;
+    const int64_t max_items = ragged_max_items(M, G);
+    int32_t* n_items = (int32_t*)(items + max_items);
+    hipLaunchKernelGGL(ragged_plan_kernel, dim3(1), dim3(kRaggedThreads), 0, stream, group_sizes, G, M, items,
+                       n_items);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned tail_blocks = 256;
+    if (out_f32)
+        hipLaunchKernelGGL(ragged_tail_kernel<1>, dim3(tail_blocks), dim3(256), 0, stream, group_sizes, G, M, N, out);
+    else
+        hipLaunchKernelGGL(ragged_tail_kernel<0>, dim3(tail_blocks), dim3(256), 0, stream, group_sizes, G, M, N, out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t grid = max_items * (N / kRaggedTN);
+    if (out_f32)
+        hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,
+                           (const uint16_t*)rhs, items, n_items, out, M, K, N);
+    else
+        hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,
+                           (const uint16_t*)rhs, items, n_items, out, M, K, N);
+    return hipGetLastError();
+}
+
+}  // namespace bsattn

@@ -252,6 +252,30 @@ int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* 
 int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
                              int cap, int* n);
 
+/* ---- Ragged dot -------------------------------------------------------------------
+ * "Pallas-Triton kernels and kernel auto-tuning", section "Ragged Dot (Group Matrix
+ * Multiplication)": rhs is a stack of G expert matrices; the rows of lhs go to the
+ * experts in order, group g taking the next group_sizes[g] rows, and output row i
+ * is lhs row i times its group's matrix:
+ *   lhs          bf16 [M][K] row-major (device);
+ *   rhs          bf16 [G][K][N] row-major (device);
+ *   group_sizes  int32 [G] (device); a negative size counts as 0, and rows past M
+ *                are dropped (groups are clamped to [0, M));
+ *   out          [M][N], bf16 (out_dtype BSATTN_BF16, round to nearest even) or fp32
+ *                (BSATTN_F32); rows past the sum of the sizes are written as 0.
+ * fp32 accumulation.  K % 64 == 0, N % 128 == 0, K*N*2 < 2^31 (one expert is read
+ * through a buffer with a 32-bit range), else BSATTN_ERR_SHAPE; dtype must be
+ * BSATTN_BF16 (else BSATTN_ERR_UNSUPPORTED).  lhs, rhs, out and workspace 16-byte
+ * aligned, group_sizes 4-byte aligned (BSATTN_ERR_ALIGN); out or the workspace
+ * overlapping an input or each other gives BSATTN_ERR_ALIAS.  The workspace
+ * (bsattn_ragged_dot_workspace_size bytes, owned by the caller) holds the work
+ * plan: one item per (128-row tile, group) pair that share rows.  Asynchronous on
+ * stream; nothing is allocated. */
+int bsattn_ragged_dot_workspace_size(int M, int G, size_t* bytes);
+int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
+                      int K, int N, int G, int dtype, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of

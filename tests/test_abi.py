@@ -284,3 +284,32 @@ def test_elem_configs(lib):
             assert (c.tile_q, c.waves) in ((64, 2), (128, 4), (256, 8)) and c.stages in (2, 3)
         assert any(c.tile_q == 256 for c in cfgs)  # row pairs
         assert not any(c.tile_q == 256 for c in bs.list_configs_elem(__import__("torch").bfloat16, D, 64, 64))
+
+
+def test_ragged_argument_checks(lib):
+    """Ragged dot: every call below fails a host check (fake pointers)."""
+    p = ctypes.c_void_p
+    f = lib.bsattn_ragged_dot
+    # lhs rhs sizes out M K N G dtype out_dtype ws wsb stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), 256, 128, 256, 4, 1, 0, p(9 * A), 16, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    for i in (0, 1, 2, 3, 10):
+        assert call(i, None) == NULL
+    assert call(4, 0) == SHAPE and call(7, 0) == SHAPE
+    assert call(5, 96) == SHAPE and call(6, 200) == SHAPE          # K % 64, N % 128
+    big = list(ok)
+    big[5], big[6] = 1 << 20, 1024
+    assert f(*big) == SHAPE                                         # one expert of 2 GiB
+    assert call(8, 0) == UNSUP and call(9, 5) == UNSUP
+    assert call(11, 16) == WS
+    ok[11] = 1 << 16
+    assert call(0, p(A + 8)) == ALIGN and call(2, p(5 * A + 2)) == ALIGN and call(10, p(9 * A + 4)) == ALIGN
+    assert call(3, p(A + 64)) == ALIAS and call(10, p(7 * A + 256)) == ALIAS
+    n = ctypes.c_size_t(0)
+    assert lib.bsattn_ragged_dot_workspace_size(256, 4, ctypes.byref(n)) == OK
+    assert n.value == (2 + 4) * 16 + 16
+    assert lib.bsattn_ragged_dot_workspace_size(0, 4, ctypes.byref(n)) == SHAPE

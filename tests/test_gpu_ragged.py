@@ -1,0 +1,118 @@
+"""Ragged dot on the GPU (bsattn_ragged_dot) against the fp64 oracle on identical
+seeded bf16 inputs.
+
+Tolerance, derived from the arithmetic: products of bf16 values are exact in
+fp32; fp32 accumulation of K products in any order errs by at most
+K * 2^-24 * sum_k |x_k w_k|; a bf16 output adds a rounding of at most 2^-8
+|out| (half an ulp of 8 significant bits).  Every element is checked against
+that bound, and the mean error must be well below it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import bs, ensure_built, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, K, N, G, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = torch.randn(G, K, N, generator=g).to(torch.bfloat16)
+    return x, w
+
+
+def _check(x, w, sizes, out_dtype, what, rows=None):
+    """GPU result for sizes (as given, may hold negatives / overflow) against the
+    oracle on the sizes the library uses (negatives as 0, groups clamped to M)."""
+    ensure_built()
+    M, K = x.shape
+    G, _, N = w.shape
+    say("ragged", what, (M, K, N, G), out_dtype)
+    out = bs.ragged_dot(x.cuda(), w.cuda(), torch.as_tensor(sizes, dtype=torch.int32).cuda(),
+                        out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    eff, left = [], M
+    for s in sizes:
+        s = max(int(s), 0)
+        eff.append(min(s, left))
+        left -= eff[-1]
+    ref = oracle.ragged_dot(x, w, eff)
+    # |x| |w| row by row for the bound (fp64)
+    xa = np.abs(x.double().numpy())
+    wa = np.abs(w.double().numpy())
+    mag = np.zeros((M, N))
+    start = 0
+    for gi, s in enumerate(eff):
+        mag[start:start + s] = xa[start:start + s] @ wa[gi]
+        start += s
+    got = out.double().cpu().numpy()
+    if rows is not None:
+        got, ref, mag = got[rows], ref[rows], mag[rows]
+    bound = K * 2.0 ** -24 * mag + (2.0 ** -8 * np.abs(ref) if out_dtype == torch.bfloat16 else 0.0)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound + 1e-30), (what, float((err - bound).max()))
+    tail = ref == 0.0
+    assert np.all(got[np.all(tail, axis=1)] == 0.0), (what, "rows of no group must be 0")
+    # the accumulation error is far below its worst case; a bf16 output's rounding
+    # error is spread evenly up to half an ulp (between 2^-9 and 2^-8 of |out|), so
+    # its mean ratio to the 2^-8 |out| bound is about 0.35
+    rel = err[bound > 0] / bound[bound > 0]
+    assert rel.mean() < (0.25 if out_dtype == torch.float32 else 0.5), (what, float(rel.mean()))
+    return float(rel.max())
+
+
+CASES = [
+    # M, K, N, G, sizes
+    (128, 64, 128, 1, [128]),                       # one tile, one group
+    (300, 128, 256, 3, [100, 0, 150]),              # an empty group, a zero tail (50 rows)
+    (257, 64, 128, 5, [1, 2, 3, 4, 247]),           # many groups in one tile, ragged M
+    (512, 192, 384, 4, [130, 126, 129, 127]),       # every tile split between groups
+    (200, 64, 128, 3, [-5, 120, 500]),              # a negative size (0) and an overflow (clamped)
+    (1024, 256, 128, 2, [0, 1024]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:4])))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_ragged_small(case, out_dtype):
+    M, K, N, G, sizes = case
+    x, w = _inputs(M, K, N, G, seed=M + K + N)
+    _check(x, w, sizes, out_dtype, str(case))
+
+
+def test_ragged_two_calls_reuse_workspace():
+    """Two calls in a row on one workspace with different group sizes."""
+    ensure_built()
+    x, w = _inputs(384, 128, 256, 3, seed=5)
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    for sizes in ([200, 100, 84], [10, 300, 0]):
+        out = bs.ragged_dot(x.cuda(), w.cuda(), torch.tensor(sizes, dtype=torch.int32).cuda(),
+                            out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.ragged_dot(x, w, sizes)
+        assert np.allclose(out.double().cpu().numpy(), ref, rtol=0, atol=1e-2)
+
+
+def test_ragged_workload_sampled_rows():
+    """The full-size workload (M 32768, K 2048, N 2048, 8 experts) on sampled rows,
+    in the launch configuration bench.py times."""
+    wl = W.RAGGED_WORKLOADS["ragged_bf16"]
+    x, w, sizes = W.make_ragged(wl)
+    g = np.random.default_rng(11)
+    starts = np.concatenate([[0], np.cumsum(sizes.numpy())])
+    rows = set(int(r) for r in g.integers(0, wl.M, 24))
+    rows |= {int(s) for s in starts[:-1]} | {int(s) - 1 for s in starts[1:]}  # group edges
+    rows = np.array(sorted(r for r in rows if 0 <= r < wl.M))
+    ensure_built()
+    out = bs.ragged_dot(x.cuda(), w.cuda(), sizes.cuda())
+    torch.cuda.synchronize()
+    # oracle on the sampled rows only: each row against its own expert
+    grp = np.searchsorted(starts, rows, side="right") - 1
+    ref = np.stack([x[r].double().numpy() @ w[gi].double().numpy() for r, gi in zip(rows, grp)])
+    mag = np.stack([np.abs(x[r].double().numpy()) @ np.abs(w[gi].double().numpy()) for r, gi in zip(rows, grp)])
+    got = out.double().cpu().numpy()[rows]
+    bound = wl.K * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= bound)

@@ -23,6 +23,11 @@ Element-level mask workload (block states + bit tiles, see bsattn.h):
                     below the diagonal full, diagonal blocks partial through one shared
                     lower-triangular tile (query i keeps keys j <= i)
 
+Ragged dot workload (grouped matrix multiplication):
+
+  ragged_bf16       M=32768 K=2048 N=2048 G=8 bf16; rows routed to expert g with
+                    probability ~ 1/(g+1) (seed 3)
+
 Recipe: Q, K, V ~ N(0, 1) drawn in that order from one torch CPU generator seeded 0,
 each of shape [B,H,S,D] in fp32, then rounded to bf16 (round-to-nearest-even) for
 the bf16 workloads.  Random mask extras come from a separate torch CPU generator
@@ -156,6 +161,37 @@ def make_mask(w: Workload):
     if w.mask_kind == "token_causal":  # the non-empty blocks of the element mask
         return mask_causal(B, H, n_q, n_k)
     raise ValueError(w.mask_kind)
+
+
+@dataclass(frozen=True)
+class RaggedWorkload:
+    name: str
+    M: int
+    K: int
+    N: int
+    G: int
+    seed: int = 0
+
+
+# Ragged dot ("Pallas-Triton kernels and kernel auto-tuning", section "Ragged Dot"):
+# a mixture-of-experts layer's shape: M tokens routed to G experts.
+RAGGED_WORKLOADS = {
+    "ragged_bf16": RaggedWorkload("ragged_bf16", 32768, 2048, 2048, 8, 3),
+}
+
+
+def make_ragged(w: RaggedWorkload):
+    """lhs [M, K], rhs [G, K, N] ~ N(0, 1) rounded to bf16 (one CPU generator,
+    seed w.seed, lhs first), and group sizes: each of the M rows goes to expert g
+    with probability proportional to 1 / (g + 1) (a skewed routing, seeded),
+    counted per expert (int32 [G], sum M)."""
+    g = torch.Generator().manual_seed(w.seed)
+    lhs = torch.randn(w.M, w.K, generator=g).to(torch.bfloat16)
+    rhs = torch.randn(w.G, w.K, w.N, generator=g).to(torch.bfloat16)
+    probs = 1.0 / torch.arange(1, w.G + 1, dtype=torch.float64)
+    choice = torch.multinomial(probs / probs.sum(), w.M, replacement=True, generator=g)
+    sizes = torch.bincount(choice, minlength=w.G).to(torch.int32)
+    return lhs, rhs, sizes
 
 
 def pack_tiles(bits):
