@@ -12,7 +12,8 @@ line on stdout:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
 
 Element-level mask workloads (--workload causal_elem_bf16) run bsattn_fwd_elem
-the same way, counting 4*D FLOPs per kept (query, key) element.
+the same way, counting 4*D FLOPs per kept (query, key) element.  --workload
+ragged_bf16 runs the ragged dot (grouped matmul, 2*K*N FLOPs per grouped row).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -35,6 +36,7 @@ KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
                   "block_sparse_flash_mask_amd/csrc/attn_bf16_pp.hip",
                   "block_sparse_flash_mask_amd/csrc/bf16_layout.h",
                   "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
+                  "block_sparse_flash_mask_amd/csrc/ragged_dot.hip",
                   "block_sparse_flash_mask_amd/csrc/common.h"]
 
 
@@ -202,6 +204,88 @@ def bench_elem(args, torch, bs, W):
     print(json.dumps(res), flush=True)
 
 
+def bench_ragged(args, torch, bs, W):
+    """One step = bsattn_ragged_dot (plan + product) on resident inputs."""
+    import numpy as np
+    w = W.RAGGED_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs" % w.name)
+    x, wt, sizes = W.make_ragged(w)
+    xd, wd, sd = x.to(dev), wt.to(dev), sizes.to(dev)
+    rows = min(int(sizes.clamp(min=0).sum()), w.M)
+    flops = 2.0 * w.K * w.N * rows
+    out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    n = bs.ragged_plan(sd, w.M).numel()
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    step = lambda: bs.ragged_dot(xd, wd, sd, out=out, workspace=ws)
+    log("bench: warmup %d, timed %d steps" % (args.warmup, args.steps))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    plan_ws = bs.ragged_plan(sd, w.M)
+    prod = lambda: bs.ragged_dot_planned(xd, wd, plan_ws, out=out)
+    for _ in range(3):
+        prod()
+    torch.cuda.synchronize()
+    ms_kernel = timed(prod, args.steps)
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    traffic = traffic_from_profiles(w.name, (128, 128, 4, 2))
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "ragged_dot_kernel", "kernel_ms": ms_kernel}
+    if traffic:
+        roofline["hbm_gbs"] = traffic / (ms_kernel * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "ragged dot (grouped matmul) effective TFLOP/s + % bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
+                   "group_sizes": [int(v) for v in sizes], "tile": [128, 128, 64],
+                   "flops_per_step": flops},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        log("bench: timing the CPU oracle on a bounded sample")
+        # the first rows of every group, scaled so the oracle runs ~budget seconds
+        def sample(frac):
+            take = [max(1, int(int(v) * frac)) if int(v) > 0 else 0 for v in sizes]
+            starts = np.concatenate([[0], np.cumsum(sizes.numpy())])[:-1]
+            idx = np.concatenate([np.arange(s0, s0 + t) for s0, t in zip(starts, take)])
+            return x[torch.as_tensor(idx)].contiguous(), take
+        xs, take = sample(0.002)
+        t0 = time.perf_counter()
+        oracle.ragged_dot(xs, wt, take)
+        t_cal = time.perf_counter() - t0
+        frac = min(1.0, 0.002 * args.cpu_budget / max(t_cal, 1e-6))
+        xs, take = sample(frac)
+        t0 = time.perf_counter()
+        oracle.ragged_dot(xs, wt, take)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 2.0 * w.K * w.N * sum(take) / t / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": "the first %.2f %% of every group's rows (%d rows); %.1f s"
+                                         % (100 * frac, sum(take), t)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +325,9 @@ def main():
         build.build()
     if args.workload in W.ELEM_WORKLOADS:
         bench_elem(args, torch, bs, W)
+        return
+    if args.workload in W.RAGGED_WORKLOADS:
+        bench_ragged(args, torch, bs, W)
         return
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -95,6 +95,8 @@ def library():
         "bsattn_list_configs_elem": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
         "bsattn_ragged_dot_workspace_size": ([i32, i32, szp], i32),
         "bsattn_ragged_dot": ([p, p, p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
+        "bsattn_ragged_plan": ([p, i32, i32, p, sz, p], i32),
+        "bsattn_ragged_dot_planned": ([p, p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
         "bsattn_load_tune_cache": ([ctypes.c_char_p], i32),
         "bsattn_clear_tune_cache": ([], None),
     }
@@ -398,6 +400,32 @@ def ragged_dot(lhs, rhs, group_sizes, *, out=None, out_dtype=None, workspace=Non
     rc = lib.bsattn_ragged_dot(_ptr(lhs), _ptr(rhs), _ptr(group_sizes), _ptr(out), M, K, N, G,
                                _dtype_code(lhs), code, _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream))
+    _check(rc)
+    return out
+
+
+def ragged_plan(group_sizes, M, *, workspace=None, stream=None):
+    """The work plan of a ragged dot (bsattn_ragged_plan); returns the workspace."""
+    G = group_sizes.shape[0]
+    n = ctypes.c_size_t(0)
+    lib = library()
+    _check(lib.bsattn_ragged_dot_workspace_size(M, G, ctypes.byref(n)))
+    ws = _workspace(n.value, group_sizes.device, workspace)
+    _check(lib.bsattn_ragged_plan(_ptr(group_sizes), M, G, _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+    return ws
+
+
+def ragged_dot_planned(lhs, rhs, plan_ws, *, out=None, out_dtype=None, stream=None):
+    """The ragged-dot product alone on a plan from ragged_plan()."""
+    M, K = lhs.shape
+    G, _, N = rhs.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=lhs.device)
+    rc = library().bsattn_ragged_dot_planned(_ptr(lhs), _ptr(rhs), _ptr(out), M, K, N, G,
+                                             _dtype_code(lhs), _dtype_code(out), _ptr(plan_ws),
+                                             plan_ws.numel() * plan_ws.element_size(),
+                                             _stream(stream))
     _check(rc)
     return out
 

@@ -633,31 +633,69 @@ int bsattn_ragged_dot_workspace_size(int M, int G, size_t* bytes) {
     return BSATTN_OK;
 }
 
-int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
-                      int K, int N, int G, int dtype, int out_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-    if (!lhs || !rhs || !group_sizes || !out || !workspace) return BSATTN_ERR_NULL;
+int bsattn_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!group_sizes || !workspace) return BSATTN_ERR_NULL;
+    if (M <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
+    if (workspace_bytes < ragged_ws_bytes(M, G)) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(group_sizes, 4) || !is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
+    if (overlap(workspace, ragged_ws_bytes(M, G), group_sizes, (size_t)G * 4)) return BSATTN_ERR_ALIAS;
+    const hipError_t e = launch_ragged_plan(group_sizes, M, G, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
+                              int dtype, int out_dtype, const void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (!lhs || !rhs || !out || !workspace) return BSATTN_ERR_NULL;
     if (M <= 0 || K <= 0 || N <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
     if (K % 64 != 0 || N % 128 != 0) return BSATTN_ERR_SHAPE;
     if ((int64_t)K * N * 2 >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;  // one expert per buffer
     if (ragged_max_items(M, G) * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
     if (out_dtype != BSATTN_BF16 && out_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
-    if (workspace_bytes < ragged_ws_bytes(M, G)) return BSATTN_ERR_WORKSPACE;
-    if (!is_aligned(lhs, 16) || !is_aligned(rhs, 16) || !is_aligned(out, 16) ||
-        !is_aligned(group_sizes, 4) || !is_aligned(workspace, 16))
+    const size_t nw = ragged_ws_bytes(M, G);
+    if (workspace_bytes < nw) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(lhs, 16) || !is_aligned(rhs, 16) || !is_aligned(out, 16) || !is_aligned(workspace, 16))
         return BSATTN_ERR_ALIGN;
     const size_t nl = (size_t)M * K * 2, nr = (size_t)G * K * N * 2;
     const size_t no = (size_t)M * N * (out_dtype == BSATTN_F32 ? 4 : 2);
-    const size_t nw = ragged_ws_bytes(M, G), ng = (size_t)G * 4;
-    if (overlap(out, no, lhs, nl) || overlap(out, no, rhs, nr) || overlap(out, no, group_sizes, ng) ||
-        overlap(out, no, workspace, nw) || overlap(workspace, nw, lhs, nl) ||
-        overlap(workspace, nw, rhs, nr) || overlap(workspace, nw, group_sizes, ng))
+    if (overlap(out, no, lhs, nl) || overlap(out, no, rhs, nr) || overlap(out, no, workspace, nw) ||
+        overlap(workspace, nw, lhs, nl) || overlap(workspace, nw, rhs, nr))
         return BSATTN_ERR_ALIAS;
-    const hipError_t e = launch_ragged_dot(lhs, rhs, group_sizes, out, M, K, N, G,
-                                           out_dtype == BSATTN_F32, workspace, (hipStream_t)stream);
+    const hipError_t e = launch_ragged_planned(lhs, rhs, out, M, K, N, G, out_dtype == BSATTN_F32, workspace,
+                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
+}
+
+int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
+                      int K, int N, int G, int dtype, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!lhs || !rhs || !group_sizes || !out || !workspace) return BSATTN_ERR_NULL;
+    if (M <= 0 || K <= 0 || N <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
+    if (K % 64 != 0 || N % 128 != 0) return BSATTN_ERR_SHAPE;
+    if ((int64_t)K * N * 2 >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    if (ragged_max_items(M, G) * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    if (out_dtype != BSATTN_BF16 && out_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
+    const size_t nw = ragged_ws_bytes(M, G);
+    if (workspace_bytes < nw) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(lhs, 16) || !is_aligned(rhs, 16) || !is_aligned(out, 16) ||
+        !is_aligned(group_sizes, 4) || !is_aligned(workspace, 16))
+        return BSATTN_ERR_ALIGN;
+    const size_t no = (size_t)M * N * (out_dtype == BSATTN_F32 ? 4 : 2), ng = (size_t)G * 4;
+    if (overlap(out, no, group_sizes, ng)) return BSATTN_ERR_ALIAS;
+    const size_t nl = (size_t)M * K * 2, nr = (size_t)G * K * N * 2;
+    if (overlap(out, no, lhs, nl) || overlap(out, no, rhs, nr) || overlap(out, no, workspace, nw) ||
+        overlap(workspace, nw, lhs, nl) || overlap(workspace, nw, rhs, nr) ||
+        overlap(workspace, nw, group_sizes, ng))
+        return BSATTN_ERR_ALIAS;
+    int rc = bsattn_ragged_plan(group_sizes, M, G, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return bsattn_ragged_dot_planned(lhs, rhs, out, M, K, N, G, dtype, out_dtype, workspace, workspace_bytes,
+                                     stream);
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,

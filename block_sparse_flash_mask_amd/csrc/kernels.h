@@ -35,12 +35,14 @@ hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int6
                                const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
 
 // Ragged dot (ragged_dot.hip): the work-item bound of a plan (one item per
-// (128-row tile, group) pair that share rows), the workspace it needs, and the
-// launch (plan, zero tail, products) on stream.
-inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
+// (128-row tile, group) pair that share rows, plus the zero-fill items of the rows
+// past the last group), the plan's bytes (items, then their count), the plan
+// launch and the product launch on a plan.
+inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 127) / 128 + G + 1; }
 inline size_t ragged_ws_bytes(int64_t M, int64_t G) { return (size_t)ragged_max_items(M, G) * 16 + 16; }
-hipError_t launch_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
-                             int K, int N, int G, int out_f32, void* workspace, hipStream_t stream);
+hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace, hipStream_t stream);
+hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
+                                 int out_f32, const void* workspace, hipStream_t stream);
 
 // Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block
 // lists in LDS, so they take masks of at most this many key blocks per row.

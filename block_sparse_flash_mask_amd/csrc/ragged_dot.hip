@@ -11,8 +11,9 @@
 // sizes, clamped into [0, M]) and the work items: one item per (128-row tile, group)
 // pair that share rows, in group order, each with the row range [lo, hi) it owns
 // (the compaction idea of the attention path: a tile visits only the groups that
-// touch it).  A tile that straddles a group boundary is visited once per group and
-// each visit stores only its own rows, so no two items write the same row.
+// touch it), then items with group -1 for the rows past the last group, which are
+// only zeroed.  A tile that straddles a boundary is visited once per owner and each
+// visit stores only its own rows, so no two items write the same row.
 //
 // Kernel: one workgroup of 4 waves per (item, 128-column tile); wave w owns 32 rows.
 // C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on v_mfma_f32_32x32x16_bf16: the expert
@@ -91,28 +92,17 @@ __global__ __launch_bounds__(kRaggedThreads) void ragged_plan_kernel(const int32
         }
         __syncthreads();
     }
-    if (tid == 0) n_items[0] = (int32_t)carry[1];
-}
-
-// Rows [total, M) that no group owns are zero: a grid-stride fill run before the
-// products (it reads the sizes itself).
-template <int OUT_F32>
-__global__ __launch_bounds__(256) void ragged_tail_kernel(const int32_t* __restrict__ group_sizes, int G, int M,
-                                                          int N, void* __restrict__ out) {
-    __shared__ int64_t total_s;
-    if (threadIdx.x == 0) {
-        int64_t t = 0;
-        for (int g = 0; g < G; ++g) t += group_sizes[g] > 0 ? group_sizes[g] : 0;
-        total_s = t < M ? t : M;
+    // rows [total, M) of no group: zero-fill items
+    const int64_t total = carry[0] < M ? carry[0] : M;
+    const int64_t t0 = total / kRaggedTM;
+    const int64_t n_tail = total < M ? (M - 1) / kRaggedTM - t0 + 1 : 0;
+    for (int64_t i = tid; i < n_tail; i += kRaggedThreads) {
+        const int64_t t = t0 + i;
+        const int64_t lo = total > t * kRaggedTM ? total : t * kRaggedTM;
+        const int64_t hi = M < (t + 1) * kRaggedTM ? M : (t + 1) * kRaggedTM;
+        items[carry[1] + i] = make_int4((int)t, -1, (int)lo, (int)hi);
     }
-    __syncthreads();
-    const int64_t first = total_s * N, last = (int64_t)M * N;
-    for (int64_t i = first + (int64_t)blockIdx.x * 256 + threadIdx.x; i < last; i += (int64_t)gridDim.x * 256) {
-        if constexpr (OUT_F32)
-            ((float*)out)[i] = 0.f;
-        else
-            ((uint16_t*)out)[i] = 0;
-    }
+    if (tid == 0) n_items[0] = (int32_t)(carry[1] + n_tail);
 }
 
 template <int OUT_F32>
@@ -134,6 +124,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int wave_s = wave_uniform(wave);
     const int n0 = nt * kRaggedTN;
+    if (grp < 0) {  // rows of no group: zeros
+        for (int r = lo + (tid >> 5); r < hi; r += 256 / 32) {
+            const int c = n0 + 4 * (tid & 31);
+            if constexpr (OUT_F32)
+                *(float4*)((float*)out + (size_t)r * N + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                *(uint2*)((uint16_t*)out + (size_t)r * N + c) = make_uint2(0u, 0u);
+        }
+        return;
+    }
 
     // this lane's lhs row (rows outside [lo, hi) are computed on a valid row and
     // never stored)
@@ -232,22 +232,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 }
 
-hipError_t launch_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,
-                             int K, int N, int G, int out_f32, void* workspace, hipStream_t stream) {
+hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace, hipStream_t stream) {
     int4* items = (int4*)workspace;
-    const int64_t max_items = ragged_max_items(M, G);
-    int32_t* n_items = (int32_t*)(items + max_items);
+    int32_t* n_items = (int32_t*)(items + ragged_max_items(M, G));
     hipLaunchKernelGGL(ragged_plan_kernel, dim3(1), dim3(kRaggedThreads), 0, stream, group_sizes, G, M, items,
                        n_items);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned tail_blocks = 256;
-    if (out_f32)
-        hipLaunchKernelGGL(ragged_tail_kernel<1>, dim3(tail_blocks), dim3(256), 0, stream, group_sizes, G, M, N, out);
-    else
-        hipLaunchKernelGGL(ragged_tail_kernel<0>, dim3(tail_blocks), dim3(256), 0, stream, group_sizes, G, M, N, out);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
+                                 int out_f32, const void* workspace, hipStream_t stream) {
+    const int4* items = (const int4*)workspace;
+    const int64_t max_items = ragged_max_items(M, G);
+    const int32_t* n_items = (const int32_t*)(items + max_items);
     const int64_t grid = max_items * (N / kRaggedTN);
     if (out_f32)
         hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,

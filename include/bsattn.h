@@ -276,6 +276,18 @@ int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_siz
                       int K, int N, int G, int dtype, int out_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* The two steps of bsattn_ragged_dot on their own.  bsattn_ragged_plan reads
+ * group_sizes and writes the work plan into workspace (items of int32 {row tile,
+ * group or -1 for rows of no group, first row, end row}, then their count);
+ * bsattn_ragged_dot_planned runs the product (and the zero rows) on a plan made
+ * for the same M and G and only reads the workspace.  A workspace holding no such
+ * plan gives undefined values in out (item fields are not re-checked). */
+int bsattn_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
+                              int dtype, int out_dtype, const void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of

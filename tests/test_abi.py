@@ -311,5 +311,20 @@ def test_ragged_argument_checks(lib):
     assert call(3, p(A + 64)) == ALIAS and call(10, p(7 * A + 256)) == ALIAS
     n = ctypes.c_size_t(0)
     assert lib.bsattn_ragged_dot_workspace_size(256, 4, ctypes.byref(n)) == OK
-    assert n.value == (2 + 4) * 16 + 16
+    assert n.value == (2 + 4 + 1) * 16 + 16
+    g = lib.bsattn_ragged_plan
+    assert g(None, 256, 4, p(9 * A), 4096, None) == NULL and g(p(5 * A), 0, 4, p(9 * A), 4096, None) == SHAPE
+    assert g(p(5 * A), 256, 4, p(9 * A), 16, None) == WS and g(p(5 * A + 2), 256, 4, p(9 * A), 4096, None) == ALIGN
+    assert g(p(5 * A), 256, 4, p(5 * A - 64), 4096, None) == ALIAS
+    h = lib.bsattn_ragged_dot_planned
+    okp = [p(A), p(3 * A), p(7 * A), 256, 128, 256, 4, 1, 0, p(9 * A), 16, None]
+
+    def callp(i, x):
+        a = list(okp)
+        a[i] = x
+        return h(*a)
+    assert callp(0, None) == NULL and callp(9, None) == NULL and callp(5, 100) == SHAPE
+    assert callp(10, 16) == WS and callp(7, 0) == UNSUP
+    okp[10] = 4096
+    assert callp(2, p(A + 64)) == ALIAS and callp(9, p(9 * A + 8)) == ALIGN
     assert lib.bsattn_ragged_dot_workspace_size(0, 4, ctypes.byref(n)) == SHAPE

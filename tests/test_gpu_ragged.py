@@ -116,3 +116,17 @@ def test_ragged_workload_sampled_rows():
     got = out.double().cpu().numpy()[rows]
     bound = wl.K * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref)
     assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_ragged_planned_equals_one_shot():
+    """bsattn_ragged_plan + bsattn_ragged_dot_planned gives bit for bit the result
+    of bsattn_ragged_dot (the same plan and product kernels)."""
+    ensure_built()
+    x, w = _inputs(700, 128, 256, 4, seed=17)
+    sizes = torch.tensor([300, 0, 250, 90], dtype=torch.int32).cuda()  # 60-row zero tail
+    a = bs.ragged_dot(x.cuda(), w.cuda(), sizes)
+    ws = bs.ragged_plan(sizes, 700)
+    b = bs.ragged_dot_planned(x.cuda(), w.cuda(), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.all(b[640:] == 0)
