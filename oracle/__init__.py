@@ -67,6 +67,11 @@ def configure(lib):
     lib.oracle_fwd_rows_elem.restype = i32
     lib.oracle_ragged_dot.argtypes = [p, p, i32, p, i64, i64, i64, i64, p, i32]
     lib.oracle_ragged_dot.restype = i32
+    lib.oracle_bwd.argtypes = [p, p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p, p, p, i32]
+    lib.oracle_bwd.restype = i32
+    lib.oracle_bwd_sample.argtypes = [p, p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32,
+                                      p, i64, p, p, i64, p, p, i32]
+    lib.oracle_bwd_sample.restype = i32
     lib.oracle_probs.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p]
     lib.oracle_probs.restype = i32
     lib.oracle_compact.argtypes = [p, i64, i64, p, p]
@@ -257,6 +262,56 @@ def ragged_dot(lhs, rhs, group_sizes, nthreads=0):
     if rc:
         raise ValueError("oracle_ragged_dot failed with code %d" % rc)
     return out
+
+
+def _bwd_inputs(q, k, v, dout, mask, block_q, block_k):
+    qa, dt = _as_raw(q)
+    ka, dk_ = _as_raw(k)
+    va, dv_ = _as_raw(v)
+    oa, do_ = _as_raw(dout)
+    if len({dt, dk_, dv_, do_}) != 1:
+        raise TypeError("q, k, v and dout must share a dtype")
+    if oa.shape != qa.shape:
+        raise ValueError("dout shape %s != q shape %s" % (oa.shape, qa.shape))
+    m = _mask_u8(mask)
+    return qa, ka, va, oa, dt, m, _shape(qa, m, block_q, block_k)
+
+
+def bwd(q, k, v, dout, mask, block_q, block_k, scale, nthreads=0):
+    """Gradients of the forward for the upstream gradient dout (header of
+    oracle.c, "Backward").  All arrays [B,H,S,D]; mask [B,H,S/block_q,S/block_k].
+    Returns (dq, dk, dv), float64 [B,H,S,D]."""
+    lib = _load()
+    qa, ka, va, oa, dt, m, (B, H, S, D) = _bwd_inputs(q, k, v, dout, mask, block_q, block_k)
+    dq = np.empty((B, H, S, D), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = lib.oracle_bwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, oa.ctypes.data, dt,
+                        m.ctypes.data, B, H, S, D, block_q, block_k, float(np.float32(scale)),
+                        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_bwd failed with code %d" % rc)
+    return dq, dk, dv
+
+
+def bwd_sample(q, k, v, dout, mask, block_q, block_k, scale, q_rows, k_rows, nthreads=0):
+    """dq of the flat query rows q_rows and dk, dv of the flat key rows k_rows
+    (flat row = (b*H + h)*S + s).  Returns (dq [nq,D], dk [nk,D], dv [nk,D])."""
+    lib = _load()
+    qa, ka, va, oa, dt, m, (B, H, S, D) = _bwd_inputs(q, k, v, dout, mask, block_q, block_k)
+    qr = np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray(k_rows, dtype=np.int64))
+    dq = np.empty((max(len(qr), 1), D), dtype=np.float64)
+    dk = np.empty((max(len(kr), 1), D), dtype=np.float64)
+    dv = np.empty_like(dk)
+    rc = lib.oracle_bwd_sample(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, oa.ctypes.data, dt,
+                               m.ctypes.data, B, H, S, D, block_q, block_k,
+                               float(np.float32(scale)), qr.ctypes.data, len(qr), dq.ctypes.data,
+                               kr.ctypes.data, len(kr), dk.ctypes.data, dv.ctypes.data,
+                               int(nthreads))
+    if rc:
+        raise ValueError("oracle_bwd_sample failed with code %d" % rc)
+    return dq[:len(qr)], dk[:len(kr)], dv[:len(kr)]
 
 
 def probs(q, k, v, mask, block_q, block_k, scale):

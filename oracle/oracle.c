@@ -51,6 +51,24 @@
  * kept elements in place of the active keys; a row with no kept element has
  * out = 0 and lse = -inf.
  *
+ * Backward (oracle_bwd, oracle_bwd_sample).  "Writing Pallas Kernels for JAX",
+ * section "The Empathy of the Void": a hand-written kernel gets no automatic
+ * gradient, its author supplies one.  The
+ * gradient of the forward above is fixed by the chain rule.  For an upstream
+ * gradient dout = dL/dout, with P[r][j] = exp(s[r][j] - lse[r]) over the active
+ * keys of row r (0 elsewhere):
+ *   dv[j]    = sum_r P[r][j] dout[r]
+ *   dP[r][j] = dout[r] . v[j]
+ *   delta[r] = sum_j P[r][j] dP[r][j]
+ *   dS[r][j] = P[r][j] (dP[r][j] - delta[r])
+ *   dq[r]    = scale sum_j dS[r][j] k[j]
+ *   dk[j]    = scale sum_r dS[r][j] q[r]
+ * lse and delta of every row come from the oracle's own two-pass forward (never
+ * from the caller).  Pass A walks each query row (its scores, lse, P, dP, delta,
+ * dq); pass B walks each key row over the query rows that see its block and
+ * accumulates dk and dv.  Sums run over ascending j, r and d.  Rows with no active
+ * key have dq = 0 and add nothing to any dk or dv.
+ *
  * Ragged dot (oracle_ragged_dot): "Pallas-Triton kernels and kernel auto-tuning",
  * section "Ragged Dot (Group Matrix Multiplication)": the right-hand side is a
  * stack of G expert matrices rhs[g][K][N]; the rows of lhs[M][K] are assigned to
@@ -301,6 +319,225 @@ int oracle_fwd_rows_elem(const void* q, const void* k, const void* v, int dtype,
     p.pbits = pbits;
     p.n_tiles = n_tiles;
     return run_rows(&p, rows, n_rows, out_rows, lse_rows, nthreads);
+}
+
+/* ---- backward ---------------------------------------------------------- */
+
+/* Pass A for one query row: lse and delta of the row, and (if dq_row) its dq.
+ * sbuf holds S doubles, pbuf S doubles. */
+static void bwd_row(const problem* p, const void* dout, int64_t bh, int64_t s, double* lse_out,
+                    double* delta_out, double* dq_row, double* sbuf, double* pbuf) {
+    const int64_t D = p->D;
+    const int64_t qi = s / p->block_q;
+    const uint8_t* mrow = p->mask + (bh * p->n_q + qi) * p->n_k;
+    const int64_t qbase = (bh * p->S + s) * D;
+    int64_t n = 0;
+    double m = -INFINITY;
+    for (int64_t kj = 0; kj < p->n_k; ++kj) {
+        if (!mrow[kj]) continue;
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            const int64_t kbase = (bh * p->S + j) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dot += widen(p->q, p->dtype, qbase + d) * widen(p->k, p->dtype, kbase + d);
+            sbuf[n] = p->scale * dot;
+            if (sbuf[n] > m) m = sbuf[n];
+            ++n;
+        }
+    }
+    if (dq_row)
+        for (int64_t d = 0; d < D; ++d) dq_row[d] = 0.0;
+    if (n == 0) {
+        *lse_out = -INFINITY;
+        *delta_out = 0.0;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < n; ++t) l += exp(sbuf[t] - m);
+    const double lse = m + log(l);
+    /* P and dP of the active keys; delta */
+    double delta = 0.0;
+    int64_t t = 0;
+    for (int64_t kj = 0; kj < p->n_k; ++kj) {
+        if (!mrow[kj]) continue;
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j, ++t) {
+            const int64_t vbase = (bh * p->S + j) * D;
+            double dp = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dp += widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, vbase + d);
+            sbuf[t] = exp(sbuf[t] - lse); /* P */
+            pbuf[t] = dp;                  /* dP */
+            delta += sbuf[t] * dp;
+        }
+    }
+    *lse_out = lse;
+    *delta_out = delta;
+    if (!dq_row) return;
+    t = 0;
+    for (int64_t kj = 0; kj < p->n_k; ++kj) {
+        if (!mrow[kj]) continue;
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j, ++t) {
+            const int64_t kbase = (bh * p->S + j) * D;
+            const double ds = sbuf[t] * (pbuf[t] - delta);
+            for (int64_t d = 0; d < D; ++d) dq_row[d] += ds * widen(p->k, p->dtype, kbase + d);
+        }
+    }
+    for (int64_t d = 0; d < D; ++d) dq_row[d] *= p->scale;
+}
+
+/* Pass B for one key row j of head bh: dk and dv from the query rows whose block
+ * sees j's block.  lse and delta are the head's per-row values from pass A. */
+static void bwd_key(const problem* p, const void* dout, int64_t bh, int64_t j, const double* lse,
+                    const double* delta, double* dk_row, double* dv_row) {
+    const int64_t D = p->D, kj = j / p->block_k;
+    const int64_t kbase = (bh * p->S + j) * D;
+    for (int64_t d = 0; d < D; ++d) dk_row[d] = dv_row[d] = 0.0;
+    for (int64_t qi = 0; qi < p->n_q; ++qi) {
+        if (!p->mask[(bh * p->n_q + qi) * p->n_k + kj]) continue;
+        for (int64_t r = qi * p->block_q; r < (qi + 1) * p->block_q; ++r) {
+            const int64_t qbase = (bh * p->S + r) * D;
+            double dot = 0.0, dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                dot += widen(p->q, p->dtype, qbase + d) * widen(p->k, p->dtype, kbase + d);
+                dp += widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);
+            }
+            const double P = exp(p->scale * dot - lse[r]);
+            const double ds = P * (dp - delta[r]);
+            for (int64_t d = 0; d < D; ++d) {
+                dv_row[d] += P * widen(dout, p->dtype, qbase + d);
+                dk_row[d] += ds * widen(p->q, p->dtype, qbase + d);
+            }
+        }
+    }
+    for (int64_t d = 0; d < D; ++d) dk_row[d] *= p->scale;
+}
+
+/* Pass A over every query row of the heads flagged in want (NULL = all heads):
+ * lse and delta into [B*H*S] arrays. */
+static int bwd_stats(const problem* p, const void* dout, const uint8_t* want, double* lse,
+                     double* delta) {
+    const int64_t S = p->S, rows = p->B * p->H * S;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        double* pbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        if (!sbuf || !pbuf) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r)
+                if (!want || want[r / S]) bwd_row(p, dout, r / S, r % S, lse + r, delta + r, NULL, sbuf, pbuf);
+        }
+        free(sbuf);
+        free(pbuf);
+    }
+    return failed;
+}
+
+/* Full backward: dq, dk, dv are double[B][H][S][D]. */
+int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+               const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q,
+               int64_t block_k, float scale, double* dq, double* dk, double* dv, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    int rc = check(&p);
+    if (rc) return rc;
+    if (!dout || !dq || !dk || !dv) return 1;
+    set_threads(nthreads);
+    const int64_t rows = B * H * S;
+    double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+    int failed = !lse || !delta;
+    if (!failed) {
+#pragma omp parallel
+        {
+            double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+            double* pbuf = (double*)malloc(sizeof(double) * (size_t)S);
+            if (!sbuf || !pbuf) {
+#pragma omp atomic write
+                failed = 1;
+            } else {
+#pragma omp for schedule(dynamic, 16)
+                for (int64_t r = 0; r < rows; ++r)
+                    bwd_row(&p, dout, r / S, r % S, lse + r, delta + r, dq + r * D, sbuf, pbuf);
+            }
+            free(sbuf);
+            free(pbuf);
+        }
+    }
+    if (!failed) {
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t bh = r / S;
+            bwd_key(&p, dout, bh, r % S, lse + bh * S, delta + bh * S, dk + r * D, dv + r * D);
+        }
+    }
+    free(lse);
+    free(delta);
+    return failed ? 9 : 0;
+}
+
+/* Sampled backward: dq of the flat query rows q_rows[i] = (b*H + h)*S + s into
+ * dq_rows[n_q_rows][D]; dk and dv of the flat key rows k_rows[i] into
+ * dk_rows / dv_rows [n_k_rows][D].  Pass A runs only over the heads that hold a
+ * sampled key row. */
+int oracle_bwd_sample(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                      const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D,
+                      int64_t block_q, int64_t block_k, float scale, const int64_t* q_rows,
+                      int64_t n_q_rows, double* dq_rows, const int64_t* k_rows, int64_t n_k_rows,
+                      double* dk_rows, double* dv_rows, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    int rc = check(&p);
+    if (rc) return rc;
+    if (!dout || (n_q_rows > 0 && (!q_rows || !dq_rows)) ||
+        (n_k_rows > 0 && (!k_rows || !dk_rows || !dv_rows)))
+        return 1;
+    const int64_t rows = B * H * S;
+    for (int64_t i = 0; i < n_q_rows; ++i)
+        if (q_rows[i] < 0 || q_rows[i] >= rows) return 2;
+    for (int64_t i = 0; i < n_k_rows; ++i)
+        if (k_rows[i] < 0 || k_rows[i] >= rows) return 2;
+    set_threads(nthreads);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* sbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        double* pbuf = (double*)malloc(sizeof(double) * (size_t)S);
+        if (!sbuf || !pbuf) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < n_q_rows; ++i) {
+                double lse, delta;
+                bwd_row(&p, dout, q_rows[i] / S, q_rows[i] % S, &lse, &delta, dq_rows + i * D, sbuf, pbuf);
+            }
+        }
+        free(sbuf);
+        free(pbuf);
+    }
+    if (failed || n_k_rows == 0) return failed ? 9 : 0;
+    uint8_t* want = (uint8_t*)calloc((size_t)(B * H), 1);
+    double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+    failed = !want || !lse || !delta;
+    if (!failed) {
+        for (int64_t i = 0; i < n_k_rows; ++i) want[k_rows[i] / S] = 1;
+        failed = bwd_stats(&p, dout, want, lse, delta);
+    }
+    if (!failed) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_k_rows; ++i) {
+            const int64_t bh = k_rows[i] / S;
+            bwd_key(&p, dout, bh, k_rows[i] % S, lse + bh * S, delta + bh * S, dk_rows + i * D,
+                    dv_rows + i * D);
+        }
+    }
+    free(want);
+    free(lse);
+    free(delta);
+    return failed ? 9 : 0;
 }
 
 /* Dense probability matrix P[b][h][s][j] (zero where masked), for tiny shapes:

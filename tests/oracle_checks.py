@@ -40,6 +40,18 @@ Ragged dot (expert matrices stacked on the right, rows assigned in order):
   ragged_linear     out(X, a W1 + b W2) == a out(X, W1) + b out(X, W2)
   ragged_tail       rows past the sum of the sizes are 0; empty groups change nothing
   ragged_bf16       bf16 inputs give the same result as their exact fp64 values
+Backward (gradients for an upstream gradient dout):
+  bwd_autograd      torch autograd (fp64, CPU) through a dense masked softmax
+                    attention built from plain torch ops, empty rows included
+  bwd_finite_diff   central differences of sum(dout * out) through the forward
+                    oracle, on entries of q, k and v
+  bwd_sums          per head: dk summed over keys is 0 (a shift of every key
+                    changes no softmax); dv summed over keys is dout summed over
+                    the rows that see any key; keys no row sees and rows that see
+                    no key get exact zeros
+  bwd_constant_v    V == c gives dq == dk == 0
+  bwd_linear_dout   the gradients are linear in dout
+  bwd_sample_match  the sampled entry point equals the full backward
 """
 import json
 import math
@@ -450,11 +462,133 @@ def ragged_bf16(orc):
     _close(out, ref, 0.0, "bf16 widening")
 
 
+# ---- backward ----------------------------------------------------------------
+
+BWD_CASES = [
+    # B, H, S, D, block_q, block_k, p, seed, dtype, scale
+    (1, 2, 12, 4, 3, 4, 0.6, 31, torch.float64, 0.8),
+    (2, 1, 16, 8, 4, 2, 0.5, 32, torch.float64, -0.45),
+    (1, 2, 32, 16, 8, 16, 0.6, 33, torch.bfloat16, 0.25),
+    (1, 1, 24, 6, 6, 4, 0.5, 34, torch.float32, 1.1),
+]
+
+
+def _bwd_case(B, H, S, D, bq, bk, p, seed, dt):
+    q = _rand((B, H, S, D), seed, dt)
+    k = _rand((B, H, S, D), seed + 100, dt)
+    v = _rand((B, H, S, D), seed + 200, dt)
+    do = _rand((B, H, S, D), seed + 300, dt)
+    mask = _mask(B, H, S // bq, S // bk, p, seed, empty_rows=[(0, 0, 1)])
+    return q, k, v, do, mask
+
+
+def _autograd_grads(q, k, v, do, mask, bq, bk, scale):
+    """Plain torch ops in fp64 with autograd: scores, -inf where masked, row
+    softmax (rows with no visible key contribute 0), times V."""
+    full = torch.as_tensor(expand_mask(mask, bq, bk))
+    qq, kk, vv = (t.to(torch.float64).clone().requires_grad_(True) for t in (q, k, v))
+    s = float(np.float32(scale)) * torch.matmul(qq, kk.transpose(-1, -2))
+    anyk = full.any(dim=-1, keepdim=True)
+    s = s.masked_fill(~full, float("-inf")).masked_fill(~anyk, 0.0)
+    pr = torch.softmax(s, dim=-1) * anyk
+    out = torch.matmul(pr, vv)
+    loss = (out * do.to(torch.float64)).sum()
+    return [g.numpy() for g in torch.autograd.grad(loss, (qq, kk, vv))]
+
+
+def bwd_autograd(orc):
+    for (B, H, S, D, bq, bk, p, seed, dt, scale) in BWD_CASES:
+        q, k, v, do, mask = _bwd_case(B, H, S, D, bq, bk, p, seed, dt)
+        got = orc.bwd(q, k, v, do, mask, bq, bk, scale)
+        want = _autograd_grads(q, k, v, do, mask, bq, bk, scale)
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            _close(a, b, 1e-11, "%s %s" % (name, dt))
+
+
+def bwd_finite_diff(orc):
+    B, H, S, D, bq, bk, scale = 1, 1, 8, 3, 2, 4, 0.7
+    q, k, v, do, mask = _bwd_case(B, H, S, D, bq, bk, 0.7, 41, torch.float64)
+    mask[0, 0, 2, :] = 0  # one query block sees nothing
+    mask[0, 0, 0, 0] = 1
+    dq, dk, dv = orc.bwd(q, k, v, do, mask, bq, bk, scale)
+    arrs = {"q": q.numpy().copy(), "k": k.numpy().copy(), "v": v.numpy().copy()}
+    grads = {"q": dq, "k": dk, "v": dv}
+    g = np.random.default_rng(41)
+
+    def loss():
+        out, _ = orc.fwd(arrs["q"], arrs["k"], arrs["v"], mask, bq, bk, scale)
+        return float(np.sum(out * do.numpy()))
+
+    h = 1e-5
+    for name in ("q", "k", "v"):
+        for _ in range(8):
+            idx = (0, 0, int(g.integers(S)), int(g.integers(D)))
+            x0 = arrs[name][idx]
+            arrs[name][idx] = x0 + h
+            lp = loss()
+            arrs[name][idx] = x0 - h
+            lm = loss()
+            arrs[name][idx] = x0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grads[name][idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, grads[name][idx])
+
+
+def bwd_sums(orc):
+    for (B, H, S, D, bq, bk, p, seed, dt, scale) in BWD_CASES:
+        q, k, v, do, mask = _bwd_case(B, H, S, D, bq, bk, p, seed, dt)
+        mask[0, 0, :, 0] = 0  # key block 0 of head (0, 0): seen by no row
+        dq, dk, dv = orc.bwd(q, k, v, do, mask, bq, bk, scale)
+        full = expand_mask(mask, bq, bk)
+        seen_row = full.any(axis=-1)   # [B,H,S] rows that see a key
+        seen_key = full.any(axis=-2)   # [B,H,S] keys some row sees
+        _close(dk.sum(axis=2), np.zeros((B, H, D)), 1e-11, "sum dk")
+        want_dv = (do.to(torch.float64).numpy() * seen_row[..., None]).sum(axis=2)
+        _close(dv.sum(axis=2), want_dv, 1e-11, "sum dv")
+        assert np.all(dq[~seen_row] == 0.0)
+        assert np.all(dk[~seen_key] == 0.0) and np.all(dv[~seen_key] == 0.0)
+        assert (~seen_key).any() and (~seen_row).any()
+
+
+def bwd_constant_v(orc):
+    B, H, S, D, bq, bk, p, seed, dt, scale = BWD_CASES[1]
+    q, k, _, do, mask = _bwd_case(B, H, S, D, bq, bk, p, seed, dt)
+    v = torch.full((B, H, S, D), -1.75, dtype=torch.float64)
+    dq, dk, dv = orc.bwd(q, k, v, do, mask, bq, bk, scale)
+    _close(dq, np.zeros_like(dq), 1e-12, "dq")
+    _close(dk, np.zeros_like(dk), 1e-12, "dk")
+    assert np.abs(dv).max() > 0.1
+
+
+def bwd_linear_dout(orc):
+    B, H, S, D, bq, bk, p, seed, dt, scale = BWD_CASES[0]
+    q, k, v, do1, mask = _bwd_case(B, H, S, D, bq, bk, p, seed, dt)
+    do2 = _rand((B, H, S, D), 77)
+    a, b = 0.75, -2.5
+    g1 = orc.bwd(q, k, v, do1, mask, bq, bk, scale)
+    g2 = orc.bwd(q, k, v, do2, mask, bq, bk, scale)
+    g3 = orc.bwd(q, k, v, a * do1 + b * do2, mask, bq, bk, scale)
+    for x1, x2, x3 in zip(g1, g2, g3):
+        _close(x3, a * x1 + b * x2, 1e-11, "linearity")
+
+
+def bwd_sample_match(orc):
+    B, H, S, D, bq, bk, p, seed, dt, scale = BWD_CASES[2]
+    q, k, v, do, mask = _bwd_case(B, H, S, D, bq, bk, p, seed, dt)
+    dq, dk, dv = orc.bwd(q, k, v, do, mask, bq, bk, scale)
+    qr = [0, 5, 17, S + 3, 2 * S - 1]
+    kr = [1, 16, 31, S, 2 * S - 2]
+    sq, sk, sv = orc.bwd_sample(q, k, v, do, mask, bq, bk, scale, qr, kr)
+    _close(sq, dq.reshape(-1, D)[qr], 0.0, "dq rows")
+    _close(sk, dk.reshape(-1, D)[kr], 0.0, "dk rows")
+    _close(sv, dv.reshape(-1, D)[kr], 0.0, "dv rows")
+
+
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
        bf16_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
        elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_one_group,
-       ragged_permute, ragged_linear, ragged_tail, ragged_bf16]
+       ragged_permute, ragged_linear, ragged_tail, ragged_bf16, bwd_autograd, bwd_finite_diff,
+       bwd_sums, bwd_constant_v, bwd_linear_dout, bwd_sample_match]
 
 
 def run_all(orc):

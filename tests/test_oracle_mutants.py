@@ -66,6 +66,22 @@ MUTANTS = {
                                "widen(rhs, dtype, (g * K + (n % K)) * N + (k % N))")],
     "ragged_tail_not_zeroed": [("for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;",
                                 "for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 1.0;")],
+    "bwd_no_delta": [("const double ds = sbuf[t] * (pbuf[t] - delta);", "const double ds = sbuf[t] * pbuf[t];"),
+                     ("const double ds = P * (dp - delta[r]);", "const double ds = P * dp;")],
+    "bwd_delta_unweighted": [("delta += sbuf[t] * dp;", "delta += dp;")],
+    "bwd_dk_no_scale": [("for (int64_t d = 0; d < D; ++d) dk_row[d] *= p->scale;", "")],
+    "bwd_dq_no_scale": [("for (int64_t d = 0; d < D; ++d) dq_row[d] *= p->scale;", "")],
+    "bwd_dv_uses_ds": [("dv_row[d] += P * widen(dout, p->dtype, qbase + d);",
+                        "dv_row[d] += ds * widen(dout, p->dtype, qbase + d);")],
+    "bwd_dq_uses_v": [("dq_row[d] += ds * widen(p->k, p->dtype, kbase + d);",
+                       "dq_row[d] += ds * widen(p->v, p->dtype, kbase + d);")],
+    "bwd_dk_uses_dout": [("dk_row[d] += ds * widen(p->q, p->dtype, qbase + d);",
+                          "dk_row[d] += ds * widen(dout, p->dtype, qbase + d);")],
+    "bwd_lse_drops_max": [("const double lse = m + log(l);", "const double lse = log(l);")],
+    "bwd_key_sees_next_block": [("if (!p->mask[(bh * p->n_q + qi) * p->n_k + kj]) continue;",
+                                 "if (!p->mask[(bh * p->n_q + qi) * p->n_k + (kj + 1) % p->n_k]) continue;")],
+    "bwd_dp_sign": [("dp += widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);",
+                     "dp -= widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);")],
     "compact_skips_last_column": [("for (int64_t kj = 0; kj < n_k; ++kj)\n            if (mask[r * n_k + kj])",
                                    "for (int64_t kj = 0; kj < n_k - 1; ++kj)\n            if (mask[r * n_k + kj])")],
 }
