@@ -93,6 +93,12 @@ def library():
         "bsattn_fwd_elem": ([p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
                              p, sz, cfgp, p], i32),
         "bsattn_list_configs_elem": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
+        "bsattn_bwd_workspace_size": ([i32, i32, i32, i32, i32, szp], i32),
+        "bsattn_bwd": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p, sz,
+                        p], i32),
+        "bsattn_bwd_plan": ([p, i32, i32, i32, i32, i32, p, sz, p], i32),
+        "bsattn_bwd_planned": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p,
+                                sz, p], i32),
         "bsattn_ragged_dot_workspace_size": ([i32, i32, szp], i32),
         "bsattn_ragged_dot": ([p, p, p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
         "bsattn_ragged_plan": ([p, i32, i32, p, sz, p], i32),
@@ -429,6 +435,69 @@ def ragged_dot_planned(lhs, rhs, plan_ws, *, out=None, out_dtype=None, stream=No
     _check(rc)
     return out
 
+
+def bwd_workspace_size(B, H, S, block_q, block_k):
+    n = ctypes.c_size_t(0)
+    _check(library().bsattn_bwd_workspace_size(B, H, S, block_q, block_k, ctypes.byref(n)))
+    return n.value
+
+
+def _grads(q, grad_dtype, dq, dk, dv):
+    gd = grad_dtype or q.dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device) if dq is None else dq
+    dk = torch.empty(q.shape, dtype=gd, device=q.device) if dk is None else dk
+    dv = torch.empty(q.shape, dtype=gd, device=q.device) if dv is None else dv
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise ValueError("dq, dk, dv must have one dtype")
+    return dq, dk, dv
+
+
+def bwd(q, k, v, out, lse, dout, block_mask, block_q, block_k, scale=None, *, grad_dtype=None,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the forward (bsattn_bwd) for the upstream gradient dout, from
+    the forward's out and lse.  Returns (dq, dk, dv) in grad_dtype (default: the
+    input dtype; torch.float32 for fp32 gradients)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    block_mask = _mask_u8(block_mask)
+    if tuple(block_mask.shape) != (B, H, S // block_q, S // block_k):
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    if scale is None:
+        scale = default_scale(D)
+    dq, dk, dv = _grads(q, grad_dtype, dq, dk, dv)
+    ws = _workspace(bwd_workspace_size(B, H, S, block_q, block_k), q.device, workspace)
+    rc = library().bsattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                              _ptr(block_mask), B, H, S, D, block_q, block_k, float(scale),
+                              _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return dq, dk, dv
+
+
+def bwd_plan(block_mask, S, block_q, block_k, *, workspace=None, stream=None):
+    """The mask-dependent step of bwd() (bsattn_bwd_plan); returns the workspace."""
+    block_mask = _mask_u8(block_mask)
+    B, H, n_q, n_k = block_mask.shape
+    if (n_q * block_q, n_k * block_k) != (S, S):
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    ws = _workspace(bwd_workspace_size(B, H, S, block_q, block_k), block_mask.device, workspace)
+    _check(library().bsattn_bwd_plan(_ptr(block_mask), B, H, S, block_q, block_k, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+    return ws
+
+
+def bwd_planned(q, k, v, out, lse, dout, plan_ws, block_q, block_k, scale=None, *, grad_dtype=None,
+                dq=None, dk=None, dv=None, stream=None):
+    """The gradient kernels alone on a plan from bwd_plan() (bsattn_bwd_planned)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    dq, dk, dv = _grads(q, grad_dtype, dq, dk, dv)
+    rc = library().bsattn_bwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), B, H,
+                                      S, D, block_q, block_k, float(scale), _dtype_code(q), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(plan_ws),
+                                      plan_ws.numel() * plan_ws.element_size(), _stream(stream))
+    _check(rc)
+    return dq, dk, dv
 
 def list_configs(dtype, D, block_q, block_k):
     """Tile configs built for this shape, in the library's preference order."""

@@ -72,6 +72,27 @@ PlanLayout plan_layout(int64_t BH, int n_q, int n_k) {
 
 size_t fwd_ws_bytes(int64_t BH, int n_q, int n_k) { return plan_layout(BH, n_q, n_k).bytes; }
 
+// Backward workspace: the forward plan (rows, for dq), then per key block the
+// count and the query-block list padded to n_q (for dk, dv), then the per-row
+// (lse * log2 e, dout . out) pairs.
+struct BwdLayout {
+    PlanLayout fwd;
+    int64_t C;  // key blocks (columns): B * H * n_k
+    size_t ccounts, clists, ld, plan_bytes, bytes;
+};
+
+BwdLayout bwd_layout(int64_t BH, int S, int n_q, int n_k) {
+    BwdLayout L;
+    L.fwd = plan_layout(BH, n_q, n_k);
+    L.C = BH * n_k;
+    L.ccounts = L.fwd.bytes;
+    L.clists = L.ccounts + align_up((size_t)L.C * 4);
+    L.ld = L.clists + align_up((size_t)(L.C * n_q) * 4);
+    L.plan_bytes = L.ld;
+    L.bytes = L.ld + align_up((size_t)(BH * S) * 8);
+    return L;
+}
+
 int check_grid(int B, int H, int n_q, int n_k) {
     if (B <= 0 || H <= 0 || n_q <= 0 || n_k <= 0) return BSATTN_ERR_SHAPE;
     const int64_t R = (int64_t)B * H * n_q;
@@ -696,6 +717,145 @@ int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_siz
     if (rc) return rc;
     return bsattn_ragged_dot_planned(lhs, rhs, out, M, K, N, G, dtype, out_dtype, workspace, workspace_bytes,
                                      stream);
+}
+
+// ---- backward ------------------------------------------------------------------
+
+int bsattn_bwd_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes) {
+    if (!bytes) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    const int rc = check_grid(B, H, S / block_q, S / block_k);
+    if (rc) return rc;
+    *bytes = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k).bytes;
+    return BSATTN_OK;
+}
+
+int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int block_k, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!block_mask || !workspace) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    if (!block_ok(block_q) || !block_ok(block_k)) return BSATTN_ERR_UNSUPPORTED;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const int rc = check_grid(B, H, n_q, n_k);
+    if (rc) return rc;
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k);
+    if (workspace_bytes < L.plan_bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
+    if (overlap(block_mask, (size_t)L.fwd.R * n_k, workspace, L.plan_bytes)) return BSATTN_ERR_ALIAS;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    hipError_t e = launch_plan(block_mask, L.fwd.R, n_q, n_k, (int32_t*)ws, (int32_t*)(ws + L.fwd.lists),
+                               L.fwd.chunk, (int32_t*)(ws + L.fwd.order), L.fwd.pchunk,
+                               (int32_t*)(ws + L.fwd.porder), st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_bwd_cols(block_mask, L.C, n_q, n_k, (int32_t*)(ws + L.ccounts), (int32_t*)(ws + L.clists), st);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                       int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return BSATTN_ERR_NULL;
+    int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
+    if (rc) return rc;
+    if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    if (grad_dtype != BSATTN_BF16 && grad_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    const void* al16[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    for (const void* p : al16)
+        if (!is_aligned(p, 16)) return BSATTN_ERR_ALIGN;
+    if (!is_aligned(lse, 4)) return BSATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return BSATTN_ERR_SCALE;
+    const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;
+    const size_t ng = (size_t)B * H * S * D * (grad_dtype == BSATTN_F32 ? 4 : 2);
+    // written: dq, dk, dv and the ld region of the workspace; read: everything else
+    const void* wr[] = {dq, dk, dv, (const char*)workspace + L.ld};
+    const size_t wn[] = {ng, ng, ng, L.bytes - L.ld};
+    const void* rd[] = {q, k, v, out, dout, lse, workspace};
+    const size_t rn[] = {nt, nt, nt, nt, nt, nl, L.plan_bytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlap(wr[i], wn[i], rd[j], rn[j])) return BSATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(wr[i], wn[i], wr[j], wn[j])) return BSATTN_ERR_ALIAS;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    hipError_t e = launch_bwd_prep(out, dout, lse, ws + L.ld, L.fwd.R * block_q, D, st);
+    if (e != hipSuccess) return hip_fail(e);
+    BwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.dout = (const uint16_t*)dout;
+    a.ld = (const float2*)(ws + L.ld);
+    a.row_counts = (const int32_t*)ws;
+    a.row_lists = (const int32_t*)(ws + L.fwd.lists);
+    a.row_order = (const int32_t*)(ws + L.fwd.order);
+    a.n_rows = (int)L.fwd.R;
+    a.chunk_q = (int)L.fwd.chunk;
+    a.col_counts = (const int32_t*)(ws + L.ccounts);
+    a.col_lists = (const int32_t*)(ws + L.clists);
+    a.n_cols = (int)L.C;
+    a.chunk_k = (int)xcd_chunk(L.C);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.S = S;
+    a.n_q = n_q;
+    a.n_k = n_k;
+    a.block_q = block_q;
+    a.block_k = block_k;
+    a.qsteps_log2 = block_q == 128 ? 2 : 1;
+    a.ksteps_log2 = block_k == 128 ? 2 : 1;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    e = launch_bwd_main(a, D, grad_dtype == BSATTN_F32, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
+}
+
+int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+               const uint8_t* block_mask, int B, int H, int S, int D, int block_q, int block_k, float scale,
+               int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !block_mask || !dq || !dk || !dv || !workspace)
+        return BSATTN_ERR_NULL;
+    int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
+    if (rc) return rc;
+    if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
+    if (grad_dtype != BSATTN_BF16 && grad_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    // the plan step writes the workspace: it must not overlap any tensor argument
+    const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;
+    const size_t ng = (size_t)B * H * S * D * (grad_dtype == BSATTN_F32 ? 4 : 2);
+    const void* ts[] = {q, k, v, out, dout, lse, dq, dk, dv};
+    const size_t tn[] = {nt, nt, nt, nt, nt, nl, ng, ng, ng};
+    for (int i = 0; i < 9; ++i)
+        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    // every other check of bsattn_bwd_planned runs before the plan is launched
+    const void* al16[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    for (const void* p : al16)
+        if (!is_aligned(p, 16)) return BSATTN_ERR_ALIGN;
+    if (!is_aligned(lse, 4)) return BSATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return BSATTN_ERR_SCALE;
+    for (int i = 6; i < 9; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(ts[i], tn[i], ts[j], tn[j])) return BSATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 9; ++j)
+            if (overlap(ts[i], tn[i], ts[j], tn[j])) return BSATTN_ERR_ALIAS;
+    }
+    rc = bsattn_bwd_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return bsattn_bwd_planned(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                              grad_dtype, workspace, workspace_bytes, stream);
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,

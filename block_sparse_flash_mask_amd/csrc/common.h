@@ -52,6 +52,34 @@ struct FwdArgs {
     uint32_t qsign32;  // 0x80000000 flips an fp32 sign (scale < 0)
 };
 
+// Everything a backward launch needs (both main kernels take the same struct).
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    const float2* ld;  // per row: (lse * log2 e, or +inf for lse = -inf; dout . out)
+    // dq: the forward plan -- per mask row the count and the key-block list padded
+    // to n_k, and the dispatch order of the rows in chunks of chunk_q per XCD.
+    const int32_t* row_counts;
+    const int32_t* row_lists;
+    const int32_t* row_order;
+    int n_rows, chunk_q;
+    // dk, dv: per key block (column, (b*H + h)*n_k + kj) the count and the
+    // query-block list padded to n_q; columns go to the XCDs in chunks of chunk_k.
+    const int32_t* col_counts;
+    const int32_t* col_lists;
+    int n_cols, chunk_k;
+    void* dq;
+    void* dk;
+    void* dv;
+    int S, n_q, n_k, block_q, block_k;
+    int qsteps_log2;  // log2(block_q / 32)
+    int ksteps_log2;  // log2(block_k / 32)
+    float c;          // scale * log2(e)
+    float scale;
+};
+
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Exchange with the lane 32 positions away (the other half of the wave).

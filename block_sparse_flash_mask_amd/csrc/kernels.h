@@ -44,6 +44,16 @@ hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* wo
 hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
                                  int out_f32, const void* workspace, hipStream_t stream);
 
+// Backward (attn_bwd.hip): per-row (lse * log2 e, dout . out) into ld (float2
+// [rows]), the column form of the mask (per key block: count, query-block list
+// padded to n_q), and the dk/dv and dq kernels (bf16 inputs, D 64 or 128, block
+// sizes 64 or 128; gradients bf16 or fp32).
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, void* ld, int64_t rows, int D,
+                           hipStream_t stream);
+hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int32_t* counts, int32_t* lists,
+                           hipStream_t stream);
+hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, hipStream_t stream);
+
 // Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block
 // lists in LDS, so they take masks of at most this many key blocks per row.
 constexpr int kPairMaxBlocks = 2048;

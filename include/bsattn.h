@@ -288,6 +288,53 @@ int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M
                               int dtype, int out_dtype, const void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ---- Backward ---------------------------------------------------------------------
+ * Gradients of the forward above ("Writing Pallas Kernels for JAX", section "The
+ * Empathy of the Void": a hand-written kernel gets no automatic gradient, its
+ * author writes one).  For the upstream gradient dout = dL/dout, with
+ * P[r][j] = exp(scale * q_r . k_j - lse_r) on the active keys of row r (0 elsewhere):
+ *   dv_j = sum_r P[r][j] dout_r,            dP[r][j] = dout_r . v_j,
+ *   delta_r = dout_r . out_r,               dS[r][j] = P[r][j] (dP[r][j] - delta_r),
+ *   dq_r = scale sum_j dS[r][j] k_j,        dk_j = scale sum_r dS[r][j] q_r.
+ * Arguments:
+ *   q, k, v, out, dout  bf16 [B][H][S][D] (device; out and lse as written by the
+ *                       forward of the same q, k, v, mask and scale);
+ *   lse                 float [B][H][S] (device; -inf marks a row that saw no key);
+ *   block_mask          uint8 [B][H][S/block_q][S/block_k] (device), as the forward;
+ *   dq, dk, dv          [B][H][S][D] (device), bf16 (grad_dtype BSATTN_BF16, round to
+ *                       nearest even) or fp32 (BSATTN_F32); every element is written
+ *                       (rows and keys that no active block touches get 0).
+ * dtype must be BSATTN_BF16, D 64 or 128, block_q and block_k 64 or 128
+ * (BSATTN_ERR_UNSUPPORTED); shapes as the forward (BSATTN_ERR_SHAPE).  q, k, v, out,
+ * dout, dq, dk, dv and the workspace 16-byte aligned, lse 4-byte aligned
+ * (BSATTN_ERR_ALIGN); scale finite (BSATTN_ERR_SCALE); dq, dk, dv or the
+ * workspace overlapping any other array argument or each other gives
+ * BSATTN_ERR_ALIAS.  fp32 accumulation; the results do not depend on the launch
+ * order (no atomics).  The workspace (bsattn_bwd_workspace_size bytes, owned by
+ * the caller) holds the plan -- the forward plan of bsattn_plan (row lists, for
+ * dq), then per key block (b, h, kj) its count and ascending list of query blocks
+ * padded to n_q (int32, for dk and dv) -- and a per-row scratch of 8 bytes
+ * (lse * log2 e, dout . out).  Asynchronous on stream; nothing is allocated. */
+int bsattn_bwd_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes);
+int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               const void* dout, const uint8_t* block_mask, int B, int H, int S, int D, int block_q,
+               int block_k, float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two steps of bsattn_bwd on their own.  bsattn_bwd_plan reads the mask and
+ * writes the plan part of the workspace (it depends on the mask and shape only,
+ * so one plan serves every backward call with that mask);
+ * bsattn_bwd_planned runs the gradient kernels on it (reading the plan, writing
+ * the per-row scratch).  The lists' entries are clamped into range, so a
+ * workspace holding no such plan gives wrong values but no access out of
+ * bounds. */
+int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int block_k,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, int B, int H, int S, int D, int block_q, int block_k,
+                       float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of

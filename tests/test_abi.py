@@ -328,3 +328,62 @@ def test_ragged_argument_checks(lib):
     okp[10] = 4096
     assert callp(2, p(A + 64)) == ALIAS and callp(9, p(9 * A + 8)) == ALIGN
     assert lib.bsattn_ragged_dot_workspace_size(0, 4, ctypes.byref(n)) == SHAPE
+
+
+def test_bwd_argument_checks(lib):
+    """Backward: every call below fails a host check (fake pointers)."""
+    p = ctypes.c_void_p
+    B, H, S, D, bq, bk = 1, 2, 256, 128, 128, 64
+    n = ctypes.c_size_t(0)
+    assert lib.bsattn_bwd_workspace_size(B, H, S, bq, bk, ctypes.byref(n)) == OK
+    rnd = lambda x: (x + 255) // 256 * 256
+    R, nk, nq = B * H * (S // bq), S // bk, S // bq
+    fwd = ctypes.c_size_t(0)
+    assert lib.bsattn_workspace_size(B, H, S, bq, bk, ctypes.byref(fwd)) == OK
+    C = B * H * nk
+    assert n.value == fwd.value + rnd(C * 4) + rnd(C * nq * 4) + rnd(B * H * S * 8)
+    wsn = n.value
+    assert lib.bsattn_bwd_workspace_size(B, H, 250, bq, bk, ctypes.byref(n)) == SHAPE
+    assert lib.bsattn_bwd_workspace_size(B, H, S, bq, bk, None) == NULL
+
+    f = lib.bsattn_bwd
+    # q k v out lse dout mask B H S D bq bk scale dtype dq dk dv gdtype ws wsb stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), p(9 * A), p(11 * A), p(13 * A), B, H, S, D, bq, bk, 0.1, 1,
+          p(15 * A), p(17 * A), p(19 * A), 1, p(21 * A), wsn, None]
+
+    def call(i, x, base=ok):
+        a = list(base)
+        a[i] = x
+        return f(*a)
+    for i in (0, 1, 2, 3, 4, 5, 6, 15, 16, 17, 19):
+        assert call(i, None) == NULL, i
+    assert call(9, 250) == SHAPE and call(7, 0) == SHAPE
+    assert call(10, 96) == UNSUP and call(11, 32) == UNSUP and call(14, 0) == UNSUP  # D, block, fp32 inputs
+    assert call(18, 7) == UNSUP
+    assert call(20, wsn - 1) == WS
+    for i in (0, 3, 5, 15, 19):
+        assert call(i, p(ok[i].value + 8)) == ALIGN, i
+    assert call(4, p(9 * A + 2)) == ALIGN
+    assert call(13, float("nan")) == SCALE and call(13, math.inf) == SCALE
+    assert call(19, p(3 * A + 64)) == ALIAS                 # workspace over k
+    assert call(15, p(A + 128)) == ALIAS                    # dq over q
+    assert call(16, p(15 * A + 64)) == ALIAS                # dk over dq
+    assert call(17, p(9 * A)) == ALIAS                      # dv over lse
+    g = lib.bsattn_bwd_plan
+    assert g(None, B, H, S, bq, bk, p(21 * A), wsn, None) == NULL
+    assert g(p(13 * A), B, H, S, 32, bk, p(21 * A), wsn, None) == UNSUP
+    assert g(p(13 * A), B, H, S, bq, bk, p(21 * A), 64, None) == WS
+    assert g(p(13 * A), B, H, S, bq, bk, p(21 * A + 4), wsn, None) == ALIGN
+    assert g(p(13 * A), B, H, S, bq, bk, p(13 * A - 64), wsn, None) == ALIAS
+    h = lib.bsattn_bwd_planned
+    okp = ok[:6] + ok[7:]
+
+    def callp(i, x):
+        a = list(okp)
+        a[i] = x
+        return h(*a)
+    for i in (0, 5, 14, 18):
+        assert callp(i, None) == NULL, i
+    assert callp(19, 64) == WS and callp(13, 0) == UNSUP and callp(9, 96) == UNSUP
+    assert callp(14, p(11 * A + 32)) == ALIAS               # dq over dout
+    assert callp(18, p(15 * A + 64)) == ALIAS               # workspace over dq
