@@ -11,6 +11,11 @@ line on stdout:
              the current kernel source exists under profiles/) HBM traffic
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
 
+--backward runs the backward of a block-mask workload instead (bsattn_bwd: plan,
+per-row prep, dk/dv and dq kernels; 10*D FLOPs per active score element, the
+two products of the forward plus dP, dK and dQ); its roofline is the dk/dv
+kernel alone (8*D FLOPs per active element: S, dP, dV, dK).
+
 Element-level mask workloads (--workload causal_elem_bf16) run bsattn_fwd_elem
 the same way, counting 4*D FLOPs per kept (query, key) element.  --workload
 ragged_bf16 runs the ragged dot (grouped matmul, 2*K*N FLOPs per grouped row).
@@ -37,6 +42,7 @@ KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
                   "block_sparse_flash_mask_amd/csrc/bf16_layout.h",
                   "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
                   "block_sparse_flash_mask_amd/csrc/ragged_dot.hip",
+                  "block_sparse_flash_mask_amd/csrc/attn_bwd.hip",
                   "block_sparse_flash_mask_amd/csrc/common.h"]
 
 
@@ -286,6 +292,102 @@ def bench_ragged(args, torch, bs, W):
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_bwd(w, q, k, v, do, mask, budget_s):
+    """Time the fp64 oracle's full backward on whole heads of the workload, one
+    head at a time until the budget is spent."""
+    import oracle
+    import torch
+    oracle.build(force=False)
+    nthreads = oracle.max_threads()
+    flops, t_used, heads = 0.0, 0.0, 0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        sl = lambda t: t[b:b + 1, h:h + 1].contiguous()
+        elems = int(mask[b, h].ne(0).sum()) * w.block_q * w.block_k
+        t0 = time.perf_counter()
+        oracle.bwd(sl(q), sl(k), sl(v), sl(do), sl(mask), w.block_q, w.block_k, w.scale)
+        t_used += time.perf_counter() - t0
+        flops += 10.0 * w.D * elems
+        heads += 1
+        if t_used >= budget_s:
+            break
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": "the full backward of the first %d of %d heads; %.1f s" % (heads, w.B * w.H, t_used)}
+
+
+def bench_bwd(args, torch, bs, W):
+    """One step = bsattn_bwd (plan, prep, dk/dv kernel, dq kernel) on resident
+    q, k, v, out, lse, dout."""
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("the backward is built for bf16 inputs")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs (backward)" % w.name)
+    q, k, v, mask = W.make_inputs(w)
+    g = torch.Generator().manual_seed(99)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod, md = (t.to(dev) for t in (q, k, v, do, mask))
+    nnz = int(mask.ne(0).sum())
+    elems = nnz * w.block_q * w.block_k
+    flops = 10.0 * w.D * elems
+    out, lse = bs.fwd(qd, kd, vd, md, w.block_q, w.block_k, w.scale)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(bs.bwd_workspace_size(w.B, w.H, w.S, w.block_q, w.block_k), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    step = lambda: bs.bwd(qd, kd, vd, out, lse, dod, md, w.block_q, w.block_k, w.scale, dq=dq, dk=dk,
+                          dv=dv, workspace=ws)
+    log("bench: warmup %d, timed %d steps" % (args.warmup, args.steps))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    # each kernel of the step alone, on the plan and scratch the step left in ws
+    part = lambda p: (lambda: bs.bwd_planned(qd, kd, vd, out, lse, dod, ws, w.block_q, w.block_k, w.scale,
+                                             dq=dq, dk=dk, dv=dv, parts=p))
+    ms = {}
+    for name, p in (("prep", bs.BWD_PREP), ("dkdv", bs.BWD_DKDV), ("dq", bs.BWD_DQ)):
+        for _ in range(3):
+            part(p)()
+        torch.cuda.synchronize()
+        ms[name] = timed(part(p), args.steps)
+    achieved = 8.0 * w.D * elems / (ms["dkdv"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(w.name + "_bwd", ("dkdv",)),
+                "kernel": "bwd_dkdv_kernel", "kernel_ms": ms["dkdv"],
+                "kernels_ms": ms,
+                "dq_tflops": 6.0 * w.D * elems / (ms["dq"] * 1e-3) / 1e12}
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "block-sparse attn bwd effective TFLOP/s (10*D per active element) + % bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name + " backward", "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_k": w.block_k, "mask": w.mask_kind,
+                   "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
+                   "grad_dtype": "bf16", "flops_per_step": flops},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's backward on whole heads")
+        res["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, mask, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +397,8 @@ def main():
     ap.add_argument("--config", default=None, help="tile config tq,tk,waves,stages (default: autotune)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (bsattn_bwd) of the block-mask workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (to scale HBM "
                          "byte counters against a kernel of known traffic)")
@@ -328,6 +432,9 @@ def main():
         return
     if args.workload in W.RAGGED_WORKLOADS:
         bench_ragged(args, torch, bs, W)
+        return
+    if args.backward:
+        bench_bwd(args, torch, bs, W)
         return
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -97,8 +97,8 @@ def library():
         "bsattn_bwd": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p, sz,
                         p], i32),
         "bsattn_bwd_plan": ([p, i32, i32, i32, i32, i32, p, sz, p], i32),
-        "bsattn_bwd_planned": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p,
-                                sz, p], i32),
+        "bsattn_bwd_planned": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, i32,
+                                p, sz, p], i32),
         "bsattn_ragged_dot_workspace_size": ([i32, i32, szp], i32),
         "bsattn_ragged_dot": ([p, p, p, p, i32, i32, i32, i32, i32, i32, p, sz, p], i32),
         "bsattn_ragged_plan": ([p, i32, i32, p, sz, p], i32),
@@ -485,16 +485,20 @@ def bwd_plan(block_mask, S, block_q, block_k, *, workspace=None, stream=None):
     return ws
 
 
+BWD_PREP, BWD_DQ, BWD_DKDV, BWD_ALL = 4, 1, 2, 7
+
+
 def bwd_planned(q, k, v, out, lse, dout, plan_ws, block_q, block_k, scale=None, *, grad_dtype=None,
-                dq=None, dk=None, dv=None, stream=None):
-    """The gradient kernels alone on a plan from bwd_plan() (bsattn_bwd_planned)."""
+                dq=None, dk=None, dv=None, parts=BWD_ALL, stream=None):
+    """The gradient kernels alone on a plan from bwd_plan() (bsattn_bwd_planned);
+    parts is an OR of BWD_PREP, BWD_DQ, BWD_DKDV."""
     B, H, S, D = _check_inputs(q, k, v)
     if scale is None:
         scale = default_scale(D)
     dq, dk, dv = _grads(q, grad_dtype, dq, dk, dv)
     rc = library().bsattn_bwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), B, H,
                                       S, D, block_q, block_k, float(scale), _dtype_code(q), _ptr(dq),
-                                      _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(plan_ws),
+                                      _ptr(dk), _ptr(dv), _dtype_code(dq), int(parts), _ptr(plan_ws),
                                       plan_ws.numel() * plan_ws.element_size(), _stream(stream))
     _check(rc)
     return dq, dk, dv

@@ -757,9 +757,10 @@ int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q,
 
 int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, int B, int H, int S, int D, int block_q, int block_k, float scale,
-                       int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace,
+                       int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts, void* workspace,
                        size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return BSATTN_ERR_NULL;
+    if (parts <= 0 || parts > (BSATTN_BWD_PREP | BSATTN_BWD_DQ | BSATTN_BWD_DKDV)) return BSATTN_ERR_UNSUPPORTED;
     int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
     if (rc) return rc;
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
@@ -787,8 +788,11 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
     }
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    hipError_t e = launch_bwd_prep(out, dout, lse, ws + L.ld, L.fwd.R * block_q, D, st);
-    if (e != hipSuccess) return hip_fail(e);
+    hipError_t e = hipSuccess;
+    if (parts & BSATTN_BWD_PREP) {
+        e = launch_bwd_prep(out, dout, lse, ws + L.ld, L.fwd.R * block_q, D, st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     BwdArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -816,7 +820,8 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
     a.ksteps_log2 = block_k == 128 ? 2 : 1;
     a.c = scale * kLog2e;
     a.scale = scale;
-    e = launch_bwd_main(a, D, grad_dtype == BSATTN_F32, st);
+    e = launch_bwd_main(a, D, grad_dtype == BSATTN_F32, (parts & BSATTN_BWD_DQ) != 0,
+                        (parts & BSATTN_BWD_DKDV) != 0, st);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }
@@ -855,7 +860,7 @@ int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, con
     rc = bsattn_bwd_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
     if (rc) return rc;
     return bsattn_bwd_planned(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
-                              grad_dtype, workspace, workspace_bytes, stream);
+                              grad_dtype, BSATTN_BWD_ALL, workspace, workspace_bytes, stream);
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,

@@ -433,14 +433,17 @@ hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int
 }
 
 template <int D, int OUT_F32>
-static hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_main(const BwdArgs& a, bool do_dq, bool do_dkdv, hipStream_t stream) {
     const dim3 gk(8 * a.chunk_k), gq(8 * a.chunk_q);
-    if (a.block_k == 128)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, OUT_F32>), gk, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, OUT_F32>), gk, dim3(128), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (do_dkdv) {
+        if (a.block_k == 128)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, OUT_F32>), gk, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, OUT_F32>), gk, dim3(128), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!do_dq) return hipSuccess;
     if (a.block_q == 128)
         hipLaunchKernelGGL((bwd_dq_kernel<D, 4, OUT_F32>), gq, dim3(256), 0, stream, a);
     else
@@ -448,9 +451,10 @@ static hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, hipStream_t stream) {
-    if (D == 128) return out_f32 ? launch_main<128, 1>(a, stream) : launch_main<128, 0>(a, stream);
-    return out_f32 ? launch_main<64, 1>(a, stream) : launch_main<64, 0>(a, stream);
+hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, bool do_dq, bool do_dkdv, hipStream_t stream) {
+    if (D == 128)
+        return out_f32 ? launch_main<128, 1>(a, do_dq, do_dkdv, stream) : launch_main<128, 0>(a, do_dq, do_dkdv, stream);
+    return out_f32 ? launch_main<64, 1>(a, do_dq, do_dkdv, stream) : launch_main<64, 0>(a, do_dq, do_dkdv, stream);
 }
 
 }  // namespace bsattn

@@ -52,7 +52,7 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
                            hipStream_t stream);
 hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int32_t* counts, int32_t* lists,
                            hipStream_t stream);
-hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, bool do_dq, bool do_dkdv, hipStream_t stream);
 
 // Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block
 // lists in LDS, so they take masks of at most this many key blocks per row.

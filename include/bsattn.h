@@ -324,15 +324,21 @@ int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, con
 /* The two steps of bsattn_bwd on their own.  bsattn_bwd_plan reads the mask and
  * writes the plan part of the workspace (it depends on the mask and shape only,
  * so one plan serves every backward call with that mask);
- * bsattn_bwd_planned runs the gradient kernels on it (reading the plan, writing
- * the per-row scratch).  The lists' entries are clamped into range, so a
- * workspace holding no such plan gives wrong values but no access out of
- * bounds. */
+ * bsattn_bwd_planned runs the gradient kernels on it.  parts selects them (a
+ * nonzero OR of the flags below, else BSATTN_ERR_UNSUPPORTED; BSATTN_BWD_ALL
+ * is what bsattn_bwd runs): PREP writes the per-row scratch from out, lse and
+ * dout; DQ writes dq; DKDV writes dk and dv.  DQ and DKDV read the scratch, so a
+ * call without PREP relies on an earlier call with PREP on the same workspace,
+ * out, lse and dout (a caller with no gradient for q runs PREP | DKDV).  Arrays
+ * a call does not write are left untouched.  The lists' entries are clamped
+ * into range, so a workspace holding no such plan gives wrong values but no
+ * access out of bounds. */
+enum { BSATTN_BWD_PREP = 4, BSATTN_BWD_DQ = 1, BSATTN_BWD_DKDV = 2, BSATTN_BWD_ALL = 7 };
 int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int block_k,
                     void* workspace, size_t workspace_bytes, void* stream);
 int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, int B, int H, int S, int D, int block_q, int block_k,
-                       float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+                       float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section

@@ -376,14 +376,15 @@ def test_bwd_argument_checks(lib):
     assert g(p(13 * A), B, H, S, bq, bk, p(21 * A + 4), wsn, None) == ALIGN
     assert g(p(13 * A), B, H, S, bq, bk, p(13 * A - 64), wsn, None) == ALIAS
     h = lib.bsattn_bwd_planned
-    okp = ok[:6] + ok[7:]
+    okp = ok[:6] + ok[7:19] + [7] + ok[19:]
 
     def callp(i, x):
         a = list(okp)
         a[i] = x
         return h(*a)
-    for i in (0, 5, 14, 18):
+    for i in (0, 5, 14, 19):
         assert callp(i, None) == NULL, i
-    assert callp(19, 64) == WS and callp(13, 0) == UNSUP and callp(9, 96) == UNSUP
+    assert callp(20, 64) == WS and callp(13, 0) == UNSUP and callp(9, 96) == UNSUP
+    assert callp(18, 0) == UNSUP and callp(18, 8) == UNSUP   # parts
     assert callp(14, p(11 * A + 32)) == ALIAS               # dq over dout
-    assert callp(18, p(15 * A + 64)) == ALIAS               # workspace over dq
+    assert callp(19, p(15 * A + 64)) == ALIAS               # workspace over dq

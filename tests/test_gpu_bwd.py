@@ -170,3 +170,27 @@ def test_bwd_workload_dense_sampled():
         for name, gg, r, bb in (("dq", gq, rq, bnd[0]), ("dk", gk, rk, bnd[1]), ("dv", gv, rv, bnd[2])):
             got = gg.reshape(-1, D)[torch.as_tensor(rows, device="cuda")]
             _check(name, got, r, bb[loc], True, "%s head %d" % (w.name, bh))
+
+
+def test_bwd_parts():
+    """parts = PREP | DKDV writes dk, dv only (dq untouched) and equals the full
+    call; DQ alone on that workspace then gives the full call's dq."""
+    ensure_built()
+    B, H, S, D, bq, bk = 1, 2, 512, 64, 64, 128
+    q, k, v = (t.cuda() for t in rand_qkv(B, H, S, D, torch.bfloat16, 51))
+    do = torch.randn(B, H, S, D, device="cuda").to(torch.bfloat16)
+    mask = rand_mask(B, H, S // bq, S // bk, 0.5, 51).cuda()
+    out, lse = bs.fwd(q, k, v, mask, bq, bk)
+    full = bs.bwd(q, k, v, out, lse, do, mask, bq, bk)
+    ws = bs.bwd_plan(mask, S, bq, bk)
+    sentinel = torch.full_like(q, 7.0)
+    dq = sentinel.clone()
+    _, dk, dv = bs.bwd_planned(q, k, v, out, lse, do, ws, bq, bk, dq=dq, parts=bs.BWD_PREP | bs.BWD_DKDV)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, sentinel)
+    assert torch.equal(dk, full[1]) and torch.equal(dv, full[2])
+    dk2, dv2 = sentinel.clone(), sentinel.clone()
+    dq2, _, _ = bs.bwd_planned(q, k, v, out, lse, do, ws, bq, bk, dk=dk2, dv=dv2, parts=bs.BWD_DQ)
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, full[0])
+    assert torch.equal(dk2, sentinel) and torch.equal(dv2, sentinel)
