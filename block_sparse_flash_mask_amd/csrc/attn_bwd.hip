@@ -118,9 +118,12 @@ __global__ __launch_bounds__(256) void bwd_cols_kernel(const uint8_t* __restrict
     counts[col] = cnt;
 }
 
-// dK and dV of one key block.  WAVES * 32 = block_k keys per workgroup.
+// dK and dV of one key block.  WAVES * 32 = block_k keys per workgroup.  The
+// register budget is cut for two waves per SIMD with D = 128 (K, V fragments and
+// the dK, dV accumulators alone take 192 VGPRs) and three with D = 64.
 template <int D, int WAVES, int OUT_F32>
-__global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 3 : 2))) void bwd_dkdv_kernel(
+    BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-row tile of Q or dO
     typedef DmaPlan<D, WAVES, 32> P;
     constexpr int KS = G::KS, MD = G::MD;
@@ -281,7 +284,8 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_kernel(BwdArgs a) {
 
 // dQ of one query block.  WAVES * 32 = block_q queries per workgroup.
 template <int D, int WAVES, int OUT_F32>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 4 : 2))) void bwd_dq_kernel(
+    BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-key tile of K or V
     typedef DmaPlan<D, WAVES, 32> P;
     constexpr int KS = G::KS, MD = G::MD;
