@@ -72,24 +72,33 @@ PlanLayout plan_layout(int64_t BH, int n_q, int n_k) {
 
 size_t fwd_ws_bytes(int64_t BH, int n_q, int n_k) { return plan_layout(BH, n_q, n_k).bytes; }
 
-// Backward workspace: the forward plan (rows, for dq), then per key block the
-// count and the query-block list padded to n_q (for dk, dv), then the per-row
-// (lse * log2 e, dout . out) pairs.
+// Backward workspace.  Plan part: the forward plan (rows, for dq), per key block
+// the count and the query-block list padded to n_q, the dk/dv work items
+// (C + max_slots int4), the cut key blocks (max_slots / 2 int4) and the two
+// counts.  Scratch part (written by every backward call): the per-row
+// (lse * log2 e, dout . out) pairs, and the fp32 partial dK, dV of the pieces of
+// cut key blocks (max_slots slots of 2 * block_k * 128 floats).
 struct BwdLayout {
     PlanLayout fwd;
-    int64_t C;  // key blocks (columns): B * H * n_k
-    size_t ccounts, clists, ld, plan_bytes, bytes;
+    int64_t C;          // key blocks (columns): B * H * n_k
+    int64_t max_slots;  // partial slots for pieces of cut key blocks
+    size_t ccounts, clists, items, splits, nout, ld, scratch, plan_bytes, bytes;
 };
 
-BwdLayout bwd_layout(int64_t BH, int S, int n_q, int n_k) {
+BwdLayout bwd_layout(int64_t BH, int S, int n_q, int n_k, int block_k) {
     BwdLayout L;
     L.fwd = plan_layout(BH, n_q, n_k);
     L.C = BH * n_k;
+    L.max_slots = std::max<int64_t>(16, (L.C / 4 + 1) & ~(int64_t)1);
     L.ccounts = L.fwd.bytes;
     L.clists = L.ccounts + align_up((size_t)L.C * 4);
-    L.ld = L.clists + align_up((size_t)(L.C * n_q) * 4);
-    L.plan_bytes = L.ld;
-    L.bytes = L.ld + align_up((size_t)(BH * S) * 8);
+    L.items = L.clists + align_up((size_t)(L.C * n_q) * 4);
+    L.splits = L.items + align_up((size_t)(L.C + L.max_slots) * 16);
+    L.nout = L.splits + align_up((size_t)(L.max_slots / 2) * 16);
+    L.plan_bytes = L.nout + align_up(8);
+    L.ld = L.plan_bytes;
+    L.scratch = L.ld + align_up((size_t)(BH * S) * 8);
+    L.bytes = L.scratch + align_up((size_t)L.max_slots * 2 * block_k * 128 * 4);
     return L;
 }
 
@@ -727,7 +736,7 @@ int bsattn_bwd_workspace_size(int B, int H, int S, int block_q, int block_k, siz
     if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
     const int rc = check_grid(B, H, S / block_q, S / block_k);
     if (rc) return rc;
-    *bytes = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k).bytes;
+    *bytes = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k, block_k).bytes;
     return BSATTN_OK;
 }
 
@@ -740,7 +749,7 @@ int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q,
     const int n_q = S / block_q, n_k = S / block_k;
     const int rc = check_grid(B, H, n_q, n_k);
     if (rc) return rc;
-    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k);
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k, block_k);
     if (workspace_bytes < L.plan_bytes) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
     if (overlap(block_mask, (size_t)L.fwd.R * n_k, workspace, L.plan_bytes)) return BSATTN_ERR_ALIAS;
@@ -751,6 +760,9 @@ int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q,
                                (int32_t*)(ws + L.fwd.porder), st);
     if (e != hipSuccess) return hip_fail(e);
     e = launch_bwd_cols(block_mask, L.C, n_q, n_k, (int32_t*)(ws + L.ccounts), (int32_t*)(ws + L.clists), st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_bwd_split((const int32_t*)(ws + L.ccounts), L.C, n_q, (int)L.max_slots, ws + L.items, ws + L.splits,
+                         (int32_t*)(ws + L.nout), st);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }
@@ -766,7 +778,7 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
     if (grad_dtype != BSATTN_BF16 && grad_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
     const int n_q = S / block_q, n_k = S / block_k;
-    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k);
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, n_q, n_k, block_k);
     if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     const void* al16[] = {q, k, v, out, dout, dq, dk, dv, workspace};
     for (const void* p : al16)
@@ -804,10 +816,15 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
     a.row_order = (const int32_t*)(ws + L.fwd.order);
     a.n_rows = (int)L.fwd.R;
     a.chunk_q = (int)L.fwd.chunk;
-    a.col_counts = (const int32_t*)(ws + L.ccounts);
     a.col_lists = (const int32_t*)(ws + L.clists);
+    a.items = (const int4*)(ws + L.items);
+    a.n_items = (const int32_t*)(ws + L.nout);
+    a.splits = (const int4*)(ws + L.splits);
+    a.scratch = (float*)(ws + L.scratch);
     a.n_cols = (int)L.C;
-    a.chunk_k = (int)xcd_chunk(L.C);
+    a.chunk_k = (int)xcd_chunk(L.C + L.max_slots);
+    a.max_slots = (int)L.max_slots;
+    a.max_splits = (int)(L.max_slots / 2);
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -836,7 +853,7 @@ int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, con
     if (rc) return rc;
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
     if (grad_dtype != BSATTN_BF16 && grad_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
-    const BwdLayout L = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k);
+    const BwdLayout L = bwd_layout((int64_t)B * H, S, S / block_q, S / block_k, block_k);
     if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     // the plan step writes the workspace: it must not overlap any tensor argument
     const size_t nt = (size_t)B * H * S * D * 2, nl = (size_t)B * H * S * 4;

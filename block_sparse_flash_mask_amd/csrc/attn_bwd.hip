@@ -18,8 +18,14 @@
 //                    that saw no key, becomes +inf so that its P is 0).
 //   bwd_cols_kernel  the column form of the block mask: per key block (b, h, kj)
 //                    the ascending list of query blocks that see it.
-//   bwd_dkdv_kernel  one workgroup per key block (32 keys per wave), walking the
-//                    block's query-block list in 32-query steps.  Per step and wave:
+//   bwd_split_kernel the dk/dv work items: one per key block, except that a
+//                    block seen by more query blocks than a piece length T is cut
+//                    into pieces of T (a few global key blocks seen by every query
+//                    block would otherwise be the critical path of the launch).
+//                    T is the smallest power of two >= total / 1024 whose pieces
+//                    fit the scratch slots.
+//   bwd_dkdv_kernel  one workgroup per item (32 keys per wave), walking its
+//                    query-block list in 32-query steps.  Per step and wave:
 //                      S = Q K^T, dP = dO V^T   (A = Q, dO rows from LDS in the K
 //                                               layout, B = the wave's K, V rows
 //                                               held in VGPRs; lane = key column)
@@ -33,6 +39,8 @@
 //   bwd_dq_kernel    one workgroup per query block (32 queries per wave), walking
 //                    the mask row's key-block list in 32-key steps:
 //                      S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//   bwd_reduce_kernel  per cut key block: its pieces' fp32 partials summed in
+//                    piece order, dK scaled, stored.
 // The two main kernels recompute S and dP each (dq is not accumulated across
 // workgroups: no atomics, deterministic results).  Tiles stream HBM -> LDS by
 // buffer loads with the LDS flag in the operand layouts of bf16_layout.h, two
@@ -118,6 +126,105 @@ __global__ __launch_bounds__(256) void bwd_cols_kernel(const uint8_t* __restrict
     counts[col] = cnt;
 }
 
+// Inclusive scan over the 1024 threads of a workgroup (wave scans, then a scan of
+// the wave totals).
+__device__ __forceinline__ int64_t bwd_block_scan(int64_t x, int64_t* wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int64_t t = lane < 16 ? wave_tot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int64_t y = __shfl_up(t, off, 64);
+            if (lane >= off) t += y;
+        }
+        if (lane < 16) wave_tot[lane] = t;
+    }
+    __syncthreads();
+    const int64_t r = x + (wave > 0 ? wave_tot[wave - 1] : 0);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int64_t bwd_block_sum(int64_t x, int64_t* wave_tot) {
+    const int64_t incl = bwd_block_scan(x, wave_tot);
+    __shared__ int64_t total;
+    if (threadIdx.x == 1023) total = incl;
+    __syncthreads();
+    const int64_t t = total;
+    __syncthreads();
+    return t;
+}
+
+// One workgroup of 1024 threads: the dk/dv work items (header) from the column
+// counts.  items holds at most C + max_slots entries, splits at most max_slots / 2.
+__global__ __launch_bounds__(1024) void bwd_split_kernel(const int32_t* __restrict__ counts, int64_t C, int n_q,
+                                                         int max_slots, int4* __restrict__ items,
+                                                         int4* __restrict__ splits, int32_t* __restrict__ n_out) {
+    __shared__ int64_t wave_tot[16];
+    __shared__ int64_t carry[3];  // items, slots, splits before this chunk
+    const int tid = threadIdx.x;
+    auto cnt_of = [&](int64_t c) -> int {
+        const int x = counts[c];
+        return x < 0 ? 0 : (x > n_q ? n_q : x);
+    };
+    int64_t total = 0;
+    for (int64_t c0 = 0; c0 < C; c0 += 1024) total += c0 + tid < C ? cnt_of(c0 + tid) : 0;
+    total = bwd_block_sum(total, wave_tot);
+    int T = 8;
+    while ((int64_t)T * 1024 < total) T <<= 1;
+    for (;; T <<= 1) {  // ends: once T >= n_q no column is cut
+        int64_t pieces = 0;
+        for (int64_t c0 = 0; c0 < C; c0 += 1024)
+            if (c0 + tid < C) {
+                const int x = cnt_of(c0 + tid);
+                pieces += x > T ? (x + T - 1) / T : 0;
+            }
+        if (bwd_block_sum(pieces, wave_tot) <= max_slots || T >= n_q) break;
+    }
+    if (tid == 0) carry[0] = carry[1] = carry[2] = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < C; c0 += 1024) {
+        const int64_t c = c0 + tid;
+        const int x = c < C ? cnt_of(c) : 0;
+        const bool cut = c < C && x > T;
+        const int np = cut ? (x + T - 1) / T : 0;
+        const int64_t n_it = c < C ? (cut ? np : 1) : 0;
+        const int64_t it_incl = bwd_block_scan(n_it, wave_tot);
+        const int64_t sl_incl = bwd_block_scan(np, wave_tot);
+        const int64_t sp_incl = bwd_block_scan(cut ? 1 : 0, wave_tot);
+        const int64_t it0 = carry[0] + it_incl - n_it, sl0 = carry[1] + sl_incl - np;
+        if (c < C) {
+            if (cut) {
+                for (int p = 0; p < np; ++p) {
+                    const int len = x - p * T < T ? x - p * T : T;
+                    items[it0 + p] = make_int4((int)c, p * T, len, (int)(sl0 + p));
+                }
+                splits[carry[2] + sp_incl - 1] = make_int4((int)c, (int)sl0, np, 0);
+            } else {
+                items[it0] = make_int4((int)c, 0, x, -1);
+            }
+        }
+        __syncthreads();
+        if (tid == 1023) {
+            carry[0] += it_incl;
+            carry[1] += sl_incl;
+            carry[2] += sp_incl;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        n_out[0] = (int32_t)carry[0];
+        n_out[1] = (int32_t)carry[2];
+    }
+}
+
 // dK and dV of one key block.  WAVES * 32 = block_k keys per workgroup.  The
 // register budget is cut for two waves per SIMD with D = 128 (K, V fragments and
 // the dK, dV accumulators alone take 192 VGPRs) and three with D = 64.
@@ -131,15 +238,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     __shared__ __attribute__((aligned(1024))) uint8_t qk1[G::BYTES], qv1[G::BYTES], ok1[G::BYTES], ov1[G::BYTES];
     __shared__ __attribute__((aligned(1024))) float2 ld0[128], ld1[128];
 
-    const int slot = bwd_slot(a, nullptr, a.chunk_k, a.n_cols);
-    if (slot < 0) return;
+    // items per XCD chunk from the plan's item count (the grid is sized for the
+    // most items a plan can hold)
+    int n_it = wave_uniform(a.n_items[0]);
+    n_it = n_it < a.n_cols + a.max_slots ? n_it : a.n_cols + a.max_slots;
+    const int item = bwd_slot(a, nullptr, (n_it + 7) >> 3, n_it);
+    if (item < 0) return;
+    const int4 it = a.items[item];
+    // (fields clamped into range: a malformed plan gives wrong values, never an
+    // access out of bounds)
+    int col = wave_uniform(it.x), part_slot = wave_uniform(it.w);
+    col = col < 0 ? 0 : (col >= a.n_cols ? a.n_cols - 1 : col);
+    part_slot = part_slot >= a.max_slots ? a.max_slots - 1 : part_slot;
+    int first = wave_uniform(it.y), cnt = wave_uniform(it.z);
+    first = first < 0 ? 0 : (first > a.n_q ? a.n_q : first);
+    cnt = cnt < 0 ? 0 : (cnt > a.n_q - first ? a.n_q - first : cnt);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int wave_s = wave_uniform(wave);
-    const int bh = slot / a.n_k;
-    const int kj = slot - bh * a.n_k;
-    int cnt = wave_uniform(a.col_counts[slot]);
-    cnt = cnt < 0 ? 0 : (cnt > a.n_q ? a.n_q : cnt);
-    const int32_t* lst = a.col_lists + (size_t)slot * a.n_q;
+    const int bh = col / a.n_k;
+    const int kj = col - bh * a.n_k;
+    const int32_t* lst = a.col_lists + (size_t)col * a.n_q + first;
     const size_t head = (size_t)bh * a.S * D;
     const int key = kj * a.block_k + wave * 32 + l32;
 
@@ -266,6 +384,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     }
 
     // dK^T, dV^T: lane (h, key) holds d = 32md + 8g + 4h + u in register 4g + u.
+    if (part_slot >= 0) {  // a piece of a cut key block: fp32 partials, dK unscaled
+        float* base = a.scratch + (size_t)part_slot * 2 * a.block_k * D + (size_t)(wave * 32 + l32) * D;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * md + 8 * g4 + 4 * h;
+                *(float4*)(base + d0) = make_float4(dka[md][4 * g4], dka[md][4 * g4 + 1], dka[md][4 * g4 + 2],
+                                                    dka[md][4 * g4 + 3]);
+                *(float4*)(base + (size_t)a.block_k * D + d0) =
+                    make_float4(dva[md][4 * g4], dva[md][4 * g4 + 1], dva[md][4 * g4 + 2], dva[md][4 * g4 + 3]);
+            }
+        return;
+    }
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -416,6 +548,42 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         }
 }
 
+// One workgroup per cut key block: dK = scale * sum of its pieces' partials and
+// dV = sum of theirs, in piece order (deterministic).
+template <int D, int OUT_F32>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+    const int sp = blockIdx.x;
+    if (sp >= wave_uniform(a.n_items[1]) || sp >= a.max_splits) return;
+    const int4 s = a.splits[sp];
+    const int col = s.x < 0 ? 0 : (s.x >= a.n_cols ? a.n_cols - 1 : s.x);
+    const int slot0 = s.y < 0 ? 0 : (s.y >= a.max_slots ? a.max_slots - 1 : s.y);
+    const int np = s.z < 0 ? 0 : (s.z > a.max_slots - slot0 ? a.max_slots - slot0 : s.z);
+    const int bh = col / a.n_k, kj = col - bh * a.n_k;
+    const size_t out0 = ((size_t)bh * a.S + (size_t)kj * a.block_k) * D;
+    const int n4 = a.block_k * D / 4;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = k4;
+        for (int p = 0; p < np; ++p) {
+            const float* base = a.scratch + (size_t)(slot0 + p) * 2 * a.block_k * D;
+            const float4 x = ((const float4*)base)[i];
+            const float4 y = ((const float4*)(base + (size_t)a.block_k * D))[i];
+            k4.x += x.x; k4.y += x.y; k4.z += x.z; k4.w += x.w;
+            v4.x += y.x; v4.y += y.y; v4.z += y.z; v4.w += y.w;
+        }
+        const float xk[4] = {k4.x * a.scale, k4.y * a.scale, k4.z * a.scale, k4.w * a.scale};
+        const float xv[4] = {v4.x, v4.y, v4.z, v4.w};
+        store4<D>(a.dk, out0 + 4 * (size_t)i, xk, OUT_F32);
+        store4<D>(a.dv, out0 + 4 * (size_t)i, xv, OUT_F32);
+    }
+}
+
+hipError_t launch_bwd_split(const int32_t* counts, int64_t C, int n_q, int max_slots, void* items, void* splits,
+                            int32_t* n_out, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_split_kernel, dim3(1), dim3(1024), 0, stream, counts, C, n_q, max_slots, (int4*)items,
+                       (int4*)splits, n_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, void* ld, int64_t rows, int D,
                            hipStream_t stream) {
     const int rpb = 256 / (D / 8);
@@ -444,8 +612,13 @@ static hipError_t launch_main(const BwdArgs& a, bool do_dq, bool do_dkdv, hipStr
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, OUT_F32>), gk, dim3(256), 0, stream, a);
         else
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, OUT_F32>), gk, dim3(128), 0, stream, a);
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.max_splits > 0) {
+            hipLaunchKernelGGL((bwd_reduce_kernel<D, OUT_F32>), dim3(a.max_splits), dim3(256), 0, stream, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     if (!do_dq) return hipSuccess;
     if (a.block_q == 128)

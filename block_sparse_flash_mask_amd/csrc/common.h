@@ -65,11 +65,21 @@ struct BwdArgs {
     const int32_t* row_lists;
     const int32_t* row_order;
     int n_rows, chunk_q;
-    // dk, dv: per key block (column, (b*H + h)*n_k + kj) the count and the
-    // query-block list padded to n_q; columns go to the XCDs in chunks of chunk_k.
-    const int32_t* col_counts;
+    // dk, dv: per key block (column, (b*H + h)*n_k + kj) the query-block list
+    // padded to n_q, and the work items over them: {column, first list entry,
+    // entries, partial slot or -1}.  A column with more entries than the plan's
+    // piece length is cut into pieces whose fp32 partial dK and dV go to scratch
+    // slots ([slot][2][block_k][D]: dK unscaled, then dV), summed in piece order by
+    // the reduce kernel (splits: {column, first slot, pieces, 0}).  n_items holds
+    // the item and split counts.  The dk/dv grid holds 8 * chunk_k workgroups
+    // (chunk_k for the most items a plan can hold); the kernel deals the plan's
+    // items to the XCDs in contiguous chunks of ceil(items / 8).
     const int32_t* col_lists;
-    int n_cols, chunk_k;
+    const int4* items;
+    const int32_t* n_items;
+    const int4* splits;
+    float* scratch;
+    int n_cols, chunk_k, max_slots, max_splits;
     void* dq;
     void* dk;
     void* dv;

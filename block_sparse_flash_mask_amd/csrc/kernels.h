@@ -52,6 +52,10 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
                            hipStream_t stream);
 hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int32_t* counts, int32_t* lists,
                            hipStream_t stream);
+// The dk/dv work items (BwdArgs) from the column counts: at most C + max_slots
+// items (int4) and max_slots / 2 splits (int4); n_out = {items, splits}.
+hipError_t launch_bwd_split(const int32_t* counts, int64_t C, int n_q, int max_slots, void* items, void* splits,
+                            int32_t* n_out, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, bool do_dq, bool do_dkdv, hipStream_t stream);
 
 // Row-pair variants (tile_q = 2 * block_q = 256) build the union of two block

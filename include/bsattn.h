@@ -313,8 +313,11 @@ int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M
  * order (no atomics).  The workspace (bsattn_bwd_workspace_size bytes, owned by
  * the caller) holds the plan -- the forward plan of bsattn_plan (row lists, for
  * dq), then per key block (b, h, kj) its count and ascending list of query blocks
- * padded to n_q (int32, for dk and dv) -- and a per-row scratch of 8 bytes
- * (lse * log2 e, dout . out).  Asynchronous on stream; nothing is allocated. */
+ * padded to n_q (int32, for dk and dv), and the dk/dv work items: a key block
+ * seen by many query blocks is cut into pieces whose fp32 partial sums are added
+ * in piece order -- and a scratch part: 8 bytes per row (lse * log2 e,
+ * dout . out) and the partial sums (max(16, B*H*(S/block_k)/4) slots of
+ * 2 * block_k * 128 floats).  Asynchronous on stream; nothing is allocated. */
 int bsattn_bwd_workspace_size(int B, int H, int S, int block_q, int block_k, size_t* bytes);
 int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                const void* dout, const uint8_t* block_mask, int B, int H, int S, int D, int block_q,

@@ -341,7 +341,9 @@ def test_bwd_argument_checks(lib):
     fwd = ctypes.c_size_t(0)
     assert lib.bsattn_workspace_size(B, H, S, bq, bk, ctypes.byref(fwd)) == OK
     C = B * H * nk
-    assert n.value == fwd.value + rnd(C * 4) + rnd(C * nq * 4) + rnd(B * H * S * 8)
+    slots = max(16, (C // 4 + 1) & ~1)
+    assert n.value == (fwd.value + rnd(C * 4) + rnd(C * nq * 4) + rnd((C + slots) * 16) + rnd(slots // 2 * 16)
+                       + rnd(8) + rnd(B * H * S * 8) + rnd(slots * 2 * bk * 128 * 4))
     wsn = n.value
     assert lib.bsattn_bwd_workspace_size(B, H, 250, bq, bk, ctypes.byref(n)) == SHAPE
     assert lib.bsattn_bwd_workspace_size(B, H, S, bq, bk, None) == NULL

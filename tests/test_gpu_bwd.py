@@ -72,12 +72,15 @@ def _check(name, got, ref, bound, grad_bf16, what):
     return float(err.max())
 
 
-def _run(B, H, S, D, bq, bk, scale, seed, grad_dtype, p=0.5, what=""):
+def _run(B, H, S, D, bq, bk, scale, seed, grad_dtype, p=0.5, what="", global_cols=()):
     ensure_built()
     q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed)
     g = torch.Generator().manual_seed(seed + 1)
     do = torch.randn(B, H, S, D, generator=g).to(torch.bfloat16)
     mask = rand_mask(B, H, S // bq, S // bk, p, seed, diag=False, empty_rows=[(0, 0, 1)])
+    for c in global_cols:  # key blocks every query block sees (but the empty row)
+        mask[:, :, :, c] = 1
+        mask[0, 0, 1, :] = 0
     mask[0, -1, :, 0] = 0  # key block 0 of the last head: seen by no query block
     say("bwd", what, (B, H, S, D), (bq, bk), scale, grad_dtype)
     qd, kd, vd, dod, md = (t.cuda() for t in (q, k, v, do, mask))
@@ -194,3 +197,24 @@ def test_bwd_parts():
     torch.cuda.synchronize()
     assert torch.equal(dq2, full[0])
     assert torch.equal(dk2, sentinel) and torch.equal(dv2, sentinel)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_cut_key_blocks(D):
+    """Key blocks seen by every query block are cut into pieces (partial sums in
+    fp32 scratch, added in piece order): S 2048 with 64-blocks gives 32 query
+    blocks per column, far above the piece length, on two global columns."""
+    _run(1, 2, 2048, D, 64, 64, 1.0 / np.sqrt(D), 61 + D, torch.bfloat16, p=0.15, what="cut columns",
+         global_cols=(1, 2))
+    ensure_built()
+    B, H, S, b = 1, 2, 2048, 64
+    q, k, v = (t.cuda() for t in rand_qkv(B, H, S, D, torch.bfloat16, 62))
+    do = torch.randn(B, H, S, D, device="cuda").to(torch.bfloat16)
+    mask = rand_mask(B, H, S // b, S // b, 0.15, 62).cuda()
+    mask[:, :, :, 3] = 1
+    out, lse = bs.fwd(q, k, v, mask, b, b)
+    g1 = bs.bwd(q, k, v, out, lse, do, mask, b, b)
+    g2 = bs.bwd(q, k, v, out, lse, do, mask, b, b)
+    torch.cuda.synchronize()
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
