@@ -108,22 +108,28 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     }
 }
 
-// One thread per key block (column): the ascending list of query blocks whose
-// mask byte is nonzero.  Threads of a wave take adjacent columns, so each mask
-// row is read in contiguous runs.
+// One wave per key block (column): the ascending list of query blocks whose mask
+// byte is nonzero.  Lane l tests query block q0 + l; a ballot and a prefix count
+// of the lower lanes place each hit.
 __global__ __launch_bounds__(256) void bwd_cols_kernel(const uint8_t* __restrict__ mask, int64_t C, int n_q,
                                                        int n_k, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ lists) {
-    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (col >= C) return;
+    const int lane = threadIdx.x & 63;
     const int64_t bh = col / n_k;
     const int kj = (int)(col - bh * n_k);
     const uint8_t* m = mask + bh * n_q * n_k + kj;
     int32_t* lst = lists + col * n_q;
     int cnt = 0;
-    for (int qi = 0; qi < n_q; ++qi)
-        if (m[(int64_t)qi * n_k]) lst[cnt++] = qi;
-    counts[col] = cnt;
+    for (int q0 = 0; q0 < n_q; q0 += 64) {
+        const int qi = q0 + lane;
+        const bool hit = qi < n_q && m[(int64_t)qi * n_k] != 0;
+        const uint64_t bal = __ballot(hit);
+        if (hit) lst[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = qi;
+        cnt += __popcll(bal);
+    }
+    if (lane == 0) counts[col] = cnt;
 }
 
 // Inclusive scan over the 1024 threads of a workgroup (wave scans, then a scan of
@@ -548,11 +554,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         }
 }
 
-// One workgroup per cut key block: dK = scale * sum of its pieces' partials and
-// dV = sum of theirs, in piece order (deterministic).
+// kReduceParts workgroups per cut key block: dK = scale * sum of its pieces'
+// partials and dV = sum of theirs, in piece order (deterministic).
+constexpr int kReduceParts = 8;
 template <int D, int OUT_F32>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
-    const int sp = blockIdx.x;
+    const int sp = blockIdx.x / kReduceParts, part = blockIdx.x % kReduceParts;
     if (sp >= wave_uniform(a.n_items[1]) || sp >= a.max_splits) return;
     const int4 s = a.splits[sp];
     const int col = s.x < 0 ? 0 : (s.x >= a.n_cols ? a.n_cols - 1 : s.x);
@@ -560,8 +567,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
     const int np = s.z < 0 ? 0 : (s.z > a.max_slots - slot0 ? a.max_slots - slot0 : s.z);
     const int bh = col / a.n_k, kj = col - bh * a.n_k;
     const size_t out0 = ((size_t)bh * a.S + (size_t)kj * a.block_k) * D;
-    const int n4 = a.block_k * D / 4;
-    for (int i = threadIdx.x; i < n4; i += 256) {
+    const int n4 = a.block_k * D / 4;  // float4 per block; kReduceParts workgroups share them
+    for (int i = part * 256 + threadIdx.x; i < n4; i += 256 * kReduceParts) {
         float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = k4;
         for (int p = 0; p < np; ++p) {
             const float* base = a.scratch + (size_t)(slot0 + p) * 2 * a.block_k * D;
@@ -599,7 +606,7 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
 
 hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int32_t* counts, int32_t* lists,
                            hipStream_t stream) {
-    const unsigned grid = (unsigned)((C + 255) / 256);
+    const unsigned grid = (unsigned)((C + 3) / 4);
     hipLaunchKernelGGL(bwd_cols_kernel, dim3(grid), dim3(256), 0, stream, mask, C, n_q, n_k, counts, lists);
     return hipGetLastError();
 }
@@ -615,7 +622,8 @@ static hipError_t launch_main(const BwdArgs& a, bool do_dq, bool do_dkdv, hipStr
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.max_splits > 0) {
-            hipLaunchKernelGGL((bwd_reduce_kernel<D, OUT_F32>), dim3(a.max_splits), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((bwd_reduce_kernel<D, OUT_F32>), dim3(a.max_splits * kReduceParts), dim3(256), 0,
+                               stream, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
