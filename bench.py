@@ -72,6 +72,22 @@ def traffic_from_profiles(workload, cfg):
     return entry.get("hbm_bytes_per_launch") if entry else None
 
 
+def cold_ms(torch, stream, fn, n):
+    """Average duration of fn with L2 and MALL flushed before each call: a 1 GiB
+    device buffer is rewritten (untimed) so none of the step's inputs are cached."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    total = 0.0
+    for i in range(n):
+        flush.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    del flush
+    return total / n
+
 def cpu_baseline(w, q, k, v, mask, budget_s):
     """Time the fp64 oracle on a bounded, evenly spaced sample of query rows."""
     import numpy as np
@@ -353,6 +369,7 @@ def bench_bwd(args, torch, bs, W):
         step()
     torch.cuda.synchronize()
     ms_step = timed(step, args.steps)
+    ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
     # each kernel of the step alone, on the plan and scratch the step left in ws
     part = lambda p: (lambda: bs.bwd_planned(qd, kd, vd, out, lse, dod, ws, w.block_q, w.block_k, w.scale,
                                              dq=dq, dk=dk, dv=dv, parts=p))
@@ -381,6 +398,8 @@ def bench_bwd(args, torch, bs, W):
                    "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
                    "grad_dtype": "bf16", "flops_per_step": flops},
         "roofline": roofline,
+        "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
+                 "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle's backward on whole heads")
@@ -480,6 +499,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     log("bench: %.4f ms/step (events), %.4f ms/step (wall)" % (ms_step, wall * 1e3 / args.steps))
+    ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
 
     # The dominant kernel alone: the attention launch of the step (same plan, same
     # tile config, same grid) on a plan made once, K launches bracketed by HIP
@@ -521,6 +541,8 @@ def main():
                    "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
                    "tile_config": list(cfg), "flops_per_step": flops},
         "roofline": roofline,
+        "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
+                 "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
