@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, FP8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -97,6 +97,8 @@ def _as_raw(x):
         x = x.contiguous()
         if x.dtype == torch.bfloat16:
             return x.view(torch.int16).numpy(), BF16
+        if x.dtype == torch.float8_e4m3fn:
+            return x.view(torch.uint8).numpy(), FP8
         if x.dtype == torch.float32:
             return x.numpy(), F32
         if x.dtype == torch.float64:

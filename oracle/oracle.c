@@ -26,7 +26,10 @@
  *     an all -inf row is undefined).
  *   - lse is the natural logarithm of the row's sum of exp(score).
  *   - Inputs are widened exactly to double; scale is the caller's fp32 value
- *     widened, applied as scale * (q . k).
+ *     widened, applied as scale * (q . k).  Inputs may be fp32, bf16, fp64 or fp8
+ *     (e4m3, OCP form: "JAX Pallas and Blackwell", section "What the Tutorial
+ *     Covers", names fp8 among the precisions a kernel switches to); the method is
+ *     the same on the widened values.
  *
  * Two passes per row, with no online rescaling and no tiling:
  *   pass 1: s_j = scale * sum_d q[r][d] * k[j][d]   (d ascending, j ascending over
@@ -86,7 +89,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_FP8 = 3 };
 
 typedef struct {
     const void* q;
@@ -103,9 +106,18 @@ typedef struct {
     int64_t n_tiles;
 } problem;
 
-/* Exact widening of one element to double.  bf16 is the top 16 bits of an fp32. */
+/* Exact widening of one element to double.  bf16 is the top 16 bits of an fp32.
+ * fp8 is e4m3 in the OCP form: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent 0 is subnormal (m/8 * 2^-6), no infinities, S.1111.111 is NaN. */
 static double widen(const void* base, int dtype, int64_t idx) {
     if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORC_FP8) {
+        const uint8_t b = ((const uint8_t*)base)[idx];
+        const int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+        if (e == 15 && m == 7) return NAN;
+        const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+        return sgn ? -mag : mag;
+    }
     if (dtype == ORC_BF16) {
         uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
         float f;
@@ -120,7 +132,7 @@ static int check(const problem* p) {
     if (p->B <= 0 || p->H <= 0 || p->S <= 0 || p->D <= 0) return 2;
     if (p->block_q <= 0 || p->block_k <= 0) return 2;
     if (p->S % p->block_q != 0 || p->S % p->block_k != 0) return 2;
-    if (p->dtype < ORC_F32 || p->dtype > ORC_F64) return 3;
+    if (p->dtype < ORC_F32 || p->dtype > ORC_FP8) return 3;
     if (p->pidx) {
         if (!p->pbits || p->n_tiles < 0 || p->block_k % 32 != 0) return 4;
         /* every partial block must name an existing tile */
@@ -614,7 +626,7 @@ int oracle_ragged_dot(const void* lhs, const void* rhs, int dtype, const int32_t
                       int64_t G, int64_t M, int64_t K, int64_t N, double* out, int nthreads) {
     if (!lhs || !rhs || !group_sizes || !out) return 1;
     if (G <= 0 || M < 0 || K <= 0 || N <= 0) return 2;
-    if (dtype < ORC_F32 || dtype > ORC_F64) return 3;
+    if (dtype < ORC_F32 || dtype > ORC_FP8) return 3;
     int64_t total = 0;
     for (int64_t g = 0; g < G; ++g) {
         if (group_sizes[g] < 0) return 2;

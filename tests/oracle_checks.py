@@ -22,6 +22,8 @@ What pins what:
                     with a large c it also checks the max subtraction
   rows_match_full   the selected-rows entry point equals the full forward
   bf16_widening     bf16 inputs give the same result as their exact fp64 values
+  fp8_widening      every e4m3 byte (one key per query, so out = v) equals torch's
+                    float8_e4m3fn -> float64 conversion; NaN codes give NaN
   compact_brute     CSR compaction equals np.nonzero per row
 Element-level masks (block states 0/1/partial + bit tiles):
   elem_brute        dense literal -inf softmax over the expanded element mask
@@ -85,7 +87,7 @@ def _close(a, b, tol=TOL, what=""):
     assert a.shape == b.shape, (what, a.shape, b.shape)
     fin_a, fin_b = np.isfinite(a), np.isfinite(b)
     assert np.array_equal(fin_a, fin_b), (what, "finite pattern differs")
-    assert np.array_equal(a[~fin_a], b[~fin_b]), (what, "non-finite values differ")
+    assert np.array_equal(a[~fin_a], b[~fin_b], equal_nan=True), (what, "non-finite values differ")
     if fin_a.any():
         err = np.max(np.abs(a[fin_a] - b[fin_b]))
         scale = max(1.0, float(np.max(np.abs(b[fin_b]))))
@@ -111,6 +113,7 @@ CASES = [
     (1, 2, 12, 5, 3, 4, 0.5, 3, torch.float32, 1.3),
     (2, 2, 32, 16, 8, 16, 0.5, 4, torch.bfloat16, 0.25),
     (1, 2, 24, 6, 6, 4, 0.4, 5, torch.float64, -0.9),
+    (1, 2, 32, 16, 8, 8, 0.5, 6, torch.float8_e4m3fn, 0.3),
 ]
 
 
@@ -282,6 +285,18 @@ def bf16_widening(orc):
     o1, l1 = orc.fwd(q, k, v, mask, bq, bk, 0.3)
     o2, l2 = orc.fwd(q.double(), k.double(), v.double(), mask, bq, bk, 0.3)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def fp8_widening(orc):
+    n = 256
+    codes = torch.arange(n, dtype=torch.int32).to(torch.uint8).view(1, 1, n, 1)
+    v = codes.view(torch.float8_e4m3fn).expand(1, 1, n, 2).contiguous()
+    q = torch.zeros(1, 1, n, 2, dtype=torch.float8_e4m3fn)
+    mask = torch.eye(n, dtype=torch.uint8).view(1, 1, n, n)  # query r sees key r only
+    out, lse = orc.fwd(q, q, v, mask, 1, 1, 1.0)
+    want = v.to(torch.float64).numpy()
+    _close(out, want, 0.0, "fp8 codes")
+    _close(lse, np.zeros((1, 1, n)), 0.0, "lse of one key with score 0")
 
 
 def compact_brute(orc):
@@ -585,7 +600,7 @@ def bwd_sample_match(orc):
 
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
-       bf16_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
+       bf16_widening, fp8_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
        elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_one_group,
        ragged_permute, ragged_linear, ragged_tail, ragged_bf16, bwd_autograd, bwd_finite_diff,
        bwd_sums, bwd_constant_v, bwd_linear_dout, bwd_sample_match]

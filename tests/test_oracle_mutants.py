@@ -82,6 +82,9 @@ MUTANTS = {
                                  "if (!p->mask[(bh * p->n_q + qi) * p->n_k + (kj + 1) % p->n_k]) continue;")],
     "bwd_dp_sign": [("dp += widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);",
                      "dp -= widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);")],
+    "fp8_bias_8": [("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)")],
+    "fp8_subnormal_as_normal": [("e == 0 ? ldexp((double)m / 8.0, -6)", "e == 0 ? ldexp(1.0 + (double)m / 8.0, -7)")],
+    "fp8_sign_dropped": [("return sgn ? -mag : mag;", "return mag;")],
     "compact_skips_last_column": [("for (int64_t kj = 0; kj < n_k; ++kj)\n            if (mask[r * n_k + kj])",
                                    "for (int64_t kj = 0; kj < n_k - 1; ++kj)\n            if (mask[r * n_k + kj])")],
 }
