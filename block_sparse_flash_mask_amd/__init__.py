@@ -93,6 +93,9 @@ def library():
         "bsattn_fwd_elem": ([p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
                              p, sz, cfgp, p], i32),
         "bsattn_list_configs_elem": ([i32, i32, i32, i32, cfgp, i32, i32p], i32),
+        "bsattn_fp8_workspace_size": ([i32, i32, i32, i32, i32, i32, szp], i32),
+        "bsattn_fwd_fp8": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, sz, p], i32),
+        "bsattn_fwd_fp8_planned": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, sz, p], i32),
         "bsattn_bwd_workspace_size": ([i32, i32, i32, i32, i32, szp], i32),
         "bsattn_bwd": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p, sz,
                         p], i32),
@@ -435,6 +438,50 @@ def ragged_dot_planned(lhs, rhs, plan_ws, *, out=None, out_dtype=None, stream=No
     _check(rc)
     return out
 
+
+def fp8_workspace_size(B, H, S, D, block_q, block_k):
+    n = ctypes.c_size_t(0)
+    _check(library().bsattn_fp8_workspace_size(B, H, S, D, block_q, block_k, ctypes.byref(n)))
+    return n.value
+
+
+def fwd_fp8(q, k, v, block_mask, block_q, block_k, scale=None, *, out=None, lse=None, workspace=None,
+            stream=None):
+    """Forward with fp8 e4m3 q, k, v (torch.float8_e4m3fn), bf16 out (bsattn_fwd_fp8).
+    Returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("q, k, v must be torch.float8_e4m3fn")
+    block_mask = _mask_u8(block_mask)
+    if tuple(block_mask.shape) != (B, H, S // block_q, S // block_k):
+        raise ValueError("block_mask must be [B, H, S/block_q, S/block_k]")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ws = _workspace(fp8_workspace_size(B, H, S, D, block_q, block_k), q.device, workspace)
+    _check(library().bsattn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(out), _ptr(lse), B, H, S,
+                                    D, block_q, block_k, float(scale), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return out, lse
+
+
+def fwd_fp8_planned(q, k, v, fp8_ws, block_q, block_k, scale=None, *, out=None, lse=None, stream=None):
+    """bsattn_fwd_fp8_planned on a workspace of fp8_workspace_size() bytes whose
+    first part holds a plan written by plan(block_mask, ..., workspace=fp8_ws)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _check(library().bsattn_fwd_fp8_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S, D, block_q,
+                                            block_k, float(scale), _ptr(fp8_ws),
+                                            fp8_ws.numel() * fp8_ws.element_size(), _stream(stream)))
+    return out, lse
 
 def bwd_workspace_size(B, H, S, block_q, block_k):
     n = ctypes.c_size_t(0)

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 
-SOURCES = ["compact.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "attn_f32.hip", "ragged_dot.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["compact.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "attn_f32.hip", "ragged_dot.hip", "attn_bwd.hip", "attn_fp8.hip", "api.cpp"]
 HEADERS = ["common.h", "kernels.h"]
 
 ARCH = "gfx950"

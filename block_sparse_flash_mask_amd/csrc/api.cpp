@@ -372,6 +372,47 @@ const Variant* find_elem(int dtype, int D, int block_q, int block_k, const bsatt
     return nullptr;
 }
 
+// The fp8 workspace: the forward plan, then V rearranged per 64-key tile (B*H*S*D
+// bytes, rewritten by every call).
+struct Fp8Layout {
+    PlanLayout plan;
+    size_t vt, bytes;
+};
+
+Fp8Layout fp8_layout(int64_t BH, int S, int D, int n_q, int n_k) {
+    Fp8Layout L;
+    L.plan = plan_layout(BH, n_q, n_k);
+    L.vt = L.plan.bytes;
+    L.bytes = L.vt + align_up((size_t)(BH * S) * D);
+    return L;
+}
+
+const Variant* fp8_find(int D, int block_q) {
+    int n = 0;
+    const Variant* t = fp8_variants(&n);
+    for (int i = 0; i < n; ++i)
+        if (t[i].D == D && t[i].tile_q == block_q) return &t[i];
+    return nullptr;
+}
+
+// Checks of the fp8 forward's tensors (q, k, v e4m3; out bf16; lse fp32).
+int check_fp8_buffers(const void* q, const void* k, const void* v, const void* out, const float* lse, int B,
+                      int H, int S, int D, int block_q, int block_k, float scale) {
+    if (!q || !k || !v || !out || !lse) return BSATTN_ERR_NULL;
+    const int rc = check_fwd_shape(B, H, S, D, block_q, block_k, BSATTN_BF16);
+    if (rc) return rc;
+    if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||
+        !is_aligned(lse, 4))
+        return BSATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return BSATTN_ERR_SCALE;
+    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
+    if (overlap(out, no, q, n8) || overlap(out, no, k, n8) || overlap(out, no, v, n8) || overlap(lse, nl, q, n8) ||
+        overlap(lse, nl, k, n8) || overlap(lse, nl, v, n8) || overlap(lse, nl, out, no))
+        return BSATTN_ERR_ALIAS;
+    return BSATTN_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -726,6 +767,71 @@ int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_siz
     if (rc) return rc;
     return bsattn_ragged_dot_planned(lhs, rhs, out, M, K, N, G, dtype, out_dtype, workspace, workspace_bytes,
                                      stream);
+}
+
+// ---- fp8 forward -----------------------------------------------------------------
+
+int bsattn_fp8_workspace_size(int B, int H, int S, int D, int block_q, int block_k, size_t* bytes) {
+    if (!bytes) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    const int rc = check_grid(B, H, S / block_q, S / block_k);
+    if (rc) return rc;
+    *bytes = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k).bytes;
+    return BSATTN_OK;
+}
+
+int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int S, int D, int block_q, int block_k, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!workspace) return BSATTN_ERR_NULL;
+    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
+    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
+    const void* ts[] = {q, k, v, out, lse};
+    const size_t tn[] = {n8, n8, n8, no, nl};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    const Variant* var = fp8_find(D, block_q);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const hipError_t e = launch_fp8_vt(v, ws + L.vt, (int64_t)B * H * S / 64, D, st);
+    if (e != hipSuccess) return hip_fail(e);
+    FwdArgs a = make_args(q, k, ws + L.vt, out, lse, H, S, block_q, block_k, scale, *var);
+    a.qsign = a.qsign ? 0x80808080u : 0u;  // the sign bit of each of four e4m3 bytes
+    a.counts = (const int32_t*)ws;
+    a.list = (const int32_t*)(ws + L.plan.lists);
+    a.ell_stride = n_k;
+    a.order = (const int32_t*)(ws + L.plan.order);
+    a.nrows = (int)L.plan.R;
+    a.chunk = (int)L.plan.chunk;
+    return run_attention(a, *var, st);
+}
+
+int bsattn_fwd_fp8(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* out, float* lse,
+                   int B, int H, int S, int D, int block_q, int block_k, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (!block_mask || !workspace) return BSATTN_ERR_NULL;
+    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    if (rc) return rc;
+    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
+    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
+    const void* ts[] = {q, k, v, out, lse};
+    const size_t tn[] = {n8, n8, n8, no, nl};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    if (!fp8_find(D, block_q)) return BSATTN_ERR_UNSUPPORTED;
+    rc = bsattn_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return bsattn_fwd_fp8_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
+                                  workspace_bytes, stream);
 }
 
 // ---- backward ------------------------------------------------------------------

@@ -1,0 +1,255 @@
+// attn_fp8.hip -- block-sparse flash-attention forward with fp8 (e4m3, OCP form)
+// q, k, v, fp32 accumulation, bf16 out + fp32 lse, for gfx950.
+//
+// What is computed: the forward of attn_bf16.hip ("Writing Pallas Kernels for
+// JAX", section "Writing the Kernel Logic: Load, Compute, Store"; exact tiled
+// softmax, "Pallas-Triton kernels and kernel auto-tuning", section "Flash
+// Attention") on fp8 inputs: "JAX Pallas and Blackwell", section "What the
+// Tutorial Covers", has kernels switch to fp8 operands with fp32 accumulators.
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit
+// scales), twice the bf16 rate; the row max, exponentials and row sums stay fp32
+// (so lse is not quantised), and P is rounded to e4m3 for the P V product.
+//
+// Operand layouts (one step = 64 keys = two 32-key subtiles t):
+//   S^T = K Q^T      A = K from LDS, B = Q^T in VGPRs.  Lane (i + 32h) holds 32
+//                    bytes of row i at d = 64m + 32h .. +31 in both operands, so
+//                    the MFMA pairs equal d whatever its internal k order.
+//   O^T += V^T P^T   B = P^T: lane (j + 32h) packs its own S^T registers of both
+//                    subtiles (byte 16t + 4g + u = key 32t + 8g + 4h + u, the C
+//                    layout of the first product).  A = V^T: lane (d + 32h) needs
+//                    V[key][d] for the same 32 keys in the same byte order; a
+//                    pre-pass (fp8_vt_kernel) writes V per 64-key tile as
+//                    vt[d][64] with byte 32h + 16t + 4g + u = V[32t + 8g + 4h + u][d],
+//                    so each lane reads 32 contiguous bytes.
+// LDS: a K tile is (D/64) * 2 blocks of 2 KiB, block (t, m) holding lane l's
+// bytes K[32t + l%32][64m + 32(l/32) + 16p .. +15] in plane p at p*1024 + l*16; a
+// V^T tile is D/32 blocks, block md holding vt[32md + l%32][32(l/32) + 16p ..]
+// likewise.  Every LDS read is lane-linear 16 bytes (conflict free) and every
+// block is filled by two 1 KiB DMA instructions (buffer loads with the LDS flag,
+// one per plane) whose per-lane offset is the same for all of them.
+#include "bf16_layout.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace bsattn {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int kFp8TK = 64;     // keys per step: the K depth of the fp8 MFMA
+constexpr int kFp8Scale = 127;  // E8M0 block scale of 1.0
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kFp8Scale, 0, kFp8Scale);
+}
+
+// 32 bytes of a lane from two 1 KiB planes.
+__device__ __forceinline__ i32x8 lds32(const uint8_t* blk, int lane) {
+    const u32x4 lo = *(const u32x4*)(blk + lane * 16);
+    const u32x4 hi = *(const u32x4*)(blk + 1024 + lane * 16);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+}  // namespace
+
+// One workgroup per (b*H + h, 64-key tile): vt tile as in the header.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ vt) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * D];  // [key][d]
+    const size_t base = (size_t)blockIdx.x * 64 * D;                // tiles are contiguous per head
+    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) ((u32x4*)tile)[i] = ((const u32x4*)(v + base))[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < D * 16; i += 256) {  // output dword w of row d
+        const int d = i >> 4, w = i & 15;
+        const int key0 = 32 * ((w >> 2) & 1) + 8 * (w & 3) + 4 * (w >> 3);
+        uint32_t x = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x |= (uint32_t)tile[(key0 + u) * D + d] << (8 * u);
+        ((uint32_t*)(vt + base))[i] = x;
+    }
+}
+
+template <int D, int WAVES, int OCC>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_fp8_kernel(
+    FwdArgs a) {
+    constexpr int MQ = D / 64;       // fp8 MFMAs over d per 32x32 score tile
+    constexpr int MD = D / 32;       // 32-wide d tiles of O^T
+    constexpr int TBYTES = 64 * D;   // one K or V^T tile
+    constexpr int NK = 4 * MQ / WAVES;  // K DMA instructions per wave (1 KiB each)
+    constexpr int NV = 2 * MD / WAVES;  // V DMA instructions per wave
+    static_assert(NK * WAVES == 4 * MQ && NV * WAVES == 2 * MD, "even DMA split");
+    __shared__ __attribute__((aligned(1024))) uint8_t k0s[TBYTES], v0s[TBYTES], k1s[TBYTES], v1s[TBYTES];
+
+    int r, sub;
+    block_work(a, r, sub);
+    if (r < 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int wave_s = wave_uniform(wave);
+    const int bh = r / a.n_q;
+    const int qi = r - bh * a.n_q;
+    int beg, cnt;
+    row_list(a, r, beg, cnt);
+    const int sh = a.steps_log2;  // 64-key steps per key block
+    const int n_steps = cnt << sh;
+    const size_t head = (size_t)bh * a.S * D;  // bytes
+    const int q_row = qi * a.block_q + sub * 32 * WAVES + wave * 32 + l32;
+
+    // Q^T: lane (h, q) holds Q[q][64m + 32h .. +31]; a negative scale flips the
+    // sign bit of every byte (c = |scale| log2 e).
+    i32x8 qf[MQ];
+    {
+        const u32x4* qp = (const u32x4*)((const uint8_t*)a.q + head + (size_t)q_row * D);
+        const uint32_t sg = a.qsign;
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+            const u32x4 lo = qp[4 * m + 2 * h] ^ sg, hi = qp[4 * m + 2 * h + 1] ^ sg;
+            qf[m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    }
+
+    const uint8_t* kg = (const uint8_t*)a.k + head;
+    const uint8_t* vg = (const uint8_t*)a.v + head;  // the vt copy
+    const int nrec = a.S * D;
+    const int k_voff = l32 * D + 32 * h, v_voff = l32 * 64 + 32 * h;
+    // K instruction i: plane i & 1 of block (t, m) = (i >> 1) / MQ, (i >> 1) % MQ;
+    // V instruction i: plane i & 1 of block md = i >> 1.  Destination i KiB.
+    auto issue = [&](int key0, uint8_t* kbuf, uint8_t* vbuf) {
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int i = wave_s + j * WAVES;
+            const int p = i & 1, m = (i >> 1) % MQ, t = (i >> 1) / MQ;
+            dma16(kg, nrec, (BSATTN_LDS void*)(kbuf + i * 1024), k_voff, (key0 + 32 * t) * D + 64 * m + 16 * p);
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = wave_s + j * WAVES;
+            dma16(vg, nrec, (BSATTN_LDS void*)(vbuf + i * 1024), v_voff, key0 * D + (i >> 1) * 2048 + 16 * (i & 1));
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 oacc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+
+    auto compute = [&](const uint8_t* kbuf, const uint8_t* vbuf) {
+        f32x16 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            s[t] = f32x16{};
+#pragma unroll
+            for (int m = 0; m < MQ; ++m) s[t] = mfma_fp8(lds32(kbuf + (t * MQ + m) * 2048, lane), qf[m], s[t]);
+        }
+        // row max over the 64 keys and the lazy move of the reference max
+        float tmp[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            tmp[i] = s[0][i];
+            tmp[16 + i] = s[1][i];
+        }
+        const float mx = max_halves_nan(max_tree3<32>(tmp)) * a.c;
+        if (__ballot(mx > m_run + 8.0f) != 0) {
+            const float m_new = fmax_nan(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+            m_run = m_new;
+        }
+        // P = 2^(c S - m) (<= 2^8, inside e4m3's range); fp32 row sums; P^T in e4m3
+        i32x8 pb;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float e[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    e[u] = fast_exp2(__builtin_fmaf(s[t][4 * g + u], a.c, -m_run));
+                    tmp[16 * t + 4 * g + u] = e[u];
+                }
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
+                pb[4 * t + g] = w;
+            }
+        l_run += tree_sum<32>(tmp);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) oacc[md] = mfma_fp8(lds32(vbuf + md * 2048, lane), pb, oacc[md]);
+    };
+
+    auto entry = [&](int t) -> int {
+        const int i = t >> sh;
+        return a.list[beg + (i < cnt ? i : cnt - 1)];
+    };
+    auto key0_of = [&](int kj_raw, int t) -> int {
+        int kj = wave_uniform(kj_raw);
+        kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
+        return kj * a.block_k + (t & ((1 << sh) - 1)) * kFp8TK;
+    };
+    auto step = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur, const uint8_t* vcur) {
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of step t
+        __syncthreads();                     // everyone's landed; step t-1 fully read
+        if (t + 1 < n_steps) {
+            const int kn = key0_of(pre, t + 1);
+            pre = entry(t + 2);
+            issue(kn, kfill, vfill);
+        }
+        compute(kcur, vcur);
+    };
+
+    if (n_steps > 0) {
+        int pre = entry(1);
+        issue(key0_of(entry(0), 0), k0s, v0s);
+        for (int t = 0; t < n_steps; t += 2) {
+            step(t, pre, k1s, v1s, k0s, v0s);
+            if (t + 1 < n_steps) step(t + 1, pre, k0s, v0s, k1s, v1s);
+        }
+    }
+
+    // Epilogue: O / l in bf16, lse = ln2 (m + log2 l); a row with no key block
+    // gets 0 and -inf.
+    const bool any = n_steps > 0;
+    const float l_tot = sum_halves(l_run);
+    const float inv = any ? 1.0f / l_tot : 0.0f;
+    uint16_t* og = (uint16_t*)a.out + (size_t)bh * a.S * D + (size_t)q_row * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 o;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[u] = (__bf16)(oacc[md][4 * g4 + u] * inv);
+            *(bf16x4*)(og + 32 * md + 8 * g4 + 4 * h) = o;
+        }
+    if (h == 0) a.lse[(size_t)bh * a.S + q_row] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_fp8_vt(const void* v, void* vt, int64_t tiles, int D, hipStream_t stream) {
+    if (D == 128)
+        hipLaunchKernelGGL(fp8_vt_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint8_t*)v,
+                           (uint8_t*)vt);
+    else
+        hipLaunchKernelGGL(fp8_vt_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, stream, (const uint8_t*)v,
+                           (uint8_t*)vt);
+    return hipGetLastError();
+}
+
+template <int D, int W, int OCC>
+static hipError_t launch_fp8(const FwdArgs& a, unsigned grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_fp8_kernel<D, W, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// {dtype 2 = fp8, D, tile_q, tile_k, waves, stages, launcher}
+static const Variant kFp8Variants[] = {
+    {2, 128, 128, 64, 4, 2, &launch_fp8<128, 4, 2>}, {2, 128, 64, 64, 2, 2, &launch_fp8<128, 2, 2>},
+    {2, 64, 128, 64, 4, 2, &launch_fp8<64, 4, 3>},   {2, 64, 64, 64, 2, 2, &launch_fp8<64, 2, 3>},
+};
+
+const Variant* fp8_variants(int* n) {
+    *n = (int)(sizeof(kFp8Variants) / sizeof(kFp8Variants[0]));
+    return kFp8Variants;
+}
+
+}  // namespace bsattn

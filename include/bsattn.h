@@ -252,6 +252,32 @@ int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* 
 int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,
                              int cap, int* n);
 
+/* ---- fp8 forward ------------------------------------------------------------------
+ * The forward above with q, k, v in fp8 e4m3 (OCP form, one byte per element, the
+ * layout of torch.float8_e4m3fn), out in bf16 and lse in fp32 ("JAX Pallas and
+ * Blackwell", section "What the Tutorial Covers": kernels switch to fp8 operands
+ * with fp32 accumulators).  Both products run on the fp8 matrix cores with fp32
+ * accumulation; scores, row maxima, exponentials, row sums and lse are fp32; the
+ * softmax weights are rounded to e4m3 (relative error <= 2^-4, values below 2^-9
+ * of the row's reference maximum flushed towards 0) before they multiply V.
+ *   q, k, v  e4m3 [B][H][S][D] (device); out bf16 [B][H][S][D]; lse float
+ *            [B][H][S]; block_mask as the forward.
+ * D 64 or 128, block_q and block_k 64 or 128 (BSATTN_ERR_UNSUPPORTED); q, k, v,
+ * out and the workspace 16-byte aligned, lse 4-byte aligned (BSATTN_ERR_ALIGN);
+ * out or lse overlapping q, k, v or each other, or the workspace overlapping any
+ * of them, gives BSATTN_ERR_ALIAS; other checks as bsattn_fwd.  The workspace
+ * (bsattn_fp8_workspace_size bytes) holds the plan of bsattn_plan followed by a
+ * copy of V rearranged per 64-key tile (B*H*S*D bytes, rewritten by every call).
+ * bsattn_fwd_fp8_planned runs on a plan that bsattn_plan wrote into the first
+ * part of that workspace.  Asynchronous on stream; nothing is allocated. */
+int bsattn_fp8_workspace_size(int B, int H, int S, int D, int block_q, int block_k, size_t* bytes);
+int bsattn_fwd_fp8(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* out,
+                   float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                           int H, int S, int D, int block_q, int block_k, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ---- Ragged dot -------------------------------------------------------------------
  * "Pallas-Triton kernels and kernel auto-tuning", section "Ragged Dot (Group Matrix
  * Multiplication)": rhs is a stack of G expert matrices; the rows of lhs go to the

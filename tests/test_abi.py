@@ -390,3 +390,36 @@ def test_bwd_argument_checks(lib):
     assert callp(18, 0) == UNSUP and callp(18, 8) == UNSUP   # parts
     assert callp(14, p(11 * A + 32)) == ALIAS               # dq over dout
     assert callp(19, p(15 * A + 64)) == ALIAS               # workspace over dq
+
+
+def test_fp8_argument_checks(lib):
+    """fp8 forward: every call below fails a host check (fake pointers)."""
+    p = ctypes.c_void_p
+    B, H, S, D, bq, bk = 1, 2, 256, 128, 128, 64
+    n = ctypes.c_size_t(0)
+    assert lib.bsattn_fp8_workspace_size(B, H, S, D, bq, bk, ctypes.byref(n)) == OK
+    fwd = ctypes.c_size_t(0)
+    assert lib.bsattn_workspace_size(B, H, S, bq, bk, ctypes.byref(fwd)) == OK
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert n.value == fwd.value + rnd(B * H * S * D)
+    wsn = n.value
+    f = lib.bsattn_fwd_fp8
+    # q k v mask out lse B H S D bq bk scale ws wsb stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), p(9 * A), p(11 * A), B, H, S, D, bq, bk, 0.1, p(13 * A), wsn, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    for i in (0, 1, 2, 3, 4, 5, 13):
+        assert call(i, None) == NULL, i
+    assert call(8, 250) == SHAPE and call(9, 96) == UNSUP and call(10, 32) == UNSUP
+    assert call(14, wsn - 1) == WS
+    assert call(0, p(A + 8)) == ALIGN and call(4, p(9 * A + 8)) == ALIGN and call(13, p(13 * A + 8)) == ALIGN
+    assert call(12, float("nan")) == SCALE
+    assert call(4, p(A + 64)) == ALIAS                  # out over q
+    assert call(13, p(5 * A + 64)) == ALIAS             # workspace over v
+    g = lib.bsattn_fwd_fp8_planned
+    okp = ok[:3] + ok[4:]
+    assert g(*(okp[:12] + [p(13 * A), 64, None])) == WS
+    assert g(*(okp[:12] + [None, wsn, None])) == NULL
