@@ -11,6 +11,10 @@ line on stdout:
              the current kernel source exists under profiles/) HBM traffic
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
 
+--fp8 runs the forward of a block-mask workload with q, k, v rounded to fp8 e4m3
+(bsattn_fwd_fp8: plan, V pre-pass, fp8 attention kernel), against the fp8 MFMA
+peak; its roofline is bsattn_fwd_fp8_planned (V pre-pass + attention kernel).
+
 --backward runs the backward of a block-mask workload instead (bsattn_bwd: plan,
 per-row prep, dk/dv and dq kernels; 10*D FLOPs per active score element, the
 two products of the forward plus dP, dK and dQ); its roofline is the dk/dv
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn fwd effective TFLOP/s (active blocks) + % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_FP8_TFLOPS = 5033.2    # fp8 dense MFMA: twice the bf16 rate
 PEAK_F32_TFLOPS = 157.3     # fp32 MFMA/vector dense
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
@@ -43,6 +48,7 @@ KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
                   "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
                   "block_sparse_flash_mask_amd/csrc/ragged_dot.hip",
                   "block_sparse_flash_mask_amd/csrc/attn_bwd.hip",
+                  "block_sparse_flash_mask_amd/csrc/attn_fp8.hip",
                   "block_sparse_flash_mask_amd/csrc/common.h"]
 
 
@@ -407,6 +413,69 @@ def bench_bwd(args, torch, bs, W):
     print(json.dumps(res), flush=True)
 
 
+def bench_fp8(args, torch, bs, W):
+    """One step = bsattn_fwd_fp8 on the workload's shape and mask with e4m3 inputs."""
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs (fp8)" % w.name)
+    q, k, v, mask = W.make_inputs(w)
+    q8, k8, v8 = (t.float().to(torch.float8_e4m3fn) for t in (q, k, v))
+    qd, kd, vd, md = (t.to(dev) for t in (q8, k8, v8, mask))
+    nnz = int(mask.ne(0).sum())
+    flops = 4.0 * w.D * nnz * w.block_q * w.block_k
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(bs.fp8_workspace_size(w.B, w.H, w.S, w.D, w.block_q, w.block_k), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    step = lambda: bs.fwd_fp8(qd, kd, vd, md, w.block_q, w.block_k, w.scale, out=out, lse=lse, workspace=ws)
+    log("bench: warmup %d, timed %d steps" % (args.warmup, args.steps))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
+    planned = lambda: bs.fwd_fp8_planned(qd, kd, vd, ws, w.block_q, w.block_k, w.scale, out=out, lse=lse)
+    for _ in range(3):
+        planned()
+    torch.cuda.synchronize()
+    ms_attn = timed(planned, args.steps)
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "block-sparse attn fwd fp8 effective TFLOP/s (active blocks) + % fp8 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "pct_fp8_mfma_peak": 100.0 * value / PEAK_FP8_TFLOPS,
+        "config": {"workload": w.name + " fp8", "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_k": w.block_k, "mask": w.mask_kind,
+                   "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
+                   "out_dtype": "bf16", "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic_from_profiles(w.name + "_fp8", ("fp8",)),
+                     "kernel": "attn_fp8_kernel (+ fp8_vt_kernel)", "kernel_ms": ms_attn},
+        "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
+                 "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample (fp8 inputs)")
+        res["cpu_baseline"] = cpu_baseline(w, q8, k8, v8, mask, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +485,8 @@ def main():
     ap.add_argument("--config", default=None, help="tile config tq,tk,waves,stages (default: autotune)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the fp8 (e4m3) forward (bsattn_fwd_fp8) of the block-mask workload")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (bsattn_bwd) of the block-mask workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -454,6 +525,9 @@ def main():
         return
     if args.backward:
         bench_bwd(args, torch, bs, W)
+        return
+    if args.fp8:
+        bench_fp8(args, torch, bs, W)
         return
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

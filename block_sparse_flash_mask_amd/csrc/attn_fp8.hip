@@ -53,20 +53,37 @@ __device__ __forceinline__ i32x8 lds32(const uint8_t* blk, int lane) {
 
 }  // namespace
 
-// One workgroup per (b*H + h, 64-key tile): vt tile as in the header.
+// V rearranged per 64-key tile (header).  One workgroup per tile: the tile is
+// read into LDS with 16-byte loads, each thread transposes 4x4 byte blocks (keys
+// key0 .. key0+3 of output dword w, by d = 4*d4 .. +3) in registers into an LDS
+// copy with rows padded to 17 dwords (no bank conflicts on the column writes),
+// and the rows go out with 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ vt) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * D];  // [key][d]
-    const size_t base = (size_t)blockIdx.x * 64 * D;                // tiles are contiguous per head
-    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) ((u32x4*)tile)[i] = ((const u32x4*)(v + base))[i];
+    constexpr int D4 = D / 4;
+    __shared__ uint32_t in[64 * D4];  // [key][d4]
+    __shared__ uint32_t tr[D * 17];   // [d][w], 16 of 17 dwords used
+    const size_t base = (size_t)blockIdx.x * 64 * D;
+    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) ((u32x4*)in)[i] = ((const u32x4*)(v + base))[i];
     __syncthreads();
-    for (int i = threadIdx.x; i < D * 16; i += 256) {  // output dword w of row d
-        const int d = i >> 4, w = i & 15;
+    for (int i = threadIdx.x; i < 16 * D4; i += 256) {
+        const int w = i / D4, d4 = i % D4;
         const int key0 = 32 * ((w >> 2) & 1) + 8 * (w & 3) + 4 * (w >> 3);
-        uint32_t x = 0;
+        uint32_t x[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x |= (uint32_t)tile[(key0 + u) * D + d] << (8 * u);
-        ((uint32_t*)(vt + base))[i] = x;
+        for (int u = 0; u < 4; ++u) x[u] = in[(key0 + u) * D4 + d4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t y = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) y |= ((x[u] >> (8 * j)) & 0xffu) << (8 * u);
+            tr[(4 * d4 + j) * 17 + w] = y;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) {  // row i / 4, dwords 4 (i % 4) .. +3
+        const uint32_t* rp = tr + (i >> 2) * 17 + 4 * (i & 3);
+        ((u32x4*)(vt + base))[i] = u32x4{rp[0], rp[1], rp[2], rp[3]};
     }
 }
 
@@ -243,7 +260,7 @@ static hipError_t launch_fp8(const FwdArgs& a, unsigned grid, hipStream_t stream
 
 // {dtype 2 = fp8, D, tile_q, tile_k, waves, stages, launcher}
 static const Variant kFp8Variants[] = {
-    {2, 128, 128, 64, 4, 2, &launch_fp8<128, 4, 2>}, {2, 128, 64, 64, 2, 2, &launch_fp8<128, 2, 2>},
+    {2, 128, 128, 64, 4, 2, &launch_fp8<128, 4, 3>}, {2, 128, 64, 64, 2, 2, &launch_fp8<128, 2, 3>},
     {2, 64, 128, 64, 4, 2, &launch_fp8<64, 4, 3>},   {2, 64, 64, 64, 2, 2, &launch_fp8<64, 2, 3>},
 };
 
