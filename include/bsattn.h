@@ -255,8 +255,8 @@ int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_
 /* ---- fp8 forward ------------------------------------------------------------------
  * The forward above with q, k, v in fp8 e4m3 (OCP form, one byte per element, the
  * layout of torch.float8_e4m3fn), out in bf16 and lse in fp32 ("JAX Pallas and
- * Blackwell", section "What the Tutorial Covers": kernels switch to fp8 operands
- * with fp32 accumulators).  Both products run on the fp8 matrix cores with fp32
+ * Blackwell", section "What the Tutorial Covers": fp32 accumulators, fp8 only at
+ * the boundary, in a kernel measured against the fp8 peak).  Both products run on the fp8 matrix cores with fp32
  * accumulation; scores, row maxima, exponentials, row sums and lse are fp32; the
  * softmax weights are rounded to e4m3 (relative error <= 2^-4, values below 2^-9
  * of the row's reference maximum flushed towards 0) before they multiply V.

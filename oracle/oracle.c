@@ -28,8 +28,8 @@
  *   - Inputs are widened exactly to double; scale is the caller's fp32 value
  *     widened, applied as scale * (q . k).  Inputs may be fp32, bf16, fp64 or fp8
  *     (e4m3, OCP form: "JAX Pallas and Blackwell", section "What the Tutorial
- *     Covers", names fp8 among the precisions a kernel switches to); the method is
- *     the same on the widened values.
+ *     Covers", keeps fp32 accumulators and fp8 data); the method is the same on
+ *     the widened values.
  *
  * Two passes per row, with no online rescaling and no tiling:
  *   pass 1: s_j = scale * sum_d q[r][d] * k[j][d]   (d ascending, j ascending over
