@@ -723,7 +723,7 @@ int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M
     if (M <= 0 || K <= 0 || N <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
     if (K % 64 != 0 || N % 128 != 0) return BSATTN_ERR_SHAPE;
     if ((int64_t)K * N * 2 >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;  // one expert per buffer
-    if (ragged_max_items(M, G) * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    if (ragged_max_items(M, G) * 2 * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
     if (out_dtype != BSATTN_BF16 && out_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
     const size_t nw = ragged_ws_bytes(M, G);
@@ -748,7 +748,7 @@ int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_siz
     if (M <= 0 || K <= 0 || N <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
     if (K % 64 != 0 || N % 128 != 0) return BSATTN_ERR_SHAPE;
     if ((int64_t)K * N * 2 >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
-    if (ragged_max_items(M, G) * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    if (ragged_max_items(M, G) * 2 * (N / 128) >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
     if (dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
     if (out_dtype != BSATTN_BF16 && out_dtype != BSATTN_F32) return BSATTN_ERR_UNSUPPORTED;
     const size_t nw = ragged_ws_bytes(M, G);

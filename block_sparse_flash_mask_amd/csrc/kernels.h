@@ -35,10 +35,10 @@ hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int6
                                const int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
 
 // Ragged dot (ragged_dot.hip): the work-item bound of a plan (one item per
-// (128-row tile, group) pair that share rows, plus the zero-fill items of the rows
+// (256-row tile, group) pair that share rows, plus the zero-fill items of the rows
 // past the last group), the plan's bytes (items, then their count), the plan
 // launch and the product launch on a plan.
-inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 127) / 128 + G + 1; }
+inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 255) / 256 + G + 1; }
 inline size_t ragged_ws_bytes(int64_t M, int64_t G) { return (size_t)ragged_max_items(M, G) * 16 + 16; }
 hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace, hipStream_t stream);
 hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,

@@ -8,27 +8,32 @@
 // written as 0.  bf16 in, fp32 accumulation, bf16 or fp32 out.
 //
 // Plan (ragged_plan_kernel, one workgroup): the groups' row ranges (a scan of the
-// sizes, clamped into [0, M]) and the work items: one item per (128-row tile, group)
+// sizes, clamped into [0, M]) and the work items: one item per (256-row tile, group)
 // pair that share rows, in group order, each with the row range [lo, hi) it owns
 // (the compaction idea of the attention path: a tile visits only the groups that
 // touch it), then items with group -1 for the rows past the last group, which are
 // only zeroed.  A tile that straddles a boundary is visited once per owner and each
 // visit stores only its own rows, so no two items write the same row.
 //
-// Kernel: one workgroup of 4 waves per (item, 128-column tile); wave w owns 32 rows.
-// C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on v_mfma_f32_32x32x16_bf16: the expert
-// tile W[g][k0..k0+63][n0..n0+127] goes HBM -> LDS by buffer loads with the LDS flag
-// in the transposed-read layout of bf16_layout.h (the V layout of the attention
-// kernel, row stride N), two stages; the A operand comes from ds_read_b64_tr_b16;
-// the B operand X^T is the wave's own rows of lhs, loaded straight into VGPRs one
-// step ahead.
+// Kernels.  ragged_dot256_kernel (N % 256 == 0): one workgroup of 16 waves per
+// (item, 256-column tile), a 256 x 256 output tile, waves in a 4 (columns) x 4
+// (rows) grid, each 64 columns x 64 rows.  C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on
+// v_mfma_f32_32x32x16_bf16 with both operands from LDS: the expert tile
+// W[g][k0..k0+63][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
+// layout, row stride N; A by ds_read_b64_tr_b16) and the lhs rows X[m0..m0+255]
+// [k0..k0+63] in its K layout (row stride K; B by ds_read_b128), both by buffer
+// loads with the LDS flag, two stages.  Per 64-k step a workgroup moves 64 KiB for
+// 256 MFMAs (the 128 x 128 tile moved 32 KiB for 64), which halves the L2 -> LDS
+// bytes per MFMA.  ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
+// 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
+// wave's own lhs rows loaded straight into VGPRs one step ahead.
 #include "bf16_layout.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace bsattn {
 
-constexpr int kRaggedTM = 128;     // rows per tile
+constexpr int kRaggedTM = 256;     // rows per work item (tile)
 constexpr int kRaggedTN = 128;     // columns per tile
 constexpr int kRaggedTK = 64;      // k per step
 constexpr int kRaggedThreads = 1024;
@@ -115,12 +120,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(1024))) uint8_t w1s[G::BYTES];
 
     const int n_tiles = N / kRaggedTN;
-    const int item = blockIdx.x / n_tiles;
-    const int nt = blockIdx.x - item * n_tiles;
+    const int item = blockIdx.x / (2 * n_tiles);
+    const int rem = blockIdx.x - item * 2 * n_tiles;
+    const int half = rem / n_tiles, nt = rem - half * n_tiles;
     if (item >= wave_uniform(n_items[0])) return;
     const int4 it = items[item];
-    const int tile = wave_uniform(it.x), grp = wave_uniform(it.y);
-    const int lo = wave_uniform(it.z), hi = wave_uniform(it.w);
+    const int grp = wave_uniform(it.y);
+    const int row0 = wave_uniform(it.x) * kRaggedTM + half * 128;  // this workgroup's 128 rows
+    int lo = wave_uniform(it.z), hi = wave_uniform(it.w);
+    lo = lo > row0 ? lo : row0;
+    hi = hi < row0 + 128 ? hi : row0 + 128;
+    if (lo >= hi) return;  // the item has no rows in this half
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int wave_s = wave_uniform(wave);
     const int n0 = nt * kRaggedTN;
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // this lane's lhs row (rows outside [lo, hi) are computed on a valid row and
     // never stored)
-    int m = tile * kRaggedTM + 32 * wave + l32;
+    int m = row0 + 32 * wave + l32;
     const bool store = m >= lo && m < hi;
     m = m < M ? m : M - 1;
     const u32x4* xrow = (const u32x4*)(lhs + (size_t)m * K);
@@ -232,6 +242,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 }
 
+template <int OUT_F32>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void ragged_dot256_kernel(
+    const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
+    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N) {
+    typedef TileGeom<256, kRaggedTK> GW;  // W^T tile: "D" = 256 columns, "keys" = 64 k
+    constexpr int MDW = GW::MD;           // 8 column tiles of 32
+    constexpr int KSX = kRaggedTK / 16;   // 4 k-steps of 16 per 64-k step
+    __shared__ __attribute__((aligned(1024))) uint8_t w0s[GW::BYTES], w1s[GW::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t x0s[256 * kRaggedTK * 2], x1s[256 * kRaggedTK * 2];
+
+    const int n_tiles = N / 256;
+    const int item = blockIdx.x / n_tiles;
+    const int nt = blockIdx.x - item * n_tiles;
+    if (item >= wave_uniform(n_items[0])) return;
+    const int4 it = items[item];
+    const int tile = wave_uniform(it.x), grp = wave_uniform(it.y);
+    const int lo = wave_uniform(it.z), hi = wave_uniform(it.w);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int wave_s = wave_uniform(wave);
+    const int n0 = nt * 256, m0 = tile * kRaggedTM;
+    if (grp < 0) {  // rows of no group: zeros
+        for (int r = lo + (tid >> 6); r < hi; r += 16) {
+            const int c = n0 + 4 * (tid & 63);
+            if constexpr (OUT_F32)
+                *(float4*)((float*)out + (size_t)r * N + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                *(uint2*)((uint16_t*)out + (size_t)r * N + c) = make_uint2(0u, 0u);
+        }
+        return;
+    }
+    const int wn = wave & 3, wm = wave >> 2;  // columns 64 wn .., rows 64 wm ..
+
+    // W tile DMA (V layout, row stride N): block pair tb = 2 (wave + 8 i) of the 64
+    // blocks; lane offsets as the attention kernel's V plan with N for the row.
+    const int u = 2 * (lane & 31);
+    const int L = u & 15, gg = (u >> 4) & 1, hh = u >> 5;
+    const int w_lane = (8 * hh + (L >> 2)) * N + 32 * (lane >> 5) + 16 * gg + 4 * (L & 3);
+    const uint16_t* wg = rhs + (size_t)grp * K * N + n0;
+    const int wrec = (int)((size_t)K * N * 2 - (size_t)n0 * 2);
+    // X tile DMA (K layout, row stride K): block b = (32-row tile mt, 16-k step ks)
+    // = mt * 4 + ks; lane l's 16 bytes are X[m0 + 32 mt + kperm(l%32)][k0 + 16 ks +
+    // 8 (l/32) ..].  Rows past M read row M - 1 (never stored), so every access
+    // stays inside lhs.
+    const int xrec = M * K * 2;  // < 2^31: the launcher checks it
+    auto issue = [&](int k0, uint8_t* wbuf, uint8_t* xbuf) {
+#pragma unroll
+        for (int i = 0; i < GW::VBLK / 2 / 16; ++i) {
+            const int tb = 2 * (wave_s + i * 16);
+            const int md = tb % MDW, r = (tb / MDW) % 2, e = (tb / MDW / 2) % 2, mt = tb / MDW / 4;
+            const int uni = (k0 + 32 * mt + 16 * e + 4 * r) * N + 32 * md;
+            dma16(wg, wrec, (BSATTN_LDS void*)(wbuf + (wave_s + i * 16) * 1024), w_lane * 2, uni * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < 32 / 16; ++i) {
+            const int b = wave_s + i * 16, mt = b / KSX, ks = b % KSX;
+            int row = m0 + 32 * mt + kperm(l32);
+            row = row < M ? row : M - 1;
+            dma16(lhs, xrec, (BSATTN_LDS void*)(xbuf + b * 1024), (row * K + 16 * ks + 8 * h) * 2, k0 * 2);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    auto step = [&](const uint8_t* wbuf, const uint8_t* xbuf) {
+#pragma unroll
+        for (int ks = 0; ks < KSX; ++ks) {
+            const int mtk = ks >> 1, e = ks & 1;
+            bf16x8 xf[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                xf[j] = *(const bf16x8*)(xbuf + ((2 * wm + j) * KSX + ks) * 1024 + lane * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int md = 2 * wn + i;
+                const uint8_t* vb = wbuf + (((mtk * 2 + e) * 2) * MDW + md) * 512 + lane * 8;
+                const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb));
+                const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb + MDW * 512));
+                const bf16x8 wf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // One call site of the step, the stage chosen by the step's parity (LDS
+    // addresses are plain integers), so the accumulators keep one register
+    // assignment through the loop.
+    const int n_steps = K / kRaggedTK;
+    issue(0, w0s, x0s);
+    for (int t = 0; t < n_steps; ++t) {
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of step t
+        __syncthreads();                     // everyone's landed; step t-1 fully read
+        const bool odd = t & 1;
+        if (t + 1 < n_steps) issue((t + 1) * kRaggedTK, odd ? w0s : w1s, odd ? x0s : x1s);
+        step(odd ? w1s : w0s, odd ? x1s : x0s);
+    }
+
+    // C^T tile (i, j): lane (h, c) holds row m = m0 + 64 wm + 32 j + kperm(c) and
+    // columns n = n0 + 64 wn + 32 i + 8 g4 + 4 h + u in register 4 g4 + u.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + 64 * wm + 32 * j + kperm(l32);
+        if (m < lo || m >= hi) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int n = n0 + 64 * wn + 32 * i + 8 * g4 + 4 * h;
+                if constexpr (OUT_F32) {
+                    *(float4*)((float*)out + (size_t)m * N + n) =
+                        make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+                } else {
+                    bf16x4 o;
+#pragma unroll
+                    for (int uu = 0; uu < 4; ++uu) o[uu] = (__bf16)acc[i][j][4 * g4 + uu];
+                    *(bf16x4*)((uint16_t*)out + (size_t)m * N + n) = o;
+                }
+            }
+    }
+}
+
 hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace, hipStream_t stream) {
     int4* items = (int4*)workspace;
     int32_t* n_items = (int32_t*)(items + ragged_max_items(M, G));
@@ -245,7 +377,17 @@ hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, in
     const int4* items = (const int4*)workspace;
     const int64_t max_items = ragged_max_items(M, G);
     const int32_t* n_items = (const int32_t*)(items + max_items);
-    const int64_t grid = max_items * (N / kRaggedTN);
+    if (N % 256 == 0 && (int64_t)M * K * 2 < ((int64_t)1 << 31)) {  // lhs through one buffer range
+        const int64_t grid = max_items * (N / 256);
+        if (out_f32)
+            hipLaunchKernelGGL(ragged_dot256_kernel<1>, dim3((unsigned)grid), dim3(1024), 0, stream,
+                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
+        else
+            hipLaunchKernelGGL(ragged_dot256_kernel<0>, dim3((unsigned)grid), dim3(1024), 0, stream,
+                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
+        return hipGetLastError();
+    }
+    const int64_t grid = max_items * 2 * (N / kRaggedTN);
     if (out_f32)
         hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,
                            (const uint16_t*)rhs, items, n_items, out, M, K, N);

@@ -295,7 +295,7 @@ int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* ou
  * aligned, group_sizes 4-byte aligned (BSATTN_ERR_ALIGN); out or the workspace
  * overlapping an input or each other gives BSATTN_ERR_ALIAS.  The workspace
  * (bsattn_ragged_dot_workspace_size bytes, owned by the caller) holds the work
- * plan: one item per (128-row tile, group) pair that share rows.  Asynchronous on
+ * plan: one item per (256-row tile, group) pair that share rows.  Asynchronous on
  * stream; nothing is allocated. */
 int bsattn_ragged_dot_workspace_size(int M, int G, size_t* bytes);
 int bsattn_ragged_dot(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int M,

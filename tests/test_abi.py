@@ -311,7 +311,7 @@ def test_ragged_argument_checks(lib):
     assert call(3, p(A + 64)) == ALIAS and call(10, p(7 * A + 256)) == ALIAS
     n = ctypes.c_size_t(0)
     assert lib.bsattn_ragged_dot_workspace_size(256, 4, ctypes.byref(n)) == OK
-    assert n.value == (2 + 4 + 1) * 16 + 16
+    assert n.value == (1 + 4 + 1) * 16 + 16
     g = lib.bsattn_ragged_plan
     assert g(None, 256, 4, p(9 * A), 4096, None) == NULL and g(p(5 * A), 0, 4, p(9 * A), 4096, None) == SHAPE
     assert g(p(5 * A), 256, 4, p(9 * A), 16, None) == WS and g(p(5 * A + 2), 256, 4, p(9 * A), 4096, None) == ALIGN

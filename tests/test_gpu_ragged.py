@@ -72,6 +72,7 @@ CASES = [
     (512, 192, 384, 4, [130, 126, 129, 127]),       # every tile split between groups
     (200, 64, 128, 3, [-5, 120, 500]),              # a negative size (0) and an overflow (clamped)
     (1024, 256, 128, 2, [0, 1024]),
+    (700, 128, 512, 3, [300, 250, 100]),            # 256-column tiles, rows past M in the last tile
 ]
 
 
