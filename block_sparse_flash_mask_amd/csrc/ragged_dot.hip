@@ -15,16 +15,16 @@
 // only zeroed.  A tile that straddles a boundary is visited once per owner and each
 // visit stores only its own rows, so no two items write the same row.
 //
-// Kernels.  ragged_dot256_kernel (N % 256 == 0): one workgroup of 16 waves per
-// (item, 256-column tile), a 256 x 256 output tile, waves in a 4 (columns) x 4
-// (rows) grid, each 64 columns x 64 rows.  C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on
+// Kernels.  ragged_dot256_kernel (N % 256 == 0): one workgroup of 8 waves per
+// (item, 256-column tile), a 256 x 256 output tile, waves in a 4 (columns) x 2
+// (rows) grid, each 64 columns x 128 rows (each transposing LDS read of W feeds
+// four MFMAs).  C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on
 // v_mfma_f32_32x32x16_bf16 with both operands from LDS: the expert tile
-// W[g][k0..k0+63][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
+// W[g][k0..k0+31][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
 // layout, row stride N; A by ds_read_b64_tr_b16) and the lhs rows X[m0..m0+255]
-// [k0..k0+63] in its K layout (row stride K; B by ds_read_b128), both by buffer
-// loads with the LDS flag, two stages.  Per 64-k step a workgroup moves 64 KiB for
-// 256 MFMAs (the 128 x 128 tile moved 32 KiB for 64), which halves the L2 -> LDS
-// bytes per MFMA.  ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
+// [k0..k0+31] in its K layout (row stride K; B by ds_read_b128), both by buffer
+// loads with the LDS flag, four stages (three steps of loads in flight).  Per k a
+// workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.  ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
 // 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
 // wave's own lhs rows loaded straight into VGPRs one step ahead.
 #include "bf16_layout.h"
@@ -242,15 +242,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 }
 
+constexpr int kR256TK = 32;     // k per step of the 256 x 256 kernel
+constexpr int kR256Stages = 4;  // LDS stages: three steps of loads in flight
+
 template <int OUT_F32>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void ragged_dot256_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot256_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N) {
-    typedef TileGeom<256, kRaggedTK> GW;  // W^T tile: "D" = 256 columns, "keys" = 64 k
-    constexpr int MDW = GW::MD;           // 8 column tiles of 32
-    constexpr int KSX = kRaggedTK / 16;   // 4 k-steps of 16 per 64-k step
-    __shared__ __attribute__((aligned(1024))) uint8_t w0s[GW::BYTES], w1s[GW::BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t x0s[256 * kRaggedTK * 2], x1s[256 * kRaggedTK * 2];
+    typedef TileGeom<256, kR256TK> GW;  // W^T tile: "D" = 256 columns, "keys" = 32 k
+    constexpr int MDW = GW::MD;         // 8 column tiles of 32
+    constexpr int KSX = kR256TK / 16;   // 2 k-steps of 16 per step
+    constexpr int WB = GW::BYTES;       // 16 KiB of W, then 16 KiB of X per stage
+    static_assert(GW::VBLK / 2 == 16 && 8 * KSX == 16, "two W and two X DMAs per wave per stage");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kR256Stages * 2 * WB];
 
     const int n_tiles = N / 256;
     const int item = blockIdx.x / n_tiles;
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     const int wave_s = wave_uniform(wave);
     const int n0 = nt * 256, m0 = tile * kRaggedTM;
     if (grp < 0) {  // rows of no group: zeros
-        for (int r = lo + (tid >> 6); r < hi; r += 16) {
+        for (int r = lo + (tid >> 6); r < hi; r += 8) {
             const int c = n0 + 4 * (tid & 63);
             if constexpr (OUT_F32)
                 *(float4*)((float*)out + (size_t)r * N + c) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -272,79 +276,92 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
         }
         return;
     }
-    const int wn = wave & 3, wm = wave >> 2;  // columns 64 wn .., rows 64 wm ..
+    const int wn = wave & 3, wm = wave >> 2;  // columns 64 wn .., rows 128 wm ..
 
-    // W tile DMA (V layout, row stride N): block pair tb = 2 (wave + 8 i) of the 64
-    // blocks; lane offsets as the attention kernel's V plan with N for the row.
+    // W tile DMA (V layout, row stride N): wave w fills block pairs 2w and 2(w + 8)
+    // of the 32 blocks; lane offsets as the attention kernel's V plan with N for
+    // the row.
     const int u = 2 * (lane & 31);
     const int L = u & 15, gg = (u >> 4) & 1, hh = u >> 5;
     const int w_lane = (8 * hh + (L >> 2)) * N + 32 * (lane >> 5) + 16 * gg + 4 * (L & 3);
     const uint16_t* wg = rhs + (size_t)grp * K * N + n0;
     const int wrec = (int)((size_t)K * N * 2 - (size_t)n0 * 2);
-    // X tile DMA (K layout, row stride K): block b = (32-row tile mt, 16-k step ks)
-    // = mt * 4 + ks; lane l's 16 bytes are X[m0 + 32 mt + kperm(l%32)][k0 + 16 ks +
-    // 8 (l/32) ..].  Rows past M read row M - 1 (never stored), so every access
-    // stays inside lhs.
+    int w_uni[2], x_lane[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tb = 2 * (wave_s + 8 * i);
+        w_uni[i] = (16 * ((tb / MDW / 2) % 2) + 4 * ((tb / MDW) % 2)) * N + 32 * (tb % MDW);
+        // X tile DMA (K layout, row stride K): block b = w + 8 i = (32-row tile
+        // b / 2, 16-k step b % 2); lane l's 16 bytes are X[m0 + 32 (b/2) +
+        // kperm(l%32)][k0 + 16 (b%2) + 8 (l/32) ..].  Rows past M read row M - 1
+        // (never stored).
+        const int b = wave_s + 8 * i;
+        int xrow = m0 + 32 * (b / KSX) + kperm(l32);
+        xrow = xrow < M ? xrow : M - 1;
+        x_lane[i] = (xrow * K + 16 * (b % KSX) + 8 * h) * 2;
+    }
     const int xrec = M * K * 2;  // < 2^31: the launcher checks it
-    auto issue = [&](int k0, uint8_t* wbuf, uint8_t* xbuf) {
+    // Inline-assembly DMA (dma16_raw): with the stage picked at run time the
+    // builtin would make the compiler wait for in-flight stages before every LDS
+    // read; the explicit vmcnt waits and barriers below order it instead.
+    const u32x4 wsrc = make_rsrc(wg, wrec), xsrc = make_rsrc(lhs, xrec);
+    auto issue = [&](int t) {
+        uint8_t* wbuf = lds + (t % kR256Stages) * 2 * WB;
 #pragma unroll
-        for (int i = 0; i < GW::VBLK / 2 / 16; ++i) {
-            const int tb = 2 * (wave_s + i * 16);
-            const int md = tb % MDW, r = (tb / MDW) % 2, e = (tb / MDW / 2) % 2, mt = tb / MDW / 4;
-            const int uni = (k0 + 32 * mt + 16 * e + 4 * r) * N + 32 * md;
-            dma16(wg, wrec, (BSATTN_LDS void*)(wbuf + (wave_s + i * 16) * 1024), w_lane * 2, uni * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < 32 / 16; ++i) {
-            const int b = wave_s + i * 16, mt = b / KSX, ks = b % KSX;
-            int row = m0 + 32 * mt + kperm(l32);
-            row = row < M ? row : M - 1;
-            dma16(lhs, xrec, (BSATTN_LDS void*)(xbuf + b * 1024), (row * K + 16 * ks + 8 * h) * 2, k0 * 2);
+        for (int i = 0; i < 2; ++i) {
+            dma16_raw(wsrc, lds_addr(wbuf + (wave_s + 8 * i) * 1024), w_lane * 2, (t * kR256TK * N + w_uni[i]) * 2);
+            dma16_raw(xsrc, lds_addr(wbuf + WB + (wave_s + 8 * i) * 1024), x_lane[i], t * kR256TK * 2);
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     auto step = [&](const uint8_t* wbuf, const uint8_t* xbuf) {
 #pragma unroll
         for (int ks = 0; ks < KSX; ++ks) {
-            const int mtk = ks >> 1, e = ks & 1;
-            bf16x8 xf[2];
+            bf16x8 xf[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                xf[j] = *(const bf16x8*)(xbuf + ((2 * wm + j) * KSX + ks) * 1024 + lane * 16);
+            for (int j = 0; j < 4; ++j)
+                xf[j] = *(const bf16x8*)(xbuf + ((4 * wm + j) * KSX + ks) * 1024 + lane * 16);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int md = 2 * wn + i;
-                const uint8_t* vb = wbuf + (((mtk * 2 + e) * 2) * MDW + md) * 512 + lane * 8;
+                const uint8_t* vb = wbuf + ((ks * 2) * MDW + md) * 512 + lane * 8;
                 const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb));
                 const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(vb + MDW * 512));
                 const bf16x8 wf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
             }
         }
     };
 
-    // One call site of the step, the stage chosen by the step's parity (LDS
-    // addresses are plain integers), so the accumulators keep one register
-    // assignment through the loop.
-    const int n_steps = K / kRaggedTK;
-    issue(0, w0s, x0s);
+    // Stages 0..2 in flight before the loop; step t waits for its own stage
+    // (leaving the later ones, four DMA instructions each, outstanding), syncs,
+    // issues stage t + 3 into the buffer step t - 1 used, and computes.
+    const int n_steps = K / kR256TK;
+    for (int t = 0; t < kR256Stages - 1 && t < n_steps; ++t) issue(t);
     for (int t = 0; t < n_steps; ++t) {
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of step t
-        __syncthreads();                     // everyone's landed; step t-1 fully read
-        const bool odd = t & 1;
-        if (t + 1 < n_steps) issue((t + 1) * kRaggedTK, odd ? w0s : w1s, odd ? x0s : x1s);
-        step(odd ? w1s : w0s, odd ? x1s : x0s);
+        if (t + 2 < n_steps)
+            __builtin_amdgcn_s_waitcnt(0x3f70 | 8);  // vmcnt(8)
+        else if (t + 1 < n_steps)
+            __builtin_amdgcn_s_waitcnt(0x3f70 | 4);  // vmcnt(4)
+        else
+            __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0)
+        __syncthreads();
+        if (t + kR256Stages - 1 < n_steps) issue(t + kR256Stages - 1);
+        const uint8_t* wbuf = lds + (t % kR256Stages) * 2 * WB;
+        step(wbuf, wbuf + WB);
     }
 
-    // C^T tile (i, j): lane (h, c) holds row m = m0 + 64 wm + 32 j + kperm(c) and
+    // C^T tile (i, j): lane (h, c) holds row m = m0 + 128 wm + 32 j + kperm(c) and
     // columns n = n0 + 64 wn + 32 i + 8 g4 + 4 h + u in register 4 g4 + u.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = m0 + 64 * wm + 32 * j + kperm(l32);
+    for (int j = 0; j < 4; ++j) {
+        const int m = m0 + 128 * wm + 32 * j + kperm(l32);
         if (m < lo || m >= hi) continue;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -380,10 +397,10 @@ hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, in
     if (N % 256 == 0 && (int64_t)M * K * 2 < ((int64_t)1 << 31)) {  // lhs through one buffer range
         const int64_t grid = max_items * (N / 256);
         if (out_f32)
-            hipLaunchKernelGGL(ragged_dot256_kernel<1>, dim3((unsigned)grid), dim3(1024), 0, stream,
+            hipLaunchKernelGGL(ragged_dot256_kernel<1>, dim3((unsigned)grid), dim3(512), 0, stream,
                                (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
         else
-            hipLaunchKernelGGL(ragged_dot256_kernel<0>, dim3((unsigned)grid), dim3(1024), 0, stream,
+            hipLaunchKernelGGL(ragged_dot256_kernel<0>, dim3((unsigned)grid), dim3(512), 0, stream,
                                (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
         return hipGetLastError();
     }
