@@ -41,42 +41,42 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
 PEAK_FP8_TFLOPS = 5033.2    # fp8 dense MFMA: twice the bf16 rate
 PEAK_F32_TFLOPS = 157.3     # fp32 MFMA/vector dense
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["block_sparse_flash_mask_amd/csrc/compact.hip",
-                  "block_sparse_flash_mask_amd/csrc/attn_bf16.hip",
-                  "block_sparse_flash_mask_amd/csrc/attn_bf16_pp.hip",
-                  "block_sparse_flash_mask_amd/csrc/bf16_layout.h",
-                  "block_sparse_flash_mask_amd/csrc/attn_f32.hip",
-                  "block_sparse_flash_mask_amd/csrc/ragged_dot.hip",
-                  "block_sparse_flash_mask_amd/csrc/attn_bwd.hip",
-                  "block_sparse_flash_mask_amd/csrc/attn_fp8.hip",
-                  "block_sparse_flash_mask_amd/csrc/common.h"]
+# The sources each committed counter summary depends on (its hash is stored in
+# the summary and checked before its traffic figure is used).
+_C = "block_sparse_flash_mask_amd/csrc/"
+KERNEL_SOURCES = {
+    "fwd": [_C + f for f in ("compact.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "bf16_layout.h", "common.h")],
+    "ragged": [_C + f for f in ("ragged_dot.hip", "bf16_layout.h", "common.h")],
+    "bwd": [_C + f for f in ("compact.hip", "attn_bwd.hip", "bf16_layout.h", "common.h")],
+    "fp8": [_C + f for f in ("compact.hip", "attn_fp8.hip", "bf16_layout.h", "common.h")],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(family="fwd"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, cfg):
-    """HBM bytes per attention-kernel launch from a committed counter summary, if
-    it was taken on the current kernel source with this tile config; else None."""
+def traffic_from_profiles(workload, cfg, family="fwd"):
+    """HBM bytes per launch of the measured kernel from a committed counter
+    summary, if it was taken on the current sources of that kernel family with
+    this tile config; else None."""
     path = os.path.join(ROOT, "profiles", "attn_traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(family):
         return None
     entry = rec.get("by_config", {}).get(",".join(str(x) for x in cfg))
     return entry.get("hbm_bytes_per_launch") if entry else None
-
 
 def cold_ms(torch, stream, fn, n):
     """Average duration of fn with L2 and MALL flushed before each call: a 1 GiB
@@ -270,10 +270,11 @@ def bench_ragged(args, torch, bs, W):
     torch.cuda.synchronize()
     ms_kernel = timed(prod, args.steps)
     achieved = flops / (ms_kernel * 1e-3) / 1e12
-    traffic = traffic_from_profiles(w.name, (128, 128, 4, 2))
+    big = w.N % 256 == 0 and w.M * w.K * 2 < 2 ** 31  # the 256 x 256 tile kernel runs
+    traffic = traffic_from_profiles(w.name, (256, 256, 8, 4) if big else (128, 128, 4, 2), "ragged")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": "ragged_dot_kernel", "kernel_ms": ms_kernel}
+                "kernel": "ragged_dot256_kernel" if big else "ragged_dot_kernel", "kernel_ms": ms_kernel}
     if traffic:
         roofline["hbm_gbs"] = traffic / (ms_kernel * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
@@ -387,7 +388,7 @@ def bench_bwd(args, torch, bs, W):
         ms[name] = timed(part(p), args.steps)
     achieved = 8.0 * w.D * elems / (ms["dkdv"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(w.name + "_bwd", ("dkdv",)),
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(w.name + "_bwd", ("dkdv",), "bwd"),
                 "kernel": "bwd_dkdv_kernel", "kernel_ms": ms["dkdv"],
                 "kernels_ms": ms,
                 "dq_tflops": 6.0 * w.D * elems / (ms["dq"] * 1e-3) / 1e12}
@@ -465,7 +466,7 @@ def bench_fp8(args, torch, bs, W):
                    "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
                    "out_dtype": "bf16", "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic_from_profiles(w.name + "_fp8", ("fp8",)),
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic_from_profiles(w.name + "_fp8", ("fp8",), "fp8"),
                      "kernel": "attn_fp8_kernel (+ fp8_vt_kernel)", "kernel_ms": ms_attn},
         "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
                  "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
