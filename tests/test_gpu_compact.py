@@ -61,11 +61,21 @@ def _rnd(x):
     return (x + 255) // 256 * 256
 
 
+def _unsnake(a):
+    """Undo the dispatch layout: every other complete group of four is reversed."""
+    a = a.copy()
+    n = len(a)
+    for g0 in range(4, n - 3, 8):
+        a[g0:g0 + 4] = a[g0:g0 + 4][::-1].copy()
+    return a
+
+
 def _check_plan(mask, block_q=128, block_k=128, mask_dev=None):
     """bsattn_plan's three arrays: counts and lists equal the oracle's compaction
     bit for bit; each XCD chunk of the order holds exactly its own rows, then -1
     padding, head by head with each head's rows by non-increasing count (or by
-    non-increasing count alone when a chunk spans too many head x count bins)."""
+    non-increasing count alone when a chunk spans too many head x count bins),
+    laid out with every other complete group of four reversed."""
     ensure_built()
     B, H, n_q, n_k = mask.shape
     S = n_q * block_q
@@ -93,7 +103,7 @@ def _check_plan(mask, block_q=128, block_k=128, mask_dev=None):
         npr = p1 - p0
         assert np.array_equal(np.sort(got[:npr]), np.arange(p0, p1)), ("pairs", x)
         assert np.all(got[npr:] == -1), ("pairs", x)
-        pr = got[:npr]
+        pr = _unsnake(got[:npr])
         bh, j = pr // hq, pr % hq
         ra = bh * n_q + 2 * j
         cb = np.where(2 * j + 1 < n_q, cnt_r[np.minimum(ra + 1, R - 1)], 0)
@@ -112,7 +122,7 @@ def _check_plan(mask, block_q=128, block_k=128, mask_dev=None):
         nr = r1 - r0
         assert np.array_equal(np.sort(got[:nr]), np.arange(r0, r1)), x
         assert np.all(got[nr:] == -1), x
-        rows = got[:nr]
+        rows = _unsnake(got[:nr])
         c = counts[rows]
         by_head = ((chunk + n_q - 1) // n_q + 1) * (n_k + 1) <= 4096
         if by_head:
