@@ -285,7 +285,8 @@ def bench_ragged(args, torch, bs, W):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
-                   "group_sizes": [int(v) for v in sizes], "tile": [128, 128, 64],
+                   "group_sizes": [int(v) for v in sizes],
+                   "tile_m_n_k": [256, 256, 32] if big else [128, 128, 64],
                    "flops_per_step": flops},
         "roofline": roofline,
     }

@@ -248,7 +248,7 @@ constexpr int kR256Stages = 4;  // LDS stages: three steps of loads in flight
 template <int OUT_F32>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot256_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
-    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N) {
+    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items) {
     typedef TileGeom<256, kR256TK> GW;  // W^T tile: "D" = 256 columns, "keys" = 32 k
     constexpr int MDW = GW::MD;         // 8 column tiles of 32
     constexpr int KSX = kR256TK / 16;   // 2 k-steps of 16 per step
@@ -256,10 +256,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(GW::VBLK / 2 == 16 && 8 * KSX == 16, "two W and two X DMAs per wave per stage");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kR256Stages * 2 * WB];
 
+    // Workgroups go to the 8 XCDs round-robin by blockIdx.  XCD x = b % 8 takes the
+    // (b / 8)-th (item, column tile) of its own contiguous chunk of the item-major
+    // sequence: the column tiles of an item (the same lhs rows) and the neighbouring
+    // items of a group (the same expert tiles) then meet in one L2.
     const int n_tiles = N / 256;
-    const int item = blockIdx.x / n_tiles;
-    const int nt = blockIdx.x - item * n_tiles;
-    if (item >= wave_uniform(n_items[0])) return;
+    int n_it = wave_uniform(n_items[0]);
+    n_it = n_it < max_items ? n_it : max_items;  // (a plan never holds more)
+    const int total = n_it * n_tiles;
+    const int chunk = (total + 7) >> 3;
+    const int jx = blockIdx.x >> 3;
+    const int gi = (blockIdx.x & 7) * chunk + jx;
+    if (jx >= chunk || gi >= total) return;
+    const int item = gi / n_tiles;
+    const int nt = gi - item * n_tiles;
     const int4 it = items[item];
     const int tile = wave_uniform(it.x), grp = wave_uniform(it.y);
     const int lo = wave_uniform(it.z), hi = wave_uniform(it.w);
@@ -395,13 +405,14 @@ hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, in
     const int64_t max_items = ragged_max_items(M, G);
     const int32_t* n_items = (const int32_t*)(items + max_items);
     if (N % 256 == 0 && (int64_t)M * K * 2 < ((int64_t)1 << 31)) {  // lhs through one buffer range
-        const int64_t grid = max_items * (N / 256);
+        const int64_t grid = 8 * ((max_items * (N / 256) + 7) / 8);  // 8 XCD chunks
         if (out_f32)
             hipLaunchKernelGGL(ragged_dot256_kernel<1>, dim3((unsigned)grid), dim3(512), 0, stream,
-                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
+                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N, (int)max_items);
         else
             hipLaunchKernelGGL(ragged_dot256_kernel<0>, dim3((unsigned)grid), dim3(512), 0, stream,
-                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N);
+                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N,
+                               (int)max_items);
         return hipGetLastError();
     }
     const int64_t grid = max_items * 2 * (N / kRaggedTN);
