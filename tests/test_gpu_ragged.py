@@ -73,6 +73,10 @@ CASES = [
     (200, 64, 128, 3, [-5, 120, 500]),              # a negative size (0) and an overflow (clamped)
     (1024, 256, 128, 2, [0, 1024]),
     (700, 128, 512, 3, [300, 250, 100]),            # 256-column tiles, rows past M in the last tile
+    # more (item, 256-column tile) pairs than CUs: full rounds of 256 x 256 tiles and
+    # the partial last round as 128 x 128 tiles (an empty group, a 920-row zero tail)
+    (17920, 64, 1024, 5, [5000, 3000, 0, 6000, 3000]),
+    (8192, 64, 2048, 1, [8192]),                    # exactly one full round on 256 CUs
 ]
 
 
