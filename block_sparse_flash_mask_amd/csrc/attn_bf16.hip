@@ -92,6 +92,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // element masks on row pairs: tile + 1 of each key block of either row (0: full)
     __shared__ uint16_t pair_tile[PAIR && ELEM ? 2 * kPairMaxBlocks : 1];
     const int grp = PAIR ? wave >> 2 : 0;
+    // Q^T fragments: lane (h, q) holds Q[q][16*ks + 8*h .. +7] for every ks.
+    bf16x8 qf[NQ][KS];
+    auto load_q = [&](size_t head_q) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            // (a missing row of a row group reads the group's first row, which
+            // always exists; those values are never used)
+            const int qr = row_ok ? q_row0 + 32 * n : q_row0 - (qi - qi0) * a.block_q;
+            const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head_q + (size_t)qr * D);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 t = qp[2 * ks + h];
+                t ^= a.qsign;
+                qf[n][ks] = __builtin_bit_cast(bf16x8, t);
+            }
+        }
+    };
     if constexpr (PAIR) {
         if (a.n_k > kPairMaxBlocks) return;  // the host rejects such shapes first
         const int hq = (a.n_q + 1) >> 1;
@@ -100,6 +117,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         qi = 2 * j + grp;
         qi0 = 2 * j;
         row_ok = qi < a.n_q;
+        // the Q loads go out before the list is built (they do not depend on it)
+        q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
+        load_q((size_t)bh * a.S * D);
         const int ra = bh * a.n_q + 2 * j;
         const bool has_b = 2 * j + 1 < a.n_q;
         const int nw = (a.n_k + 31) >> 5;
@@ -151,34 +171,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
         __syncthreads();
         cnt = wave_uniform(pair_cnt[0]);
-        q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
     } else {
         bh = r / a.n_q;
         qi = r - bh * a.n_q;
         qi0 = qi;
         row_list(a, r, beg, cnt);
         q_row0 = qi * a.block_q + sub * TQ + wave * 32 * NQ + l32;
+        load_q((size_t)bh * a.S * D);
     }
     const int n_steps = cnt << sh;
     const size_t head = (size_t)bh * a.S * D;
     const uint16_t* __restrict__ kg = (const uint16_t*)a.k + head;
     const uint16_t* __restrict__ vg = (const uint16_t*)a.v + head;
 
-    // Q^T fragments: lane (h, q) holds Q[q][16*ks + 8*h .. +7] for every ks.
-    bf16x8 qf[NQ][KS];
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        // (a missing row of a row group reads the group's first row, which
-        // always exists; those values are never used)
-        const int qr = row_ok ? q_row0 + 32 * n : q_row0 - (qi - qi0) * a.block_q;
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + head + (size_t)qr * D);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 t = qp[2 * ks + h];
-            t ^= a.qsign;
-            qf[n][ks] = __builtin_bit_cast(bf16x8, t);
-        }
-    }
 
     P plan;
     plan.init(lane);
