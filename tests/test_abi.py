@@ -423,3 +423,13 @@ def test_fp8_argument_checks(lib):
     okp = ok[:3] + ok[4:]
     assert g(*(okp[:12] + [p(13 * A), 64, None])) == WS
     assert g(*(okp[:12] + [None, wsn, None])) == NULL
+
+
+def test_c_program_builds(lib):
+    """The plain-C user of the ABI (tests/c_abi_fwd.c, run by the GPU tests) compiles
+    and links against libbsattn.so, liboracle.so and the HIP runtime."""
+    import c_abi_build
+    import oracle
+    oracle.build(force=False)
+    exe = c_abi_build.build(force=True)
+    assert os.access(exe, os.X_OK)
