@@ -72,6 +72,12 @@ def configure(lib):
     lib.oracle_bwd_sample.argtypes = [p, p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32,
                                       p, i64, p, p, i64, p, p, i32]
     lib.oracle_bwd_sample.restype = i32
+    lib.oracle_bwd_elem.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64, i64, f32,
+                                    p, p, p, i32]
+    lib.oracle_bwd_elem.restype = i32
+    lib.oracle_bwd_sample_elem.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                           f32, p, i64, p, p, i64, p, p, i32]
+    lib.oracle_bwd_sample_elem.restype = i32
     lib.oracle_probs.argtypes = [p, p, p, i32, p, i64, i64, i64, i64, i64, i64, f32, p]
     lib.oracle_probs.restype = i32
     lib.oracle_compact.argtypes = [p, i64, i64, p, p]
@@ -349,3 +355,46 @@ def compact(mask):
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def bwd_elem(q, k, v, dout, states, pidx, pbits, block_q, block_k, scale, nthreads=0):
+    """Gradients of the element-mask forward (fwd_elem) for the upstream gradient
+    dout: the backward formulas over the kept (query, key) pairs.  Returns (dq,
+    dk, dv), float64 [B,H,S,D]."""
+    lib = _load()
+    B, H, S, D = tuple(q.shape)
+    qa, ka, va, oa, dt, _, _ = _bwd_inputs(q, k, v, dout, np.zeros((B, H, S // block_q, S // block_k),
+                                                                     dtype=np.uint8), block_q, block_k)
+    st, pi, pb, nt = _elem_args(states, pidx, pbits, B, H, S // block_q, S // block_k, block_q, block_k)
+    dq = np.empty((B, H, S, D), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = lib.oracle_bwd_elem(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, oa.ctypes.data, dt, st.ctypes.data,
+                             pi.ctypes.data, pb.ctypes.data, nt, B, H, S, D, block_q, block_k,
+                             float(np.float32(scale)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                             int(nthreads))
+    if rc:
+        raise ValueError("oracle_bwd_elem failed with code %d" % rc)
+    return dq, dk, dv
+
+
+def bwd_sample_elem(q, k, v, dout, states, pidx, pbits, block_q, block_k, scale, q_rows, k_rows, nthreads=0):
+    """bwd_sample for an element-level mask: dq of the flat query rows q_rows, dk
+    and dv of the flat key rows k_rows."""
+    lib = _load()
+    B, H, S, D = tuple(q.shape)
+    qa, ka, va, oa, dt, _, _ = _bwd_inputs(q, k, v, dout, np.zeros((B, H, S // block_q, S // block_k),
+                                                                     dtype=np.uint8), block_q, block_k)
+    st, pi, pb, nt = _elem_args(states, pidx, pbits, B, H, S // block_q, S // block_k, block_q, block_k)
+    qr = np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray(k_rows, dtype=np.int64))
+    dq = np.empty((max(len(qr), 1), D), dtype=np.float64)
+    dk = np.empty((max(len(kr), 1), D), dtype=np.float64)
+    dv = np.empty_like(dk)
+    rc = lib.oracle_bwd_sample_elem(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, oa.ctypes.data, dt,
+                                    st.ctypes.data, pi.ctypes.data, pb.ctypes.data, nt, B, H, S, D, block_q,
+                                    block_k, float(np.float32(scale)), qr.ctypes.data, len(qr), dq.ctypes.data,
+                                    kr.ctypes.data, len(kr), dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc:
+        raise ValueError("oracle_bwd_sample_elem failed with code %d" % rc)
+    return dq[:len(qr)], dk[:len(kr)], dv[:len(kr)]

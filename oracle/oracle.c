@@ -343,11 +343,13 @@ static void bwd_row(const problem* p, const void* dout, int64_t bh, int64_t s, d
     const int64_t qi = s / p->block_q;
     const uint8_t* mrow = p->mask + (bh * p->n_q + qi) * p->n_k;
     const int64_t qbase = (bh * p->S + s) * D;
+    const int64_t brow = (bh * p->n_q + qi) * p->n_k;
     int64_t n = 0;
     double m = -INFINITY;
     for (int64_t kj = 0; kj < p->n_k; ++kj) {
         if (!mrow[kj]) continue;
         for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;
             const int64_t kbase = (bh * p->S + j) * D;
             double dot = 0.0;
             for (int64_t d = 0; d < D; ++d)
@@ -372,7 +374,8 @@ static void bwd_row(const problem* p, const void* dout, int64_t bh, int64_t s, d
     int64_t t = 0;
     for (int64_t kj = 0; kj < p->n_k; ++kj) {
         if (!mrow[kj]) continue;
-        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j, ++t) {
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;
             const int64_t vbase = (bh * p->S + j) * D;
             double dp = 0.0;
             for (int64_t d = 0; d < D; ++d)
@@ -380,6 +383,7 @@ static void bwd_row(const problem* p, const void* dout, int64_t bh, int64_t s, d
             sbuf[t] = exp(sbuf[t] - lse); /* P */
             pbuf[t] = dp;                  /* dP */
             delta += sbuf[t] * dp;
+            ++t;
         }
     }
     *lse_out = lse;
@@ -388,10 +392,12 @@ static void bwd_row(const problem* p, const void* dout, int64_t bh, int64_t s, d
     t = 0;
     for (int64_t kj = 0; kj < p->n_k; ++kj) {
         if (!mrow[kj]) continue;
-        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j, ++t) {
+        for (int64_t j = kj * p->block_k; j < (kj + 1) * p->block_k; ++j) {
+            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;
             const int64_t kbase = (bh * p->S + j) * D;
             const double ds = sbuf[t] * (pbuf[t] - delta);
             for (int64_t d = 0; d < D; ++d) dq_row[d] += ds * widen(p->k, p->dtype, kbase + d);
+            ++t;
         }
     }
     for (int64_t d = 0; d < D; ++d) dq_row[d] *= p->scale;
@@ -405,8 +411,10 @@ static void bwd_key(const problem* p, const void* dout, int64_t bh, int64_t j, c
     const int64_t kbase = (bh * p->S + j) * D;
     for (int64_t d = 0; d < D; ++d) dk_row[d] = dv_row[d] = 0.0;
     for (int64_t qi = 0; qi < p->n_q; ++qi) {
-        if (!p->mask[(bh * p->n_q + qi) * p->n_k + kj]) continue;
+        const int64_t bi = (bh * p->n_q + qi) * p->n_k + kj;
+        if (!p->mask[bi]) continue;
         for (int64_t r = qi * p->block_q; r < (qi + 1) * p->block_q; ++r) {
+            if (!kept(p, p->mask[bi], bi, r, j)) continue;
             const int64_t qbase = (bh * p->S + r) * D;
             double dot = 0.0, dp = 0.0;
             for (int64_t d = 0; d < D; ++d) {
@@ -449,10 +457,9 @@ static int bwd_stats(const problem* p, const void* dout, const uint8_t* want, do
 }
 
 /* Full backward: dq, dk, dv are double[B][H][S][D]. */
-int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
-               const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q,
-               int64_t block_k, float scale, double* dq, double* dk, double* dv, int nthreads) {
-    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+static int run_bwd(const problem* pp, const void* dout, double* dq, double* dk, double* dv, int nthreads) {
+    const problem p = *pp;
+    const int64_t B = p.B, H = p.H, S = p.S, D = p.D;
     int rc = check(&p);
     if (rc) return rc;
     if (!dout || !dq || !dk || !dv) return 1;
@@ -490,16 +497,36 @@ int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, in
     return failed ? 9 : 0;
 }
 
+int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+               const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q,
+               int64_t block_k, float scale, double* dq, double* dk, double* dv, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    return run_bwd(&p, dout, dq, dk, dv, nthreads);
+}
+
+/* The backward with an element-level mask (block states, pidx, bit tiles as in
+ * oracle_fwd_elem): the same formulas over the kept (query, key) pairs only. */
+int oracle_bwd_elem(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    const uint8_t* mask, const int32_t* pidx, const uint32_t* pbits, int64_t n_tiles,
+                    int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+                    float scale, double* dq, double* dk, double* dv, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    if (!pidx) return 1;
+    p.pidx = pidx;
+    p.pbits = pbits;
+    p.n_tiles = n_tiles;
+    return run_bwd(&p, dout, dq, dk, dv, nthreads);
+}
+
 /* Sampled backward: dq of the flat query rows q_rows[i] = (b*H + h)*S + s into
  * dq_rows[n_q_rows][D]; dk and dv of the flat key rows k_rows[i] into
  * dk_rows / dv_rows [n_k_rows][D].  Pass A runs only over the heads that hold a
  * sampled key row. */
-int oracle_bwd_sample(const void* q, const void* k, const void* v, const void* dout, int dtype,
-                      const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D,
-                      int64_t block_q, int64_t block_k, float scale, const int64_t* q_rows,
-                      int64_t n_q_rows, double* dq_rows, const int64_t* k_rows, int64_t n_k_rows,
-                      double* dk_rows, double* dv_rows, int nthreads) {
-    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+static int run_bwd_sample(const problem* pp, const void* dout, const int64_t* q_rows, int64_t n_q_rows,
+                          double* dq_rows, const int64_t* k_rows, int64_t n_k_rows, double* dk_rows,
+                          double* dv_rows, int nthreads) {
+    const problem p = *pp;
+    const int64_t B = p.B, H = p.H, S = p.S, D = p.D;
     int rc = check(&p);
     if (rc) return rc;
     if (!dout || (n_q_rows > 0 && (!q_rows || !dq_rows)) ||
@@ -550,6 +577,29 @@ int oracle_bwd_sample(const void* q, const void* k, const void* v, const void* d
     free(lse);
     free(delta);
     return failed ? 9 : 0;
+}
+
+int oracle_bwd_sample(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                      const uint8_t* mask, int64_t B, int64_t H, int64_t S, int64_t D,
+                      int64_t block_q, int64_t block_k, float scale, const int64_t* q_rows,
+                      int64_t n_q_rows, double* dq_rows, const int64_t* k_rows, int64_t n_k_rows,
+                      double* dk_rows, double* dv_rows, int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    return run_bwd_sample(&p, dout, q_rows, n_q_rows, dq_rows, k_rows, n_k_rows, dk_rows, dv_rows, nthreads);
+}
+
+int oracle_bwd_sample_elem(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                           const uint8_t* mask, const int32_t* pidx, const uint32_t* pbits, int64_t n_tiles,
+                           int64_t B, int64_t H, int64_t S, int64_t D, int64_t block_q, int64_t block_k,
+                           float scale, const int64_t* q_rows, int64_t n_q_rows, double* dq_rows,
+                           const int64_t* k_rows, int64_t n_k_rows, double* dk_rows, double* dv_rows,
+                           int nthreads) {
+    problem p = make_problem(q, k, v, dtype, mask, B, H, S, D, block_q, block_k, scale);
+    if (!pidx) return 1;
+    p.pidx = pidx;
+    p.pbits = pbits;
+    p.n_tiles = n_tiles;
+    return run_bwd_sample(&p, dout, q_rows, n_q_rows, dq_rows, k_rows, n_k_rows, dk_rows, dv_rows, nthreads);
 }
 
 /* Dense probability matrix P[b][h][s][j] (zero where masked), for tiny shapes:

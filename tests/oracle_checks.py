@@ -598,12 +598,97 @@ def bwd_sample_match(orc):
     _close(sv, dv.reshape(-1, D)[kr], 0.0, "dv rows")
 
 
+def _autograd_grads_full(q, k, v, do, full, scale):
+    """_autograd_grads for an element mask full [B,H,S,S] (True = kept)."""
+    full = torch.as_tensor(full)
+    qq, kk, vv = (t.to(torch.float64).clone().requires_grad_(True) for t in (q, k, v))
+    s = float(np.float32(scale)) * torch.matmul(qq, kk.transpose(-1, -2))
+    anyk = full.any(dim=-1, keepdim=True)
+    s = s.masked_fill(~full, float("-inf")).masked_fill(~anyk, 0.0)
+    pr = torch.softmax(s, dim=-1) * anyk
+    out = torch.matmul(pr, vv)
+    loss = (out * do.to(torch.float64)).sum()
+    return [g.numpy() for g in torch.autograd.grad(loss, (qq, kk, vv))]
+
+
+def bwd_elem_autograd(orc):
+    """Element-mask backward against fp64 autograd through the literal element mask
+    (partial tiles, empty blocks, rows that keep nothing, three dtypes)."""
+    for (B, H, S, D, bq, bk, nt, seed, dt, scale) in ELEM_CASES:
+        q = _rand((B, H, S, D), seed, dt)
+        k = _rand((B, H, S, D), seed + 100, dt)
+        v = _rand((B, H, S, D), seed + 200, dt)
+        do = _rand((B, H, S, D), seed + 300, dt)
+        st, pidx, pbits = _elem_case(B, H, S, bq, bk, nt, seed)
+        full = expand_elem(st, pidx, pbits, bq, bk)
+        got = orc.bwd_elem(q, k, v, do, st, pidx, pbits, bq, bk, scale)
+        want = _autograd_grads_full(q, k, v, do, full, scale)
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            _close(a, b, 1e-11, "elem %s %s" % (name, dt))
+        assert (~full.any(axis=-1)).any() or dt != torch.float64  # some row keeps nothing
+
+
+def _bwd_elem_vs_block(orc, fill):
+    B, H, S, D, bq, bk = 1, 2, 64, 8, 16, 32
+    q, k, v, do = (_rand((B, H, S, D), s) for s in (81, 82, 83, 84))
+    st, pidx, pbits = _elem_case(B, H, S, bq, bk, 2, 85)
+    pbits[:] = np.uint32(0xFFFFFFFF) if fill else np.uint32(0)
+    got = orc.bwd_elem(q, k, v, do, st, pidx, pbits, bq, bk, 0.5)
+    blk = (st != 0) if fill else (st == 1)
+    want = orc.bwd(q, k, v, do, blk.astype(np.uint8), bq, bk, 0.5)
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        _close(a, b, 0.0, "elem vs block %s" % name)
+
+
+def bwd_elem_tiles_all_set(orc):
+    _bwd_elem_vs_block(orc, True)
+
+
+def bwd_elem_tiles_all_clear(orc):
+    _bwd_elem_vs_block(orc, False)
+
+
+def bwd_elem_token_causal(orc):
+    """Exact token-causal (full blocks below the diagonal, one lower-triangular
+    tile on it) against the gradients of torch's causal SDPA in fp64."""
+    B, H, S, D, b = 1, 2, 96, 8, 32
+    q, k, v, do = (_rand((B, H, S, D), s) for s in (91, 92, 93, 94))
+    n = S // b
+    st = np.broadcast_to(np.tril(np.ones((n, n), dtype=np.uint8)) + np.eye(n, dtype=np.uint8), (B, H, n, n)).copy()
+    pidx = np.zeros((B, H, n, n), dtype=np.int32)
+    tri = np.tril(np.ones((b, b), dtype=bool))
+    pbits = np.packbits(tri, axis=-1, bitorder="little").view(np.uint32).reshape(1, b, b // 32)
+    got = orc.bwd_elem(q, k, v, do, st, pidx, pbits, b, b, 0.3)
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True, scale=float(np.float32(0.3)))
+    want = torch.autograd.grad((out * do).sum(), (qq, kk, vv))
+    for name, a, w in zip(("dq", "dk", "dv"), got, want):
+        _close(a, w.numpy(), 1e-11, "token causal %s" % name)
+
+
+def bwd_elem_sample_match(orc):
+    (B, H, S, D, bq, bk, nt, seed, dt, scale) = ELEM_CASES[1]
+    q = _rand((B, H, S, D), seed, dt)
+    k = _rand((B, H, S, D), seed + 100, dt)
+    v = _rand((B, H, S, D), seed + 200, dt)
+    do = _rand((B, H, S, D), seed + 300, dt)
+    st, pidx, pbits = _elem_case(B, H, S, bq, bk, nt, seed)
+    dq, dk, dv = orc.bwd_elem(q, k, v, do, st, pidx, pbits, bq, bk, scale)
+    qr = [0, 7, 33, S + 5, 2 * S - 1]
+    kr = [1, 31, 64, S + 2, 2 * S - 3]
+    sq, sk, sv = orc.bwd_sample_elem(q, k, v, do, st, pidx, pbits, bq, bk, scale, qr, kr)
+    _close(sq, dq.reshape(-1, D)[qr], 0.0, "dq rows")
+    _close(sk, dk.reshape(-1, D)[kr], 0.0, "dk rows")
+    _close(sv, dv.reshape(-1, D)[kr], 0.0, "dv rows")
+
+
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
        bf16_widening, fp8_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
        elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_one_group,
        ragged_permute, ragged_linear, ragged_tail, ragged_bf16, bwd_autograd, bwd_finite_diff,
-       bwd_sums, bwd_constant_v, bwd_linear_dout, bwd_sample_match]
+       bwd_sums, bwd_constant_v, bwd_linear_dout, bwd_sample_match, bwd_elem_autograd,
+       bwd_elem_tiles_all_set, bwd_elem_tiles_all_clear, bwd_elem_token_causal, bwd_elem_sample_match]
 
 
 def run_all(orc):

@@ -55,6 +55,13 @@ MUTANTS = {
     "elem_tile_row_from_key": [("const int64_t i = s % p->block_q, c = j % p->block_k;",
                                 "const int64_t i = j % p->block_q, c = j % p->block_k;")],
     "elem_tile_index_ignored": [("(int64_t)p->pidx[bi] * p->block_q", "(int64_t)0 * p->block_q")],
+    # backward with element masks: dk/dv or dq summed over every key of an active block
+    "bwd_dkdv_ignores_element_bits": [("            if (!kept(p, p->mask[bi], bi, r, j)) continue;\n", "")],
+    "bwd_dq_ignores_element_bits": [("            if (!kept(p, mrow[kj], brow + kj, s, j)) continue;\n"
+                                     "            const int64_t kbase = (bh * p->S + j) * D;\n"
+                                     "            const double ds",
+                                     "            const int64_t kbase = (bh * p->S + j) * D;\n"
+                                     "            const double ds")],
     "elem_partial_as_empty": [("if (!p->pidx || blk == 1) return 1;", "if (!p->pidx || blk == 1) return 1;\n    if (blk > 1) return 0;")],
     "ragged_group_start_late": [("const int64_t end = start + group_sizes[g];",
                                  "const int64_t end = start + group_sizes[g];\n        const int64_t start1 = start + (group_sizes[g] > 0);"),
@@ -78,8 +85,8 @@ MUTANTS = {
     "bwd_dk_uses_dout": [("dk_row[d] += ds * widen(p->q, p->dtype, qbase + d);",
                           "dk_row[d] += ds * widen(dout, p->dtype, qbase + d);")],
     "bwd_lse_drops_max": [("const double lse = m + log(l);", "const double lse = log(l);")],
-    "bwd_key_sees_next_block": [("if (!p->mask[(bh * p->n_q + qi) * p->n_k + kj]) continue;",
-                                 "if (!p->mask[(bh * p->n_q + qi) * p->n_k + (kj + 1) % p->n_k]) continue;")],
+    "bwd_key_sees_next_block": [("const int64_t bi = (bh * p->n_q + qi) * p->n_k + kj;",
+                                 "const int64_t bi = (bh * p->n_q + qi) * p->n_k + (kj + 1) % p->n_k;")],
     "bwd_dp_sign": [("dp += widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);",
                      "dp -= widen(dout, p->dtype, qbase + d) * widen(p->v, p->dtype, kbase + d);")],
     "fp8_bias_8": [("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)")],
