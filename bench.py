@@ -415,6 +415,96 @@ def bench_bwd(args, torch, bs, W):
     print(json.dumps(res), flush=True)
 
 
+def bench_bwd_elem(args, torch, bs, W):
+    """One step = bsattn_bwd_elem (plan, prep, dk/dv and dq kernels) of an
+    element-mask workload; 10*D FLOPs per kept (query, key) element."""
+    w = W.ELEM_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s inputs (element-mask backward)" % w.name)
+    q, k, v, _ = W.make_inputs(w)
+    st, pidx, pbits = W.make_elem_mask(w)
+    g = torch.Generator().manual_seed(99)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    sd, pd, bd = st.to(dev), pidx.to(dev), pbits.to(dev)
+    kept = W.kept_elements(st, pidx, pbits, w.block_q, w.block_k)
+    flops = 10.0 * w.D * kept
+    out, lse = bs.fwd_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(bs.bwd_workspace_size(w.B, w.H, w.S, w.block_q, w.block_k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    step = lambda: bs.bwd_elem(qd, kd, vd, out, lse, dod, sd, pd, bd, w.block_q, w.block_k, w.scale, dq=dq,
+                               dk=dk, dv=dv, workspace=ws)
+    log("bench: warmup %d, timed %d steps" % (args.warmup, args.steps))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
+    part = lambda p: (lambda: bs.bwd_planned_elem(qd, kd, vd, out, lse, dod, sd, pd, bd, ws, w.block_q, w.block_k,
+                                                  w.scale, dq=dq, dk=dk, dv=dv, parts=p))
+    ms = {}
+    for name, p in (("prep", bs.BWD_PREP), ("dkdv", bs.BWD_DKDV), ("dq", bs.BWD_DQ)):
+        for _ in range(3):
+            part(p)()
+        torch.cuda.synchronize()
+        ms[name] = timed(part(p), args.steps)
+    achieved = 8.0 * w.D * kept / (ms["dkdv"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": traffic_from_profiles(w.name + "_bwd", ("dkdv",), "bwd"),
+                "kernel": "bwd_dkdv_kernel (element masks)", "kernel_ms": ms["dkdv"], "kernels_ms": ms}
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "block-sparse attn bwd effective TFLOP/s (10*D per kept element) + % bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name + " backward", "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_k": w.block_k, "mask": w.mask_kind,
+                   "kept_elements": kept, "grad_dtype": "bf16", "flops_per_step": flops},
+        "roofline": roofline,
+        "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
+                 "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's element-mask backward on sampled rows")
+        import numpy as np
+        import oracle
+        oracle.build(force=False)
+        total = w.B * w.H * w.S
+        # 6*D FLOPs per kept key of a dq row (scores, dP, dq); a token-causal row s keeps s + 1
+        fl_of = lambda rows: float(sum(6 * w.D * (int(r) % w.S + 1) for r in rows))
+        calib = np.arange(0, total, max(1, total // 64), dtype=np.int64)[:64]
+        t0 = time.perf_counter()
+        oracle.bwd_sample_elem(q, k, v, do, st, pidx, pbits, w.block_q, w.block_k, w.scale, calib, [])
+        per_row = (time.perf_counter() - t0) / len(calib)
+        n = int(min(total, max(len(calib), args.cpu_budget / max(per_row, 1e-9))))
+        stride = max(1, total // n)
+        rows = np.arange(0, total, stride, dtype=np.int64)[:n]
+        t0 = time.perf_counter()
+        oracle.bwd_sample_elem(q, k, v, do, st, pidx, pbits, w.block_q, w.block_k, w.scale, rows, [])
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": fl_of(rows) / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+                               "kind": "oracle",
+                               "sample": "dq of %d of %d query rows (every %dth), 6*D FLOPs per kept key; %.1f s"
+                                         % (len(rows), total, stride, t)}
+    print(json.dumps(res), flush=True)
+
+
 def bench_fp8(args, torch, bs, W):
     """One step = bsattn_fwd_fp8 on the workload's shape and mask with e4m3 inputs."""
     w = W.WORKLOADS[args.workload]
@@ -520,7 +610,10 @@ def main():
         from block_sparse_flash_mask_amd import build
         build.build()
     if args.workload in W.ELEM_WORKLOADS:
-        bench_elem(args, torch, bs, W)
+        if args.backward:
+            bench_bwd_elem(args, torch, bs, W)
+        else:
+            bench_elem(args, torch, bs, W)
         return
     if args.workload in W.RAGGED_WORKLOADS:
         bench_ragged(args, torch, bs, W)

@@ -99,6 +99,10 @@ def library():
         "bsattn_bwd_workspace_size": ([i32, i32, i32, i32, i32, szp], i32),
         "bsattn_bwd": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p, sz,
                         p], i32),
+        "bsattn_bwd_elem": ([p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p,
+                             i32, p, sz, p], i32),
+        "bsattn_bwd_planned_elem": ([p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, i32, p,
+                                     p, p, i32, i32, p, sz, p], i32),
         "bsattn_bwd_plan": ([p, i32, i32, i32, i32, i32, p, sz, p], i32),
         "bsattn_bwd_planned": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, i32,
                                 p, sz, p], i32),
@@ -516,6 +520,45 @@ def bwd(q, k, v, out, lse, dout, block_mask, block_q, block_k, scale=None, *, gr
                               _ptr(block_mask), B, H, S, D, block_q, block_k, float(scale),
                               _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return dq, dk, dv
+
+
+def bwd_elem(q, k, v, out, lse, dout, block_states, partial_index, partial_bits, block_q, block_k, scale=None, *,
+             grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the element-mask forward (fwd_elem) for the upstream gradient
+    dout (bsattn_bwd_elem).  Returns (dq, dk, dv)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    n_tiles = _elem_tensors(block_states, partial_index, partial_bits)
+    if tuple(block_states.shape) != (B, H, S // block_q, S // block_k):
+        raise ValueError("block_states must be [B, H, S/block_q, S/block_k]")
+    if scale is None:
+        scale = default_scale(D)
+    dq, dk, dv = _grads(q, grad_dtype, dq, dk, dv)
+    ws = _workspace(bwd_workspace_size(B, H, S, block_q, block_k), q.device, workspace)
+    rc = library().bsattn_bwd_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(block_states),
+                                   _ptr(partial_index), _ptr(partial_bits), n_tiles, B, H, S, D, block_q,
+                                   block_k, float(scale),
+                                   _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return dq, dk, dv
+
+
+def bwd_planned_elem(q, k, v, out, lse, dout, block_states, partial_index, partial_bits, plan_ws, block_q,
+                     block_k, scale=None, *, grad_dtype=None, dq=None, dk=None, dv=None, parts=7, stream=None):
+    """The element-mask gradient kernels alone on a plan from bwd_plan(block_states)
+    (bsattn_bwd_planned_elem); parts is an OR of BWD_PREP, BWD_DQ, BWD_DKDV."""
+    B, H, S, D = _check_inputs(q, k, v)
+    n_tiles = _elem_tensors(block_states, partial_index, partial_bits)
+    if scale is None:
+        scale = default_scale(D)
+    dq, dk, dv = _grads(q, grad_dtype, dq, dk, dv)
+    rc = library().bsattn_bwd_planned_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                           _ptr(block_states), _ptr(partial_index), _ptr(partial_bits), n_tiles,
+                                           B, H, S, D, block_q, block_k, float(scale), _dtype_code(q), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), _dtype_code(dq), int(parts), _ptr(plan_ws),
+                                           plan_ws.numel() * plan_ws.element_size(), _stream(stream))
     _check(rc)
     return dq, dk, dv
 

@@ -873,10 +873,13 @@ int bsattn_bwd_plan(const uint8_t* block_mask, int B, int H, int S, int block_q,
     return BSATTN_OK;
 }
 
-int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                       const void* dout, int B, int H, int S, int D, int block_q, int block_k, float scale,
-                       int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+// bsattn_bwd_planned, and with states != NULL the element-mask kernels (the
+// element arguments were checked by the caller).
+static int bwd_planned_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                            int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts, void* workspace,
+                            size_t workspace_bytes, void* stream, const uint8_t* states, const int32_t* pidx,
+                            const uint32_t* pbits, int n_tiles) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return BSATTN_ERR_NULL;
     if (parts <= 0 || parts > (BSATTN_BWD_PREP | BSATTN_BWD_DQ | BSATTN_BWD_DKDV)) return BSATTN_ERR_UNSUPPORTED;
     int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
@@ -943,16 +946,30 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
     a.ksteps_log2 = block_k == 128 ? 2 : 1;
     a.c = scale * kLog2e;
     a.scale = scale;
+    a.states = states;
+    a.pidx = pidx;
+    a.pbits = pbits;
+    a.n_tiles = n_tiles;
     e = launch_bwd_main(a, D, grad_dtype == BSATTN_F32, (parts & BSATTN_BWD_DQ) != 0,
                         (parts & BSATTN_BWD_DKDV) != 0, st);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }
 
-int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
-               const uint8_t* block_mask, int B, int H, int S, int D, int block_q, int block_k, float scale,
-               int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace, size_t workspace_bytes,
-               void* stream) {
+int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                       int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return bwd_planned_impl(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                            grad_dtype, parts, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, 0);
+}
+
+// bsattn_bwd; with pidx != NULL block_mask holds block states and the element
+// kernels run (bsattn_bwd_elem, which checked the element arguments).
+static int bwd_impl(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                    const uint8_t* block_mask, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                    int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream, const int32_t* pidx, const uint32_t* pbits, int n_tiles) {
     if (!q || !k || !v || !out || !lse || !dout || !block_mask || !dq || !dk || !dv || !workspace)
         return BSATTN_ERR_NULL;
     int rc = check_fwd_shape(B, H, S, D, block_q, block_k, dtype);
@@ -982,8 +999,57 @@ int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, con
     }
     rc = bsattn_bwd_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
     if (rc) return rc;
-    return bsattn_bwd_planned(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
-                              grad_dtype, BSATTN_BWD_ALL, workspace, workspace_bytes, stream);
+    return bwd_planned_impl(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                            grad_dtype, BSATTN_BWD_ALL, workspace, workspace_bytes, stream,
+                            pidx ? block_mask : nullptr, pidx, pbits, n_tiles);
+}
+
+int bsattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+               const uint8_t* block_mask, int B, int H, int S, int D, int block_q, int block_k, float scale,
+               int dtype, void* dq, void* dk, void* dv, int grad_dtype, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    return bwd_impl(q, k, v, out, lse, dout, block_mask, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                    grad_dtype, workspace, workspace_bytes, stream, nullptr, nullptr, 0);
+}
+
+int bsattn_bwd_planned_elem(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, const uint8_t* block_states, const int32_t* partial_index,
+                            const uint32_t* partial_bits, int n_tiles, int B, int H, int S, int D, int block_q,
+                            int block_k, float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+                            int parts, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_states || !partial_index || !partial_bits) return BSATTN_ERR_NULL;
+    const int rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    if (!is_aligned(partial_index, 4) || !is_aligned(partial_bits, 4)) return BSATTN_ERR_ALIGN;
+    return bwd_planned_impl(q, k, v, out, lse, dout, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                            grad_dtype, parts, workspace, workspace_bytes, stream, block_states, partial_index,
+                            partial_bits, n_tiles);
+}
+
+int bsattn_bwd_elem(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, const uint8_t* block_states, const int32_t* partial_index,
+                    const uint32_t* partial_bits, int n_tiles, int B, int H, int S, int D, int block_q,
+                    int block_k, float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_states || !partial_index || !partial_bits) return BSATTN_ERR_NULL;
+    int rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    if (!is_aligned(partial_index, 4) || !is_aligned(partial_bits, 4)) return BSATTN_ERR_ALIGN;
+    // the gradients and the workspace must not overlap the element mask
+    const size_t nb = (size_t)B * H * (S / block_q) * (S / block_k);
+    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 32) * 4;
+    const size_t ng = (size_t)B * H * S * D * (grad_dtype == BSATTN_F32 ? 4 : 2);
+    size_t wsb = 0;
+    if (bsattn_bwd_workspace_size(B, H, S, block_q, block_k, &wsb) == BSATTN_OK) {
+        const void* wr[] = {dq, dk, dv, workspace};
+        const size_t wn[] = {ng, ng, ng, wsb};
+        for (int i = 0; i < 4; ++i)
+            if (wr[i] && (overlap(wr[i], wn[i], block_states, nb) || overlap(wr[i], wn[i], partial_index, nb * 4) ||
+                          overlap(wr[i], wn[i], partial_bits, nbits)))
+                return BSATTN_ERR_ALIAS;
+    }
+    return bwd_impl(q, k, v, out, lse, dout, block_states, B, H, S, D, block_q, block_k, scale, dtype, dq, dk, dv,
+                    grad_dtype, workspace, workspace_bytes, stream, partial_index, partial_bits, n_tiles);
 }
 
 int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_config* cfgs,

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(1024) void bwd_split_kernel(const int32_t* __restri
 // dK and dV of one key block.  WAVES * 32 = block_k keys per workgroup.  The
 // register budget is cut for two waves per SIMD with D = 128 (K, V fragments and
 // the dK, dV accumulators alone take 192 VGPRs) and three with D = 64.
-template <int D, int WAVES, int OUT_F32>
+template <int D, int WAVES, int OUT_F32, int ELEM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 3 : 2))) void bwd_dkdv_kernel(
     BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-row tile of Q or dO
@@ -316,8 +316,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
             dma16(ldg, a.S * 8, (BSATTN_LDS void*)ldb, (lane & 15) * 16, q0 * 8);
     };
 
+    // Element masks: bit i of the result keeps register i's (query, key) pair of
+    // the step (32 queries from 32 * rr of query block qb; the lane's key is
+    // wave * 32 + l32 of key block kj, bit l32 of word `wave` of a tile row).
+    auto keep_bits = [&](int qb, int rr) -> uint32_t {
+        if constexpr (!ELEM) return 0xffffu;
+        const size_t bi = ((size_t)bh * a.n_q + qb) * a.n_k + kj;
+        if (a.states[bi] <= 1) return 0xffffu;
+        int tile = a.pidx[bi];
+        tile = tile < 0 ? 0 : (tile >= a.n_tiles ? a.n_tiles - 1 : tile);
+        const int wpr = a.block_k >> 5;
+        const uint32_t* row = a.pbits + ((size_t)tile * a.block_q + rr * 32 + 8 * h) * wpr + wave;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m |= ((row[(16 * (i >> 3) + (i & 7)) * wpr] >> l32) & 1u) << i;
+        return m;
+    };
+
     auto compute = [&](const uint8_t* qk, const uint8_t* qv, const uint8_t* ok, const uint8_t* ov,
-                       const float2* ldb) {
+                       const float2* ldb, uint32_t keep) {
         // S = Q K^T and dP = dO V^T: register i of lane (h, key) holds query
         // 16(i/8) + 8h + i%8 of the step.
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -336,8 +353,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
             for (int j = 0; j < 4; ++j) {
                 const float4 x = lp[j];  // queries 2j, 2j+1 of the run: (lse2, delta) each
                 const int i0 = 8 * e + 2 * j;
-                const float p0 = fast_exp2(__builtin_fmaf(s[i0], a.c, -x.x));
-                const float p1 = fast_exp2(__builtin_fmaf(s[i0 + 1], a.c, -x.z));
+                float p0 = fast_exp2(__builtin_fmaf(s[i0], a.c, -x.x));
+                float p1 = fast_exp2(__builtin_fmaf(s[i0 + 1], a.c, -x.z));
+                if constexpr (ELEM) {
+                    p0 = ((keep >> i0) & 1u) ? p0 : 0.f;
+                    p1 = ((keep >> (i0 + 1)) & 1u) ? p1 : 0.f;
+                }
                 pb[e][2 * j] = (__bf16)p0;
                 pb[e][2 * j + 1] = (__bf16)p1;
                 db[e][2 * j] = (__bf16)(p0 * (dp[i0] - x.y));
@@ -375,8 +396,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
                     const float2* ldb, uint8_t* nqk, uint8_t* nqv, uint8_t* nok, uint8_t* nov, float2* nld) {
         __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of step t
         __syncthreads();                     // everyone's DMA landed; step t-1 fully read
+        const uint32_t keep = keep_bits(blk_cur, t & ((1 << spb_log2) - 1));  // (before q0_for moves on)
         if (t + 1 < n_steps) issue(q0_for(t + 1), nqk, nqv, nok, nov, nld);
-        compute(qk, qv, ok, ov, ldb);
+        compute(qk, qv, ok, ov, ldb, keep);
     };
 
     if (n_steps > 0) {
@@ -421,7 +443,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
 }
 
 // dQ of one query block.  WAVES * 32 = block_q queries per workgroup.
-template <int D, int WAVES, int OUT_F32>
+template <int D, int WAVES, int OUT_F32, int ELEM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 4 : 2))) void bwd_dq_kernel(
     BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-key tile of K or V
@@ -485,7 +507,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
                   (k0 * D + P::v_uniform(wave_s, i)) * 2);
     };
 
-    auto compute = [&](const uint8_t* kk, const uint8_t* kv, const uint8_t* vk) {
+    // Element masks: this lane's tile-row word for the step's 32 keys (32 * rr of key
+    // block kb), shifted so that bit 16(i/8) + i%8 keeps register i's key.
+    auto keep_bits = [&](int kb, int rr) -> uint32_t {
+        if constexpr (!ELEM) return 0xffffffffu;
+        const size_t bi = (size_t)r * a.n_k + kb;
+        if (a.states[bi] <= 1) return 0xffffffffu;
+        int tile = a.pidx[bi];
+        tile = tile < 0 ? 0 : (tile >= a.n_tiles ? a.n_tiles - 1 : tile);
+        const int wpr = a.block_k >> 5;
+        return a.pbits[((size_t)tile * a.block_q + wave * 32 + l32) * wpr + rr] >> (8 * h);
+    };
+
+    auto compute = [&](const uint8_t* kk, const uint8_t* kv, const uint8_t* vk, uint32_t keep) {
         // S^T = K Q^T, dP^T = V dO^T: register i of lane (h, q) holds key
         // 16(i/8) + 8h + i%8 of the step.
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -499,7 +533,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         bf16x8 db[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(s[i], a.c, -myld.x));
+            float p = fast_exp2(__builtin_fmaf(s[i], a.c, -myld.x));
+            if constexpr (ELEM) p = ((keep >> (16 * (i >> 3) + (i & 7))) & 1u) ? p : 0.f;
             db[i >> 3][i & 7] = (__bf16)(p * (dp[i] - myld.y));
         }
         // dQ^T += K^T dS^T (A by the transposing read of K).
@@ -528,8 +563,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
                     uint8_t* nvk) {
         __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
         __syncthreads();
+        const uint32_t keep = keep_bits(blk_cur, t & ((1 << spb_log2) - 1));  // (before k0_for moves on)
         if (t + 1 < n_steps) issue(k0_for(t + 1), nkk, nkv, nvk);
-        compute(kk, kv, vk);
+        compute(kk, kv, vk, keep);
     };
 
     if (n_steps > 0) {
@@ -611,14 +647,14 @@ hipError_t launch_bwd_cols(const uint8_t* mask, int64_t C, int n_q, int n_k, int
     return hipGetLastError();
 }
 
-template <int D, int OUT_F32>
+template <int D, int OUT_F32, int ELEM>
 static hipError_t launch_main(const BwdArgs& a, bool do_dq, bool do_dkdv, hipStream_t stream) {
     const dim3 gk(8 * a.chunk_k), gq(8 * a.chunk_q);
     if (do_dkdv) {
         if (a.block_k == 128)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, OUT_F32>), gk, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, OUT_F32, ELEM>), gk, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, OUT_F32>), gk, dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, OUT_F32, ELEM>), gk, dim3(128), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.max_splits > 0) {
@@ -630,16 +666,24 @@ static hipError_t launch_main(const BwdArgs& a, bool do_dq, bool do_dkdv, hipStr
     }
     if (!do_dq) return hipSuccess;
     if (a.block_q == 128)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, 4, OUT_F32>), gq, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, 4, OUT_F32, ELEM>), gq, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, 2, OUT_F32>), gq, dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, 2, OUT_F32, ELEM>), gq, dim3(128), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_main(const BwdArgs& a, int D, int out_f32, bool do_dq, bool do_dkdv, hipStream_t stream) {
+    if (a.states) {  // element-level masks
+        if (D == 128)
+            return out_f32 ? launch_main<128, 1, 1>(a, do_dq, do_dkdv, stream)
+                           : launch_main<128, 0, 1>(a, do_dq, do_dkdv, stream);
+        return out_f32 ? launch_main<64, 1, 1>(a, do_dq, do_dkdv, stream)
+                       : launch_main<64, 0, 1>(a, do_dq, do_dkdv, stream);
+    }
     if (D == 128)
-        return out_f32 ? launch_main<128, 1>(a, do_dq, do_dkdv, stream) : launch_main<128, 0>(a, do_dq, do_dkdv, stream);
-    return out_f32 ? launch_main<64, 1>(a, do_dq, do_dkdv, stream) : launch_main<64, 0>(a, do_dq, do_dkdv, stream);
+        return out_f32 ? launch_main<128, 1, 0>(a, do_dq, do_dkdv, stream)
+                       : launch_main<128, 0, 0>(a, do_dq, do_dkdv, stream);
+    return out_f32 ? launch_main<64, 1, 0>(a, do_dq, do_dkdv, stream) : launch_main<64, 0, 0>(a, do_dq, do_dkdv, stream);
 }
 
 }  // namespace bsattn

@@ -88,6 +88,13 @@ struct BwdArgs {
     int ksteps_log2;  // log2(block_k / 32)
     float c;          // scale * log2(e)
     float scale;
+    // Element-level masks (the ELEM kernels only): block states [B][H][n_q][n_k]
+    // (0 empty, 1 full, else partial), the bit tile of each partial block, and the
+    // tiles [n_tiles][block_q][block_k / 32].
+    const uint8_t* states;
+    const int32_t* pidx;
+    const uint32_t* pbits;
+    int n_tiles;
 };
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -370,6 +370,35 @@ int bsattn_bwd_planned(const void* q, const void* k, const void* v, const void* 
                        float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype, int parts,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward of the element-level-mask forward (bsattn_fwd_elem): the gradients
+ * above with P[r][j] = 0 for every (query, key) pair the element mask drops
+ * ("Writing Pallas Kernels for JAX", section "Writing the Kernel Logic": a score
+ * counts only where the mask tile is set; section "The Empathy of the Void": the
+ * kernel's author writes its gradient).  block_states, partial_index,
+ * partial_bits and n_tiles as in bsattn_fwd_elem (device; a tile index outside
+ * [0, n_tiles) is clamped); out and lse are that forward's (a row that keeps
+ * nothing has lse = -inf and gets dq = 0).  Other arguments, the workspace
+ * (bsattn_bwd_workspace_size bytes: the plan is built from the nonzero block
+ * states) and the error behaviour as bsattn_bwd; in addition NULL mask arrays give
+ * BSATTN_ERR_NULL, n_tiles outside [1, 32767] BSATTN_ERR_SHAPE, partial_index or
+ * partial_bits not 4-byte aligned BSATTN_ERR_ALIGN, and dq, dk, dv or the
+ * workspace overlapping the mask arrays BSATTN_ERR_ALIAS.  Asynchronous on
+ * stream; nothing is allocated. */
+int bsattn_bwd_elem(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, const uint8_t* block_states, const int32_t* partial_index,
+                    const uint32_t* partial_bits, int n_tiles, int B, int H, int S, int D, int block_q,
+                    int block_k, float scale, int dtype, void* dq, void* dk, void* dv, int grad_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The gradient kernels of bsattn_bwd_elem alone, on a plan that bsattn_bwd_plan
+ * made from the same block_states (as bsattn_bwd_planned for the block mask;
+ * parts as there).  Argument checks as bsattn_bwd_elem and bsattn_bwd_planned. */
+int bsattn_bwd_planned_elem(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, const uint8_t* block_states, const int32_t* partial_index,
+                            const uint32_t* partial_bits, int n_tiles, int B, int H, int S, int D,
+                            int block_q, int block_k, float scale, int dtype, void* dq, void* dk, void* dv,
+                            int grad_dtype, int parts, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Autotuner ("Pallas-Triton kernels and kernel auto-tuning", section
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of

@@ -433,3 +433,29 @@ def test_c_program_builds(lib):
     oracle.build(force=False)
     exe = c_abi_build.build(force=True)
     assert os.access(exe, os.X_OK)
+
+
+def test_bwd_elem_argument_checks(lib):
+    """Backward with element-level masks: the element arguments' host checks, and
+    the backward's own checks still reached through this entry point."""
+    p = ctypes.c_void_p
+    B, H, S, D, bq, bk = 1, 2, 256, 128, 128, 64
+    n = ctypes.c_size_t(0)
+    assert lib.bsattn_bwd_workspace_size(B, H, S, bq, bk, ctypes.byref(n)) == OK
+    f = lib.bsattn_bwd_elem
+    # q k v out lse dout states pidx pbits n_tiles B H S D bq bk scale dtype dq dk dv gdtype ws wsb stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), p(9 * A), p(11 * A), p(13 * A), p(14 * A), p(15 * A), 2,
+          B, H, S, D, bq, bk, 0.1, 1, p(17 * A), p(19 * A), p(21 * A), 1, p(23 * A), n.value, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+    for i in (0, 6, 7, 8, 18, 22):
+        assert call(i, None) == NULL, i
+    assert call(9, 0) == SHAPE and call(9, 40000) == SHAPE       # n_tiles
+    assert call(12, 250) == SHAPE                                  # S
+    assert call(7, p(14 * A + 2)) == ALIGN and call(8, p(15 * A + 1)) == ALIGN
+    assert call(13, 96) == UNSUP                                   # D
+    assert call(22, p(15 * A)) == ALIAS                            # workspace over the bit tiles
+    assert call(23, n.value - 1) == WS
