@@ -1,15 +1,21 @@
 """Benchmark of the block-sparse flash-attention forward on one MI355X.
 
-One step = one bsattn_fwd call (the plan: mask compaction and dispatch order, then
-the fused attention kernel) over the workload's resident inputs.  Prints ONE JSON
-line on stdout:
-  value      effective TFLOP/s = 4*D*(active score elements) / (time per step)
-  roofline   the attention kernel alone (bsattn_fwd_planned: the step's launch on
-             a plan made once): its average duration over K launches
-             timed with HIP events on the stream it runs on, achieved TFLOP/s
-             against the bf16 dense MFMA peak, and (when a counter summary for
-             the current kernel source exists under profiles/) HBM traffic
-  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows
+Default workload: causal_bf16 (B2 H32 S8192 D128, 128x128 blocks, lower-
+triangular block mask), the largest block-mask workload that the oracle's
+parity cases also cover.  One step = the two launches of bsattn_fwd (the plan:
+mask compaction and dispatch order, then the fused attention kernel) over the
+workload's resident inputs.  Prints ONE JSON line on stdout:
+  value      effective TFLOP/s = 4*D*(active score elements) / (time per step),
+             cold: L2 and MALL are flushed (untimed 1 GiB rewrite) before every
+             timed step; "warm" beside it times back-to-back steps
+  roofline   the attention kernel: the average duration of its launch inside
+             the timed steps (HIP events on the stream it runs on), achieved
+             TFLOP/s against the bf16 dense MFMA peak derived from rocminfo
+             (CUs x max engine clock x 4096 FLOP/clk/CU), and (when a counter
+             summary for the current kernel source exists under profiles/) HBM
+             traffic per launch
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows,
+             with the host's CPU model and logical CPU count
 
 --fp8 runs the forward of a block-mask workload with q, k, v rounded to fp8 e4m3
 (bsattn_fwd_fp8: plan, V pre-pass, fp8 attention kernel), against the fp8 MFMA
@@ -37,10 +43,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn fwd effective TFLOP/s (active blocks) + % bf16 MFMA peak"
-PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
-PEAK_FP8_TFLOPS = 5033.2    # fp8 dense MFMA: twice the bf16 rate
-PEAK_F32_TFLOPS = 157.3     # fp32 MFMA/vector dense
+# MI355X published dense peaks (256 CU x 2.4 GHz): bf16 MFMA 4096 FLOP/clk/CU,
+# fp8 twice that, fp32 MFMA 256 FLOP/clk/CU.  main() re-derives them from the
+# compute-unit count and maximum engine clock rocminfo reports for the GPU
+# (device_peaks) and records which it used in PEAK_SOURCE.
+FLOP_PER_CLK_CU = {"bf16": 4096, "fp8": 8192, "f32": 256}
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_SOURCE = "published MI355X figures (256 CU x 2400 MHz)"
 # The sources each committed counter summary depends on (its hash is stored in
 # the summary and checked before its traffic figure is used).
 _C = "block_sparse_flash_mask_amd/csrc/"
@@ -54,6 +66,63 @@ KERNEL_SOURCES = {
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def device_peaks():
+    """(compute units, max engine clock in MHz, agent name) of the first gfx9 GPU
+    agent that rocminfo lists, or None if rocminfo is unavailable."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return parse_rocminfo(txt)
+
+
+def parse_rocminfo(txt):
+    """The first gfx9 GPU agent of a rocminfo listing: (compute units, max clock
+    MHz, name), or None."""
+    for agent in txt.split("*******")[1:]:
+        fields = {}
+        for line in agent.splitlines():
+            if ":" in line:
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip(), val.strip())
+        if fields.get("Device Type") == "GPU" and fields.get("Name", "").startswith("gfx9"):
+            try:
+                return int(fields["Compute Unit"]), int(fields["Max Clock Freq. (MHz)"]), fields["Name"]
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+def set_peaks():
+    """Set the PEAK_* globals from rocminfo (CUs x max clock x FLOP/clk/CU)."""
+    global PEAK_BF16_TFLOPS, PEAK_FP8_TFLOPS, PEAK_F32_TFLOPS, PEAK_SOURCE
+    dev = device_peaks()
+    if dev is None:
+        log("bench: rocminfo gave no GPU agent; using the published peaks")
+        return
+    cu, mhz, name = dev
+    PEAK_BF16_TFLOPS = cu * mhz * 1e6 * FLOP_PER_CLK_CU["bf16"] / 1e12
+    PEAK_FP8_TFLOPS = cu * mhz * 1e6 * FLOP_PER_CLK_CU["fp8"] / 1e12
+    PEAK_F32_TFLOPS = cu * mhz * 1e6 * FLOP_PER_CLK_CU["f32"] / 1e12
+    PEAK_SOURCE = "rocminfo %s: %d CU x %d MHz x 4096 bf16 FLOP/clk/CU" % (name, cu, mhz)
+    log("bench: peak %.1f TFLOP/s bf16 (%s)" % (PEAK_BF16_TFLOPS, PEAK_SOURCE))
+
+
+def host_cpu():
+    """(CPU model name, logical CPUs) of the host that runs the oracle."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.partition(":")[2].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
 
 
 def kernel_source_hash(family="fwd"):
@@ -116,8 +185,9 @@ def cpu_baseline(w, q, k, v, mask, budget_s):
     oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, rows)
     t = time.perf_counter() - t0
     fl = flops_row(rows)
+    model, nproc = host_cpu()
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": "%d of %d query rows (every %dth), each over its full key list; %.1f s"
                       % (len(rows), total, stride, t)}
 
@@ -140,8 +210,9 @@ def cpu_baseline_elem(w, q, k, v, st, pidx, pbits, kept_per_row, budget_s):
     oracle.fwd_rows_elem(q, k, v, st, pidx, pbits, w.block_q, w.block_k, w.scale, rows)
     t = time.perf_counter() - t0
     fl = float(sum(4 * w.D * kept_per_row(int(r)) for r in rows))
+    model, nproc = host_cpu()
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": "%d of %d query rows (every %dth), each over its kept keys; %.1f s"
                       % (len(rows), total, stride, t)}
 
@@ -311,6 +382,7 @@ def bench_ragged(args, torch, bs, W):
         t = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": 2.0 * w.K * w.N * sum(take) / t / 1e12, "unit": "TFLOP/s",
                                "cores": oracle.max_threads(), "kind": "oracle",
+                               "cpu_model": host_cpu()[0], "nproc": host_cpu()[1],
                                "sample": "the first %.2f %% of every group's rows (%d rows); %.1f s"
                                          % (100 * frac, sum(take), t)}
     print(json.dumps(res), flush=True)
@@ -336,6 +408,7 @@ def cpu_baseline_bwd(w, q, k, v, do, mask, budget_s):
         if t_used >= budget_s:
             break
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": host_cpu()[0], "nproc": host_cpu()[1],
             "sample": "the full backward of the first %d of %d heads; %.1f s" % (heads, w.B * w.H, t_used)}
 
 
@@ -499,7 +572,7 @@ def bench_bwd_elem(args, torch, bs, W):
         oracle.bwd_sample_elem(q, k, v, do, st, pidx, pbits, w.block_q, w.block_k, w.scale, rows, [])
         t = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": fl_of(rows) / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": host_cpu()[0], "nproc": host_cpu()[1],
                                "sample": "dq of %d of %d query rows (every %dth), 6*D FLOPs per kept key; %.1f s"
                                          % (len(rows), total, stride, t)}
     print(json.dumps(res), flush=True)
@@ -573,7 +646,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dense_bf16")
+    ap.add_argument("--workload", default="causal_bf16",
+                    help="workload name (default: causal_bf16, B2 H32 S8192 D128, the largest block-mask "
+                         "workload on one GPU)")
     ap.add_argument("--config", default=None, help="tile config tq,tk,waves,stages (default: autotune)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -591,6 +666,7 @@ def main():
               "MI355X (no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    set_peaks()
     import torch
 
     import block_sparse_flash_mask_amd as bs
@@ -624,6 +700,17 @@ def main():
     if args.fp8:
         bench_fp8(args, torch, bs, W)
         return
+    bench_fwd(args, torch, bs, W)
+
+
+def bench_fwd(args, torch, bs, W):
+    """One step = the forward of a block-mask workload: the plan (mask
+    compaction, dispatch order) and the attention kernel, exactly the two
+    launches of bsattn_fwd, on resident inputs.  The headline is cold: before
+    every timed step a 1 GiB device buffer is rewritten (untimed), which evicts
+    L2 and MALL, so each step reads its inputs from HBM.  HIP events on the
+    launch stream bracket each step and, inside it, the attention launch; warm
+    figures (back-to-back steps) are reported beside them."""
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -649,43 +736,59 @@ def main():
             log("  tune id=%d cfg=%s t_mean=%.4e t_std=%.2e" % (r.id, r.config, r.t_mean_s,
                                                               r.t_std_s))
 
-    def step():
-        bs.fwd(qd, kd, vd, md, w.block_q, w.block_k, w.scale, out=out, lse=lse, workspace=ws,
-               config=cfg)
-
     stream = torch.cuda.current_stream()
-    log("bench: warmup %d, timed %d steps, config %s" % (args.warmup, args.steps, cfg))
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    log("bench: %.4f ms/step (events), %.4f ms/step (wall)" % (ms_step, wall * 1e3 / args.steps))
-    ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
 
-    # The dominant kernel alone: the attention launch of the step (same plan, same
-    # tile config, same grid) on a plan made once, K launches bracketed by HIP
-    # events on the launch stream.
-    plan_ws = bs.plan(md, w.S, w.block_q, w.block_k)
-    for _ in range(3):
-        bs.fwd_planned(qd, kd, vd, plan_ws, w.block_q, w.block_k, w.scale, out=out, lse=lse,
-                       config=cfg)
+    def plan():
+        bs.plan(md, w.S, w.block_q, w.block_k, workspace=ws)
+
+    def attn():
+        bs.fwd_planned(qd, kd, vd, ws, w.block_q, w.block_k, w.scale, out=out, lse=lse, config=cfg)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    log("bench: warmup %d, timed %d steps (cold: L2 and MALL flushed before each), config %s"
+        % (args.warmup, args.steps, cfg))
+    for _ in range(args.warmup):
+        plan()
+        attn()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
+    t0 = time.perf_counter()
+    step_ms, attn_ms = 0.0, 0.0
+    for i in range(args.steps):
+        flush.fill_(i & 0xff)  # untimed: evicts L2 and MALL
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        plan()
+        e1.record(stream)
+        attn()
+        e2.record(stream)
+        torch.cuda.synchronize()
+        step_ms += e0.elapsed_time(e2)
+        attn_ms += e1.elapsed_time(e2)
+    wall = time.perf_counter() - t0
+    del flush
+    ms_step = step_ms / args.steps
+    ms_attn = attn_ms / args.steps
+    log("bench: cold %.4f ms/step, attention kernel %.4f ms (events); %.4f ms/step incl. flushes (wall)"
+        % (ms_step, ms_attn, wall * 1e3 / args.steps))
+
+    # warm: back-to-back steps, then back-to-back attention launches on the plan
+    w0, w1 = ev(), ev()
+    w0.record(stream)
     for _ in range(args.steps):
-        bs.fwd_planned(qd, kd, vd, plan_ws, w.block_q, w.block_k, w.scale, out=out, lse=lse,
-                       config=cfg)
-    a1.record(stream)
+        plan()
+        attn()
+    w1.record(stream)
     torch.cuda.synchronize()
-    ms_attn = a0.elapsed_time(a1) / args.steps
+    warm_step = w0.elapsed_time(w1) / args.steps
+    w0.record(stream)
+    for _ in range(args.steps):
+        attn()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_attn = w0.elapsed_time(w1) / args.steps
+    log("bench: warm %.4f ms/step, attention kernel %.4f ms" % (warm_step, warm_attn))
+
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     achieved = flops / (ms_attn * 1e-3) / 1e12
@@ -694,7 +797,8 @@ def main():
                 "frac": achieved / peak, "traffic": traffic,
                 "kernel": ("attn_bf16_pp_kernel" if cfg[0] == 128 and cfg[2] == 8 else "attn_bf16_kernel") if bf16
                           else "attn_f32_kernel",
-                "kernel_ms": ms_attn}
+                "kernel_ms": ms_attn, "timing": "cold steps (the attention launch of each timed step)",
+                "peak_source": PEAK_SOURCE}
     if traffic:
         roofline["hbm_gbs"] = traffic / (ms_attn * 1e-3) / 1e9
 
@@ -710,8 +814,10 @@ def main():
                    "active_blocks": nnz, "density": nnz / (w.B * w.H * w.n_q * w.n_k),
                    "tile_config": list(cfg), "flops_per_step": flops},
         "roofline": roofline,
-        "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
-                 "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
+        "timing": "cold: L2 and MALL flushed (1 GiB rewrite, untimed) before each timed step",
+        "warm": {"ms_per_step": warm_step, "value": flops / (warm_step * 1e-3) / 1e12,
+                 "kernel_ms": warm_attn, "kernel_tflops": flops / (warm_attn * 1e-3) / 1e12,
+                 "note": "back-to-back steps, caches warm"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

@@ -6,6 +6,7 @@
 // allocated on the forward path.
 #include <algorithm>
 #include <cerrno>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -193,7 +194,22 @@ const Variant* find(int dtype, int D, int block_q, int block_k, const bsattn_til
 }
 
 // ---- tuning cache -------------------------------------------------------------
-typedef std::tuple<int, int, int, int, int, int64_t> TuneKey;  // dtype, D, bq, bk, S, B*H
+// Key: dtype, D, block_q, block_k, S, B*H, and the mask statistic: the mean
+// number of active key blocks per mask row in half-octaves,
+// round(2 log2(nnz / rows)) (-1 for an empty mask).  Masks of one shape whose
+// mean row lengths differ by more than about 41 % tune to separate entries.
+typedef std::tuple<int, int, int, int, int, int64_t> ShapeKey;  // dtype, D, bq, bk, S, B*H
+typedef std::tuple<int, int, int, int, int, int64_t, int> TuneKey;  // ShapeKey + mask bucket
+
+int mask_bucket(int64_t nnz, int64_t rows) {
+    if (nnz <= 0 || rows <= 0) return -1;
+    return (int)std::lround(2.0 * std::log2((double)nnz / (double)rows));
+}
+
+ShapeKey shape_of(const TuneKey& k) {
+    return ShapeKey(std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k), std::get<4>(k),
+                    std::get<5>(k));
+}
 
 struct TuneEntry {
     bsattn_tile_config cfg;
@@ -203,12 +219,22 @@ struct TuneEntry {
 std::mutex g_tune_mu;
 std::map<TuneKey, TuneEntry> g_tune;
 
-bool tune_lookup(const TuneKey& key, bsattn_tile_config* out) {
-    std::lock_guard<std::mutex> lk(g_tune_mu);
-    auto it = g_tune.find(key);
-    if (it == g_tune.end()) return false;
+// A call that does not know its mask statistic (bsattn_fwd with an automatic
+// config) takes the shape's entry of the densest mask bucket.  Caller holds
+// g_tune_mu.
+bool densest_entry(const ShapeKey& k, bsattn_tile_config* out) {
+    auto it = g_tune.upper_bound(TuneKey(std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k),
+                                         std::get<4>(k), std::get<5>(k), INT32_MAX));
+    if (it == g_tune.begin()) return false;
+    --it;
+    if (shape_of(it->first) != k) return false;
     *out = it->second.cfg;
     return true;
+}
+
+bool tune_lookup_shape(const ShapeKey& key, bsattn_tile_config* out) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    return densest_entry(key, out);
 }
 
 bool json_number(const std::string& obj, const char* name, double* out) {
@@ -242,17 +268,18 @@ bool read_cache(const char* path, std::map<TuneKey, TuneEntry>* into) {
         const size_t e = text.find('}', p);
         if (e == std::string::npos) break;
         const std::string obj = text.substr(p, e - p + 1);
-        double dt, D, bq, bk, S, BH, tq, tk, w, st, tm = 0.0;
+        double dt, D, bq, bk, S, BH, mb, tq, tk, w, st, tm = 0.0;
         if (json_number(obj, "dtype", &dt) && json_number(obj, "D", &D) &&
             json_number(obj, "block_q", &bq) && json_number(obj, "block_k", &bk) &&
             json_number(obj, "S", &S) && json_number(obj, "BH", &BH) &&
+            json_number(obj, "mask_bucket", &mb) &&
             json_number(obj, "tile_q", &tq) && json_number(obj, "tile_k", &tk) &&
             json_number(obj, "waves", &w) && json_number(obj, "stages", &st)) {
             json_number(obj, "t_mean_s", &tm);
             TuneEntry te;
             te.cfg = bsattn_tile_config{(int)tq, (int)tk, (int)w, (int)st};
             te.t_mean_s = tm;
-            (*into)[TuneKey((int)dt, (int)D, (int)bq, (int)bk, (int)S, (int64_t)BH)] = te;
+            (*into)[TuneKey((int)dt, (int)D, (int)bq, (int)bk, (int)S, (int64_t)BH, (int)mb)] = te;
         }
         p = e;
     }
@@ -270,10 +297,10 @@ bool write_cache(const char* path, const std::map<TuneKey, TuneEntry>& m) {
         const TuneEntry& e = kv.second;
         std::fprintf(f,
                      "  {\"dtype\": %d, \"D\": %d, \"block_q\": %d, \"block_k\": %d, \"S\": %d, "
-                     "\"BH\": %lld, \"tile_q\": %d, \"tile_k\": %d, \"waves\": %d, \"stages\": %d, "
-                     "\"t_mean_s\": %.6e}%s\n",
+                     "\"BH\": %lld, \"mask_bucket\": %d, \"tile_q\": %d, \"tile_k\": %d, \"waves\": %d, "
+                     "\"stages\": %d, \"t_mean_s\": %.6e}%s\n",
                      std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k),
-                     std::get<4>(k), (long long)std::get<5>(k), e.cfg.tile_q, e.cfg.tile_k,
+                     std::get<4>(k), (long long)std::get<5>(k), std::get<6>(k), e.cfg.tile_q, e.cfg.tile_k,
                      e.cfg.waves, e.cfg.stages, e.t_mean_s, (++i < m.size()) ? "," : "");
     }
     std::fprintf(f, "]}\n");
@@ -304,7 +331,7 @@ const Variant* choose(int dtype, int D, int S, int64_t BH, int block_q, int bloc
     bool bad = false;
     if (env_config(&c, &bad)) return find(dtype, D, block_q, block_k, c);
     if (bad) return nullptr;
-    if (tune_lookup(TuneKey(dtype, D, block_q, block_k, S, BH), &c)) {
+    if (tune_lookup_shape(ShapeKey(dtype, D, block_q, block_k, S, BH), &c)) {
         const Variant* v = find(dtype, D, block_q, block_k, c);
         if (v) return v;
     }
@@ -434,6 +461,7 @@ const char* bsattn_status_string(int status) {
         case BSATTN_ERR_SCALE: return "BSATTN_ERR_SCALE: scale is not finite";
         case BSATTN_ERR_ALIAS: return "BSATTN_ERR_ALIAS: an output overlaps an input or the other output";
         case BSATTN_ERR_HIP: return "BSATTN_ERR_HIP: a HIP runtime call failed";
+        case BSATTN_ERR_IO: return "BSATTN_ERR_IO: a tuning-cache file could not be read or written";
         default: return "BSATTN: unknown status";
     }
 }
@@ -565,8 +593,8 @@ int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block
 }
 
 int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,
-                         const int32_t* col_idx, void* out, float* lse, int B, int H, int S,
-                         int D, int block_q, int block_k, float scale, int dtype,
+                         const int32_t* col_idx, size_t col_idx_len, void* out, float* lse, int B,
+                         int H, int S, int D, int block_q, int block_k, float scale, int dtype,
                          const bsattn_tile_config* cfg, void* stream) {
     if (!row_ptr || !col_idx) return BSATTN_ERR_NULL;
     const int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
@@ -579,6 +607,7 @@ int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int3
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
     a.row_ptr = row_ptr;
     a.list = col_idx;
+    a.list_len = (int64_t)std::min<size_t>(col_idx_len, (size_t)INT32_MAX);  // row_ptr values are int32
     a.ell_stride = 0;
     a.nrows = (int)(is_pair(*var) ? L.P : L.R);
     a.chunk = (int)xcd_chunk(a.nrows);
@@ -1085,6 +1114,17 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     const Variant* t = variants(dtype, &nv);
     std::vector<bsattn_tune_result> res;
     hipStream_t s = (hipStream_t)stream;
+    // The mask statistic of the cache key: active blocks counted on a host copy
+    // of the mask, read in stream order (tuning is not on the call path).
+    const int64_t R = (int64_t)B * H * (S / block_q), n_k = S / block_k;
+    int64_t nnz = 0;
+    {
+        std::vector<uint8_t> host((size_t)(R * n_k));
+        hipError_t he = hipMemcpyAsync(host.data(), block_mask, host.size(), hipMemcpyDeviceToHost, s);
+        if (he == hipSuccess) he = hipStreamSynchronize(s);
+        if (he != hipSuccess) return hip_fail(he);
+        for (uint8_t b : host) nnz += b != 0;
+    }
     std::vector<hipEvent_t> ev((size_t)iters + 1);
     for (auto& e : ev) {
         const hipError_t he = hipEventCreate(&e);
@@ -1141,7 +1181,7 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
     if (n_results) *n_results = (int)res.size();
     if (results)
         for (int i = 0; i < cap && i < (int)res.size(); ++i) results[i] = res[(size_t)i];
-    const TuneKey key(dtype, D, block_q, block_k, S, (int64_t)B * H);
+    const TuneKey key(dtype, D, block_q, block_k, S, (int64_t)B * H, mask_bucket(nnz, R));
     {
         std::lock_guard<std::mutex> lk(g_tune_mu);
         g_tune[key] = TuneEntry{res[0].cfg, res[0].t_mean_s};
@@ -1149,16 +1189,32 @@ int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* 
             std::map<TuneKey, TuneEntry> merged;
             read_cache(cache_path, &merged);
             merged[key] = g_tune[key];
-            if (!write_cache(cache_path, merged)) return BSATTN_ERR_NULL;
+            if (!write_cache(cache_path, merged)) return BSATTN_ERR_IO;
         }
     }
+    return BSATTN_OK;
+}
+
+int bsattn_tune_lookup(int dtype, int D, int B, int H, int S, int block_q, int block_k, long long nnz,
+                       bsattn_tile_config* cfg) {
+    if (!cfg) return BSATTN_ERR_NULL;
+    if (B <= 0 || H <= 0 || S <= 0 || block_q <= 0 || block_k <= 0) return BSATTN_ERR_SHAPE;
+    if (S % block_q != 0 || S % block_k != 0) return BSATTN_ERR_SHAPE;
+    const int64_t R = (int64_t)B * H * (S / block_q);
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    if (nnz < 0)
+        return densest_entry(ShapeKey(dtype, D, block_q, block_k, S, (int64_t)B * H), cfg) ? BSATTN_OK
+                                                                                         : BSATTN_ERR_UNSUPPORTED;
+    auto it = g_tune.find(TuneKey(dtype, D, block_q, block_k, S, (int64_t)B * H, mask_bucket(nnz, R)));
+    if (it == g_tune.end()) return BSATTN_ERR_UNSUPPORTED;
+    *cfg = it->second.cfg;
     return BSATTN_OK;
 }
 
 int bsattn_load_tune_cache(const char* cache_path) {
     if (!cache_path) return BSATTN_ERR_NULL;
     std::map<TuneKey, TuneEntry> m;
-    if (!read_cache(cache_path, &m)) return BSATTN_ERR_NULL;
+    if (!read_cache(cache_path, &m)) return BSATTN_ERR_IO;
     std::lock_guard<std::mutex> lk(g_tune_mu);
     for (const auto& kv : m) g_tune[kv.first] = kv.second;
     return BSATTN_OK;

@@ -247,6 +247,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // cvt, the sum tree), 16 elements per lane per 32-key tile and query tile,
     // spread over the NQ*KS MFMAs of that tile.
     constexpr int SCHED_VALU = 56 / KS;
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
     struct SAcc { f32x16 v[NQ][MT]; };
     struct PTile { bf16x8 v[NQ][MT][2]; };
 
@@ -279,7 +281,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = s.v[n][mt][i];
-            const float mx = max_halves_nan(max_tree3<16 * MT>(tmp)) * a.c;
+            const float raw = max_halves_nan(max_tree3<16 * MT>(tmp));
+            // (element masks: a tile row may keep no score, raw = -inf; with
+            // scale = 0 the product -inf * 0 would be NaN)
+            const float mx = (ELEM && raw == -INFINITY) ? -INFINITY : raw * a.c;
             if (__ballot(mx > m_run[n] + 8.0f) != 0) {
                 const float m_new = fmax_nan(m_run[n], mx);
                 // (element masks: a row may still have no kept score, m = -inf;
@@ -294,8 +299,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
     };
 
-    // P = 2^(c S - m) in bf16, and its row sums into l.
-    auto exps = [&](const SAcc& s) -> PTile {
+    // P = 2^(c S - m) in bf16, and its row sums into l.  On a partial step of an
+    // element mask (MASKED) a dropped score (S = -inf) gives P = 0 by a select,
+    // not through the exponent: with scale = 0, -inf * 0 would be NaN.
+    auto exps = [&](const SAcc& s, auto masked) -> PTile {
+        constexpr bool MASKED = decltype(masked)::value;
         PTile p;
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
@@ -306,7 +314,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_use));
+                    float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_use));
+                    if constexpr (MASKED) e = s.v[n][mt][i] == -INFINITY ? 0.f : e;
                     tmp[16 * mt + i] = e;
                     p.v[n][mt][i >> 3][i & 7] = (__bf16)e;
                 }
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         update_max(s);
         SAcc s_next;
         if constexpr (NEXT) s_next = qk(knext);
-        const PTile p = exps(s);
+        const PTile p = exps(s, no{});
         pv(p, vcur);
         if constexpr (NEXT) {
             s = s_next;
@@ -375,8 +384,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 #endif
         }
     };
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
 
     // Plain schedule: K and V of step t share a stage, ST stages in flight.  The
     // body of step t waits until only the DMA of later steps is outstanding,
@@ -390,9 +397,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // Element masks: the list entries of the steps in flight (e1 = this step, e2 =
     // the next with three stages), and the kept-bit test applied to S.
     int e1 = 0, e2 = 0;
-    auto apply_tile = [&](SAcc& s, int e, int t) {
+    auto apply_tile = [&](SAcc& s, int e, int t) -> bool {
         int tile = (e >> 16) - 1;  // -1: full block
-        if (tile < 0) return;
+        if (tile < 0) return false;
         tile = tile < a.n_tiles ? tile : a.n_tiles - 1;  // (a plan never holds more)
         const int qr = q_row0 - qi * a.block_q;  // this lane's row inside the block
         const int ko = (t & ((1 << sh) - 1)) * TK;
@@ -406,6 +413,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int i = 0; i < 16; ++i)
                 if (!((w >> (16 * (i >> 3) + (i & 7))) & 1u)) s.v[0][mt][i] = -INFINITY;
         }
+        return true;
     };
     auto plain = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur,
                      const uint8_t* vcur) {
@@ -425,13 +433,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
         if (mine(t)) {
             SAcc s = qk(kcur);
+            bool partial = false;
             if constexpr (ELEM && PAIR)  // this group's own tile of the block
-                apply_tile(s, (int)pair_tile[grp * kPairMaxBlocks + (e_cur & 0xffff)] << 16, t);
+                partial = apply_tile(s, (int)pair_tile[grp * kPairMaxBlocks + (e_cur & 0xffff)] << 16, t);
             else if constexpr (ELEM)
-                apply_tile(s, e_cur, t);
+                partial = apply_tile(s, e_cur, t);
             update_max(s);
-            const PTile p = exps(s);
-            pv(p, vcur);
+            if (ELEM && partial) {
+                const PTile p = exps(s, yes{});
+                pv(p, vcur);
+            } else {
+                const PTile p = exps(s, no{});
+                pv(p, vcur);
+            }
         }
     };
 

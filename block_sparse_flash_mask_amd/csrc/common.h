@@ -27,6 +27,7 @@ struct FwdArgs {
     const int32_t* counts;
     const int32_t* list;
     int ell_stride;
+    int64_t list_len;  // CSR form: entries in list (each row's span is clamped into it)
     void* out;
     float* lse;
     int H, S, n_q, n_k;
@@ -185,8 +186,12 @@ __device__ __forceinline__ void row_list(const FwdArgs& a, int r, int& beg, int&
         beg = r * a.ell_stride;
         cnt = a.counts[r];
     } else {
-        beg = a.row_ptr[r];
-        cnt = a.row_ptr[r + 1] - beg;
+        // caller's CSR: keep the span [beg, beg + cnt) inside list[0 .. list_len)
+        const int64_t b0 = a.row_ptr[r], e0 = a.row_ptr[r + 1];
+        const int64_t b1 = b0 < 0 ? 0 : (b0 > a.list_len ? a.list_len : b0);
+        const int64_t e1 = e0 < b1 ? b1 : (e0 > a.list_len ? a.list_len : e0);
+        beg = (int)b1;
+        cnt = (int)(e1 - b1 > a.n_k ? a.n_k : e1 - b1);
     }
     // A row lists each key block at most once: a larger count is malformed input.
     cnt = cnt < 0 ? 0 : (cnt > a.n_k ? a.n_k : cnt);

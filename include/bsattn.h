@@ -56,7 +56,8 @@ typedef enum {
     BSATTN_ERR_SCALE = 6,       /* scale is NaN or infinite */
     BSATTN_ERR_ALIAS = 7,       /* out or lse overlaps q, k or v (or each other), or
                                    a forward workspace overlaps any of them */
-    BSATTN_ERR_HIP = 8          /* a HIP runtime call failed */
+    BSATTN_ERR_HIP = 8,         /* a HIP runtime call failed */
+    BSATTN_ERR_IO = 9           /* a tuning-cache file could not be read or written */
 } bsattn_status;
 
 /* Kernel tiling of the attention kernel (the autotuner's search space).
@@ -187,12 +188,16 @@ int bsattn_fwd_planned(const void* q, const void* k, const void* v, void* out, f
  * (row_ptr, col_idx as that call wrote them, for the same mask).  This is the
  * attention step of bsattn_fwd reading CSR lists instead of a plan, for callers
  * that keep the mask in CSR form; workgroups go in mask-row order (no
- * longest-first dispatch).  row_ptr must be a valid CSR of B*H*(S/block_q) rows
- * over col_idx: per-row counts are clamped to [0, S/block_k] and entries into
- * [0, S/block_k), but row_ptr values are trusted.  cfg as in bsattn_fwd_config. */
+ * longest-first dispatch).  row_ptr holds B*H*(S/block_q) + 1 entries and
+ * col_idx col_idx_len entries (both on the device).  Malformed lists give
+ * undefined values in out and lse but never an access outside them: each row's
+ * span [row_ptr[r], row_ptr[r+1]) is clamped into [0, col_idx_len), its count to
+ * at most S/block_k, and each entry into [0, S/block_k).  col_idx_len = 0 with a
+ * non-NULL col_idx is allowed (every row is then empty).  cfg as in
+ * bsattn_fwd_config. */
 int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,
-                         const int32_t* col_idx, void* out, float* lse, int B, int H, int S,
-                         int D, int block_q, int block_k, float scale, int dtype,
+                         const int32_t* col_idx, size_t col_idx_len, void* out, float* lse, int B,
+                         int H, int S, int D, int block_q, int block_k, float scale, int dtype,
                          const bsattn_tile_config* cfg, void* stream);
 
 /* Number of tile configs built for (dtype, D, block_q, block_k), and the configs
@@ -403,20 +408,32 @@ int bsattn_bwd_planned_elem(const void* q, const void* k, const void* v, const v
  * "Auto-tuning": parameterise tile sizes, warps and pipeline depth, time every
  * point, keep the fastest).  Times bsattn_fwd_config for every built config of
  * this shape on the caller's buffers (warmup runs, then iters timed runs each,
- * with HIP events on stream), writes the fastest to *best, records it in the
- * in-process cache used by bsattn_fwd for this shape, and, if cache_path is not
- * NULL, merges it into that JSON file.  results (may be NULL) receives up to cap
- * rows sorted by t_mean; *n_results gets the number of configs timed.  out and
- * lse are overwritten.  This call synchronises the stream and may take seconds. */
+ * with HIP events on stream), writes the fastest to *best and records it in the
+ * in-process cache under the key (dtype, D, block_q, block_k, S, B*H, mask
+ * bucket), where the mask bucket is round(2 log2(active blocks / mask rows))
+ * (-1 for an empty mask), counted on a host copy of block_mask; if cache_path is
+ * not NULL it also merges the entry into that JSON file (BSATTN_ERR_IO if the file
+ * cannot be written).  results (may be NULL) receives up to cap rows sorted by
+ * t_mean; *n_results gets the number of configs timed.  out and lse are
+ * overwritten.  This call synchronises the stream and may take seconds. */
 int bsattn_autotune(const void* q, const void* k, const void* v, const uint8_t* block_mask,
                     void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
                     float scale, int dtype, void* workspace, size_t workspace_bytes, int warmup,
                     int iters, bsattn_tile_config* best, bsattn_tune_result* results, int cap,
                     int* n_results, const char* cache_path, void* stream);
 
+/* The tuned config for a mask of nnz active blocks on this shape (the entry of
+ * its mask bucket), or with nnz < 0 the shape's entry of the densest mask bucket
+ * tuned or loaded, which is also what bsattn_fwd and an all-zero cfg use (they do
+ * not read the mask on the host).  Returns
+ * BSATTN_OK and writes *cfg, BSATTN_ERR_UNSUPPORTED if no such entry exists,
+ * BSATTN_ERR_NULL / BSATTN_ERR_SHAPE for a NULL cfg or a bad shape.  Host only. */
+int bsattn_tune_lookup(int dtype, int D, int B, int H, int S, int block_q, int block_k, long long nnz,
+                       bsattn_tile_config* cfg);
+
 /* Load tuned configs from a JSON file written by bsattn_autotune into the
- * in-process cache.  Returns BSATTN_OK, or BSATTN_ERR_NULL if the file cannot be
- * read. */
+ * in-process cache (an entry of the same key is replaced).  Returns BSATTN_OK,
+ * BSATTN_ERR_NULL for a NULL path, or BSATTN_ERR_IO if the file cannot be read. */
 int bsattn_load_tune_cache(const char* cache_path);
 
 /* Clear the in-process tuning cache. */

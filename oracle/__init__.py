@@ -246,8 +246,10 @@ def fwd_rows_elem(q, k, v, states, pidx, pbits, block_q, block_k, scale, rows, n
 
 def ragged_dot(lhs, rhs, group_sizes, nthreads=0):
     """Ragged dot ("Pallas-Triton kernels and kernel auto-tuning", section "Ragged
-    Dot"): lhs [M, K], rhs [G, K, N], group_sizes [G] (int, >= 0, sum <= M).
-    Returns out float64 [M, N]; rows past the sum of the sizes are 0."""
+    Dot"): lhs [M, K], rhs [G, K, N], group_sizes [G] int.  Group g takes the
+    next rows in order; a negative size counts as 0 and a group takes at most
+    the rows that remain; rows after the last group's are 0.  Returns out
+    float64 [M, N]."""
     lib = _load()
     la, dt = _as_raw(lhs)
     ra, dt2 = _as_raw(rhs)

@@ -671,22 +671,23 @@ int oracle_max_threads(void) {
 }
 
 /* Ragged dot: out is double[M][N].  Returns 0 on success, nonzero on a bad
- * argument (nothing written). */
+ * argument (nothing written).
+ *
+ * Group sizes the page leaves open (it assumes sizes that tile the rows):
+ * group g takes the next rows in order; a negative size counts as 0 rows, and
+ * a group takes at most the rows that remain (so the sizes never reach past
+ * row M - 1); rows after the last group's are 0. */
 int oracle_ragged_dot(const void* lhs, const void* rhs, int dtype, const int32_t* group_sizes,
                       int64_t G, int64_t M, int64_t K, int64_t N, double* out, int nthreads) {
     if (!lhs || !rhs || !group_sizes || !out) return 1;
     if (G <= 0 || M < 0 || K <= 0 || N <= 0) return 2;
     if (dtype < ORC_F32 || dtype > ORC_FP8) return 3;
-    int64_t total = 0;
-    for (int64_t g = 0; g < G; ++g) {
-        if (group_sizes[g] < 0) return 2;
-        total += group_sizes[g];
-    }
-    if (total > M) return 2;
     set_threads(nthreads);
     int64_t start = 0;
     for (int64_t g = 0; g < G; ++g) {
-        const int64_t end = start + group_sizes[g];
+        int64_t rows = group_sizes[g] < 0 ? 0 : (int64_t)group_sizes[g];
+        if (rows > M - start) rows = M - start;
+        const int64_t end = start + rows;
 #pragma omp parallel for schedule(static)
         for (int64_t i = start; i < end; ++i)
             for (int64_t n = 0; n < N; ++n) {
@@ -697,7 +698,7 @@ int oracle_ragged_dot(const void* lhs, const void* rhs, int dtype, const int32_t
             }
         start = end;
     }
-    for (int64_t i = total; i < M; ++i)
+    for (int64_t i = start; i < M; ++i)
         for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;
     return 0;
 }

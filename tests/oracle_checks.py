@@ -37,6 +37,7 @@ Element-level masks (block states 0/1/partial + bit tiles):
   elem_rows_match   the selected-rows entry point equals the full forward
 Ragged dot (expert matrices stacked on the right, rows assigned in order):
   ragged_hand       a 4-row example worked out by hand (expert 1 empty, a tail row)
+  ragged_sizes      negative and overflowing group sizes, worked out by hand (tests/golden)
   ragged_one_group  one group of all rows equals numpy matmul
   ragged_permute    reordering the experts with their row blocks reorders the rows
   ragged_linear     out(X, a W1 + b W2) == a out(X, W1) + b out(X, W2)
@@ -425,6 +426,15 @@ def ragged_hand(orc):
     assert np.array_equal(out, np.array([[2, 3], [46, 51], [82, 91], [0, 0]], dtype=np.float64))
 
 
+def ragged_sizes(orc):
+    ex = json.load(open(os.path.join(HERE, "golden", "ragged_sizes.json")))
+    lhs = np.array(ex["lhs"], dtype=np.float64)
+    rhs = np.array(ex["rhs"], dtype=np.float64)
+    for case in ex["cases"]:
+        out = orc.ragged_dot(lhs, rhs, case["sizes"])
+        assert np.array_equal(out, np.array(case["out"], dtype=np.float64)), case["sizes"]
+
+
 def _ragged_inputs(M, K, N, G, seed, dt=torch.float64):
     x = _rand((M, K), seed, dt)
     w = _rand((G, K, N), seed + 1, dt)
@@ -685,7 +695,7 @@ def bwd_elem_sample_match(orc):
 ALL = [hand_example, brute_force, sdpa_dense, sdpa_block_causal, block_diagonal, probs_sum,
        constant_v, zero_query, empty_rows, linearity, key_permutation, shift, rows_match_full,
        bf16_widening, fp8_widening, compact_brute, elem_brute, elem_tiles_all_set, elem_tiles_all_clear,
-       elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_one_group,
+       elem_token_causal, elem_empty_row, elem_rows_match, ragged_hand, ragged_sizes, ragged_one_group,
        ragged_permute, ragged_linear, ragged_tail, ragged_bf16, bwd_autograd, bwd_finite_diff,
        bwd_sums, bwd_constant_v, bwd_linear_dout, bwd_sample_match, bwd_elem_autograd,
        bwd_elem_tiles_all_set, bwd_elem_tiles_all_clear, bwd_elem_token_causal, bwd_elem_sample_match]

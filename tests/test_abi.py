@@ -14,7 +14,7 @@ import block_sparse_flash_mask_amd as bs
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bsattn.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, SCALE, ALIAS, HIP = range(9)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, SCALE, ALIAS, HIP, IO = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -175,14 +175,17 @@ def test_planned_argument_checks(lib):
 def test_compacted_argument_checks(lib):
     p = ctypes.c_void_p
     f = lib.bsattn_fwd_compacted
-    args = [p(A), p(3 * A), p(5 * A), p(7 * A), p(8 * A), p(9 * A), p(11 * A), 1, 1, 256, 64,
+    args = [p(A), p(3 * A), p(5 * A), p(7 * A), p(8 * A), 1024, p(9 * A), p(11 * A), 1, 1, 256, 64,
             64, 64, 0.1, 1, None, None]
     bad = list(args)
     bad[3] = None
     assert f(*bad) == NULL
     bad = list(args)
-    bad[9] = 100
+    bad[10] = 100
     assert f(*bad) == SHAPE
+    bad = list(args)
+    bad[14] = math.inf
+    assert f(*bad) == SCALE
 
 
 def test_autotune_argument_checks(lib):
@@ -203,15 +206,48 @@ def test_autotune_argument_checks(lib):
     assert f(*bad) == WS
 
 
+def _cache_entry(S, BH, bucket, cfg, t=1.0e-4):
+    return ('  {"dtype": 1, "D": 128, "block_q": 128, "block_k": 128, "S": %d, "BH": %d, '
+            '"mask_bucket": %d, "tile_q": %d, "tile_k": %d, "waves": %d, "stages": %d, '
+            '"t_mean_s": %.6e}' % ((S, BH, bucket) + tuple(cfg) + (t,)))
+
+
 def test_tune_cache_roundtrip(lib, tmp_path):
     path = tmp_path / "tune.json"
-    path.write_text('{"bsattn_tune_cache": 1, "entries": [\n'
-                    '  {"dtype": 1, "D": 128, "block_q": 128, "block_k": 128, "S": 2048, '
-                    '"BH": 64, "tile_q": 128, "tile_k": 32, "waves": 4, "stages": 1, '
-                    '"t_mean_s": 1.0e-04}\n]}\n')
-    assert lib.bsattn_load_tune_cache(str(path).encode()) == OK
-    assert lib.bsattn_load_tune_cache(str(tmp_path / "missing.json").encode()) == NULL
+    path.write_text('{"bsattn_tune_cache": 1, "entries": [\n' + _cache_entry(2048, 64, 8, (128, 32, 4, 3))
+                    + '\n]}\n')
     lib.bsattn_clear_tune_cache()
+    assert lib.bsattn_load_tune_cache(str(path).encode()) == OK
+    assert lib.bsattn_load_tune_cache(str(tmp_path / "missing.json").encode()) == IO
+    assert lib.bsattn_load_tune_cache(None) == NULL
+    lib.bsattn_clear_tune_cache()
+
+
+def test_tune_cache_keys_on_mask_statistic(lib, tmp_path):
+    """Two masks of one shape (B*H = 64 heads of S = 2048, 1024 mask rows) with
+    mean row lengths 16 (bucket 8) and 4 (bucket 4) keep separate entries;
+    bsattn_tune_lookup picks by the caller's active-block count, and a call that
+    does not know it (nnz < 0, like bsattn_fwd) gets the densest bucket."""
+    path = tmp_path / "tune.json"
+    path.write_text('{"bsattn_tune_cache": 1, "entries": [\n'
+                    + _cache_entry(2048, 64, 4, (128, 64, 4, 2)) + ',\n'
+                    + _cache_entry(2048, 64, 8, (256, 128, 8, 2)) + '\n]}\n')
+    lib.bsattn_clear_tune_cache()
+    assert lib.bsattn_load_tune_cache(str(path).encode()) == OK
+    look = lambda nnz: bs.tune_lookup(__import__("torch").bfloat16, 128, 4, 16, 2048, 128, 128, nnz)
+    assert look(16384).as_tuple() == (256, 128, 8, 2)      # 16 blocks per row
+    assert look(4096).as_tuple() == (128, 64, 4, 2)        # 4 blocks per row
+    assert look(4 * 1024 + 300).as_tuple() == (128, 64, 4, 2)  # same half-octave
+    assert look(-1).as_tuple() == (256, 128, 8, 2)         # mask statistic unknown
+    assert look(1024) is None                               # 1 block per row: not tuned
+    assert bs.tune_lookup(__import__("torch").bfloat16, 128, 4, 16, 4096, 128, 128, -1) is None
+    cfg = bs.TileConfig()
+    f = lib.bsattn_tune_lookup
+    assert f(1, 128, 4, 16, 2048, 128, 128, 16384, None) == NULL
+    assert f(1, 128, 4, 16, 2000, 128, 128, 16384, ctypes.byref(cfg)) == SHAPE
+    assert f(1, 128, 0, 16, 2048, 128, 128, 16384, ctypes.byref(cfg)) == SHAPE
+    lib.bsattn_clear_tune_cache()
+    assert look(16384) is None
 
 
 def test_elem_argument_checks(lib):
@@ -459,3 +495,83 @@ def test_bwd_elem_argument_checks(lib):
     assert call(13, 96) == UNSUP                                   # D
     assert call(22, p(15 * A)) == ALIAS                            # workspace over the bit tiles
     assert call(23, n.value - 1) == WS
+
+
+# ---- the Python binding refuses bad tensor arguments before any library call ----
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    m = torch.ones(1, 1, 1, 1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.fwd(q, q, q, m, 128, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.plan(m, 128, 128, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.ragged_dot(torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(1, 8, 8, dtype=torch.bfloat16),
+                      torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        bs.fwd(None, q, q, m, 128, 128)
+
+
+def test_binding_tensor_checks():
+    """_check_tensor, the check every mask, index, bit-tile, output, gradient and
+    workspace tensor goes through (here with host tensors standing in for the
+    device one): device, contiguity, dtype, shape and size."""
+    import torch
+    cpu = torch.device("cpu")
+    t = torch.zeros(2, 3, dtype=torch.int32)
+    assert bs._check_tensor(t, "t", cpu, (torch.int32,), (2, 3), 24) is t
+    with pytest.raises(ValueError, match="must be on"):
+        bs._check_tensor(t, "t", torch.device("meta"))
+    with pytest.raises(ValueError, match="contiguous"):
+        bs._check_tensor(t.t(), "t", cpu)
+    with pytest.raises(TypeError, match="dtype"):
+        bs._check_tensor(t, "t", cpu, (torch.float32,))
+    with pytest.raises(ValueError, match="shape"):
+        bs._check_tensor(t, "t", cpu, shape=(3, 2))
+    with pytest.raises(ValueError, match="too small"):
+        bs._check_tensor(t, "t", cpu, min_bytes=25)
+    with pytest.raises(TypeError):
+        bs._check_tensor([1, 2], "t", cpu)
+    # masks: bool is viewed as uint8, other dtypes refused; device and shape checked
+    m = torch.ones(1, 2, 3, 3, dtype=torch.bool)
+    assert bs._mask_u8(m, cpu, (1, 2, 3, 3)).dtype == torch.uint8
+    with pytest.raises(TypeError):
+        bs._mask_u8(m.to(torch.int32), cpu)
+    with pytest.raises(ValueError, match="shape"):
+        bs._mask_u8(m, cpu, (1, 2, 3, 4))
+    with pytest.raises(ValueError, match="must be on"):
+        bs._mask_u8(m, torch.device("meta"), (1, 2, 3, 3))
+    # element-mask tensors
+    st = torch.zeros(1, 2, 3, 3, dtype=torch.uint8)
+    pidx = torch.zeros(1, 2, 3, 3, dtype=torch.int32)
+    bits = torch.zeros(2, 128, 4, dtype=torch.int32)
+    assert bs._elem_tensors(st, pidx, bits, cpu, (1, 2, 3, 3)) == 2
+    with pytest.raises(ValueError):
+        bs._elem_tensors(st, pidx[:, :, :2].contiguous(), bits, cpu)
+    with pytest.raises(TypeError):
+        bs._elem_tensors(st, pidx.to(torch.int64), bits, cpu)
+    with pytest.raises(ValueError):
+        bs._check_bits(bits, 128, 64)
+    # outputs: given out / lse must match q's shape and dtype
+    q = torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16)
+    o, l = bs._outputs(q, None, None)
+    assert o.shape == q.shape and o.dtype == q.dtype and l.shape == (1, 2, 256) and l.dtype == torch.float32
+    with pytest.raises(TypeError):
+        bs._outputs(q, torch.zeros(1, 2, 256, 64), None)
+    with pytest.raises(ValueError):
+        bs._outputs(q, None, torch.zeros(1, 2, 255))
+    with pytest.raises(ValueError):
+        bs._outputs(q, torch.zeros(1, 2, 256, 63, dtype=torch.bfloat16), None)
+    # gradients
+    with pytest.raises(ValueError):
+        bs._grads(q, None, torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16), None,
+                  torch.zeros(1, 2, 256, 64, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        bs._grads(q, torch.float16, None, None, None)
+    with pytest.raises(ValueError, match="multiple"):
+        bs._mask_shape(q.shape, 128, 96)
+    # workspaces
+    with pytest.raises(ValueError, match="too small"):
+        bs._workspace(1000, cpu, torch.zeros(999, dtype=torch.uint8))

@@ -13,3 +13,40 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+SAMPLE_ROCMINFO = """
+*******
+Agent 1
+*******
+  Name:                    Intel(R) Xeon(R) Platinum
+  Marketing Name:          Intel(R) Xeon(R) Platinum
+  Device Type:             CPU
+  Max Clock Freq. (MHz):   3800
+  Compute Unit:            96
+*******
+Agent 2
+*******
+  Name:                    gfx950
+  Marketing Name:          AMD Instinct MI355X
+  Device Type:             GPU
+  Cache Info:
+    L2:                      4096(0x1000) KB
+  Max Clock Freq. (MHz):   2400
+  Compute Unit:            256
+  SIMDs per CU:            4
+  ISA Info:
+    ISA 1
+      Name:                    amdgcn-amd-amdhsa--gfx950:sramecc+:xnack-
+"""
+
+
+def test_peak_from_rocminfo():
+    """The bf16 peak is CUs x max engine clock x 4096 FLOP/clk/CU of the GPU
+    agent (the CPU agent and the nested ISA name are skipped)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.parse_rocminfo(SAMPLE_ROCMINFO) == (256, 2400, "gfx950")
+    assert bench.parse_rocminfo("no agents here") is None
+    cu, mhz, _ = bench.parse_rocminfo(SAMPLE_ROCMINFO)
+    assert abs(cu * mhz * 1e6 * bench.FLOP_PER_CLK_CU["bf16"] / 1e12 - 2516.58) < 0.01

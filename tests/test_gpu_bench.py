@@ -26,7 +26,8 @@ def _bench(*args):
     return json.loads(lines[0])
 
 
-@pytest.mark.parametrize("workload,cfg", [("dense_bf16", "256,128,8,2"), ("tiny_f32", "64,64,2,1")])
+@pytest.mark.parametrize("workload,cfg", [("causal_bf16", "256,128,8,2"), ("dense_bf16", "256,128,8,2"),
+                                          ("tiny_f32", "64,64,2,1")])
 def test_bench_line(workload, cfg):
     res = _bench("--workload", workload, "--config", cfg)
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
@@ -45,3 +46,13 @@ def test_bench_line(workload, cfg):
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert abs(rf["achieved"] - flops / (rf["kernel_ms"] * 1e-3) / 1e12) <= 1e-6 * rf["achieved"]
     assert 0 < rf["frac"] < 1
+    # the kernel runs inside the (cold) step; warm figures beside the headline
+    assert rf["kernel_ms"] <= res["ms_per_step"] * (1 + 1e-6)
+    assert res["warm"]["ms_per_step"] > 0 and res["warm"]["kernel_ms"] > 0
+    assert "rocminfo" in rf["peak_source"] or "published" in rf["peak_source"]
+
+
+def test_bench_default_workload_is_causal():
+    res = _bench("--config", "256,128,8,2")
+    assert res["config"]["workload"] == "causal_bf16"
+    assert res["config"]["active_blocks"] == 133120

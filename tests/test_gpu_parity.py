@@ -115,13 +115,15 @@ def test_edge_cases(dtype):
     _run_full(q, k2, v, mask, b, b, 0.125, what="shifted keys")
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("bk", [128, 64])
-def test_long_rows_every_config(bk):
+def test_long_rows_every_config(bk, D):
     """Rows with more than 64 active key blocks (kernels that hold the row's list
-    64 entries at a time must reload it): block-causal, S = 16384, every config,
-    on sampled rows from the first and the last query blocks."""
+    64 entries at a time must reload it): block-causal, S = 16384, every config
+    of both head dims (the row-pair configs included), on sampled rows from the
+    first and the last query blocks."""
     ensure_built()
-    B, H, S, D, bq = 1, 1, 16384, 128, 128
+    B, H, S, bq = 1, 1, 16384, 128
     q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=51)
     n_q, n_k = S // bq, S // bk
     qi = torch.arange(n_q)[:, None]
@@ -133,7 +135,7 @@ def test_long_rows_every_config(bk):
     qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
     idx = torch.as_tensor(rows, device="cuda")
     for cfg in bs.list_configs(torch.bfloat16, D, bq, bk):
-        say("long rows", bk, cfg)
+        say("long rows", D, bk, cfg)
         out, lse = bs.fwd(qd, kd, vd, md, bq, bk, 0.088, config=cfg)
         torch.cuda.synchronize()
         compare(out.reshape(-1, D)[idx], lse.reshape(-1)[idx], ro, rl, "bf16", "long rows %s" % (cfg,))

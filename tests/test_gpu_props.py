@@ -122,3 +122,31 @@ def test_autotune_and_cache(tmp_path):
     torch.cuda.synchronize()
     compare(out, lse, ro, rl, "bf16", "cached")
     bs.clear_tune_cache()
+
+
+def test_autotune_two_masks_one_shape(tmp_path):
+    """A dense and a sparse mask of one shape tune into separate cache entries
+    (the key holds the mask statistic), each found again by its block count."""
+    ensure_built()
+    B, H, S, D, b = 1, 4, 2048, 128, 128
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=83)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    n = S // b
+    dense = torch.ones(B, H, n, n, dtype=torch.uint8)
+    sparse = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    idx = torch.arange(n)
+    sparse[:, :, idx, idx] = 1                      # one block per row
+    path = tmp_path / "tune.json"
+    bs.clear_tune_cache()
+    picks = {}
+    for name, m in (("dense", dense), ("sparse", sparse)):
+        say("autotune", name)
+        best, _ = bs.autotune(qd, kd, vd, m.cuda(), b, b, 0.09, warmup=1, iters=2, cache_path=str(path))
+        picks[name] = (int(m.sum()), best.as_tuple())
+    entries = [e for e in json.load(open(path))["entries"] if e["S"] == S and e["BH"] == B * H]
+    buckets = sorted(e["mask_bucket"] for e in entries)
+    assert buckets == [0, 8], buckets                # mean 1 and 16 blocks per row
+    for name, (nnz, cfg) in picks.items():
+        assert bs.tune_lookup(torch.bfloat16, D, B, H, S, b, b, nnz).as_tuple() == cfg, name
+    assert bs.tune_lookup(torch.bfloat16, D, B, H, S, b, b, -1).as_tuple() == picks["dense"][1]
+    bs.clear_tune_cache()

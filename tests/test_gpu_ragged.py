@@ -26,7 +26,8 @@ def _inputs(M, K, N, G, seed):
 
 def _check(x, w, sizes, out_dtype, what, rows=None):
     """GPU result for sizes (as given, may hold negatives / overflow) against the
-    oracle on the sizes the library uses (negatives as 0, groups clamped to M)."""
+    oracle on the same sizes (its reading: a negative size is 0 rows, a group
+    takes at most the rows that remain)."""
     ensure_built()
     M, K = x.shape
     G, _, N = w.shape
@@ -34,20 +35,9 @@ def _check(x, w, sizes, out_dtype, what, rows=None):
     out = bs.ragged_dot(x.cuda(), w.cuda(), torch.as_tensor(sizes, dtype=torch.int32).cuda(),
                         out_dtype=out_dtype)
     torch.cuda.synchronize()
-    eff, left = [], M
-    for s in sizes:
-        s = max(int(s), 0)
-        eff.append(min(s, left))
-        left -= eff[-1]
-    ref = oracle.ragged_dot(x, w, eff)
-    # |x| |w| row by row for the bound (fp64)
-    xa = np.abs(x.double().numpy())
-    wa = np.abs(w.double().numpy())
-    mag = np.zeros((M, N))
-    start = 0
-    for gi, s in enumerate(eff):
-        mag[start:start + s] = xa[start:start + s] @ wa[gi]
-        start += s
+    ref = oracle.ragged_dot(x, w, sizes)
+    # sum_k |x_k w_k| per element for the bound: the oracle on |x| and |w|
+    mag = oracle.ragged_dot(x.double().abs(), w.double().abs(), sizes)
     got = out.double().cpu().numpy()
     if rows is not None:
         got, ref, mag = got[rows], ref[rows], mag[rows]

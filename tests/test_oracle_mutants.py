@@ -63,16 +63,21 @@ MUTANTS = {
                                      "            const int64_t kbase = (bh * p->S + j) * D;\n"
                                      "            const double ds")],
     "elem_partial_as_empty": [("if (!p->pidx || blk == 1) return 1;", "if (!p->pidx || blk == 1) return 1;\n    if (blk > 1) return 0;")],
-    "ragged_group_start_late": [("const int64_t end = start + group_sizes[g];",
-                                 "const int64_t end = start + group_sizes[g];\n        const int64_t start1 = start + (group_sizes[g] > 0);"),
+    "ragged_group_start_late": [("const int64_t end = start + rows;",
+                                 "const int64_t end = start + rows;\n        const int64_t start1 = start + (rows > 0);"),
                                 ("for (int64_t i = start; i < end; ++i)\n            for (int64_t n = 0; n < N; ++n) {",
                                  "for (int64_t i = start1; i < end; ++i)\n            for (int64_t n = 0; n < N; ++n) {")],
     "ragged_next_expert": [("widen(rhs, dtype, (g * K + k) * N + n)",
                             "widen(rhs, dtype, (((g + 1) % G) * K + k) * N + n)")],
     "ragged_rhs_transposed": [("widen(rhs, dtype, (g * K + k) * N + n)",
                                "widen(rhs, dtype, (g * K + (n % K)) * N + (k % N))")],
-    "ragged_tail_not_zeroed": [("for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;",
-                                "for (int64_t i = total; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 1.0;")],
+    "ragged_tail_not_zeroed": [("for (int64_t i = start; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;",
+                                "for (int64_t i = start; i < M; ++i)\n        for (int64_t n = 0; n < N; ++n) out[i * N + n] = 1.0;")],
+    # group sizes outside [0, rows left]: a negative size taken by magnitude, the
+    # last group clamped one row short
+    "ragged_negative_size_abs": [("int64_t rows = group_sizes[g] < 0 ? 0 : (int64_t)group_sizes[g];",
+                                  "int64_t rows = group_sizes[g] < 0 ? -(int64_t)group_sizes[g] : (int64_t)group_sizes[g];")],
+    "ragged_clamp_short": [("if (rows > M - start) rows = M - start;", "if (rows > M - start) rows = M - start - 1;")],
     "bwd_no_delta": [("const double ds = sbuf[t] * (pbuf[t] - delta);", "const double ds = sbuf[t] * pbuf[t];"),
                      ("const double ds = P * (dp - delta[r]);", "const double ds = P * dp;")],
     "bwd_delta_unweighted": [("delta += sbuf[t] * dp;", "delta += dp;")],
