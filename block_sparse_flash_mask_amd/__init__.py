@@ -79,6 +79,8 @@ def library():
         "bsattn_fwd_config": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
                                cfgp, p], i32),
         "bsattn_plan": ([p, i32, i32, i32, i32, i32, p, sz, p], i32),
+        "bsattn_fwd_noalloc": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, cfgp, p], i32),
+        "bsattn_noalloc_max_bytes": ([], sz),
         "bsattn_fwd_planned": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, sz,
                                 cfgp, p], i32),
         "bsattn_fwd_compacted": ([p, p, p, p, p, sz, p, p, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -294,6 +296,25 @@ def fwd(q, k, v, block_mask, block_q, block_k, scale=None, *, out=None, lse=None
                                _stream(stream))
     _check(rc)
     return out, lse
+
+
+def fwd_noalloc(q, k, v, block_mask, block_q, block_k, scale, out, lse, *, config=None, stream=None):
+    """bsattn_fwd_noalloc: the forward with its plan in the library's fixed
+    device array (no allocation by the library; the caller passes out and lse).
+    Calls that overlap on one GPU race on that array."""
+    B, H, S, D = _check_inputs(q, k, v)
+    block_mask = _mask_u8(block_mask, q.device, _mask_shape(q.shape, block_q, block_k))
+    _check_tensor(out, "out", q.device, (q.dtype,), q.shape)
+    _check_tensor(lse, "lse", q.device, (torch.float32,), q.shape[:3])
+    rc = library().bsattn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(out), _ptr(lse),
+                                      B, H, S, D, block_q, block_k, float(scale), _dtype_code(q), _cfg(config),
+                                      _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def noalloc_max_bytes():
+    return library().bsattn_noalloc_max_bytes()
 
 
 def plan(block_mask, S, block_q, block_k, *, workspace=None, stream=None):

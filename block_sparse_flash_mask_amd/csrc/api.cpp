@@ -440,6 +440,38 @@ int check_fp8_buffers(const void* q, const void* k, const void* v, const void* o
 }
 
 
+// ---- forward with no allocation: the plan in a fixed device array ----------------
+// For callers that cannot allocate (graph capture, tight serving loops): the
+// forward's plan lives in this file-scope device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` only names the symbol; its device address (one
+// per GPU) comes from hipGetSymbolAddress, taken once per device with that device
+// current and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the calling thread's current device.
+int scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return BSATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!p) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BSATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -590,6 +622,29 @@ int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block
                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return bsattn_fwd_config(q, k, v, block_mask, out, lse, B, H, S, D, block_q, block_k, scale,
                              dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+size_t bsattn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int bsattn_fwd_noalloc(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                       void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+                       float scale, int dtype, const bsattn_tile_config* cfg, void* stream) {
+    if (!block_mask) return BSATTN_ERR_NULL;
+    int rc = check_fwd_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, dtype, scale);
+    if (rc) return rc;
+    if (fwd_ws_bytes((int64_t)B * H, S / block_q, S / block_k) > kNoAllocScratchBytes)
+        return BSATTN_ERR_WORKSPACE;
+    // Resolve the tile config before any device work.
+    const Variant* var = choose(dtype, D, S, (int64_t)B * H, block_q, block_k, cfg);
+    if (!var || (is_pair(*var) && S / block_k > kPairMaxBlocks)) return BSATTN_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc) return rc;
+    // The plan launch rewrites every byte the attention launch reads.
+    rc = bsattn_plan(block_mask, B, H, S, block_q, block_k, ws, kNoAllocScratchBytes, stream);
+    if (rc) return rc;
+    return bsattn_fwd_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, dtype, ws,
+                              kNoAllocScratchBytes, cfg, stream);
 }
 
 int bsattn_fwd_compacted(const void* q, const void* k, const void* v, const int32_t* row_ptr,

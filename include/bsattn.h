@@ -184,6 +184,26 @@ int bsattn_fwd_planned(const void* q, const void* k, const void* v, void* out, f
                        const void* workspace, size_t workspace_bytes,
                        const bsattn_tile_config* cfg, void* stream);
 
+/* bsattn_fwd_config for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the plan goes to a fixed device array inside the library instead of a caller
+ * workspace, of bsattn_noalloc_max_bytes() = 16 MiB per GPU, held until the
+ * process ends.  This call allocates nothing and calls no allocating routine.
+ * Arguments, layouts and checks as bsattn_fwd_config (cfg may be NULL); a shape
+ * whose plan (bsattn_workspace_size) exceeds the array returns
+ * BSATTN_ERR_WORKSPACE before any device work.  The array of the calling
+ * thread's current device is used, which must be the device of stream.  Every
+ * call on one GPU shares that GPU's array, and each call's plan launch rewrites
+ * all of it that its attention launch reads, so nothing needs clearing between
+ * calls; but calls that overlap on one GPU (other streams, other host threads)
+ * race on the array and must be serialised by the caller. */
+int bsattn_fwd_noalloc(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                       void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
+                       float scale, int dtype, const bsattn_tile_config* cfg, void* stream);
+
+/* Size in bytes of the fixed device array bsattn_fwd_noalloc plans into. */
+size_t bsattn_noalloc_max_bytes(void);
+
 /* The attention kernel alone, on lists already built by bsattn_compact_mask
  * (row_ptr, col_idx as that call wrote them, for the same mask).  This is the
  * attention step of bsattn_fwd reading CSR lists instead of a plan, for callers

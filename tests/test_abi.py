@@ -575,3 +575,29 @@ def test_binding_tensor_checks():
     # workspaces
     with pytest.raises(ValueError, match="too small"):
         bs._workspace(1000, cpu, torch.zeros(999, dtype=torch.uint8))
+
+
+def test_noalloc_argument_checks(lib):
+    """bsattn_fwd_noalloc: host checks as bsattn_fwd_config, and a plan larger
+    than the fixed array (bsattn_noalloc_max_bytes) is refused before any HIP call."""
+    p = ctypes.c_void_p
+    f = lib.bsattn_fwd_noalloc
+    assert lib.bsattn_noalloc_max_bytes() == 16 << 20
+    # q k v mask out lse B H S D bq bk scale dtype cfg stream
+    ok = [p(A), p(3 * A), p(5 * A), p(7 * A), p(9 * A), p(11 * A), 1, 1, 256, 64, 64, 64, 0.1, 1, None, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return f(*a)
+
+    assert call(3, None) == NULL and call(0, None) == NULL and call(5, None) == NULL
+    assert call(8, 100) == SHAPE and call(9, 96) == UNSUP
+    assert call(12, math.nan) == SCALE
+    assert call(4, p(1 * A)) == ALIAS
+    assert call(14, ctypes.byref(bs.TileConfig(256, 64, 8, 2))) == UNSUP  # no pairs for block_q 64
+    # 64 heads of 512 x 512 blocks: the plan needs more than 16 MiB
+    big = list(ok)
+    big[7], big[8], big[10], big[11] = 64, 65536, 128, 128
+    big[0], big[1], big[2], big[4], big[5] = p(1 << 40), p(2 << 40), p(3 << 40), p(4 << 40), p(5 << 40)
+    assert f(*big) == WS
