@@ -105,9 +105,12 @@ BwdLayout bwd_layout(int64_t BH, int S, int n_q, int n_k, int block_k) {
 
 int check_grid(int B, int H, int n_q, int n_k) {
     if (B <= 0 || H <= 0 || n_q <= 0 || n_k <= 0) return BSATTN_ERR_SHAPE;
-    const int64_t R = (int64_t)B * H * n_q;
-    if (R * n_k >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;  // list entries are int32
+    // Bound each product before the next one, so no int64 product can overflow.
+    const int64_t BH = (int64_t)B * H;  // < 2^62
+    if (BH >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;
+    const int64_t R = BH * n_q;  // < 2^62
     if (R >= ((int64_t)1 << 31) / 2) return BSATTN_ERR_SHAPE;
+    if (R * n_k >= ((int64_t)1 << 31)) return BSATTN_ERR_SHAPE;  // list entries are int32
     return BSATTN_OK;
 }
 
@@ -781,9 +784,12 @@ int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_
 
 // ---- ragged dot ------------------------------------------------------------------
 
+// The plan's item count is an int32 (and every item index fits one).
+static bool ragged_items_ok(int M, int G) { return ragged_max_items(M, G) < ((int64_t)1 << 30); }
+
 int bsattn_ragged_dot_workspace_size(int M, int G, size_t* bytes) {
     if (!bytes) return BSATTN_ERR_NULL;
-    if (M <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
+    if (M <= 0 || G <= 0 || !ragged_items_ok(M, G)) return BSATTN_ERR_SHAPE;
     *bytes = ragged_ws_bytes(M, G);
     return BSATTN_OK;
 }
@@ -791,7 +797,7 @@ int bsattn_ragged_dot_workspace_size(int M, int G, size_t* bytes) {
 int bsattn_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace,
                        size_t workspace_bytes, void* stream) {
     if (!group_sizes || !workspace) return BSATTN_ERR_NULL;
-    if (M <= 0 || G <= 0) return BSATTN_ERR_SHAPE;
+    if (M <= 0 || G <= 0 || !ragged_items_ok(M, G)) return BSATTN_ERR_SHAPE;
     if (workspace_bytes < ragged_ws_bytes(M, G)) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(group_sizes, 4) || !is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
     if (overlap(workspace, ragged_ws_bytes(M, G), group_sizes, (size_t)G * 4)) return BSATTN_ERR_ALIAS;
