@@ -6,6 +6,7 @@
 // allocated on the forward path.
 #include <algorithm>
 #include <cerrno>
+#include <cfloat>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -363,6 +364,11 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float*
     while ((var.tile_k << a.steps_log2) < block_k) ++a.steps_log2;
     const bool neg = std::signbit(scale) && scale != 0.0f;
     a.c = std::fabs(scale) * kLog2e;
+    // A zero scale makes every score 0: a uniform softmax over the kept keys.  The
+    // kernels get the smallest normal float instead, so an element mask's dropped
+    // score (-inf) times c stays -inf rather than NaN, while for any |q . k| < 2^100
+    // c * (q . k) stays below 2^-26 and every exponent still rounds to exactly 1.
+    if (a.c == 0.0f) a.c = FLT_MIN;
     a.qsign = neg ? 0x80008000u : 0u;
     a.qsign32 = neg ? 0x80000000u : 0u;
     return a;

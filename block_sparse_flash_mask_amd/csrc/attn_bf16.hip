@@ -61,7 +61,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     constexpr int KS = G::KS, MT = G::MT, MD = G::MD;
     static_assert(!PAIR || (WAVES == 8 && NQ == 1 && !PIPE), "row pairs: two 4-wave groups");
 
-    static_assert(ST == 2 || (ST == 3 && !PIPE), "three stages use the plain schedule");
+    static_assert(ST == 2 || (ST == 3 && !PIPE) || (ST == 1 && !PIPE && !PAIR && !ELEM),
+                  "three stages use the plain schedule; one stage the 4-wave block-mask kernel");
     static_assert(!ELEM || (!PIPE && NQ == 1), "element masks: plain schedule, one 32-row tile per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t k0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t v0s[G::BYTES];
@@ -281,10 +282,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmp[16 * mt + i] = s.v[n][mt][i];
-            const float raw = max_halves_nan(max_tree3<16 * MT>(tmp));
-            // (element masks: a tile row may keep no score, raw = -inf; with
-            // scale = 0 the product -inf * 0 would be NaN)
-            const float mx = (ELEM && raw == -INFINITY) ? -INFINITY : raw * a.c;
+            const float mx = max_halves_nan(max_tree3<16 * MT>(tmp)) * a.c;
             if (__ballot(mx > m_run[n] + 8.0f) != 0) {
                 const float m_new = fmax_nan(m_run[n], mx);
                 // (element masks: a row may still have no kept score, m = -inf;
@@ -299,11 +297,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
     };
 
-    // P = 2^(c S - m) in bf16, and its row sums into l.  On a partial step of an
-    // element mask (MASKED) a dropped score (S = -inf) gives P = 0 by a select,
-    // not through the exponent: with scale = 0, -inf * 0 would be NaN.
-    auto exps = [&](const SAcc& s, auto masked) -> PTile {
-        constexpr bool MASKED = decltype(masked)::value;
+    // P = 2^(c S - m) in bf16, and its row sums into l.  (c > 0 always: a zero
+    // scale arrives as the smallest normal float, so a dropped element's
+    // S = -inf gives -inf, never -inf * 0.)
+    auto exps = [&](const SAcc& s) -> PTile {
         PTile p;
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
@@ -314,8 +311,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_use));
-                    if constexpr (MASKED) e = s.v[n][mt][i] == -INFINITY ? 0.f : e;
+                    const float e = fast_exp2(__builtin_fmaf(s.v[n][mt][i], a.c, -m_use));
                     tmp[16 * mt + i] = e;
                     p.v[n][mt][i >> 3][i & 7] = (__bf16)e;
                 }
@@ -363,7 +359,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         update_max(s);
         SAcc s_next;
         if constexpr (NEXT) s_next = qk(knext);
-        const PTile p = exps(s, no{});
+        const PTile p = exps(s);
         pv(p, vcur);
         if constexpr (NEXT) {
             s = s_next;
@@ -397,9 +393,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // Element masks: the list entries of the steps in flight (e1 = this step, e2 =
     // the next with three stages), and the kept-bit test applied to S.
     int e1 = 0, e2 = 0;
-    auto apply_tile = [&](SAcc& s, int e, int t) -> bool {
+    auto apply_tile = [&](SAcc& s, int e, int t) {
         int tile = (e >> 16) - 1;  // -1: full block
-        if (tile < 0) return false;
+        if (tile < 0) return;
         tile = tile < a.n_tiles ? tile : a.n_tiles - 1;  // (a plan never holds more)
         const int qr = q_row0 - qi * a.block_q;  // this lane's row inside the block
         const int ko = (t & ((1 << sh) - 1)) * TK;
@@ -413,7 +409,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             for (int i = 0; i < 16; ++i)
                 if (!((w >> (16 * (i >> 3) + (i & 7))) & 1u)) s.v[0][mt][i] = -INFINITY;
         }
-        return true;
     };
     auto plain = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur,
                      const uint8_t* vcur) {
@@ -433,23 +428,34 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         }
         if (mine(t)) {
             SAcc s = qk(kcur);
-            bool partial = false;
             if constexpr (ELEM && PAIR)  // this group's own tile of the block
-                partial = apply_tile(s, (int)pair_tile[grp * kPairMaxBlocks + (e_cur & 0xffff)] << 16, t);
+                apply_tile(s, (int)pair_tile[grp * kPairMaxBlocks + (e_cur & 0xffff)] << 16, t);
             else if constexpr (ELEM)
-                partial = apply_tile(s, e_cur, t);
+                apply_tile(s, e_cur, t);
             update_max(s);
-            if (ELEM && partial) {
-                const PTile p = exps(s, yes{});
-                pv(p, vcur);
-            } else {
-                const PTile p = exps(s, no{});
-                pv(p, vcur);
-            }
+            const PTile p = exps(s);
+            pv(p, vcur);
         }
     };
 
-    if (n_steps > 0 && PIPE) {
+    if (n_steps > 0 && ST == 1) {
+        // One stage: copy, wait, barrier, compute, then a barrier before the next
+        // copy overwrites the stage -- the copy never overlaps the compute.
+        int pre = entry(0);
+        for (int t = 0; t < n_steps; ++t) {
+            const int kn = key0_of(pre, t);
+            pre = entry(t + 1);
+            if (t > 0) __syncthreads();  // everyone is done reading step t - 1
+            issue_k(kn, k0s);
+            issue_v(kn, v0s);
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+            __syncthreads();
+            SAcc s = qk(k0s);
+            update_max(s);
+            const PTile p = exps(s);
+            pv(p, v0s);
+        }
+    } else if (n_steps > 0 && PIPE) {
         const int k0 = key0_of(entry(0), 0);
         const int k1 = key0_of(entry(1), 1);
         int pre = entry(2);
@@ -554,6 +560,15 @@ static const Variant kBf16Variants[] = {
     BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 2, 1), BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 3, 1),
     BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(128, 2, 64, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(128, 1, 32, 2, 0, 3, 1),
+    // the rest of the tuning space (tile_q 64/128, tile_k 32/64/128, 2/4 waves,
+    // 1-3 stages) that fits the LDS and the registers
+    BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 2, 3), BSATTN_BF16_VARIANT(128, 2, 64, 1, 0, 3, 1),
+    BSATTN_BF16_VARIANT(128, 2, 128, 1, 0, 2, 1), BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 2, 1),
+    BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 3, 1), BSATTN_BF16_VARIANT(128, 4, 128, 1, 0, 2, 1),
+    BSATTN_BF16_VARIANT(128, 4, 32, 1, 0, 1, 3), BSATTN_BF16_VARIANT(128, 4, 64, 1, 0, 1, 2),
+    BSATTN_BF16_VARIANT(128, 4, 128, 1, 0, 1, 1), BSATTN_BF16_VARIANT(128, 2, 32, 1, 0, 1, 3),
+    BSATTN_BF16_VARIANT(128, 2, 64, 1, 0, 1, 2), BSATTN_BF16_VARIANT(128, 2, 128, 1, 0, 1, 1),
+    BSATTN_BF16_VARIANT(128, 2, 32, 2, 0, 1, 1), BSATTN_BF16_VARIANT(128, 2, 64, 2, 0, 1, 1),
     {1, 128, 128, 32, 8, 3, &launch_bf16_pp<128>},
     BSATTN_BF16_PAIR(128, 32, 3, 2), BSATTN_BF16_PAIR(128, 64, 3, 2),
     BSATTN_BF16_PAIR(128, 64, 2, 2), BSATTN_BF16_PAIR(128, 128, 2, 2),
@@ -562,6 +577,16 @@ static const Variant kBf16Variants[] = {
     BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 2, 1),  BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 2, 1),
     BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 3, 2),  BSATTN_BF16_VARIANT(64, 2, 32, 1, 1, 2, 2),
     BSATTN_BF16_VARIANT(64, 1, 64, 2, 0, 2, 1),
+    BSATTN_BF16_VARIANT(64, 2, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 2, 3),
+    BSATTN_BF16_VARIANT(64, 2, 128, 1, 0, 2, 1), BSATTN_BF16_VARIANT(64, 2, 128, 1, 0, 3, 1),
+    BSATTN_BF16_VARIANT(64, 2, 32, 2, 0, 2, 1), BSATTN_BF16_VARIANT(64, 2, 32, 2, 0, 3, 1),
+    BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 3, 1), BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 3, 1),
+    BSATTN_BF16_VARIANT(64, 4, 32, 1, 0, 3, 3), BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 3, 1),
+    BSATTN_BF16_VARIANT(64, 4, 32, 1, 0, 1, 4), BSATTN_BF16_VARIANT(64, 4, 64, 1, 0, 1, 3),
+    BSATTN_BF16_VARIANT(64, 4, 128, 1, 0, 1, 2), BSATTN_BF16_VARIANT(64, 2, 32, 1, 0, 1, 4),
+    BSATTN_BF16_VARIANT(64, 2, 64, 1, 0, 1, 3), BSATTN_BF16_VARIANT(64, 2, 128, 1, 0, 1, 2),
+    BSATTN_BF16_VARIANT(64, 2, 32, 2, 0, 1, 1), BSATTN_BF16_VARIANT(64, 2, 64, 2, 0, 1, 1),
+    BSATTN_BF16_VARIANT(64, 2, 128, 2, 0, 1, 1),
     {1, 64, 128, 32, 8, 3, &launch_bf16_pp<64>},
     BSATTN_BF16_PAIR(64, 64, 3, 4), BSATTN_BF16_PAIR(64, 64, 2, 4), BSATTN_BF16_PAIR(64, 128, 2, 2),
 };
