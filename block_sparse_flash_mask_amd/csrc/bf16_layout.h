@@ -76,6 +76,50 @@ struct DmaPlan {
     }
 };
 
+// K tile in the row-chunk layout.  The 1 KiB-per-(mt, ks) layout above makes
+// every DMA instruction touch 32 rows for 32 bytes each, and the L2 -> CU path
+// serves such an instruction at about a quarter of the rate of one that reads
+// 8 rows x 128 contiguous bytes (measured on MI355X: ~16 against ~58 bytes per
+// clock per CU from L2).  Here a 1 KiB chunk holds 8 consecutive rows x one
+// 128-byte segment (64 elements) of each, chunk (r/8)*NSEG + seg, so each DMA
+// instruction reads whole 128-byte lines.  Inside a chunk row r%8 sits at
+// (r%8)*128 and its 16-byte unit c at slot c ^ x(r), x(r) = (r/2)%8: the
+// MFMA operand read (16 lanes reading 16 different rows at one unit) then hits
+// 16 distinct 16-byte bank groups.  Rows are stored in natural order; the read
+// applies kperm, so the fragment lane l gets is still
+// K[32mt + kperm(l%32)][16ks + 8(l/32) .. +7].
+template <int D, int WAVES, int TK>
+struct KRowPlan {
+    static constexpr int NSEG = D / 64;          // 128-byte segments per row
+    static constexpr int NCH = TK / 8 * NSEG;    // 1 KiB chunks per tile
+    static constexpr int NK = NCH / WAVES;       // DMA instructions per wave
+    static_assert(D % 64 == 0 && NCH % WAVES == 0, "even DMA split over whole segments");
+    int dma_lane[2];  // element offset of lane l's 16 bytes, chunk row-group parity 0 / 1
+    int rd_lane[4];   // byte offset of lane l's fragment for k-step ks with ks % 4 = index
+
+    __device__ __forceinline__ void init(int lane) {
+        // DMA: lane l fills slot l%8 of row l/8 of the chunk; that slot holds unit
+        // c = (l%8) ^ x(row), and x(8 g + l/8) = (l/16) | 4 (g%2).
+#pragma unroll
+        for (int p = 0; p < 2; ++p) dma_lane[p] = (lane >> 3) * D + 8 * ((lane & 7) ^ (lane >> 4) ^ (4 * p));
+        const int rho = kperm(lane & 31), hh = lane >> 5, x = (rho >> 1) & 7;
+        // unit c = 2 (ks%4) + hh of row rho: slot c ^ x = 2 ((ks%4) ^ (x/2)) + (hh ^ x%2)
+        const int base = (rho >> 3) * NSEG * 1024 + (rho & 7) * 128 + 16 * (hh ^ (x & 1));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rd_lane[k] = base + 32 * (k ^ (x >> 1));
+    }
+    // DMA instruction i of wave w fills chunk ch = w + i*WAVES: its first element
+    // relative to the tile's first key, and the parity of its row group.
+    __device__ __forceinline__ static int uniform(int w, int i) {
+        const int ch = w + i * WAVES;
+        return 8 * (ch / NSEG) * D + (ch % NSEG) * 64;
+    }
+    __device__ __forceinline__ static int parity(int w, int i) { return ((w + i * WAVES) / NSEG) & 1; }
+    __device__ __forceinline__ int dma_off(int w, int i) const { return parity(w, i) ? dma_lane[1] : dma_lane[0]; }
+    // Byte offset of fragment (mt, ks) less the lane part rd_lane[ks % 4].
+    static constexpr int frag(int mt, int ks) { return mt * 4 * NSEG * 1024 + (ks / 4) * 1024; }
+};
+
 // 16-byte HBM -> LDS DMA per lane through a raw buffer resource over
 // [base, base + nrec): global byte offset voff (per lane) + soff (uniform); the
 // lane's 16 bytes land at lds + 16 * lane.  A buffer load (rather than a global

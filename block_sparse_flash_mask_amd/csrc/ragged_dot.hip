@@ -22,9 +22,10 @@
 // v_mfma_f32_32x32x16_bf16 with both operands from LDS: the expert tile
 // W[g][k0..k0+31][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
 // layout, row stride N; A by ds_read_b64_tr_b16) and the lhs rows X[m0..m0+255]
-// [k0..k0+31] in its K layout (row stride K; B by ds_read_b128), both by buffer
+// [k0..k0+31] in 16-row x 64-byte chunks (B by ds_read_b128), both by buffer
 // loads with the LDS flag, four stages (three steps of loads in flight).  Per k a
-// workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.  ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
+// workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.
+// ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
 // 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
 // wave's own lhs rows loaded straight into VGPRs one step ahead.
 #include "bf16_layout.h"
@@ -301,14 +302,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 2; ++i) {
         const int tb = 2 * (wave_s + 8 * i);
         w_uni[i] = (16 * ((tb / MDW / 2) % 2) + 4 * ((tb / MDW) % 2)) * N + 32 * (tb % MDW);
-        // X tile DMA (K layout, row stride K): block b = w + 8 i = (32-row tile
-        // b / 2, 16-k step b % 2); lane l's 16 bytes are X[m0 + 32 (b/2) +
-        // kperm(l%32)][k0 + 16 (b%2) + 8 (l/32) ..].  Rows past M read row M - 1
-        // (never stored).
-        const int b = wave_s + 8 * i;
-        int xrow = m0 + 32 * (b / KSX) + kperm(l32);
+        // X tile DMA, row-chunk layout: chunk c = w + 8 i holds rows m0 + 16 c ..
+        // + 15, all 32 k of the step (64 bytes each), row r%16 at (r%16)*64 and its
+        // 16-byte unit u at slot u ^ ((r/4)%4).  Lane l fills slot l%4 of row l/4,
+        // so one instruction reads 16 rows x 64 contiguous bytes (a quarter-line
+        // pattern, 32 rows x 32 bytes, runs at half that rate from L2).  Rows past
+        // M read row M - 1 (never stored).
+        int xrow = m0 + 16 * (wave_s + 8 * i) + (lane >> 2);
         xrow = xrow < M ? xrow : M - 1;
-        x_lane[i] = (xrow * K + 16 * (b % KSX) + 8 * h) * 2;
+        x_lane[i] = (xrow * K + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2;
+    }
+    // Read side: lane (h, c) takes X[32 T + kperm(c)][k0 + 16 ks + 8 h ..] (the B
+    // operand of 32-row tile T, k-step ks) at T * 2048 + x_rd[ks]; 16 lanes read 16
+    // rows at one unit and meet 16 distinct 16-byte bank groups.
+    int x_rd[KSX];
+    {
+        const int rho = kperm(l32), y = (rho >> 2) & 3;
+#pragma unroll
+        for (int ks = 0; ks < KSX; ++ks)
+            x_rd[ks] = (rho >> 4) * 1024 + (rho & 15) * 64 + 16 * (h ^ (y & 1)) + 32 * (ks ^ (y >> 1));
     }
     const int xrec = M * K * 2;  // < 2^31: the launcher checks it
     // Inline-assembly DMA (dma16_raw): with the stage picked at run time the
@@ -335,7 +347,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             bf16x8 xf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xf[j] = *(const bf16x8*)(xbuf + ((4 * wm + j) * KSX + ks) * 1024 + lane * 16);
+                xf[j] = *(const bf16x8*)(xbuf + (4 * wm + j) * 2048 + x_rd[ks]);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int md = 2 * wn + i;
