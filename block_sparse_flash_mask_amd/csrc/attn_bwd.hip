@@ -239,6 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-row tile of Q or dO
     typedef DmaPlan<D, WAVES, 32> P;
+    typedef KRowPlan<D, WAVES, 32> KP;
     constexpr int KS = G::KS, MD = G::MD;
     __shared__ __attribute__((aligned(1024))) uint8_t qk0[G::BYTES], qv0[G::BYTES], ok0[G::BYTES], ov0[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t qk1[G::BYTES], qv1[G::BYTES], ok1[G::BYTES], ov1[G::BYTES];
@@ -292,15 +293,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
 
     P plan;
     plan.init(lane);
+    KP kplan;
+    kplan.init(lane);
     const int nrec = a.S * D * 2;
-    const int k_voff = plan.k_lane * 2, v_voff = plan.v_lane * 2;
+    const int v_voff = plan.v_lane * 2;
     const uint16_t* qg = a.q + head;
     const uint16_t* og = a.dout + head;
     const float2* ldg = a.ld + (size_t)bh * a.S;
     auto issue = [&](int q0, uint8_t* qk, uint8_t* qv, uint8_t* ok, uint8_t* ov, float2* ldb) {
 #pragma unroll
-        for (int i = 0; i < P::NK; ++i) {
-            const int soff = (q0 * D + P::k_uniform(wave_s, i)) * 2;
+        for (int i = 0; i < KP::NK; ++i) {
+            const int soff = (q0 * D + KP::uniform(wave_s, i)) * 2, k_voff = kplan.dma_off(wave_s, i) * 2;
             dma16(qg, nrec, (BSATTN_LDS void*)(qk + (wave_s + i * WAVES) * 1024), k_voff, soff);
             dma16(og, nrec, (BSATTN_LDS void*)(ok + (wave_s + i * WAVES) * 1024), k_voff, soff);
         }
@@ -340,9 +343,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qa = *(const bf16x8*)(qk + ks * 1024 + lane * 16);
+            const bf16x8 qa = *(const bf16x8*)(qk + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-            const bf16x8 oa = *(const bf16x8*)(ok + ks * 1024 + lane * 16);
+            const bf16x8 oa = *(const bf16x8*)(ok + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
         }
         bf16x8 pb[2], db[2];
@@ -448,6 +451,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     BwdArgs a) {
     typedef TileGeom<D, 32> G;  // one 32-key tile of K or V
     typedef DmaPlan<D, WAVES, 32> P;
+    typedef KRowPlan<D, WAVES, 32> KP;
     constexpr int KS = G::KS, MD = G::MD;
     __shared__ __attribute__((aligned(1024))) uint8_t kk0[G::BYTES], kv0[G::BYTES], vk0[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t kk1[G::BYTES], kv1[G::BYTES], vk1[G::BYTES];
@@ -490,14 +494,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
 
     P plan;
     plan.init(lane);
+    KP kplan;
+    kplan.init(lane);
     const int nrec = a.S * D * 2;
-    const int k_voff = plan.k_lane * 2, v_voff = plan.v_lane * 2;
+    const int v_voff = plan.v_lane * 2;
     const uint16_t* kg = a.k + head;
     const uint16_t* vg = a.v + head;
     auto issue = [&](int k0, uint8_t* kk, uint8_t* kv, uint8_t* vk) {
 #pragma unroll
-        for (int i = 0; i < P::NK; ++i) {
-            const int soff = (k0 * D + P::k_uniform(wave_s, i)) * 2;
+        for (int i = 0; i < KP::NK; ++i) {
+            const int soff = (k0 * D + KP::uniform(wave_s, i)) * 2, k_voff = kplan.dma_off(wave_s, i) * 2;
             dma16(kg, nrec, (BSATTN_LDS void*)(kk + (wave_s + i * WAVES) * 1024), k_voff, soff);
             dma16(vg, nrec, (BSATTN_LDS void*)(vk + (wave_s + i * WAVES) * 1024), k_voff, soff);
         }
@@ -525,9 +531,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 ka = *(const bf16x8*)(kk + ks * 1024 + lane * 16);
+            const bf16x8 ka = *(const bf16x8*)(kk + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-            const bf16x8 va = *(const bf16x8*)(vk + ks * 1024 + lane * 16);
+            const bf16x8 va = *(const bf16x8*)(vk + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[ks], dp, 0, 0, 0);
         }
         bf16x8 db[2];

@@ -20,10 +20,10 @@
 // (rows) grid, each 64 columns x 128 rows (each transposing LDS read of W feeds
 // four MFMAs).  C^T[n][m] = sum_k W^T[n][k] X^T[k][m] on
 // v_mfma_f32_32x32x16_bf16 with both operands from LDS: the expert tile
-// W[g][k0..k0+31][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
+// W[g][k0..k0+63][n0..n0+255] in the transposed-read layout of bf16_layout.h (the V
 // layout, row stride N; A by ds_read_b64_tr_b16) and the lhs rows X[m0..m0+255]
-// [k0..k0+31] in 16-row x 64-byte chunks (B by ds_read_b128), both by buffer
-// loads with the LDS flag, four stages (three steps of loads in flight).  Per k a
+// [k0..k0+63] in 8-row x 128-byte swizzled chunks (B by ds_read_b128), both by
+// buffer loads with the LDS flag, two stages (one step of loads in flight).  Per k a
 // workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.
 // ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
 // 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
@@ -243,19 +243,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 }
 
-constexpr int kR256TK = 32;     // k per step of the 256 x 256 kernel
-constexpr int kR256Stages = 4;  // LDS stages: three steps of loads in flight
+// The 256 x 256 kernel walks K in steps of TKS with NST LDS stages of W (TKS x 256)
+// and X (256 x TKS) each, NST - 1 steps of loads in flight.  64-deep steps in two
+// stages (128 KiB) ran 1.5 % faster on the 8-expert workload than 32-deep steps in
+// four stages, and clearly faster than 32-deep steps in two or three.
+constexpr int kR256TK = 64;
+constexpr int kR256Stages = 2;
 
-template <int OUT_F32>
+template <int OUT_F32, int TKS, int NST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot256_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items) {
-    typedef TileGeom<256, kR256TK> GW;  // W^T tile: "D" = 256 columns, "keys" = 32 k
+    typedef TileGeom<256, TKS> GW;      // W^T tile: "D" = 256 columns, "keys" = TKS k
     constexpr int MDW = GW::MD;         // 8 column tiles of 32
-    constexpr int KSX = kR256TK / 16;   // 2 k-steps of 16 per step
-    constexpr int WB = GW::BYTES;       // 16 KiB of W, then 16 KiB of X per stage
-    static_assert(GW::VBLK / 2 == 16 && 8 * KSX == 16, "two W and two X DMAs per wave per stage");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kR256Stages * 2 * WB];
+    constexpr int KSX = TKS / 16;       // k-steps of 16 per step
+    constexpr int WB = GW::BYTES;       // W bytes per stage, then as many of X
+    constexpr int NDW = TKS / 16;       // W (and X) DMA instructions per wave per stage
+    static_assert(GW::VBLK / 2 == 8 * NDW, "W DMA split over the 8 waves");
+    static_assert(NST >= 2 && NST * 2 * WB <= 160 * 1024, "LDS stages");
+    // X chunk layout: a 1 KiB chunk holds XR rows x TKS k (XU 16-byte units per
+    // row), row r%XR at (r%XR) * 2 TKS and unit u at slot u ^ y(r), y(r) =
+    // (r / XP) % XU with XP rows per 256-byte bank period: 16 lanes reading 16
+    // consecutive rows at one unit meet 16 distinct 16-byte bank groups.
+    constexpr int XU = TKS / 8, XR = 1024 / (2 * TKS), XP = 256 / (2 * TKS);
+    static_assert(256 / XR == 8 * NDW, "X DMA split over the 8 waves");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * 2 * WB];
 
     // Workgroups go to the 8 XCDs round-robin by blockIdx.  XCD x = b % 8 takes the
     // (b / 8)-th (item, column tile) of its own contiguous chunk of the item-major
@@ -289,38 +301,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const int wn = wave & 3, wm = wave >> 2;  // columns 64 wn .., rows 128 wm ..
 
-    // W tile DMA (V layout, row stride N): wave w fills block pairs 2w and 2(w + 8)
-    // of the 32 blocks; lane offsets as the attention kernel's V plan with N for
-    // the row.
+    // W tile DMA (V layout, row stride N): wave w fills block pairs 2(w + 8 i);
+    // lane offsets as the attention kernel's V plan with N for the row.
     const int u = 2 * (lane & 31);
     const int L = u & 15, gg = (u >> 4) & 1, hh = u >> 5;
     const int w_lane = (8 * hh + (L >> 2)) * N + 32 * (lane >> 5) + 16 * gg + 4 * (L & 3);
     const uint16_t* wg = rhs + (size_t)grp * K * N + n0;
     const int wrec = (int)((size_t)K * N * 2 - (size_t)n0 * 2);
-    int w_uni[2], x_lane[2];
+    int w_uni[NDW], x_lane[NDW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NDW; ++i) {
         const int tb = 2 * (wave_s + 8 * i);
-        w_uni[i] = (16 * ((tb / MDW / 2) % 2) + 4 * ((tb / MDW) % 2)) * N + 32 * (tb % MDW);
-        // X tile DMA, row-chunk layout: chunk c = w + 8 i holds rows m0 + 16 c ..
-        // + 15, all 32 k of the step (64 bytes each), row r%16 at (r%16)*64 and its
-        // 16-byte unit u at slot u ^ ((r/4)%4).  Lane l fills slot l%4 of row l/4,
-        // so one instruction reads 16 rows x 64 contiguous bytes (a quarter-line
-        // pattern, 32 rows x 32 bytes, runs at half that rate from L2).  Rows past
-        // M read row M - 1 (never stored).
-        int xrow = m0 + 16 * (wave_s + 8 * i) + (lane >> 2);
+        w_uni[i] = (32 * (tb / MDW / 4) + 16 * ((tb / MDW / 2) % 2) + 4 * ((tb / MDW) % 2)) * N + 32 * (tb % MDW);
+        // X tile DMA: chunk c = w + 8 i holds rows m0 + XR c ..; lane l fills slot
+        // l % XU of row l / XU, i.e. unit (l % XU) ^ y(row): one instruction reads
+        // XR rows x 2 TKS contiguous bytes (whole 128-byte lines at TKS = 64; the
+        // 32 rows x 32 bytes of an operand-ordered block run at a quarter of that
+        // rate from L2).  Rows past M read row M - 1 (never stored).
+        const int c = wave_s + 8 * i;
+        const int r = XR * c + lane / XU;
+        int xrow = m0 + r;
         xrow = xrow < M ? xrow : M - 1;
-        x_lane[i] = (xrow * K + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2;
+        x_lane[i] = (xrow * K + 8 * ((lane % XU) ^ ((r / XP) % XU))) * 2;
     }
     // Read side: lane (h, c) takes X[32 T + kperm(c)][k0 + 16 ks + 8 h ..] (the B
-    // operand of 32-row tile T, k-step ks) at T * 2048 + x_rd[ks]; 16 lanes read 16
-    // rows at one unit and meet 16 distinct 16-byte bank groups.
+    // operand of 32-row tile T, k-step ks) at T * 32 * 2 TKS + x_rd[ks].
     int x_rd[KSX];
     {
-        const int rho = kperm(l32), y = (rho >> 2) & 3;
+        const int rho = kperm(l32), y = (rho / XP) % XU;
 #pragma unroll
         for (int ks = 0; ks < KSX; ++ks)
-            x_rd[ks] = (rho >> 4) * 1024 + (rho & 15) * 64 + 16 * (h ^ (y & 1)) + 32 * (ks ^ (y >> 1));
+            x_rd[ks] = (rho / XR) * 1024 + (rho % XR) * 2 * TKS + 16 * ((2 * ks + h) ^ y);
     }
     const int xrec = M * K * 2;  // < 2^31: the launcher checks it
     // Inline-assembly DMA (dma16_raw): with the stage picked at run time the
@@ -328,11 +339,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // read; the explicit vmcnt waits and barriers below order it instead.
     const u32x4 wsrc = make_rsrc(wg, wrec), xsrc = make_rsrc(lhs, xrec);
     auto issue = [&](int t) {
-        uint8_t* wbuf = lds + (t % kR256Stages) * 2 * WB;
+        uint8_t* wbuf = lds + (t % NST) * 2 * WB;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            dma16_raw(wsrc, lds_addr(wbuf + (wave_s + 8 * i) * 1024), w_lane * 2, (t * kR256TK * N + w_uni[i]) * 2);
-            dma16_raw(xsrc, lds_addr(wbuf + WB + (wave_s + 8 * i) * 1024), x_lane[i], t * kR256TK * 2);
+        for (int i = 0; i < NDW; ++i) {
+            dma16_raw(wsrc, lds_addr(wbuf + (wave_s + 8 * i) * 1024), w_lane * 2, (t * TKS * N + w_uni[i]) * 2);
+            dma16_raw(xsrc, lds_addr(wbuf + WB + (wave_s + 8 * i) * 1024), x_lane[i], t * TKS * 2);
         }
     };
 
@@ -346,8 +357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int ks = 0; ks < KSX; ++ks) {
             bf16x8 xf[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xf[j] = *(const bf16x8*)(xbuf + (4 * wm + j) * 2048 + x_rd[ks]);
+            for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(xbuf + (4 * wm + j) * 64 * TKS + x_rd[ks]);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int md = 2 * wn + i;
@@ -361,21 +371,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
 
-    // Stages 0..2 in flight before the loop; step t waits for its own stage
-    // (leaving the later ones, four DMA instructions each, outstanding), syncs,
-    // issues stage t + 3 into the buffer step t - 1 used, and computes.
-    const int n_steps = K / kR256TK;
-    for (int t = 0; t < kR256Stages - 1 && t < n_steps; ++t) issue(t);
+    // Stages 0..NST-2 in flight before the loop; step t waits until only the
+    // later stages' DMAs (2 NDW instructions each) are outstanding, syncs, issues
+    // stage t + NST - 1 into the buffer step t - 1 used, and computes.
+    const int n_steps = K / TKS;
+    for (int t = 0; t < NST - 1 && t < n_steps; ++t) issue(t);
     for (int t = 0; t < n_steps; ++t) {
-        if (t + 2 < n_steps)
-            __builtin_amdgcn_s_waitcnt(0x3f70 | 8);  // vmcnt(8)
-        else if (t + 1 < n_steps)
-            __builtin_amdgcn_s_waitcnt(0x3f70 | 4);  // vmcnt(4)
-        else
-            __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0)
+        int ahead = n_steps - 1 - t;
+        ahead = ahead < NST - 2 ? ahead : NST - 2;
+        if constexpr (NST >= 4) {
+            if (ahead >= 2)
+                __builtin_amdgcn_s_waitcnt(0x3f70 | (4 * NDW));  // vmcnt(2 stages)
+            else if (ahead == 1)
+                __builtin_amdgcn_s_waitcnt(0x3f70 | (2 * NDW));  // vmcnt(1 stage)
+            else
+                __builtin_amdgcn_s_waitcnt(0x3f70);              // vmcnt(0)
+        } else if constexpr (NST == 3) {
+            if (ahead >= 1)
+                __builtin_amdgcn_s_waitcnt(0x3f70 | (2 * NDW));
+            else
+                __builtin_amdgcn_s_waitcnt(0x3f70);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x3f70);
+        }
         __syncthreads();
-        if (t + kR256Stages - 1 < n_steps) issue(t + kR256Stages - 1);
-        const uint8_t* wbuf = lds + (t % kR256Stages) * 2 * WB;
+        if (t + NST - 1 < n_steps) issue(t + NST - 1);
+        const uint8_t* wbuf = lds + (t % NST) * 2 * WB;
         step(wbuf, wbuf + WB);
     }
 
@@ -419,10 +440,10 @@ hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, in
     if (N % 256 == 0 && (int64_t)M * K * 2 < ((int64_t)1 << 31)) {  // lhs through one buffer range
         const int64_t grid = 8 * ((max_items * (N / 256) + 7) / 8);  // 8 XCD chunks
         if (out_f32)
-            hipLaunchKernelGGL(ragged_dot256_kernel<1>, dim3((unsigned)grid), dim3(512), 0, stream,
+            hipLaunchKernelGGL((ragged_dot256_kernel<1, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0, stream,
                                (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N, (int)max_items);
         else
-            hipLaunchKernelGGL(ragged_dot256_kernel<0>, dim3((unsigned)grid), dim3(512), 0, stream,
+            hipLaunchKernelGGL((ragged_dot256_kernel<0, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0, stream,
                                (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N,
                                (int)max_items);
         return hipGetLastError();

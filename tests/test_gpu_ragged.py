@@ -67,6 +67,10 @@ CASES = [
     # the partial last round as 128 x 128 tiles (an empty group, a 920-row zero tail)
     (17920, 64, 1024, 5, [5000, 3000, 0, 6000, 3000]),
     (8192, 64, 2048, 1, [8192]),                    # exactly one full round on 256 CUs
+    # 304 tiles of four 64-deep k-steps: a whole round and a partial one; an empty
+    # group, a 300-row zero tail
+    (9000, 256, 2048, 4, [3000, 2500, 0, 3200]),
+    (5000, 512, 1024, 3, [1000, 2000, 1900]),      # eight k-steps per tile, a zero tail
 ]
 
 
