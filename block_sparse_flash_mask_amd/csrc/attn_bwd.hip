@@ -240,6 +240,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     typedef TileGeom<D, 32> G;  // one 32-row tile of Q or dO
     typedef DmaPlan<D, WAVES, 32> P;
     typedef KRowPlan<D, WAVES, 32> KP;
+    // Q and dO tiles for the S and dP MFMAs: row-chunk layout, except with element
+    // masks, whose extra registers would then spill; those keep the 1 KiB-per-k-step
+    // blocks of DmaPlan.
+    constexpr bool RK = !ELEM;
     constexpr int KS = G::KS, MD = G::MD;
     __shared__ __attribute__((aligned(1024))) uint8_t qk0[G::BYTES], qv0[G::BYTES], ok0[G::BYTES], ov0[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t qk1[G::BYTES], qv1[G::BYTES], ok1[G::BYTES], ov1[G::BYTES];
@@ -303,7 +307,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
     auto issue = [&](int q0, uint8_t* qk, uint8_t* qv, uint8_t* ok, uint8_t* ov, float2* ldb) {
 #pragma unroll
         for (int i = 0; i < KP::NK; ++i) {
-            const int soff = (q0 * D + KP::uniform(wave_s, i)) * 2, k_voff = kplan.dma_off(wave_s, i) * 2;
+            const int soff = (q0 * D + (RK ? KP::uniform(wave_s, i) : P::k_uniform(wave_s, i))) * 2;
+            const int k_voff = (RK ? kplan.dma_off(wave_s, i) : plan.k_lane) * 2;
             dma16(qg, nrec, (BSATTN_LDS void*)(qk + (wave_s + i * WAVES) * 1024), k_voff, soff);
             dma16(og, nrec, (BSATTN_LDS void*)(ok + (wave_s + i * WAVES) * 1024), k_voff, soff);
         }
@@ -343,9 +348,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, D
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qa = *(const bf16x8*)(qk + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
+            const int kfo = RK ? KP::frag(0, ks) + kplan.rd_lane[ks & 3] : ks * 1024 + lane * 16;
+            const bf16x8 qa = *(const bf16x8*)(qk + kfo);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-            const bf16x8 oa = *(const bf16x8*)(ok + KP::frag(0, ks) + kplan.rd_lane[ks & 3]);
+            const bf16x8 oa = *(const bf16x8*)(ok + kfo);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
         }
         bf16x8 pb[2], db[2];
