@@ -342,7 +342,7 @@ def bench_ragged(args, torch, bs, W):
     ms_kernel = timed(prod, args.steps)
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     big = w.N % 256 == 0 and w.M * w.K * 2 < 2 ** 31  # the 256 x 256 tile kernel runs
-    traffic = traffic_from_profiles(w.name, (256, 256, 8, 4) if big else (128, 128, 4, 2), "ragged")
+    traffic = traffic_from_profiles(w.name, (256, 256, 8, 2) if big else (128, 128, 4, 2), "ragged")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": "ragged_dot256_kernel" if big else "ragged_dot_kernel", "kernel_ms": ms_kernel}
@@ -357,7 +357,7 @@ def bench_ragged(args, torch, bs, W):
         "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
                    "group_sizes": [int(v) for v in sizes],
-                   "tile_m_n_k": [256, 256, 32] if big else [128, 128, 64],
+                   "tile_m_n_k": [256, 256, 64] if big else [128, 128, 64],
                    "flops_per_step": flops},
         "roofline": roofline,
     }
