@@ -93,6 +93,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     // element masks on row pairs: tile + 1 of each key block of either row (0: full)
     __shared__ uint16_t pair_tile[PAIR && ELEM ? 2 * kPairMaxBlocks : 1];
     const int grp = PAIR ? wave >> 2 : 0;
+    // A barrier that orders LDS accesses only (waits for this wave's LDS operations,
+    // not for its global loads, which __syncthreads would drain as well).
+    auto lds_sync = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
     // Q^T fragments: lane (h, q) holds Q[q][16*ks + 8*h .. +7] for every ks.
     bf16x8 qf[NQ][KS];
     auto load_q = [&](size_t head_q) {
@@ -118,21 +125,28 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         qi = 2 * j + grp;
         qi0 = 2 * j;
         row_ok = qi < a.n_q;
-        // the Q loads go out before the list is built (they do not depend on it)
-        q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
-        load_q((size_t)bh * a.S * D);
         const int ra = bh * a.n_q + 2 * j;
         const bool has_b = 2 * j + 1 < a.n_q;
-        const int nw = (a.n_k + 31) >> 5;
-        for (int w = tid; w < 2 * nw; w += WAVES * 64) pair_bits[(w / nw) * (kPairMaxBlocks / 32) + w % nw] = 0;
-        __syncthreads();
+        // The rows' first list entries, then the Q loads: the Q loads do not depend on
+        // the list and stay in flight while it is built (its barriers order LDS only,
+        // and a wait for the entries, issued first, leaves the later Q loads out).
+        int lb[2], lc[2], ent[2];
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            if (side == 1 && !has_b) break;
-            int b0, c0;
-            row_list(a, ra + side, b0, c0);
+            lb[side] = lc[side] = 0;
+            if (side == 0 || has_b) row_list(a, ra + side, lb[side], lc[side]);
+            ent[side] = tid < lc[side] ? a.list[lb[side] + tid] : 0;
+        }
+        q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
+        load_q((size_t)bh * a.S * D);
+        const int nw = (a.n_k + 31) >> 5;
+        for (int w = tid; w < 2 * nw; w += WAVES * 64) pair_bits[(w / nw) * (kPairMaxBlocks / 32) + w % nw] = 0;
+        lds_sync();
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int b0 = lb[side], c0 = lc[side];
             for (int i = tid; i < c0; i += WAVES * 64) {
-                int kj = a.list[b0 + i];
+                int kj = i == tid ? ent[side] : a.list[b0 + i];
                 int tile1 = 0;
                 if constexpr (ELEM) {
                     tile1 = kj < 0 ? 0 : kj >> 16;
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
                 if constexpr (ELEM) pair_tile[side * kPairMaxBlocks + kj] = (uint16_t)tile1;
             }
         }
-        __syncthreads();
+        lds_sync();
         if (wave == 0) {
             // Compact the union bitmap: lane l takes word l of each 64-word chunk.
             int base = 0;
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
             }
             if (lane == 0) pair_cnt[0] = base;
         }
-        __syncthreads();
+        lds_sync();
         cnt = wave_uniform(pair_cnt[0]);
     } else {
         bh = r / a.n_q;
