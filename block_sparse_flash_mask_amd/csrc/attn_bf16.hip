@@ -522,6 +522,49 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 
     // Epilogue: O / l in bf16 (round to nearest even), lse = ln2 * (m + log2 l).
     // A row that saw no key block (m never left -inf) gets 0 and -inf.
+    // A lane holds 8 bytes of its row per (md, g4), so storing straight from the
+    // registers writes 32 rows x 16 bytes per instruction (a quarter of each line).
+    // Where the stage arrays can hold every wave's 32 x D tile, the tile goes
+    // through LDS instead (16-byte units XOR-swizzled by row) and leaves as whole
+    // rows, 64 / (D / 8) rows per instruction.
+    constexpr int CPR = D / 8;                     // 16-byte units per output row
+    constexpr int REG = 32 * D * 2;                // one wave's tile
+    constexpr int WPA = G::BYTES / REG;            // tiles per stage array
+    constexpr int NARR = ST > 2 ? 6 : 4;           // k0s v0s k1s v1s (k2s v2s)
+    constexpr bool STAGED = NQ == 1 && WPA >= 1 && WAVES <= WPA * NARR;
+    if constexpr (STAGED) {
+        __syncthreads();  // every wave is done with the last step's stage
+        if (!row_ok) return;
+        const bool any = (PAIR || ELEM) ? m_run[0] != -INFINITY : n_steps > 0;
+        const float l_tot = sum_halves(l_run[0]);
+        const float inv = any ? 1.0f / l_tot : 0.0f;
+        const int arr = wave / (WPA > 0 ? WPA : 1);
+        uint8_t* const arrs[6] = {k0s, v0s, k1s, v1s, k2s, v2s};
+        uint8_t* tile = arrs[arr] + (wave % (WPA > 0 ? WPA : 1)) * REG;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                // d = 32 md + 8 g4 + 4 h .. +3: unit 4 md + g4, half h
+                const int c = 4 * md + g4;
+                bf16x4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[u] = (__bf16)(oacc[0][md][4 * g4 + u] * inv);
+                *(bf16x4*)(tile + l32 * (2 * D) + ((c ^ (l32 & (CPR - 1))) << 4) + 8 * h) = o;
+            }
+        constexpr int RPI = 64 / CPR;  // rows per store instruction
+        const int row0 = q_row0 - l32;
+        uint16_t* og = (uint16_t*)a.out + head + (size_t)row0 * D;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int rr = RPI * i + lane / CPR, c = lane % CPR;
+            const u32x4 v = *(const u32x4*)(tile + rr * (2 * D) + ((c ^ (rr & (CPR - 1))) << 4));
+            *(u32x4*)(og + (size_t)rr * D + 8 * c) = v;
+        }
+        if (h == 0)
+            a.lse[(size_t)bh * a.S + q_row0] = any ? (m_run[0] + log2f(l_tot)) * kLn2 : -INFINITY;
+        return;
+    }
     if (!row_ok) return;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
