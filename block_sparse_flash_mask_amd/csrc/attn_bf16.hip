@@ -130,15 +130,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         // The rows' first list entries, then the Q loads: the Q loads do not depend on
         // the list and stay in flight while it is built (its barriers order LDS only,
         // and a wait for the entries, issued first, leaves the later Q loads out).
+        // (Padded lists: the entry loads need no count, so they go out first, then
+        // the Q loads, then the count loads, which travel the scalar path.)
         int lb[2], lc[2], ent[2];
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            lb[side] = lc[side] = 0;
-            if (side == 0 || has_b) row_list(a, ra + side, lb[side], lc[side]);
-            ent[side] = tid < lc[side] ? a.list[lb[side] + tid] : 0;
+            ent[side] = 0;
+            if ((side == 0 || has_b) && a.ell_stride > 0 && tid < a.n_k)
+                ent[side] = a.list[(size_t)(ra + side) * a.ell_stride + tid];
         }
         q_row0 = qi * a.block_q + (wave & 3) * 32 + l32;
         load_q((size_t)bh * a.S * D);
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            lb[side] = lc[side] = 0;
+            if (side == 0 || has_b) {
+                row_list(a, ra + side, lb[side], lc[side]);
+                if (a.ell_stride == 0 && tid < lc[side]) ent[side] = a.list[lb[side] + tid];
+            }
+        }
         const int nw = (a.n_k + 31) >> 5;
         for (int w = tid; w < 2 * nw; w += WAVES * 64) pair_bits[(w / nw) * (kPairMaxBlocks / 32) + w % nw] = 0;
         lds_sync();
