@@ -188,7 +188,7 @@ def cpu_baseline(w, q, k, v, mask, budget_s):
     model, nproc = host_cpu()
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle", "cpu_model": model, "nproc": nproc,
-            "sample": "%d of %d query rows (every %dth), each over its full key list; %.1f s"
+            "sample": "%d of %d query rows (one in %d), each over its full key list; %.1f s"
                       % (len(rows), total, stride, t)}
 
 
@@ -213,7 +213,7 @@ def cpu_baseline_elem(w, q, k, v, st, pidx, pbits, kept_per_row, budget_s):
     model, nproc = host_cpu()
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle", "cpu_model": model, "nproc": nproc,
-            "sample": "%d of %d query rows (every %dth), each over its kept keys; %.1f s"
+            "sample": "%d of %d query rows (one in %d), each over its kept keys; %.1f s"
                       % (len(rows), total, stride, t)}
 
 
@@ -573,7 +573,7 @@ def bench_bwd_elem(args, torch, bs, W):
         t = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": fl_of(rows) / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
                                "kind": "oracle", "cpu_model": host_cpu()[0], "nproc": host_cpu()[1],
-                               "sample": "dq of %d of %d query rows (every %dth), 6*D FLOPs per kept key; %.1f s"
+                               "sample": "dq of %d of %d query rows (one in %d), 6*D FLOPs per kept key; %.1f s"
                                          % (len(rows), total, stride, t)}
     print(json.dumps(res), flush=True)
 
