@@ -55,3 +55,32 @@ def test_full_output_tuned_and_pair_configs(name):
         say("  ", stats)
         del out, lse
     bs.clear_tune_cache()
+
+
+def test_full_output_token_causal_element_mask():
+    """The exact token-causal element-mask workload (B2 H32 S8192 D128, 128x128 blocks:
+    full blocks below the diagonal, one shared lower-triangular bit tile on it) at full
+    size: every output element of the default element config and of every row-pair
+    element config (bench.py times these and keeps the fastest) against the oracle's
+    element-mask forward."""
+    ensure_built()
+    _REF.clear()
+    w = W.ELEM_WORKLOADS["causal_elem_bf16"]
+    q, k, v, _ = W.make_inputs(w)
+    st, pidx, pbits = W.make_elem_mask(w)
+    say("oracle", w.name, "full output on", oracle.max_threads(), "threads ...")
+    t0 = time.perf_counter()
+    ro, rl = oracle.fwd_elem(q, k, v, st, pidx, pbits, w.block_q, w.block_k, w.scale)
+    say("oracle", w.name, "done in %.1f s" % (time.perf_counter() - t0))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    sd, pd, bd = st.cuda(), pidx.cuda(), pbits.cuda()
+    cfgs = [None] + [c.as_tuple() for c in bs.list_configs_elem(torch.bfloat16, w.D, w.block_q, w.block_k)
+                     if c.tile_q == 256]
+    assert len(cfgs) >= 2
+    for cfg in cfgs:
+        say("full output", w.name, cfg if cfg else "(default)")
+        out, lse = bs.fwd_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale, config=cfg)
+        torch.cuda.synchronize()
+        stats = compare(out, lse, ro, rl, "bf16", "%s %s" % (w.name, cfg))
+        say("  ", stats)
+        del out, lse
