@@ -47,6 +47,22 @@ def _bound_rows(q, k, v, mask, bq, bk, scale, rows, ref):
     return 2 * (out + 2.0 ** -9 * np.abs(ref))
 
 
+def _bound_dense_full(q, k, v, scale, ref):
+    """The bounds of _bound_rows for an all-ones mask over every row, one head at a
+    time as matrix products (numpy, fp64)."""
+    B, H, S, D = q.shape
+    qf, kf, vf = (t.to(torch.float64).reshape(B * H, S, D).numpy() for t in (q, k, v))
+    out = np.empty((B * H, S, D))
+    for bh in range(B * H):
+        sc = float(np.float32(scale)) * (qf[bh] @ kf[bh].T)
+        w = np.exp(sc - sc.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        av = np.abs(vf[bh])
+        wav = w @ av
+        out[bh] = 2.0 ** -4 * wav + 2.0 ** -10 * w.max(axis=1, keepdims=True) * av.sum(0) + D * 2.0 ** -24 * wav
+    return 2 * (out.reshape(ref.shape) + 2.0 ** -9 * np.abs(ref))
+
+
 def _check(out, lse, ro, rl, bound, what):
     o = out.float().cpu().double().numpy().reshape(ro.shape)
     l = lse.cpu().double().numpy().reshape(rl.shape)
@@ -121,3 +137,22 @@ def test_fp8_workload_dense_sampled():
     gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
     bound = _bound_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, rows, ro)
     say("  max err", _check(go, gl, ro, rl, bound, "dense fp8"))
+
+
+def test_fp8_workload_dense_full():
+    """The dense shape (B4 H16 S2048 D128, 128x128 blocks) in fp8 at full size, every
+    output element against its bound."""
+    w = W.WORKLOADS["dense_bf16"]
+    ensure_built()
+    q, k, v = _fp8_inputs(w.B, w.H, w.S, w.D, 0)
+    mask = torch.ones(w.B, w.H, w.n_q, w.n_k, dtype=torch.uint8)
+    say("fwd_fp8 workload, full output", tuple(q.shape))
+    out, lse = bs.fwd_fp8(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), w.block_q, w.block_k, w.scale)
+    torch.cuda.synchronize()
+    # The oracle gets the e4m3 values widened to fp32 (exact; its own e4m3 decoding
+    # is pinned byte for byte to the same conversion) so that its inner loop skips
+    # the per-element decode: identical output, about six times sooner.
+    say("oracle, full output on", oracle.max_threads(), "threads ...")
+    ro, rl = oracle.fwd(q.float(), k.float(), v.float(), mask, w.block_q, w.block_k, w.scale)
+    bound = _bound_dense_full(q, k, v, w.scale, ro)
+    say("  max err", _check(out, lse, ro, rl, bound, "dense fp8, full output"))
