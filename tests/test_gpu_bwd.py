@@ -175,6 +175,40 @@ def test_bwd_workload_dense_sampled():
             _check(name, got, r, bb[loc], True, "%s head %d" % (w.name, bh))
 
 
+@pytest.mark.timeout(600)
+def test_bwd_workload_dense_full():
+    """The dense workload (B4 H16 S2048 D128, 128x128 blocks) at full size: every
+    element of dq, dk and dv against the oracle's full backward, each held to its
+    bound (computed one head at a time)."""
+    import time
+    w = W.WORKLOADS["dense_bf16"]
+    ensure_built()
+    q, k, v, mask = W.make_inputs(w)
+    g = torch.Generator().manual_seed(99)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    dev = [t.cuda() for t in (q, k, v, do, mask)]
+    say("bwd workload, full output", w.name, tuple(q.shape))
+    out, lse = bs.fwd(dev[0], dev[1], dev[2], dev[4], w.block_q, w.block_k, w.scale)
+    gq, gk, gv = bs.bwd(dev[0], dev[1], dev[2], out, lse, dev[3], dev[4], w.block_q, w.block_k, w.scale)
+    torch.cuda.synchronize()
+    gq, gk, gv, out = gq.cpu(), gk.cpu(), gv.cpu(), out.cpu()
+    say("oracle bwd, full output on", oracle.max_threads(), "threads ...")
+    t0 = time.perf_counter()
+    rq, rk, rv = oracle.bwd(q, k, v, do, mask, w.block_q, w.block_k, w.scale)
+    say("oracle bwd done in %.1f s" % (time.perf_counter() - t0))
+    full = np.ones((w.S, w.S), dtype=bool)  # every block active
+    assert bool(mask.all())
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for bh in range(w.B * w.H):
+        b_, h_ = divmod(bh, w.H)
+        bnd = _bounds(q[b_, h_].float(), k[b_, h_].float(), v[b_, h_].float(), do[b_, h_].float(),
+                      out[b_, h_].float(), full, w.scale, True)
+        for name, gg, r, bb in (("dq", gq, rq, bnd[0]), ("dk", gk, rk, bnd[1]), ("dv", gv, rv, bnd[2])):
+            e = _check(name, gg[b_, h_], r[b_, h_], bb, True, "%s head %d" % (w.name, bh))
+            worst[name] = max(worst[name], e)
+    say("  max err over all elements", worst)
+
+
 def test_bwd_parts():
     """parts = PREP | DKDV writes dk, dv only (dq untouched) and equals the full
     call; DQ alone on that workspace then gives the full call's dq."""
