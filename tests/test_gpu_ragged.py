@@ -117,6 +117,40 @@ def test_ragged_workload_sampled_rows():
     assert np.all(np.abs(got - ref) <= bound)
 
 
+@pytest.mark.timeout(600)
+def test_ragged_workload_full():
+    """The full-size workload (M 32768, K 2048, N 2048, 8 experts) in the launch
+    configuration bench.py times: every output element against the oracle's full
+    ragged dot, each held to its bound (the magnitude sums for the bound by a
+    float64 matrix product per group of |x| and |w|)."""
+    import time
+    wl = W.RAGGED_WORKLOADS["ragged_bf16"]
+    x, w, sizes = W.make_ragged(wl)
+    ensure_built()
+    say("ragged workload, full output", (wl.M, wl.K, wl.N, wl.G))
+    out = bs.ragged_dot(x.cuda(), w.cuda(), sizes.cuda())
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    say("oracle ragged dot, full output on", oracle.max_threads(), "threads ...")
+    t0 = time.perf_counter()
+    ref = oracle.ragged_dot(x, w, sizes)
+    say("oracle done in %.1f s" % (time.perf_counter() - t0))
+    starts = np.concatenate([[0], np.cumsum(sizes.numpy())])
+    assert starts[-1] == wl.M
+    ax = np.abs(x.double().numpy())
+    worst = 0.0
+    for gi in range(wl.G):
+        r0, r1 = int(starts[gi]), int(starts[gi + 1])
+        mag = ax[r0:r1] @ np.abs(w[gi].double().numpy())
+        bound = wl.K * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref[r0:r1])
+        err = np.abs(got[r0:r1] - ref[r0:r1])
+        assert np.all(err <= bound), ("group", gi, float((err - bound).max()))
+        rel = err[bound > 0] / bound[bound > 0]
+        assert rel.mean() < 0.5, ("group", gi, float(rel.mean()))
+        worst = max(worst, float(err.max()))
+    say("  max err over all elements", worst)
+
+
 def test_ragged_planned_equals_one_shot():
     """bsattn_ragged_plan + bsattn_ragged_dot_planned gives bit for bit the result
     of bsattn_ragged_dot (the same plan and product kernels)."""
