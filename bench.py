@@ -147,6 +147,14 @@ def traffic_from_profiles(workload, cfg, family="fwd"):
     entry = rec.get("by_config", {}).get(",".join(str(x) for x in cfg))
     return entry.get("hbm_bytes_per_launch") if entry else None
 
+def mean_std_min(xs):
+    """(mean, sample standard deviation, minimum) of a list of durations."""
+    n = len(xs)
+    m = sum(xs) / n
+    sd = (sum((x - m) ** 2 for x in xs) / (n - 1)) ** 0.5 if n > 1 else 0.0
+    return m, sd, min(xs)
+
+
 def cold_ms(torch, stream, fn, n):
     """Average duration of fn with L2 and MALL flushed before each call: a 1 GiB
     device buffer is rewritten (untimed) so none of the step's inputs are cached."""
@@ -185,11 +193,17 @@ def cpu_baseline(w, q, k, v, mask, budget_s):
     oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, rows)
     t = time.perf_counter() - t0
     fl = flops_row(rows)
+    # one thread, on the calibration rows: the per-core figure
+    t1 = time.perf_counter()
+    oracle.fwd_rows(q, k, v, mask, w.block_q, w.block_k, w.scale, calib, nthreads=1)
+    t1 = time.perf_counter() - t1
     model, nproc = host_cpu()
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": "%d of %d query rows (one in %d), each over its full key list; %.1f s"
-                      % (len(rows), total, stride, t)}
+                      % (len(rows), total, stride, t),
+            "one_thread": {"value": flops_row(calib) / t1 / 1e12, "unit": "TFLOP/s",
+                           "sample": "%d evenly spaced query rows; %.1f s" % (len(calib), t1)}}
 
 
 def cpu_baseline_elem(w, q, k, v, st, pidx, pbits, kept_per_row, budget_s):
@@ -753,7 +767,7 @@ def bench_fwd(args, torch, bs, W):
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ms, attn_ms = 0.0, 0.0
+    step_l, attn_l = [], []
     for i in range(args.steps):
         flush.fill_(i & 0xff)  # untimed: evicts L2 and MALL
         e0, e1, e2 = ev(), ev(), ev()
@@ -763,12 +777,12 @@ def bench_fwd(args, torch, bs, W):
         attn()
         e2.record(stream)
         torch.cuda.synchronize()
-        step_ms += e0.elapsed_time(e2)
-        attn_ms += e1.elapsed_time(e2)
+        step_l.append(e0.elapsed_time(e2))
+        attn_l.append(e1.elapsed_time(e2))
     wall = time.perf_counter() - t0
     del flush
-    ms_step = step_ms / args.steps
-    ms_attn = attn_ms / args.steps
+    ms_step, std_step, min_step = mean_std_min(step_l)
+    ms_attn, std_attn, min_attn = mean_std_min(attn_l)
     log("bench: cold %.4f ms/step, attention kernel %.4f ms (events); %.4f ms/step incl. flushes (wall)"
         % (ms_step, ms_attn, wall * 1e3 / args.steps))
 
@@ -797,7 +811,8 @@ def bench_fwd(args, torch, bs, W):
                 "frac": achieved / peak, "traffic": traffic,
                 "kernel": ("attn_bf16_pp_kernel" if cfg[0] == 128 and cfg[2] == 8 else "attn_bf16_kernel") if bf16
                           else "attn_f32_kernel",
-                "kernel_ms": ms_attn, "timing": "cold steps (the attention launch of each timed step)",
+                "kernel_ms": ms_attn, "kernel_ms_std": std_attn, "kernel_ms_min": min_attn,
+                "timing": "cold steps (the attention launch of each timed step)",
                 "peak_source": PEAK_SOURCE}
     if traffic:
         roofline["hbm_gbs"] = traffic / (ms_attn * 1e-3) / 1e9
@@ -806,6 +821,7 @@ def bench_fwd(args, torch, bs, W):
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "ms_per_step_std": std_step, "ms_per_step_min": min_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
         "pct_bf16_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,

@@ -207,9 +207,22 @@ static void oracle_row(const problem* p, int64_t bh, int64_t s, double* out_row,
     *lse_out = m + log(l);
 }
 
+/* Thread count of the next parallel region: nthreads if positive, else the
+ * process's default (OMP_NUM_THREADS or all cores), so that one call with an
+ * explicit count does not change the calls after it. */
+static int default_threads(void) {
+#ifdef _OPENMP
+    static int n = 0;
+    if (n == 0) n = omp_get_max_threads();  /* taken before any call sets a count */
+    return n;
+#else
+    return 1;
+#endif
+}
+
 static void set_threads(int nthreads) {
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    omp_set_num_threads(nthreads > 0 ? nthreads : default_threads());
 #else
     (void)nthreads;
 #endif
@@ -662,13 +675,7 @@ int64_t oracle_compact(const uint8_t* mask, int64_t n_rows, int64_t n_k, int32_t
     return nnz;
 }
 
-int oracle_max_threads(void) {
-#ifdef _OPENMP
-    return omp_get_max_threads();
-#else
-    return 1;
-#endif
-}
+int oracle_max_threads(void) { return default_threads(); }
 
 /* Ragged dot: out is double[M][N].  Returns 0 on success, nonzero on a bad
  * argument (nothing written).
