@@ -189,12 +189,32 @@ bool is_auto(const bsattn_tile_config* c) {
     return !c || (!c->tile_q && !c->tile_k && !c->waves && !c->stages);
 }
 
-const Variant* find(int dtype, int D, int block_q, int block_k, const bsattn_tile_config& c) {
-    int n = 0;
-    const Variant* t = variants(dtype, &n);
+const Variant* first_match(const Variant* t, int n, int dtype, int D, int block_q, int block_k,
+                           const bsattn_tile_config& c) {
     for (int i = 0; i < n; ++i)
         if (legal(t[i], dtype, D, block_q, block_k) && matches(t[i], c)) return &t[i];
     return nullptr;
+}
+
+const Variant* find(int dtype, int D, int block_q, int block_k, const bsattn_tile_config& c) {
+    int n = 0;
+    const Variant* t = variants(dtype, &n);
+    return first_match(t, n, dtype, D, block_q, block_k, c);
+}
+
+// Built-in default of table t when nothing is configured or tuned: for bf16 and
+// 128-row mask blocks the row-pair kernel (two mask rows per 8-wave workgroup,
+// each K/V tile loaded once for both; the autotuner's pick on every bf16 workload
+// measured; rows of at most kPairMaxBlocks key blocks), with the key-tile depth
+// in the given order of preference; else the first legal entry of the table.
+const Variant* builtin_default(const Variant* t, int n, int dtype, int D, int block_q, int block_k,
+                               int n_k, int tk_first, int tk_second) {
+    if (dtype == BSATTN_BF16 && block_q == 128 && n_k <= kPairMaxBlocks) {
+        for (int tk : {tk_first, tk_second})
+            if (const Variant* v = first_match(t, n, dtype, D, block_q, block_k, bsattn_tile_config{256, tk, 8, 2}))
+                return v;
+    }
+    return first_match(t, n, dtype, D, block_q, block_k, bsattn_tile_config{0, 0, 0, 0});
 }
 
 // ---- tuning cache -------------------------------------------------------------
@@ -326,8 +346,9 @@ bool env_config(bsattn_tile_config* c, bool* bad) {
 }
 
 // Choose the variant for a call: explicit config, else BSATTN_CONFIG, else the
-// tuning cache, else the first legal entry of the variant table (its order is
-// the built-in preference).
+// tuning cache, else the built-in default (128-key steps first for D = 128, 64-key
+// steps first for D = 64: the tuned picks of the dense, causal and sparse shapes
+// and of the long-context one).
 const Variant* choose(int dtype, int D, int S, int64_t BH, int block_q, int block_k,
                       const bsattn_tile_config* cfg) {
     if (!is_auto(cfg)) return find(dtype, D, block_q, block_k, *cfg);
@@ -339,7 +360,10 @@ const Variant* choose(int dtype, int D, int S, int64_t BH, int block_q, int bloc
         const Variant* v = find(dtype, D, block_q, block_k, c);
         if (v) return v;
     }
-    return find(dtype, D, block_q, block_k, bsattn_tile_config{0, 0, 0, 0});
+    int n = 0;
+    const Variant* t = variants(dtype, &n);
+    return builtin_default(t, n, dtype, D, block_q, block_k, S / block_k, D == 128 ? 128 : 64,
+                           D == 128 ? 64 : 128);
 }
 
 FwdArgs make_args(const void* q, const void* k, const void* v, void* out, float* lse, int H,
@@ -397,15 +421,14 @@ int check_elem_shape(int B, int H, int S, int block_q, int block_k, int n_tiles)
     return check_grid(B, H, S / block_q, S / block_k);
 }
 
-const Variant* find_elem(int dtype, int D, int block_q, int block_k, const bsattn_tile_config* cfg) {
+// Element masks: an explicit config, else the built-in default (64-key row-pair
+// steps first: the pick on the token-causal shape).
+const Variant* find_elem(int dtype, int D, int S, int block_q, int block_k, const bsattn_tile_config* cfg) {
     if (dtype != BSATTN_BF16) return nullptr;
     int n = 0;
     const Variant* t = bf16_elem_variants(&n);
-    const bsattn_tile_config any{0, 0, 0, 0};
-    const bsattn_tile_config& c = is_auto(cfg) ? any : *cfg;
-    for (int i = 0; i < n; ++i)
-        if (legal(t[i], dtype, D, block_q, block_k) && matches(t[i], c)) return &t[i];
-    return nullptr;
+    if (is_auto(cfg)) return builtin_default(t, n, dtype, D, block_q, block_k, S / block_k, 64, 128);
+    return first_match(t, n, dtype, D, block_q, block_k, *cfg);
 }
 
 // The fp8 workspace: the forward plan, then V rearranged per 64-key tile (B*H*S*D
@@ -722,7 +745,7 @@ int bsattn_fwd_planned_elem(const void* q, const void* k, const void* v, void* o
     if (overlap(partial_bits, nbits, out, nt) || overlap(partial_bits, nbits, lse, (size_t)B * H * S * 4) ||
         overlap(partial_bits, nbits, workspace, L.bytes))
         return BSATTN_ERR_ALIAS;
-    const Variant* var = find_elem(dtype, D, block_q, block_k, cfg);
+    const Variant* var = find_elem(dtype, D, S, block_q, block_k, cfg);
     if (!var) return BSATTN_ERR_UNSUPPORTED;
     if (is_pair(*var) && n_k > kPairMaxBlocks) return BSATTN_ERR_UNSUPPORTED;
     FwdArgs a = make_args(q, k, v, out, lse, H, S, block_q, block_k, scale, *var);
@@ -760,7 +783,7 @@ int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* 
         return BSATTN_ERR_ALIGN;
     if (check_ws_alias(workspace, need, q, k, v, out, lse, B, H, S, D, dtype)) return BSATTN_ERR_ALIAS;
     // Resolve the tile config before any device work.
-    const Variant* var = find_elem(dtype, D, block_q, block_k, cfg);
+    const Variant* var = find_elem(dtype, D, S, block_q, block_k, cfg);
     if (!var || (is_pair(*var) && S / block_k > kPairMaxBlocks)) return BSATTN_ERR_UNSUPPORTED;
     rc = bsattn_plan_elem(block_states, partial_index, n_tiles, B, H, S, block_q, block_k, workspace,
                           workspace_bytes, stream);

@@ -132,7 +132,11 @@ int bsattn_workspace_size(int B, int H, int S, int block_q, int block_k, size_t*
  *            S % block_k == 0;   scale  any finite fp32 (negative and 0 allowed);
  *   dtype    BSATTN_BF16 (fp32 accumulation, bf16 out) or BSATTN_F32.
  * The tile config comes from the environment (BSATTN_CONFIG="tq,tk,waves,stages"),
- * else from the autotuner's cache for this shape, else a built-in default. */
+ * else from the autotuner's cache for this shape, else a built-in default: for bf16
+ * with block_q 128 and at most 2048 key blocks per row the row-pair config
+ * (256, 128, 8, 2) for D 128 and (256, 64, 8, 2) for D 64 (the other key-tile
+ * depth if block_k rules the first out), otherwise the first legal entry of
+ * bsattn_list_configs. */
 int bsattn_fwd(const void* q, const void* k, const void* v, const uint8_t* block_mask,
                void* out, float* lse, int B, int H, int S, int D, int block_q, int block_k,
                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
@@ -245,7 +249,9 @@ int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_
  * as for bsattn_fwd (bsattn_workspace_size) and has the plan layout of
  * bsattn_plan, except that a list entry of a partial block is kj | (tile + 1) << 16.
  * Tile configs: bsattn_list_configs_elem (row-pair configs, tile_q 256, need
- * block_q 128 and at most 2048 key blocks per row, as for block masks). */
+ * block_q 128 and at most 2048 key blocks per row, as for block masks); with no
+ * config the row-pair (256, 64, 8, 2) where it is legal, else the first legal
+ * entry of that list. */
 
 /* Plan for an element-level mask: bsattn_plan's lists and dispatch orders over
  * the non-empty blocks, each entry carrying its tile.  Arguments and ownership as

@@ -60,9 +60,10 @@ def test_full_output_tuned_and_pair_configs(name):
 def test_full_output_token_causal_element_mask():
     """The exact token-causal element-mask workload (B2 H32 S8192 D128, 128x128 blocks:
     full blocks below the diagonal, one shared lower-triangular bit tile on it) at full
-    size: every output element of the default element config and of every row-pair
-    element config (bench.py times these and keeps the fastest) against the oracle's
-    element-mask forward."""
+    size: every output element of every row-pair element config (bench.py times these
+    and keeps the fastest) and of the first four-wave one against the oracle's
+    element-mask forward; the call with no config (the built-in default) equals the
+    (256, 64, 8, 2) row pair bit for bit."""
     ensure_built()
     _REF.clear()
     w = W.ELEM_WORKLOADS["causal_elem_bf16"]
@@ -74,13 +75,22 @@ def test_full_output_token_causal_element_mask():
     say("oracle", w.name, "done in %.1f s" % (time.perf_counter() - t0))
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     sd, pd, bd = st.cuda(), pidx.cuda(), pbits.cuda()
-    cfgs = [None] + [c.as_tuple() for c in bs.list_configs_elem(torch.bfloat16, w.D, w.block_q, w.block_k)
-                     if c.tile_q == 256]
-    assert len(cfgs) >= 2
+    listed = [c.as_tuple() for c in bs.list_configs_elem(torch.bfloat16, w.D, w.block_q, w.block_k)]
+    cfgs = [c for c in listed if c[0] == 256] + [c for c in listed if c[0] != 256][:1]
+    assert len(cfgs) >= 3
+    outs = {}
     for cfg in cfgs:
-        say("full output", w.name, cfg if cfg else "(default)")
+        say("full output", w.name, cfg)
         out, lse = bs.fwd_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale, config=cfg)
         torch.cuda.synchronize()
         stats = compare(out, lse, ro, rl, "bf16", "%s %s" % (w.name, cfg))
         say("  ", stats)
-        del out, lse
+        if cfg == (256, 64, 8, 2):
+            outs[cfg] = (out, lse)
+        else:
+            del out, lse
+    # no config: the built-in default, the row pair with 64-key steps
+    out, lse = bs.fwd_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = outs[(256, 64, 8, 2)]
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)

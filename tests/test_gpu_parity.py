@@ -219,3 +219,19 @@ def test_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
+
+
+@pytest.mark.parametrize("D,bk,pair", [(128, 128, (256, 128, 8, 2)), (128, 64, (256, 64, 8, 2)),
+                                       (64, 64, (256, 64, 8, 2)), (64, 128, (256, 64, 8, 2))])
+def test_builtin_default_is_row_pair(D, bk, pair):
+    """With no config, no BSATTN_CONFIG and no tuning entry for the shape, a bf16 call
+    with 128-row mask blocks runs the row-pair kernel: bit for bit the output of the
+    named pair config (shapes chosen to match no tuning entry of other tests)."""
+    ensure_built()
+    B, H, S = 1, 3, 896
+    q, k, v = (t.cuda() for t in rand_qkv(B, H, S, D, torch.bfloat16, seed=D + bk))
+    mask = rand_mask(B, H, S // 128, S // bk, 0.6, seed=D + bk, diag=True).cuda()
+    o1, l1 = bs.fwd(q, k, v, mask, 128, bk, 1.0 / np.sqrt(D))
+    o2, l2 = bs.fwd(q, k, v, mask, 128, bk, 1.0 / np.sqrt(D), config=pair)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
