@@ -605,9 +605,9 @@ static hipError_t launch_bf16(const FwdArgs& a, unsigned grid, hipStream_t strea
     return hipGetLastError();
 }
 
-// {dtype, D, tile_q, tile_k, waves, stages, launcher}.  The table order is the
-// built-in preference when no tuning result exists (the two-group and row-pair
-// kernels come last: they win only on particular shapes and masks).  NQ = 2 (64 query rows per
+// {dtype, D, tile_q, tile_k, waves, stages, launcher}.  With no tuning result the
+// host prefers the row-pair entries (for 128-row mask blocks), else takes the
+// first legal entry in table order.  NQ = 2 (64 query rows per
 // wave, each K/V fragment read from LDS feeding two MFMAs) runs one wave per
 // SIMD; NQ = 1 runs two to five (OCC): with D = 64 the softmax is as much VALU
 // work as with D = 128 against half the MFMA work, and four or five waves per
