@@ -50,3 +50,21 @@ def test_peak_from_rocminfo():
     assert bench.parse_rocminfo("no agents here") is None
     cu, mhz, _ = bench.parse_rocminfo(SAMPLE_ROCMINFO)
     assert abs(cu * mhz * 1e6 * bench.FLOP_PER_CLK_CU["bf16"] / 1e12 - 2516.58) < 0.01
+
+
+def test_cpu_baseline_fields():
+    """The oracle timed beside the bench line (tiny workload, short budget): its
+    rate, the threads it used, the host, and the one-thread per-core figure; the
+    one-thread run leaves the oracle's default thread count as it was."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle
+    import workloads as W
+    w = W.WORKLOADS["tiny_f32"]
+    q, k, v, mask = W.make_inputs(w)
+    n0 = oracle.max_threads()
+    cb = bench.cpu_baseline(w, q, k, v, mask, 0.2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert cb["cores"] == n0 == oracle.max_threads()
+    assert cb["nproc"] >= 1 and "query rows" in cb["sample"]
+    assert cb["one_thread"]["value"] > 0 and cb["one_thread"]["unit"] == "TFLOP/s"

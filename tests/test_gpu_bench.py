@@ -50,6 +50,9 @@ def test_bench_line(workload, cfg):
     assert rf["kernel_ms"] <= res["ms_per_step"] * (1 + 1e-6)
     assert res["warm"]["ms_per_step"] > 0 and res["warm"]["kernel_ms"] > 0
     assert "rocminfo" in rf["peak_source"] or "published" in rf["peak_source"]
+    # spread of the timed steps: min <= mean, std >= 0
+    assert 0 < res["ms_per_step_min"] <= res["ms_per_step"] * (1 + 1e-9) and res["ms_per_step_std"] >= 0
+    assert 0 < rf["kernel_ms_min"] <= rf["kernel_ms"] * (1 + 1e-9) and rf["kernel_ms_std"] >= 0
 
 
 def test_bench_default_workload_is_causal():
