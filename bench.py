@@ -593,16 +593,26 @@ def bench_bwd_elem(args, torch, bs, W):
 
 
 def bench_fp8(args, torch, bs, W):
-    """One step = bsattn_fwd_fp8 on the workload's shape and mask with e4m3 inputs."""
-    w = W.WORKLOADS[args.workload]
+    """One step = bsattn_fwd_fp8 on the workload's shape and mask with e4m3 inputs
+    (bsattn_fwd_fp8_elem for an element-mask workload, counted on kept elements)."""
+    elem = args.workload in W.ELEM_WORKLOADS
+    w = W.ELEM_WORKLOADS[args.workload] if elem else W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("bench: generating %s inputs (fp8)" % w.name)
     q, k, v, mask = W.make_inputs(w)
     q8, k8, v8 = (t.float().to(torch.float8_e4m3fn) for t in (q, k, v))
-    qd, kd, vd, md = (t.to(dev) for t in (q8, k8, v8, mask))
-    nnz = int(mask.ne(0).sum())
-    flops = 4.0 * w.D * nnz * w.block_q * w.block_k
+    qd, kd, vd = (t.to(dev) for t in (q8, k8, v8))
+    if elem:
+        st, pidx, pbits = W.make_elem_mask(w)
+        sd, pd, bd = st.to(dev), pidx.to(dev), pbits.to(dev)
+        kept = W.kept_elements(st, pidx, pbits, w.block_q, w.block_k)
+        nnz = int(st.ne(0).sum())
+        flops = 4.0 * w.D * kept
+    else:
+        md = mask.to(dev)
+        nnz = int(mask.ne(0).sum())
+        flops = 4.0 * w.D * nnz * w.block_q * w.block_k
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     ws = torch.empty(bs.fp8_workspace_size(w.B, w.H, w.S, w.D, w.block_q, w.block_k), dtype=torch.uint8,
@@ -618,14 +628,22 @@ def bench_fp8(args, torch, bs, W):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    step = lambda: bs.fwd_fp8(qd, kd, vd, md, w.block_q, w.block_k, w.scale, out=out, lse=lse, workspace=ws)
+    if elem:
+        step = lambda: bs.fwd_fp8_elem(qd, kd, vd, sd, pd, bd, w.block_q, w.block_k, w.scale, out=out, lse=lse,
+                                       workspace=ws)
+    else:
+        step = lambda: bs.fwd_fp8(qd, kd, vd, md, w.block_q, w.block_k, w.scale, out=out, lse=lse, workspace=ws)
     log("bench: warmup %d, timed %d steps" % (args.warmup, args.steps))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ms_step = timed(step, args.steps)
     ms_cold = cold_ms(torch, stream, step, min(args.steps, 20))
-    planned = lambda: bs.fwd_fp8_planned(qd, kd, vd, ws, w.block_q, w.block_k, w.scale, out=out, lse=lse)
+    if elem:
+        planned = lambda: bs.fwd_fp8_planned_elem(qd, kd, vd, bd, ws, w.block_q, w.block_k, w.scale, out=out,
+                                                  lse=lse)
+    else:
+        planned = lambda: bs.fwd_fp8_planned(qd, kd, vd, ws, w.block_q, w.block_k, w.scale, out=out, lse=lse)
     for _ in range(3):
         planned()
     torch.cuda.synchronize()
@@ -633,7 +651,8 @@ def bench_fp8(args, torch, bs, W):
     achieved = flops / (ms_attn * 1e-3) / 1e12
     value = flops / (ms_step * 1e-3) / 1e12
     res = {
-        "metric": "block-sparse attn fwd fp8 effective TFLOP/s (active blocks) + % fp8 MFMA peak",
+        "metric": "block-sparse attn fwd fp8 effective TFLOP/s (%s) + %% fp8 MFMA peak"
+                  % ("kept elements" if elem else "active blocks"),
         "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -649,9 +668,16 @@ def bench_fp8(args, torch, bs, W):
         "cold": {"ms_per_step": ms_cold, "value": flops / (ms_cold * 1e-3) / 1e12,
                  "note": "L2 and MALL flushed (1 GiB rewrite, untimed) before each step"},
     }
+    if elem:
+        res["config"]["kept_elements"] = kept
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample (fp8 inputs)")
-        res["cpu_baseline"] = cpu_baseline(w, q8, k8, v8, mask, args.cpu_budget)
+        if elem:
+            assert w.mask_kind == "token_causal"
+            kept_row = lambda r: (r % w.S) + 1  # a token-causal row keeps its s + 1 first keys
+            res["cpu_baseline"] = cpu_baseline_elem(w, q8, k8, v8, st, pidx, pbits, kept_row, args.cpu_budget)
+        else:
+            res["cpu_baseline"] = cpu_baseline(w, q8, k8, v8, mask, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 
@@ -702,6 +728,8 @@ def main():
     if args.workload in W.ELEM_WORKLOADS:
         if args.backward:
             bench_bwd_elem(args, torch, bs, W)
+        elif args.fp8:
+            bench_fp8(args, torch, bs, W)
         else:
             bench_elem(args, torch, bs, W)
         return

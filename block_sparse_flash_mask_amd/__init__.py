@@ -98,6 +98,10 @@ def library():
         "bsattn_fp8_workspace_size": ([i32, i32, i32, i32, i32, i32, szp], i32),
         "bsattn_fwd_fp8": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, sz, p], i32),
         "bsattn_fwd_fp8_planned": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, sz, p], i32),
+        "bsattn_fwd_fp8_elem": ([p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32, f32, p, sz, p],
+                                i32),
+        "bsattn_fwd_fp8_planned_elem": ([p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, i32, p, sz, p],
+                                        i32),
         "bsattn_bwd_workspace_size": ([i32, i32, i32, i32, i32, szp], i32),
         "bsattn_bwd": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p, p, p, i32, p, sz,
                         p], i32),
@@ -615,6 +619,52 @@ def fwd_fp8_planned(q, k, v, fp8_ws, block_q, block_k, scale=None, *, out=None, 
     _check(library().bsattn_fwd_fp8_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S, D, block_q,
                                             block_k, float(scale), _ptr(fp8_ws),
                                             fp8_ws.numel() * fp8_ws.element_size(), _stream(stream)))
+    return out, lse
+
+
+def fwd_fp8_elem(q, k, v, block_states, partial_index, partial_bits, block_q, block_k, scale=None, *,
+                 out=None, lse=None, workspace=None, stream=None):
+    """Forward with fp8 e4m3 q, k, v and an element-level mask (bsattn_fwd_fp8_elem);
+    bf16 out.  Returns (out, lse)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("q, k, v must be torch.float8_e4m3fn")
+    n_tiles = _elem_tensors(block_states, partial_index, partial_bits, q.device,
+                            _mask_shape(q.shape, block_q, block_k))
+    _check_bits(partial_bits, block_q, block_k)
+    if scale is None:
+        scale = default_scale(D)
+    out, lse = _outputs(q, out, lse, torch.bfloat16)
+    ws = _workspace(fp8_workspace_size(B, H, S, D, block_q, block_k), q.device, workspace)
+    _keep_alive(stream, out, lse, ws)
+    _check(library().bsattn_fwd_fp8_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(block_states), _ptr(partial_index),
+                                         _ptr(partial_bits), n_tiles, _ptr(out), _ptr(lse), B, H, S, D,
+                                         block_q, block_k, float(scale), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse
+
+
+def fwd_fp8_planned_elem(q, k, v, partial_bits, fp8_ws, block_q, block_k, scale=None, *, out=None, lse=None,
+                         stream=None):
+    """bsattn_fwd_fp8_planned_elem on a workspace of fp8_workspace_size() bytes whose
+    first part holds a plan written by plan_elem(..., workspace=fp8_ws)."""
+    B, H, S, D = _check_inputs(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("q, k, v must be torch.float8_e4m3fn")
+    _mask_shape(q.shape, block_q, block_k)
+    _check_tensor(partial_bits, "partial_bits", q.device, (torch.int32, torch.uint32))
+    if partial_bits.dim() != 3:
+        raise ValueError("partial_bits must be [n_tiles, block_q, block_k / 32]")
+    _check_bits(partial_bits, block_q, block_k)
+    _workspace(fp8_workspace_size(B, H, S, D, block_q, block_k), q.device, fp8_ws, "fp8_ws")
+    if scale is None:
+        scale = default_scale(D)
+    out, lse = _outputs(q, out, lse, torch.bfloat16)
+    _keep_alive(stream, out, lse)
+    _check(library().bsattn_fwd_fp8_planned_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, S, D,
+                                                 block_q, block_k, float(scale), _ptr(partial_bits),
+                                                 partial_bits.shape[0], _ptr(fp8_ws),
+                                                 fp8_ws.numel() * fp8_ws.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -446,9 +446,9 @@ Fp8Layout fp8_layout(int64_t BH, int S, int D, int n_q, int n_k) {
     return L;
 }
 
-const Variant* fp8_find(int D, int block_q) {
+const Variant* fp8_find(int D, int block_q, bool elem = false) {
     int n = 0;
-    const Variant* t = fp8_variants(&n);
+    const Variant* t = elem ? fp8_elem_variants(&n) : fp8_variants(&n);
     for (int i = 0; i < n; ++i)
         if (t[i].D == D && t[i].tile_q == block_q) return &t[i];
     return nullptr;
@@ -584,6 +584,7 @@ int bsattn_plan(const uint8_t* block_mask, int B, int H, int S, int block_q, int
     const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
     if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4)) return BSATTN_ERR_ALIGN;
+    if (overlap(workspace, L.bytes, block_mask, (size_t)L.R * n_k)) return BSATTN_ERR_ALIAS;
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     int32_t* counts = (int32_t*)ws;
@@ -713,6 +714,9 @@ int bsattn_plan_elem(const uint8_t* block_states, const int32_t* partial_index, 
     const PlanLayout L = plan_layout((int64_t)B * H, n_q, n_k);
     if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
     if (!is_aligned(workspace, 4) || !is_aligned(partial_index, 4)) return BSATTN_ERR_ALIGN;
+    if (overlap(workspace, L.bytes, block_states, (size_t)L.R * n_k) ||
+        overlap(workspace, L.bytes, partial_index, (size_t)L.R * n_k * 4))
+        return BSATTN_ERR_ALIAS;
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     int32_t* counts = (int32_t*)ws;
@@ -782,6 +786,13 @@ int bsattn_fwd_elem(const void* q, const void* k, const void* v, const uint8_t* 
     if (!is_aligned(workspace, 4) || !is_aligned(partial_bits, 4) || !is_aligned(partial_index, 4))
         return BSATTN_ERR_ALIGN;
     if (check_ws_alias(workspace, need, q, k, v, out, lse, B, H, S, D, dtype)) return BSATTN_ERR_ALIAS;
+    {
+        const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
+        const size_t nt = (size_t)B * H * S * D * (dtype == BSATTN_F32 ? 4 : 2);
+        if (overlap(partial_bits, nbits, out, nt) || overlap(partial_bits, nbits, lse, (size_t)B * H * S * 4) ||
+            overlap(partial_bits, nbits, workspace, need))
+            return BSATTN_ERR_ALIAS;
+    }
     // Resolve the tile config before any device work.
     const Variant* var = find_elem(dtype, D, S, block_q, block_k, cfg);
     if (!var || (is_pair(*var) && S / block_k > kPairMaxBlocks)) return BSATTN_ERR_UNSUPPORTED;
@@ -951,6 +962,79 @@ int bsattn_fwd_fp8(const void* q, const void* k, const void* v, const uint8_t* b
     if (rc) return rc;
     return bsattn_fwd_fp8_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
                                   workspace_bytes, stream);
+}
+
+// The fp8 forward with an element-level mask: the plan of bsattn_plan_elem in the
+// first part of the fp8 workspace, partial_bits as for bsattn_fwd_planned_elem.
+int bsattn_fwd_fp8_planned_elem(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                                int H, int S, int D, int block_q, int block_k, float scale,
+                                const uint32_t* partial_bits, int n_tiles, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!workspace || !partial_bits) return BSATTN_ERR_NULL;
+    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    if (rc) return rc;
+    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    const int n_q = S / block_q, n_k = S / block_k;
+    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, n_q, n_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16) || !is_aligned(partial_bits, 4)) return BSATTN_ERR_ALIGN;
+    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
+    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
+    const void* ts[] = {q, k, v, out, lse};
+    const size_t tn[] = {n8, n8, n8, no, nl};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    if (overlap(partial_bits, nbits, out, no) || overlap(partial_bits, nbits, lse, nl) ||
+        overlap(partial_bits, nbits, workspace, L.bytes))
+        return BSATTN_ERR_ALIAS;
+    const Variant* var = fp8_find(D, block_q, true);
+    if (!var) return BSATTN_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const hipError_t e = launch_fp8_vt(v, ws + L.vt, (int64_t)B * H * S / 64, D, st);
+    if (e != hipSuccess) return hip_fail(e);
+    FwdArgs a = make_args(q, k, ws + L.vt, out, lse, H, S, block_q, block_k, scale, *var);
+    a.qsign = a.qsign ? 0x80808080u : 0u;  // the sign bit of each of four e4m3 bytes
+    a.counts = (const int32_t*)ws;
+    a.list = (const int32_t*)(ws + L.plan.lists);
+    a.ell_stride = n_k;
+    a.order = (const int32_t*)(ws + L.plan.order);
+    a.nrows = (int)L.plan.R;
+    a.chunk = (int)L.plan.chunk;
+    a.pbits = partial_bits;
+    a.n_tiles = n_tiles;
+    return run_attention(a, *var, st);
+}
+
+int bsattn_fwd_fp8_elem(const void* q, const void* k, const void* v, const uint8_t* block_states,
+                        const int32_t* partial_index, const uint32_t* partial_bits, int n_tiles, void* out,
+                        float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_states || !partial_index || !partial_bits || !workspace) return BSATTN_ERR_NULL;
+    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    if (rc) return rc;
+    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+    if (rc) return rc;
+    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k);
+    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16) || !is_aligned(partial_bits, 4) || !is_aligned(partial_index, 4))
+        return BSATTN_ERR_ALIGN;
+    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
+    const void* ts[] = {q, k, v, out, lse};
+    const size_t tn[] = {n8, n8, n8, no, nl};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
+    if (overlap(partial_bits, nbits, out, no) || overlap(partial_bits, nbits, lse, nl) ||
+        overlap(partial_bits, nbits, workspace, L.bytes))
+        return BSATTN_ERR_ALIAS;
+    if (!fp8_find(D, block_q, true)) return BSATTN_ERR_UNSUPPORTED;
+    rc = bsattn_plan_elem(block_states, partial_index, n_tiles, B, H, S, block_q, block_k, workspace,
+                          workspace_bytes, stream);
+    if (rc) return rc;
+    return bsattn_fwd_fp8_planned_elem(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, partial_bits,
+                                       n_tiles, workspace, workspace_bytes, stream);
 }
 
 // ---- backward ------------------------------------------------------------------

@@ -22,6 +22,13 @@
 //                    pre-pass (fp8_vt_kernel) writes V per 64-key tile as
 //                    vt[d][64] with byte 32h + 16t + 4g + u = V[32t + 8g + 4h + u][d],
 //                    so each lane reads 32 contiguous bytes.
+// Element-level masks (ELEM = 1): the list entry of a partial block carries its bit
+// tile (kj | (tile + 1) << 16, as in the bf16 kernel); after the S MFMAs each lane
+// reads one 32-bit word of its query row per 32-key subtile and sets to -inf the
+// scores whose bit is clear (register 4g + u of subtile t is key 8g + 4h + u, so
+// the word is shifted by 4h and bit 8g + u tested).  A row may have no kept score
+// yet (m = -inf): the exponent then uses m = 0 and the rescale factor is 0, so
+// dropped scores give exact zeros; a row that keeps nothing ends with 0 and -inf.
 // LDS: a K tile is (D/64) * 2 blocks of 2 KiB, block (t, m) holding lane l's
 // bytes K[32t + l%32][64m + 32(l/32) + 16p .. +15] in plane p at p*1024 + l*16; a
 // V^T tile is D/32 blocks, block md holding vt[32md + l%32][32(l/32) + 16p ..]
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__
     }
 }
 
-template <int D, int WAVES, int OCC>
+template <int D, int WAVES, int OCC, int ELEM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void attn_fp8_kernel(
     FwdArgs a) {
     constexpr int MQ = D / 64;       // fp8 MFMAs over d per 32x32 score tile
@@ -151,7 +158,27 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
 
-    auto compute = [&](const uint8_t* kbuf, const uint8_t* vbuf) {
+    // Element masks: the kept bits of this lane's query row for step st's 64 keys
+    // (entry e of the step's key block), applied to S.
+    auto apply_tile = [&](f32x16* s, int e, int st) {
+        int tile = (e >> 16) - 1;  // -1: full block
+        if (tile < 0) return;
+        tile = tile < a.n_tiles ? tile : a.n_tiles - 1;  // (a plan never holds more)
+        const int qr = q_row - qi * a.block_q;
+        const int ko = (st & ((1 << sh) - 1)) * kFp8TK;
+        const uint32_t* wrow = a.pbits + ((size_t)tile * a.block_q + qr) * (a.block_k >> 5) + (ko >> 5);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t w = wrow[t] >> (4 * h);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (!((w >> (8 * g + u)) & 1u)) s[t][4 * g + u] = -INFINITY;
+        }
+    };
+
+    auto compute = [&](const uint8_t* kbuf, const uint8_t* vbuf, int e, int st) {
         f32x16 s[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -159,6 +186,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 #pragma unroll
             for (int m = 0; m < MQ; ++m) s[t] = mfma_fp8(lds32(kbuf + (t * MQ + m) * 2048, lane), qf[m], s[t]);
         }
+        if constexpr (ELEM) apply_tile(s, e, st);
         // row max over the 64 keys and the lazy move of the reference max
         float tmp[32];
 #pragma unroll
@@ -169,13 +197,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         const float mx = max_halves_nan(max_tree3<32>(tmp)) * a.c;
         if (__ballot(mx > m_run + 8.0f) != 0) {
             const float m_new = fmax_nan(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
+            // (element masks: a row may still have no kept score, m = -inf)
+            const float alpha = (ELEM && m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
             m_run = m_new;
         }
         // P = 2^(c S - m) (<= 2^8, inside e4m3's range); fp32 row sums; P^T in e4m3
+        // (element masks: with no kept score yet every S is -inf; use m = 0)
+        const float m_use = (ELEM && m_run == -INFINITY) ? 0.f : m_run;
         i32x8 pb;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -184,7 +215,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
                 float e[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    e[u] = fast_exp2(__builtin_fmaf(s[t][4 * g + u], a.c, -m_run));
+                    e[u] = fast_exp2(__builtin_fmaf(s[t][4 * g + u], a.c, -m_use));
                     tmp[16 * t + 4 * g + u] = e[u];
                 }
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
@@ -202,23 +233,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     };
     auto key0_of = [&](int kj_raw, int t) -> int {
         int kj = wave_uniform(kj_raw);
+        if constexpr (ELEM) kj &= 0xffff;  // element masks: tile + 1 in bits 16..30
         kj = kj < 0 ? 0 : (kj >= a.n_k ? a.n_k - 1 : kj);
         return kj * a.block_k + (t & ((1 << sh) - 1)) * kFp8TK;
     };
+    // e_next: the list entry of the step whose DMA was issued last (element masks
+    // read its bit tile when that step computes).
+    int e_next = 0;
     auto step = [&](int t, int& pre, uint8_t* kfill, uint8_t* vfill, const uint8_t* kcur, const uint8_t* vcur) {
         __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of step t
         __syncthreads();                     // everyone's landed; step t-1 fully read
+        const int e_cur = e_next;
         if (t + 1 < n_steps) {
             const int kn = key0_of(pre, t + 1);
+            if constexpr (ELEM) e_next = wave_uniform(pre);
             pre = entry(t + 2);
             issue(kn, kfill, vfill);
         }
-        compute(kcur, vcur);
+        compute(kcur, vcur, e_cur, t);
     };
 
     if (n_steps > 0) {
         int pre = entry(1);
-        issue(key0_of(entry(0), 0), k0s, v0s);
+        e_next = wave_uniform(entry(0));
+        issue(key0_of(e_next, 0), k0s, v0s);
         for (int t = 0; t < n_steps; t += 2) {
             step(t, pre, k1s, v1s, k0s, v0s);
             if (t + 1 < n_steps) step(t + 1, pre, k0s, v0s, k1s, v1s);
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
 
     // Epilogue: O / l in bf16, lse = ln2 (m + log2 l); a row with no key block
     // gets 0 and -inf.
-    const bool any = n_steps > 0;
+    const bool any = ELEM ? m_run != -INFINITY : n_steps > 0;
     const float l_tot = sum_halves(l_run);
     const float inv = any ? 1.0f / l_tot : 0.0f;
     uint16_t* og = (uint16_t*)a.out + (size_t)bh * a.S * D + (size_t)q_row * D;
@@ -253,9 +291,9 @@ hipError_t launch_fp8_vt(const void* v, void* vt, int64_t tiles, int D, hipStrea
     return hipGetLastError();
 }
 
-template <int D, int W, int OCC>
+template <int D, int W, int OCC, int ELEM = 0>
 static hipError_t launch_fp8(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fp8_kernel<D, W, OCC>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_fp8_kernel<D, W, OCC, ELEM>), dim3(grid), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -268,9 +306,20 @@ static const Variant kFp8Variants[] = {
     {2, 64, 128, 64, 4, 2, &launch_fp8<64, 4, 4>},   {2, 64, 64, 64, 2, 2, &launch_fp8<64, 2, 3>},
 };
 
+// The same four with element-level masks.
+static const Variant kFp8ElemVariants[] = {
+    {2, 128, 128, 64, 4, 2, &launch_fp8<128, 4, 3, 1>}, {2, 128, 64, 64, 2, 2, &launch_fp8<128, 2, 3, 1>},
+    {2, 64, 128, 64, 4, 2, &launch_fp8<64, 4, 4, 1>},   {2, 64, 64, 64, 2, 2, &launch_fp8<64, 2, 3, 1>},
+};
+
 const Variant* fp8_variants(int* n) {
     *n = (int)(sizeof(kFp8Variants) / sizeof(kFp8Variants[0]));
     return kFp8Variants;
+}
+
+const Variant* fp8_elem_variants(int* n) {
+    *n = (int)(sizeof(kFp8ElemVariants) / sizeof(kFp8ElemVariants[0]));
+    return kFp8ElemVariants;
 }
 
 }  // namespace bsattn

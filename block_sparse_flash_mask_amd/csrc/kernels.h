@@ -79,13 +79,15 @@ hipError_t launch_bf16_pp(const FwdArgs& a, unsigned grid, hipStream_t stream);
 
 // Tables of the built variants (attn_bf16.hip, attn_f32.hip).
 const Variant* bf16_variants(int* n);
-// The bf16 variants built for element-level masks (plain schedule, no row pairs).
+// The bf16 variants built for element-level masks (plain schedule, row pairs included).
 const Variant* bf16_elem_variants(int* n);
 const Variant* f32_variants(int* n);
 // fp8 forward (attn_fp8.hip): dtype 2, tile_k 64, one config per (D, tile_q); and
 // the pre-pass that rearranges V per 64-key tile for its P V product (tiles =
 // B*H*S/64).
 const Variant* fp8_variants(int* n);
+// The same fp8 configs with element-level masks.
+const Variant* fp8_elem_variants(int* n);
 hipError_t launch_fp8_vt(const void* v, void* vt, int64_t tiles, int D, hipStream_t stream);
 
 }  // namespace bsattn

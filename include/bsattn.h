@@ -55,7 +55,8 @@ typedef enum {
     BSATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     BSATTN_ERR_SCALE = 6,       /* scale is NaN or infinite */
     BSATTN_ERR_ALIAS = 7,       /* out or lse overlaps q, k or v (or each other), or
-                                   a forward workspace overlaps any of them */
+                                   a forward workspace overlaps any of them or the
+                                   mask arrays its plan reads */
     BSATTN_ERR_HIP = 8,         /* a HIP runtime call failed */
     BSATTN_ERR_IO = 9           /* a tuning-cache file could not be read or written */
 } bsattn_status;
@@ -308,6 +309,26 @@ int bsattn_fwd_fp8(const void* q, const void* k, const void* v, const uint8_t* b
 int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                            int H, int S, int D, int block_q, int block_k, float scale, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* The fp8 forward with an element-level mask: block_states, partial_index,
+ * partial_bits and n_tiles as for bsattn_fwd_elem ("Writing Pallas Kernels for
+ * JAX", section "Writing the Kernel Logic": the mask tile is element-level, dropped
+ * scores are -inf), q, k, v, out, lse, the workspace (bsattn_fp8_workspace_size
+ * bytes) and the precision as for bsattn_fwd_fp8.  A query row with no kept element
+ * gets out = 0 and lse = -inf.  Checks: those of bsattn_fwd_fp8 and of
+ * bsattn_fwd_elem (n_tiles in 1 .. 32767 and S / block_k <= 65536, else
+ * BSATTN_ERR_SHAPE; partial_bits and partial_index 4-byte aligned; partial_bits
+ * overlapping out, lse or the workspace gives BSATTN_ERR_ALIAS), all before any
+ * device work.  bsattn_fwd_fp8_planned_elem runs on a plan that bsattn_plan_elem
+ * wrote into the first part of that workspace (same mask, shape and n_tiles). */
+int bsattn_fwd_fp8_elem(const void* q, const void* k, const void* v, const uint8_t* block_states,
+                        const int32_t* partial_index, const uint32_t* partial_bits, int n_tiles, void* out,
+                        float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int bsattn_fwd_fp8_planned_elem(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                                int H, int S, int D, int block_q, int block_k, float scale,
+                                const uint32_t* partial_bits, int n_tiles, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ---- Ragged dot -------------------------------------------------------------------
  * "Pallas-Triton kernels and kernel auto-tuning", section "Ragged Dot (Group Matrix

@@ -150,6 +150,8 @@ def test_plan_argument_checks(lib):
     assert call(4, 32) == UNSUP and call(5, 256) == UNSUP
     assert call(7, 64) == WS
     assert call(6, p(3 * A + 2)) == ALIGN
+    # the workspace the plan writes overlapping the mask it reads (8 mask bytes at A)
+    assert call(6, p(A - 256)) == ALIAS and call(6, p(A + 4)) == ALIAS
 
 
 def test_planned_argument_checks(lib):
@@ -306,6 +308,11 @@ def test_elem_argument_checks(lib):
     assert callh(9, 16) == WS
     okh[9] = 4096
     assert callh(1, p(8 * A + 2)) == ALIGN and callh(8, p(13 * A + 2)) == ALIGN
+    # the plan's workspace over the states or the tile index it reads
+    assert callh(8, p(7 * A + 4)) == ALIAS and callh(8, p(8 * A - 64)) == ALIAS
+    # one-shot forward: bit tiles over the workspace are refused before the plan runs
+    ok[18] = 4096
+    assert call(5, p(13 * A + 256)) == ALIAS
 
 
 def test_elem_configs(lib):
@@ -459,6 +466,39 @@ def test_fp8_argument_checks(lib):
     okp = ok[:3] + ok[4:]
     assert g(*(okp[:12] + [p(13 * A), 64, None])) == WS
     assert g(*(okp[:12] + [None, wsn, None])) == NULL
+
+    # element masks: q k v states pidx bits n_tiles out lse B H S D bq bk scale ws wsb stream
+    fe = lib.bsattn_fwd_fp8_elem
+    oke = [p(A), p(3 * A), p(5 * A), p(7 * A), p(8 * A), p(15 * A), 2, p(9 * A), p(11 * A),
+           B, H, S, D, bq, bk, 0.1, p(13 * A), wsn, None]
+
+    def calle(i, x):
+        a = list(oke)
+        a[i] = x
+        return fe(*a)
+    for i in (0, 3, 4, 5, 7, 16):
+        assert calle(i, None) == NULL, i
+    assert calle(6, 0) == SHAPE and calle(6, 40000) == SHAPE and calle(11, 250) == SHAPE
+    assert calle(12, 96) == UNSUP and calle(14, 32) == UNSUP
+    assert calle(17, wsn - 1) == WS
+    assert calle(5, p(15 * A + 2)) == ALIGN and calle(4, p(8 * A + 1)) == ALIGN
+    assert calle(15, float("inf")) == SCALE
+    assert calle(5, p(9 * A + 64)) == ALIAS              # bit tiles over out
+    assert calle(5, p(13 * A + 512)) == ALIAS            # ... over the workspace
+    assert calle(16, p(5 * A + 64)) == ALIAS             # workspace over v
+    ge = lib.bsattn_fwd_fp8_planned_elem
+    # q k v out lse B H S D bq bk scale bits n_tiles ws wsb stream
+    okq = [p(A), p(3 * A), p(5 * A), p(9 * A), p(11 * A), B, H, S, D, bq, bk, 0.1, p(15 * A), 2,
+           p(13 * A), wsn, None]
+
+    def callq(i, x):
+        a = list(okq)
+        a[i] = x
+        return ge(*a)
+    assert callq(12, None) == NULL and callq(14, None) == NULL
+    assert callq(13, 0) == SHAPE and callq(15, 64) == WS
+    assert callq(12, p(15 * A + 1)) == ALIGN
+    assert callq(12, p(11 * A + 8)) == ALIAS and callq(12, p(13 * A + 128)) == ALIAS
 
 
 def test_c_program_builds(lib):
