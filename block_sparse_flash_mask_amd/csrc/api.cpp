@@ -424,9 +424,9 @@ int check_elem_shape(int B, int H, int S, int block_q, int block_k, int n_tiles)
 // Element masks: an explicit config, else the built-in default (64-key row-pair
 // steps first: the pick on the token-causal shape).
 const Variant* find_elem(int dtype, int D, int S, int block_q, int block_k, const bsattn_tile_config* cfg) {
-    if (dtype != BSATTN_BF16) return nullptr;
+    if (dtype != BSATTN_BF16 && dtype != BSATTN_F32) return nullptr;
     int n = 0;
-    const Variant* t = bf16_elem_variants(&n);
+    const Variant* t = dtype == BSATTN_BF16 ? bf16_elem_variants(&n) : f32_elem_variants(&n);
     if (is_auto(cfg)) return builtin_default(t, n, dtype, D, block_q, block_k, S / block_k, 64, 128);
     return first_match(t, n, dtype, D, block_q, block_k, *cfg);
 }
@@ -807,16 +807,12 @@ int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_
                              int cap, int* n) {
     if (!n) return BSATTN_ERR_NULL;
     if (dtype != BSATTN_F32 && dtype != BSATTN_BF16) return BSATTN_ERR_UNSUPPORTED;
-    int cnt = 0;
-    if (dtype == BSATTN_BF16) {
-        int nv = 0;
-        const Variant* t = bf16_elem_variants(&nv);
-        for (int i = 0; i < nv; ++i) {
-            if (!legal(t[i], dtype, D, block_q, block_k)) continue;
-            if (cfgs && cnt < cap)
-                cfgs[cnt] = bsattn_tile_config{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
-            ++cnt;
-        }
+    int cnt = 0, nv = 0;
+    const Variant* t = dtype == BSATTN_BF16 ? bf16_elem_variants(&nv) : f32_elem_variants(&nv);
+    for (int i = 0; i < nv; ++i) {
+        if (!legal(t[i], dtype, D, block_q, block_k)) continue;
+        if (cfgs && cnt < cap) cfgs[cnt] = bsattn_tile_config{t[i].tile_q, t[i].tile_k, t[i].waves, t[i].stages};
+        ++cnt;
     }
     *n = cnt;
     return BSATTN_OK;

@@ -12,12 +12,18 @@
 //   * after the S^T MFMA, register i of lane (h, q) holds key
 //     8*(i/4) + 4*h + i%4 of the 32-key tile, and the P V step for that register
 //     reads V[that key][d] from a row-major V tile: no transpose is needed.
+// Element-level masks (ELEM = 1): the list entry of a partial block carries its bit
+// tile (kj | (tile + 1) << 16); after the S^T MFMAs a lane reads one 32-bit word of
+// its query row per 32-key tile and sets to -inf the scores whose bit is clear (key
+// 8*(i/4) + 4*h + i%4 is bit 8*(i/4) + i%4 of the word shifted by 4*h).  While a
+// row has no kept score (m = -inf) the exponent uses m = 0 and the rescale factor
+// is 0, so dropped scores give exact zeros; a row that keeps nothing gets 0, -inf.
 #include "common.h"
 #include "kernels.h"
 
 namespace bsattn {
 
-template <int D, int WAVES, int TK>
+template <int D, int WAVES, int TK, int ELEM>
 __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
     constexpr int TQ = 32 * WAVES;
     constexpr int NT = 64 * WAVES;
@@ -73,7 +79,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
 
     for (int t = 0; t < n_steps; ++t) {
         const int blk_i = t / tpb;
-        const int kj = list_entry(a, beg + blk_i);
+        int kj, tile = -1;  // tile: the bit tile of a partial block (element masks)
+        if constexpr (ELEM) {
+            const int e = wave_uniform(a.list[beg + blk_i]);
+            tile = (e >> 16) - 1;
+            tile = tile < a.n_tiles ? tile : a.n_tiles - 1;  // (a plan never holds more)
+            kj = e & 0xffff;
+            kj = kj >= a.n_k ? a.n_k - 1 : kj;
+        } else {
+            kj = list_entry(a, beg + blk_i);
+        }
         const int key0 = kj * a.block_k + (t - blk_i * tpb) * TK;
         float4 kr[CH_T], vr[CH_T];
 #pragma unroll
@@ -107,6 +122,21 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qf[4 * s4 + 3], sacc[mt], 0, 0, 0);
             }
 
+        if constexpr (ELEM) {
+            if (tile >= 0) {
+                const int qr = q_row - qi * a.block_q;
+                const int ko = (t - blk_i * tpb) * TK;
+                const uint32_t* wrow = a.pbits + ((size_t)tile * a.block_q + qr) * (a.block_k >> 5) + (ko >> 5);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t w = wrow[mt] >> (4 * h);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) sacc[mt][i] = -INFINITY;
+                }
+            }
+        }
+
         float mx = sacc[0][0];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -114,13 +144,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[mt][i]);
         mx = __builtin_fmaxf(mx, xor32(mx));
         const float m_new = __builtin_fmaxf(m_run, mx * a.c);
-        const float alpha = fast_exp2(m_run - m_new);
+        // (element masks: no kept score yet leaves m = -inf; 2^(-inf - -inf) would be NaN)
+        const float alpha = (ELEM && m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        const float m_use = (ELEM && m_new == -INFINITY) ? 0.f : m_new;
         float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_new));
+                const float p = fast_exp2(__builtin_fmaf(sacc[mt][i], a.c, -m_use));
                 psum += p;
                 sacc[mt][i] = p;
             }
@@ -143,7 +175,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
     }
 
     const float l_tot = l_run + xor32(l_run);
-    const bool any = n_steps > 0;
+    const bool any = ELEM ? m_run != -INFINITY : n_steps > 0;
     const float inv = any ? 1.0f / l_tot : 0.0f;
     float* og = (float*)a.out + head + (size_t)q_row * D;
 #pragma unroll
@@ -161,13 +193,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(FwdArgs a) {
     if (h == 0) a.lse[(size_t)bh * a.S + q_row] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, int W, int TK>
+template <int D, int W, int TK, int ELEM>
 static hipError_t launch_f32(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_f32_kernel<D, W, TK>), dim3(grid), dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, W, TK, ELEM>), dim3(grid), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-#define BSATTN_F32_VARIANT(D, W, TK) {0, D, 32 * W, TK, W, 1, &launch_f32<D, W, TK>}
+#define BSATTN_F32_VARIANT(D, W, TK) {0, D, 32 * W, TK, W, 1, &launch_f32<D, W, TK, 0>}
+#define BSATTN_F32_ELEM(D, W, TK) {0, D, 32 * W, TK, W, 1, &launch_f32<D, W, TK, 1>}
 
 static const Variant kF32Variants[] = {
     BSATTN_F32_VARIANT(64, 2, 32),  BSATTN_F32_VARIANT(64, 2, 64),
@@ -176,9 +209,22 @@ static const Variant kF32Variants[] = {
     BSATTN_F32_VARIANT(128, 4, 32), BSATTN_F32_VARIANT(128, 4, 64),
 };
 
+// The same configs with element-level masks.
+static const Variant kF32ElemVariants[] = {
+    BSATTN_F32_ELEM(64, 2, 32),  BSATTN_F32_ELEM(64, 2, 64),
+    BSATTN_F32_ELEM(64, 4, 32),  BSATTN_F32_ELEM(64, 4, 64),
+    BSATTN_F32_ELEM(128, 2, 32), BSATTN_F32_ELEM(128, 2, 64),
+    BSATTN_F32_ELEM(128, 4, 32), BSATTN_F32_ELEM(128, 4, 64),
+};
+
 const Variant* f32_variants(int* n) {
     *n = (int)(sizeof(kF32Variants) / sizeof(kF32Variants[0]));
     return kF32Variants;
+}
+
+const Variant* f32_elem_variants(int* n) {
+    *n = (int)(sizeof(kF32ElemVariants) / sizeof(kF32ElemVariants[0]));
+    return kF32ElemVariants;
 }
 
 }  // namespace bsattn

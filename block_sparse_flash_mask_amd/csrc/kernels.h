@@ -82,6 +82,8 @@ const Variant* bf16_variants(int* n);
 // The bf16 variants built for element-level masks (plain schedule, row pairs included).
 const Variant* bf16_elem_variants(int* n);
 const Variant* f32_variants(int* n);
+// The fp32 variants with element-level masks.
+const Variant* f32_elem_variants(int* n);
 // fp8 forward (attn_fp8.hip): dtype 2, tile_k 64, one config per (D, tile_q); and
 // the pre-pass that rearranges V per 64-key tile for its P V product (tiles =
 // B*H*S/64).

@@ -244,8 +244,8 @@ int bsattn_list_configs(int dtype, int D, int block_q, int block_k, bsattn_tile_
  *                  partial block is kept iff bit j % 32 of word j / 32 of row i of
  *                  its tile is set.  Tiles may be shared (e.g. one lower-triangular
  *                  tile for every diagonal block of an exact token-causal mask).
- * A query row with no kept element gets out = 0 and lse = -inf.  bf16 only
- * (BSATTN_F32 gives BSATTN_ERR_UNSUPPORTED); 1 <= n_tiles <= 32767 and
+ * A query row with no kept element gets out = 0 and lse = -inf.  dtype bf16 or
+ * fp32 as for bsattn_fwd (fp32 runs the fp32 kernel's configs); 1 <= n_tiles <= 32767 and
  * S / block_k <= 65536, else BSATTN_ERR_SHAPE.  The workspace is the same size
  * as for bsattn_fwd (bsattn_workspace_size) and has the plan layout of
  * bsattn_plan, except that a list entry of a partial block is kj | (tile + 1) << 16.

@@ -271,7 +271,7 @@ def test_elem_argument_checks(lib):
     assert call(18, 16) == WS and call(17, None) == WS
     ok[18] = 4096  # enough workspace: alignment, aliasing and the config decide
     assert call(5, p(15 * A + 2)) == ALIGN and call(4, p(8 * A + 1)) == ALIGN
-    assert call(17, p(3 * A + 128)) == ALIAS and call(16, 0) == UNSUP
+    assert call(17, p(3 * A + 128)) == ALIAS and call(16, 2) == UNSUP
 
     g = lib.bsattn_fwd_planned_elem
     # q k v out lse B H S D bq bk scale dtype bits n_tiles ws wsb cfg stream
@@ -292,7 +292,8 @@ def test_elem_argument_checks(lib):
     assert callp(13, p(11 * A + 8)) == ALIAS      # ... lse
     assert callp(13, p(13 * A + 128)) == ALIAS    # ... the plan
     assert callp(15, p(5 * A + 64)) == ALIAS      # the plan overlaps v
-    assert callp(12, 0) == UNSUP                  # fp32: no element-mask configs
+    assert callp(12, 2) == UNSUP                  # no such dtype
+    assert callp(8, 96) == UNSUP                  # no such head dimension
 
     h = lib.bsattn_plan_elem
     # states pidx n_tiles B H S bq bk ws wsb stream
@@ -318,7 +319,7 @@ def test_elem_argument_checks(lib):
 def test_elem_configs(lib):
     n = ctypes.c_int(-1)
     assert lib.bsattn_list_configs_elem(0, 64, 64, 64, None, 0, ctypes.byref(n)) == OK
-    assert n.value == 0  # fp32: none
+    assert n.value == 2  # fp32: the two-wave kernel at 32- and 64-key steps (tile_q 64)
     for D in (64, 128):
         cfgs = bs.list_configs_elem(__import__("torch").bfloat16, D, 128, 128)
         assert len(cfgs) >= 3

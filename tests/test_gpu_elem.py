@@ -169,3 +169,67 @@ def test_workload_token_causal_sampled_rows():
     go = out.reshape(-1, w.D)[torch.as_tensor(rows, device=out.device)]
     gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
     say("  stats", compare(go, gl, ro, rl, "bf16", w.name))
+
+
+# ---- fp32 inputs -------------------------------------------------------------------
+
+def _configs_f32(D, bq, bk):
+    ensure_built()
+    return [c.as_tuple() for c in bs.list_configs_elem(torch.float32, D, bq, bk)]
+
+
+def _run_f32(q, k, v, st, pidx, pbits, bq, bk, scale, config=None, what=""):
+    ensure_built()
+    say("fwd_elem fp32", what, tuple(q.shape), bq, bk, config)
+    out, lse = bs.fwd_elem(q.cuda(), k.cuda(), v.cuda(), st.cuda(), pidx.cuda(), pbits.cuda(),
+                           bq, bk, scale, config=config)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    ro, rl = oracle.fwd_elem(q, k, v, st, pidx, pbits, bq, bk, scale)
+    return out, lse, compare(out, lse, ro, rl, "f32", what)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("blocks", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_fp32_every_config(D, blocks):
+    """fp32 inputs (the fp32 kernel, fp32 tolerances) on every built config."""
+    bq, bk = blocks
+    S = 512
+    q, k, v = rand_qkv(1, 2, S, D, torch.float32, seed=D + bq + 1)
+    st, pidx, pbits = _rand_elem(1, 2, S, bq, bk, 3, seed=bq * 7 + bk + 1)
+    cfgs = _configs_f32(D, bq, bk)
+    assert cfgs, "no fp32 element-mask config for D=%d blocks=%s" % (D, blocks)
+    for cfg in cfgs:
+        _run_f32(q, k, v, st, pidx, pbits, bq, bk, 1.0 / np.sqrt(D), cfg, "%s %s" % (blocks, cfg))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_fp32_token_causal_and_degenerate_scales(scale):
+    """fp32 exact token-causal (ragged: S = 640) with the default scale, then a zero
+    scale (uniform over the kept keys) and a negative one on random tiles."""
+    B, H, S, b, D = 1, 2, 640, 128, 64
+    q, k, v = rand_qkv(B, H, S, D, torch.float32, seed=15)
+    n = S // b
+    i = torch.arange(n).view(n, 1)
+    j = torch.arange(n).view(1, n)
+    st = ((j < i).to(torch.uint8) + 2 * (j == i).to(torch.uint8)).expand(B, H, n, n).contiguous()
+    pidx = torch.zeros(B, H, n, n, dtype=torch.int32)
+    pbits = W.pack_tiles(np.tril(np.ones((b, b), dtype=bool))[None])
+    _run_f32(q, k, v, st, pidx, pbits, b, b, 1.0 / np.sqrt(D), what="fp32 token causal")
+    st2, pidx2, pbits2 = _rand_elem(B, H, S, 128, 64, 3, seed=16)
+    _run_f32(q, k, v, st2, pidx2, pbits2, 128, 64, scale, what="fp32 scale %g" % scale)
+
+
+def test_fp32_all_set_tiles_equal_block_mask():
+    """fp32: all-set tiles give bit for bit the block-mask forward of the same config."""
+    ensure_built()
+    B, H, S, D, b = 1, 2, 512, 128, 128
+    q, k, v = (t.cuda() for t in rand_qkv(B, H, S, D, torch.float32, seed=19))
+    st, pidx, _ = _rand_elem(B, H, S, b, b, 2, seed=19, zero_row=False)
+    pbits = W.pack_tiles(np.ones((2, b, b), dtype=bool))
+    for cfg in _configs_f32(D, b, b):
+        oe, le = bs.fwd_elem(q, k, v, st.cuda(), pidx.cuda(), pbits.cuda(), b, b, config=cfg)
+        ob, lb = bs.fwd(q, k, v, (st != 0).to(torch.uint8).cuda(), b, b, config=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(oe, ob), cfg
+        assert torch.equal(le, lb), cfg
