@@ -235,3 +235,27 @@ def test_builtin_default_is_row_pair(D, bk, pair):
     o2, l2 = bs.fwd(q, k, v, mask, 128, bk, 1.0 / np.sqrt(D), config=pair)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_rows_past_the_pair_limit():
+    """Rows of more than 2048 key blocks (S = 262272, 128-key blocks, 2049 per row):
+    the row-pair configs refuse the shape, the call with no config falls back to a
+    plain config, and sampled rows match the oracle."""
+    ensure_built()
+    B, H, S, D, b = 1, 1, 2049 * 128, 64, 128
+    n = S // b
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=71)
+    g = torch.Generator().manual_seed(71)
+    mask = (torch.rand(B, H, n, n, generator=g) < 0.002).to(torch.uint8)
+    mask[..., torch.arange(n), torch.arange(n)] = 1  # the diagonal
+    mask[..., :, n - 1] = 1                          # the last key block in every row
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    with pytest.raises(bs.BsattnError):
+        bs.fwd(qd, kd, vd, md, b, b, config=(256, 64, 8, 2))
+    out, lse = bs.fwd(qd, kd, vd, md, b, b)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(B, H, S, b, 32, mask=mask)
+    ro, rl = oracle.fwd_rows(q, k, v, mask, b, b, 1.0 / np.sqrt(D), rows)
+    go = out.reshape(-1, D)[torch.as_tensor(rows, device=out.device)]
+    gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
+    say("  stats", compare(go, gl, ro, rl, "bf16", "rows past the pair limit"))
