@@ -907,24 +907,41 @@ int bsattn_fp8_workspace_size(int B, int H, int S, int D, int block_q, int block
     return BSATTN_OK;
 }
 
-int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                           int S, int D, int block_q, int block_k, float scale, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-    if (!workspace) return BSATTN_ERR_NULL;
+// Checks shared by the fp8 entry points, all on the host: tensors and shape; with
+// bit tiles (element masks) the element-mask shape and the tiles' alignment; then the
+// workspace (size, alignment, no overlap with any tensor or with the bit tiles) and
+// the config.  Fills *L.
+int check_fp8_call(const void* q, const void* k, const void* v, const void* out, const float* lse, int B, int H,
+                   int S, int D, int block_q, int block_k, float scale, const void* workspace,
+                   size_t workspace_bytes, const uint32_t* bits, int n_tiles, Fp8Layout* L) {
     int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
     if (rc) return rc;
-    const int n_q = S / block_q, n_k = S / block_k;
-    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, n_q, n_k);
-    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
-    if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
+    if (bits) {
+        rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
+        if (rc) return rc;
+    }
+    *L = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k);
+    if (workspace_bytes < L->bytes) return BSATTN_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 16) || (bits && !is_aligned(bits, 4))) return BSATTN_ERR_ALIGN;
     const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
     const void* ts[] = {q, k, v, out, lse};
     const size_t tn[] = {n8, n8, n8, no, nl};
     for (int i = 0; i < 5; ++i)
-        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
-    const Variant* var = fp8_find(D, block_q);
-    if (!var) return BSATTN_ERR_UNSUPPORTED;
-    hipStream_t st = (hipStream_t)stream;
+        if (overlap(workspace, L->bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
+    if (bits) {
+        const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
+        if (overlap(bits, nbits, out, no) || overlap(bits, nbits, lse, nl) || overlap(bits, nbits, workspace, L->bytes))
+            return BSATTN_ERR_ALIAS;
+    }
+    return fp8_find(D, block_q, bits != nullptr) ? BSATTN_OK : BSATTN_ERR_UNSUPPORTED;
+}
+
+// The V pre-pass, then the fp8 attention kernel on the plan in the workspace (bit
+// tiles: the element-mask kernel).
+int run_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int S, int D,
+            int block_q, int block_k, float scale, void* workspace, const Fp8Layout& L, const uint32_t* bits,
+            int n_tiles, hipStream_t st) {
+    const Variant* var = fp8_find(D, block_q, bits != nullptr);
     char* ws = (char*)workspace;
     const hipError_t e = launch_fp8_vt(v, ws + L.vt, (int64_t)B * H * S / 64, D, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -932,32 +949,41 @@ int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* ou
     a.qsign = a.qsign ? 0x80808080u : 0u;  // the sign bit of each of four e4m3 bytes
     a.counts = (const int32_t*)ws;
     a.list = (const int32_t*)(ws + L.plan.lists);
-    a.ell_stride = n_k;
+    a.ell_stride = S / block_k;
     a.order = (const int32_t*)(ws + L.plan.order);
     a.nrows = (int)L.plan.R;
     a.chunk = (int)L.plan.chunk;
+    if (bits) {
+        a.pbits = bits;
+        a.n_tiles = n_tiles;
+    }
     return run_attention(a, *var, st);
+}
+
+int bsattn_fwd_fp8_planned(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int S, int D, int block_q, int block_k, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!workspace) return BSATTN_ERR_NULL;
+    Fp8Layout L;
+    const int rc = check_fp8_call(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
+                                  workspace_bytes, nullptr, 0, &L);
+    if (rc) return rc;
+    return run_fp8(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace, L, nullptr, 0,
+                   (hipStream_t)stream);
 }
 
 int bsattn_fwd_fp8(const void* q, const void* k, const void* v, const uint8_t* block_mask, void* out, float* lse,
                    int B, int H, int S, int D, int block_q, int block_k, float scale, void* workspace,
                    size_t workspace_bytes, void* stream) {
     if (!block_mask || !workspace) return BSATTN_ERR_NULL;
-    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    Fp8Layout L;
+    int rc = check_fp8_call(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
+                            workspace_bytes, nullptr, 0, &L);
     if (rc) return rc;
-    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k);
-    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
-    if (!is_aligned(workspace, 16)) return BSATTN_ERR_ALIGN;
-    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
-    const void* ts[] = {q, k, v, out, lse};
-    const size_t tn[] = {n8, n8, n8, no, nl};
-    for (int i = 0; i < 5; ++i)
-        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
-    if (!fp8_find(D, block_q)) return BSATTN_ERR_UNSUPPORTED;
     rc = bsattn_plan(block_mask, B, H, S, block_q, block_k, workspace, workspace_bytes, stream);
     if (rc) return rc;
-    return bsattn_fwd_fp8_planned(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
-                                  workspace_bytes, stream);
+    return run_fp8(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace, L, nullptr, 0,
+                   (hipStream_t)stream);
 }
 
 // The fp8 forward with an element-level mask: the plan of bsattn_plan_elem in the
@@ -967,40 +993,12 @@ int bsattn_fwd_fp8_planned_elem(const void* q, const void* k, const void* v, voi
                                 const uint32_t* partial_bits, int n_tiles, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     if (!workspace || !partial_bits) return BSATTN_ERR_NULL;
-    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    Fp8Layout L;
+    const int rc = check_fp8_call(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
+                                  workspace_bytes, partial_bits, n_tiles, &L);
     if (rc) return rc;
-    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
-    if (rc) return rc;
-    const int n_q = S / block_q, n_k = S / block_k;
-    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, n_q, n_k);
-    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
-    if (!is_aligned(workspace, 16) || !is_aligned(partial_bits, 4)) return BSATTN_ERR_ALIGN;
-    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
-    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
-    const void* ts[] = {q, k, v, out, lse};
-    const size_t tn[] = {n8, n8, n8, no, nl};
-    for (int i = 0; i < 5; ++i)
-        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
-    if (overlap(partial_bits, nbits, out, no) || overlap(partial_bits, nbits, lse, nl) ||
-        overlap(partial_bits, nbits, workspace, L.bytes))
-        return BSATTN_ERR_ALIAS;
-    const Variant* var = fp8_find(D, block_q, true);
-    if (!var) return BSATTN_ERR_UNSUPPORTED;
-    hipStream_t st = (hipStream_t)stream;
-    char* ws = (char*)workspace;
-    const hipError_t e = launch_fp8_vt(v, ws + L.vt, (int64_t)B * H * S / 64, D, st);
-    if (e != hipSuccess) return hip_fail(e);
-    FwdArgs a = make_args(q, k, ws + L.vt, out, lse, H, S, block_q, block_k, scale, *var);
-    a.qsign = a.qsign ? 0x80808080u : 0u;  // the sign bit of each of four e4m3 bytes
-    a.counts = (const int32_t*)ws;
-    a.list = (const int32_t*)(ws + L.plan.lists);
-    a.ell_stride = n_k;
-    a.order = (const int32_t*)(ws + L.plan.order);
-    a.nrows = (int)L.plan.R;
-    a.chunk = (int)L.plan.chunk;
-    a.pbits = partial_bits;
-    a.n_tiles = n_tiles;
-    return run_attention(a, *var, st);
+    return run_fp8(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace, L, partial_bits, n_tiles,
+                   (hipStream_t)stream);
 }
 
 int bsattn_fwd_fp8_elem(const void* q, const void* k, const void* v, const uint8_t* block_states,
@@ -1008,29 +1006,16 @@ int bsattn_fwd_fp8_elem(const void* q, const void* k, const void* v, const uint8
                         float* lse, int B, int H, int S, int D, int block_q, int block_k, float scale,
                         void* workspace, size_t workspace_bytes, void* stream) {
     if (!block_states || !partial_index || !partial_bits || !workspace) return BSATTN_ERR_NULL;
-    int rc = check_fp8_buffers(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale);
+    Fp8Layout L;
+    int rc = check_fp8_call(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace,
+                            workspace_bytes, partial_bits, n_tiles, &L);
     if (rc) return rc;
-    rc = check_elem_shape(B, H, S, block_q, block_k, n_tiles);
-    if (rc) return rc;
-    const Fp8Layout L = fp8_layout((int64_t)B * H, S, D, S / block_q, S / block_k);
-    if (workspace_bytes < L.bytes) return BSATTN_ERR_WORKSPACE;
-    if (!is_aligned(workspace, 16) || !is_aligned(partial_bits, 4) || !is_aligned(partial_index, 4))
-        return BSATTN_ERR_ALIGN;
-    const size_t n8 = (size_t)B * H * S * D, no = n8 * 2, nl = (size_t)B * H * S * 4;
-    const void* ts[] = {q, k, v, out, lse};
-    const size_t tn[] = {n8, n8, n8, no, nl};
-    for (int i = 0; i < 5; ++i)
-        if (overlap(workspace, L.bytes, ts[i], tn[i])) return BSATTN_ERR_ALIAS;
-    const size_t nbits = (size_t)n_tiles * block_q * (block_k / 8);
-    if (overlap(partial_bits, nbits, out, no) || overlap(partial_bits, nbits, lse, nl) ||
-        overlap(partial_bits, nbits, workspace, L.bytes))
-        return BSATTN_ERR_ALIAS;
-    if (!fp8_find(D, block_q, true)) return BSATTN_ERR_UNSUPPORTED;
+    if (!is_aligned(partial_index, 4)) return BSATTN_ERR_ALIGN;
     rc = bsattn_plan_elem(block_states, partial_index, n_tiles, B, H, S, block_q, block_k, workspace,
                           workspace_bytes, stream);
     if (rc) return rc;
-    return bsattn_fwd_fp8_planned_elem(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, partial_bits,
-                                       n_tiles, workspace, workspace_bytes, stream);
+    return run_fp8(q, k, v, out, lse, B, H, S, D, block_q, block_k, scale, workspace, L, partial_bits, n_tiles,
+                   (hipStream_t)stream);
 }
 
 // ---- backward ------------------------------------------------------------------
