@@ -359,7 +359,8 @@ def bench_ragged(args, torch, bs, W):
     traffic = traffic_from_profiles(w.name, (256, 256, 8, 2) if big else (128, 128, 4, 2), "ragged")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": "ragged_dot256_kernel" if big else "ragged_dot_kernel", "kernel_ms": ms_kernel}
+                "kernel": ("ragged_dot256_kernel (+ ragged_dot_kernel for the partial last round)" if big
+                           else "ragged_dot_kernel"), "kernel_ms": ms_kernel}
     if traffic:
         roofline["hbm_gbs"] = traffic / (ms_kernel * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12

@@ -5,6 +5,7 @@
 // reaches the device.  Kernels are launched on the caller's stream and nothing is
 // allocated on the forward path.
 #include <algorithm>
+#include <atomic>
 #include <cerrno>
 #include <cfloat>
 #include <climits>
@@ -820,6 +821,20 @@ int bsattn_list_configs_elem(int dtype, int D, int block_q, int block_k, bsattn_
 
 // ---- ragged dot ------------------------------------------------------------------
 
+// Compute units of the current device, cached per device (0 if the query fails:
+// the ragged dot then runs in one launch).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // The plan's item count is an int32 (and every item index fits one).
 static bool ragged_items_ok(int M, int G) { return ragged_max_items(M, G) < ((int64_t)1 << 30); }
 
@@ -862,7 +877,7 @@ int bsattn_ragged_dot_planned(const void* lhs, const void* rhs, void* out, int M
         overlap(workspace, nw, lhs, nl) || overlap(workspace, nw, rhs, nr))
         return BSATTN_ERR_ALIAS;
     const hipError_t e = launch_ragged_planned(lhs, rhs, out, M, K, N, G, out_dtype == BSATTN_F32, workspace,
-                                               (hipStream_t)stream);
+                                               device_cu_count(), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return BSATTN_OK;
 }

@@ -41,8 +41,10 @@ hipError_t launch_compact_pack(const int32_t* counts, const int32_t* lists, int6
 inline int64_t ragged_max_items(int64_t M, int64_t G) { return (M + 255) / 256 + G + 1; }
 inline size_t ragged_ws_bytes(int64_t M, int64_t G) { return (size_t)ragged_max_items(M, G) * 16 + 16; }
 hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* workspace, hipStream_t stream);
+// n_cu: compute units of the device (the 256 x 256 kernel takes whole rounds of them,
+// the partial last round runs as quarter tiles); 0 runs everything in one launch.
 hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
-                                 int out_f32, const void* workspace, hipStream_t stream);
+                                 int out_f32, const void* workspace, int n_cu, hipStream_t stream);
 
 // Backward (attn_bwd.hip): per-row (lse * log2 e, dout . out) into ld (float2
 // [rows]), the column form of the mask (per key block: count, query-block list

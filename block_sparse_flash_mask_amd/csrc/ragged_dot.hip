@@ -28,6 +28,12 @@
 // ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
 // 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
 // wave's own lhs rows loaded straight into VGPRs one step ahead.
+// The last round.  The 256 x 256 kernel takes the whole rounds of the chip (the
+// largest multiple of the CU count of its (item, column tile) units); the rest, a
+// partial round that would leave most CUs idle, goes to ragged_dot_kernel in tail
+// mode as quarter tiles (two row halves x two 128-column halves of each unit), four
+// times as many workgroups, so the last round spreads over all CUs.  Both kernels
+// accumulate k in the same order, so the split changes no result.
 #include "bf16_layout.h"
 #include "common.h"
 #include "kernels.h"
@@ -111,20 +117,36 @@ __global__ __launch_bounds__(kRaggedThreads) void ragged_plan_kernel(const int32
     if (tid == 0) n_items[0] = (int32_t)(carry[1] + n_tail);
 }
 
+// tail_cu > 0: tail mode (N % 256 == 0), the units past the whole rounds of tail_cu
+// CUs, four workgroups per unit; tail_cu = 0: every (half item, column tile).
 template <int OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
-    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N) {
+    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items,
+    int tail_cu) {
     typedef TileGeom<kRaggedTN, kRaggedTK> G;  // W^T tile: "D" = 128 columns, "keys" = 64 k
     constexpr int KS = kRaggedTK / 16, MT = G::MT, MD = G::MD;
     __shared__ __attribute__((aligned(1024))) uint8_t w0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t w1s[G::BYTES];
 
-    const int n_tiles = N / kRaggedTN;
-    const int item = blockIdx.x / (2 * n_tiles);
-    const int rem = blockIdx.x - item * 2 * n_tiles;
-    const int half = rem / n_tiles, nt = rem - half * n_tiles;
-    if (item >= wave_uniform(n_items[0])) return;
+    int n_it = wave_uniform(n_items[0]);
+    n_it = n_it < max_items ? n_it : max_items;  // (a plan never holds more)
+    int item, half, nt;
+    if (tail_cu > 0) {
+        const int units = N / 256, total = n_it * units;
+        const int gi = total - total % tail_cu + (int)(blockIdx.x >> 2);
+        if (gi >= total) return;
+        item = gi / units;
+        half = (blockIdx.x >> 1) & 1;
+        nt = 2 * (gi - item * units) + (blockIdx.x & 1);
+    } else {
+        const int n_tiles = N / kRaggedTN;
+        item = blockIdx.x / (2 * n_tiles);
+        const int rem = blockIdx.x - item * 2 * n_tiles;
+        half = rem / n_tiles;
+        nt = rem - half * n_tiles;
+        if (item >= n_it) return;
+    }
     const int4 it = items[item];
     const int grp = wave_uniform(it.y);
     const int row0 = wave_uniform(it.x) * kRaggedTM + half * 128;  // this workgroup's 128 rows
@@ -253,7 +275,8 @@ constexpr int kR256Stages = 2;
 template <int OUT_F32, int TKS, int NST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot256_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
-    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items) {
+    const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items,
+    int tail_cu) {
     typedef TileGeom<256, TKS> GW;      // W^T tile: "D" = 256 columns, "keys" = TKS k
     constexpr int MDW = GW::MD;         // 8 column tiles of 32
     constexpr int KSX = TKS / 16;       // k-steps of 16 per step
@@ -277,10 +300,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int n_it = wave_uniform(n_items[0]);
     n_it = n_it < max_items ? n_it : max_items;  // (a plan never holds more)
     const int total = n_it * n_tiles;
-    const int chunk = (total + 7) >> 3;
+    // whole rounds of tail_cu CUs here; the rest goes to the tail kernel
+    const int whole = tail_cu > 0 ? total - total % tail_cu : total;
+    const int chunk = (whole + 7) >> 3;
     const int jx = blockIdx.x >> 3;
     const int gi = (blockIdx.x & 7) * chunk + jx;
-    if (jx >= chunk || gi >= total) return;
+    if (jx >= chunk || gi >= whole) return;
     const int item = gi / n_tiles;
     const int nt = gi - item * n_tiles;
     const int4 it = items[item];
@@ -433,28 +458,42 @@ hipError_t launch_ragged_plan(const int32_t* group_sizes, int M, int G, void* wo
 }
 
 hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, int M, int K, int N, int G,
-                                 int out_f32, const void* workspace, hipStream_t stream) {
+                                 int out_f32, const void* workspace, int n_cu, hipStream_t stream) {
     const int4* items = (const int4*)workspace;
     const int64_t max_items = ragged_max_items(M, G);
     const int32_t* n_items = (const int32_t*)(items + max_items);
+    const uint16_t* x = (const uint16_t*)lhs;
+    const uint16_t* w = (const uint16_t*)rhs;
     if (N % 256 == 0 && (int64_t)M * K * 2 < ((int64_t)1 << 31)) {  // lhs through one buffer range
-        const int64_t grid = 8 * ((max_items * (N / 256) + 7) / 8);  // 8 XCD chunks
+        const int64_t units = max_items * (N / 256);
+        const int64_t grid = 8 * ((units + 7) / 8);  // 8 XCD chunks
+        const int tail_cu = n_cu > 0 ? n_cu : 0;
         if (out_f32)
-            hipLaunchKernelGGL((ragged_dot256_kernel<1, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0, stream,
-                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N, (int)max_items);
+            hipLaunchKernelGGL((ragged_dot256_kernel<1, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0,
+                               stream, x, w, items, n_items, out, M, K, N, (int)max_items, tail_cu);
         else
-            hipLaunchKernelGGL((ragged_dot256_kernel<0, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0, stream,
-                               (const uint16_t*)lhs, (const uint16_t*)rhs, items, n_items, out, M, K, N,
-                               (int)max_items);
+            hipLaunchKernelGGL((ragged_dot256_kernel<0, kR256TK, kR256Stages>), dim3((unsigned)grid), dim3(512), 0,
+                               stream, x, w, items, n_items, out, M, K, N, (int)max_items, tail_cu);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || tail_cu == 0) return e;
+        // the partial last round: fewer than n_cu units, four workgroups each
+        const int64_t tail_grid = 4 * (units < n_cu - 1 ? units : n_cu - 1);
+        if (tail_grid == 0) return hipSuccess;
+        if (out_f32)
+            hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w, items,
+                               n_items, out, M, K, N, (int)max_items, tail_cu);
+        else
+            hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w, items,
+                               n_items, out, M, K, N, (int)max_items, tail_cu);
         return hipGetLastError();
     }
     const int64_t grid = max_items * 2 * (N / kRaggedTN);
     if (out_f32)
-        hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,
-                           (const uint16_t*)rhs, items, n_items, out, M, K, N);
+        hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items, out,
+                           M, K, N, (int)max_items, 0);
     else
-        hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)lhs,
-                           (const uint16_t*)rhs, items, n_items, out, M, K, N);
+        hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items, out,
+                           M, K, N, (int)max_items, 0);
     return hipGetLastError();
 }
 
