@@ -26,8 +26,8 @@
 // buffer loads with the LDS flag, two stages (one step of loads in flight).  Per k a
 // workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.
 // ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
-// 128-column tile), wave w owns 32 rows, the expert tile in LDS as above and the
-// wave's own lhs rows loaded straight into VGPRs one step ahead.
+// 128-column tile), wave w owns 32 rows, the expert tile in LDS as above (three
+// stages) and the wave's own lhs rows loaded straight into VGPRs, two steps ahead.
 // The last round.  The 256 x 256 kernel takes the whole rounds of the chip (the
 // largest multiple of the CU count of its (item, column tile) units); the rest, a
 // partial round that would leave most CUs idle, goes to ragged_dot_kernel in tail
@@ -126,8 +126,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int tail_cu) {
     typedef TileGeom<kRaggedTN, kRaggedTK> G;  // W^T tile: "D" = 128 columns, "keys" = 64 k
     constexpr int KS = kRaggedTK / 16, MT = G::MT, MD = G::MD;
+    // Three stages of the expert tile in LDS and three register sets of the wave's
+    // lhs rows: the loads run two steps ahead (at one wave per SIMD, the tail's case,
+    // a single step ahead left every step waiting on its loads).
     __shared__ __attribute__((aligned(1024))) uint8_t w0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t w1s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t w2s[G::BYTES];
 
     int n_it = wave_uniform(n_items[0]);
     n_it = n_it < max_items ? n_it : max_items;  // (a plan never holds more)
@@ -196,12 +200,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 acc[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
-    bf16x8 xf[KS], xn[KS];
+    bf16x8 x0[KS], x1[KS], x2[KS];
     auto load_x = [&](int k0, bf16x8 (&dst)[KS]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, xrow[(k0 + 16 * ks) / 8 + h]);
     };
-    auto step = [&](const uint8_t* wbuf) {
+    auto step = [&](const uint8_t* wbuf, const bf16x8 (&xf)[KS]) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -216,30 +220,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
     };
 
+    // Step s uses stage s % 3.  At its top: wait until this wave's loads of step s have
+    // landed (each step's loads are NV + KS vector-memory operations, in issue order,
+    // and those of step s + 1 may stay in flight), barrier (everyone's W DMA landed;
+    // everyone is done with step s - 1, whose stage the next issue refills), then
+    // issue the loads of step s + 2.
+    constexpr int PER_STEP = NV + KS;
+    static_assert(PER_STEP < 64, "vmcnt range");
     const int n_steps = K / kRaggedTK;
     issue(0, w0s);
-    load_x(0, xf);
-    for (int t = 0; t < n_steps; t += 2) {
-        // even step: tile in w0s, next into w1s
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this step's W tile and X
+    load_x(0, x0);
+    if (n_steps > 1) {
+        issue(kRaggedTK, w1s);
+        load_x(kRaggedTK, x1);
+    }
+    auto top = [&](int s) {
+        if (s + 1 < n_steps)
+            __builtin_amdgcn_s_waitcnt(0x3f70 | (PER_STEP & 15) | ((PER_STEP >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
         __syncthreads();
-        if (t + 1 < n_steps) {
-            issue((t + 1) * kRaggedTK, w1s);
-            load_x((t + 1) * kRaggedTK, xn);
-        }
-        step(w0s);
-        if (t + 1 >= n_steps) break;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) xf[ks] = xn[ks];
-        __builtin_amdgcn_s_waitcnt(0x3f70);
-        __syncthreads();
+    };
+    for (int t = 0; t < n_steps; t += 3) {
+        top(t);
         if (t + 2 < n_steps) {
-            issue((t + 2) * kRaggedTK, w0s);
-            load_x((t + 2) * kRaggedTK, xn);
+            issue((t + 2) * kRaggedTK, w2s);
+            load_x((t + 2) * kRaggedTK, x2);
         }
-        step(w1s);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) xf[ks] = xn[ks];
+        step(w0s, x0);
+        if (t + 1 >= n_steps) break;
+        top(t + 1);
+        if (t + 3 < n_steps) {
+            issue((t + 3) * kRaggedTK, w0s);
+            load_x((t + 3) * kRaggedTK, x0);
+        }
+        step(w1s, x1);
+        if (t + 2 >= n_steps) break;
+        top(t + 2);
+        if (t + 4 < n_steps) {
+            issue((t + 4) * kRaggedTK, w1s);
+            load_x((t + 4) * kRaggedTK, x1);
+        }
+        step(w2s, x2);
     }
 
     // C^T[n][m]: lane (h, m) holds n = 32 md + 8 g4 + 4 h + u for u = 0..3
