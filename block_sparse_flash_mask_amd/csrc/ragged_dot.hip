@@ -27,7 +27,8 @@
 // workgroup moves half the L2 -> LDS bytes per MFMA of the 128 x 128 tile.
 // ragged_dot_kernel (any N % 128 == 0): 4 waves per (half item,
 // 128-column tile), wave w owns 32 rows, the expert tile in LDS as above (three
-// stages) and the wave's own lhs rows loaded straight into VGPRs, two steps ahead.
+// stages) and the wave's own lhs rows loaded straight into VGPRs, two steps ahead
+// (in tail mode, below, the lhs rows go through LDS as well).
 // The last round.  The 256 x 256 kernel takes the whole rounds of the chip (the
 // largest multiple of the CU count of its (item, column tile) units); the rest, a
 // partial round that would leave most CUs idle, goes to ragged_dot_kernel in tail
@@ -117,26 +118,34 @@ __global__ __launch_bounds__(kRaggedThreads) void ragged_plan_kernel(const int32
     if (tid == 0) n_items[0] = (int32_t)(carry[1] + n_tail);
 }
 
-// tail_cu > 0: tail mode (N % 256 == 0), the units past the whole rounds of tail_cu
-// CUs, four workgroups per unit; tail_cu = 0: every (half item, column tile).
-template <int OUT_F32>
+// TAIL = 1: tail mode (N % 256 == 0, M * K * 2 < 2^31), the units past the whole
+// rounds of tail_cu CUs, four workgroups per unit, the lhs rows DMA'd into LDS as
+// 8-row x 128-byte chunks (whole lines; the 256 x 256 kernel's layout) instead of
+// per-lane loads of 32 rows x 32 bytes (a quarter of the L2 rate), which left the
+// tail's lone workgroups waiting on their loads.  TAIL = 0: every (half item, column
+// tile), lhs rows straight into VGPRs.
+template <int OUT_F32, int TAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ragged_dot_kernel(
     const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, void* __restrict__ out, int M, int K, int N, int max_items,
     int tail_cu) {
     typedef TileGeom<kRaggedTN, kRaggedTK> G;  // W^T tile: "D" = 128 columns, "keys" = 64 k
     constexpr int KS = kRaggedTK / 16, MT = G::MT, MD = G::MD;
-    // Three stages of the expert tile in LDS and three register sets of the wave's
-    // lhs rows: the loads run two steps ahead (at one wave per SIMD, the tail's case,
-    // a single step ahead left every step waiting on its loads).
+    // Three stages of the expert tile (and in tail mode of the lhs rows) in LDS, and
+    // otherwise three register sets of the wave's lhs rows: the loads run two steps
+    // ahead.
+    constexpr int XB = TAIL ? 128 * kRaggedTK * 2 : 16;  // lhs stage: 128 rows x 64 k
     __shared__ __attribute__((aligned(1024))) uint8_t w0s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t w1s[G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t w2s[G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t x0s[XB];
+    __shared__ __attribute__((aligned(1024))) uint8_t x1s[XB];
+    __shared__ __attribute__((aligned(1024))) uint8_t x2s[XB];
 
     int n_it = wave_uniform(n_items[0]);
     n_it = n_it < max_items ? n_it : max_items;  // (a plan never holds more)
     int item, half, nt;
-    if (tail_cu > 0) {
+    if constexpr (TAIL) {
         const int units = N / 256, total = n_it * units;
         const int gi = total - total % tail_cu + (int)(blockIdx.x >> 2);
         if (gi >= total) return;
@@ -178,6 +187,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool store = m >= lo && m < hi;
     m = m < M ? m : M - 1;
     const u32x4* xrow = (const u32x4*)(lhs + (size_t)m * K);
+    // Tail mode: chunk c = wave + 4 i of a stage holds rows 8c .. 8c + 7 of the 128; lane
+    // l fills slot l % 8 of row 8c + l / 8 with unit (l % 8) ^ y(row), y(row) = (row / 2)
+    // % 8, so one DMA instruction reads 8 rows x 128 contiguous bytes and the operand
+    // reads (16 lanes, 16 consecutive rows, one unit) meet 16 distinct bank groups.
+    int x_voff[4] = {0, 0, 0, 0}, x_rd[KS];
+    if constexpr (TAIL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * (wave_s + 4 * i) + lane / 8;
+            int xr = row0 + r;
+            xr = xr < M ? xr : M - 1;
+            x_voff[i] = (xr * K + 8 * ((lane % 8) ^ ((r / 2) % 8))) * 2;
+        }
+        const int rho = 32 * wave + l32, y = (rho / 2) % 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) x_rd[ks] = (rho / 8) * 1024 + (rho % 8) * 128 + 16 * ((2 * ks + h) ^ y);
+    }
+    const int xrec = TAIL ? M * K * 2 : 0;  // (tail mode only: the launcher checks it fits)
 
     // W tile DMA: the V layout of bf16_layout.h with row stride N.  Lane offsets as
     // DmaPlan<128, 4, 64>::init with D replaced by N for the row part.
@@ -187,7 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NV = G::VBLK / 2 / 4;  // DMA instructions per wave per tile
     const uint16_t* wg = rhs + (size_t)grp * K * N + n0;
     const int nrec = (int)((size_t)K * N * 2 - (size_t)n0 * 2);  // bytes from wg to the expert's end
-    auto issue = [&](int k0, uint8_t* wbuf) {
+    auto issue = [&](int k0, uint8_t* wbuf, uint8_t* xbuf) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int tb = 2 * (wave_s + i * 4);
@@ -195,17 +222,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int uni = (k0 + 32 * mt + 16 * e + 4 * r) * N + 32 * md;
             dma16(wg, nrec, (BSATTN_LDS void*)(wbuf + (wave_s + i * 4) * 1024), v_lane * 2, uni * 2);
         }
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dma16(lhs, xrec, (BSATTN_LDS void*)(xbuf + (wave_s + 4 * i) * 1024), x_voff[i], k0 * 2);
+        }
     };
 
     f32x16 acc[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
-    bf16x8 x0[KS], x1[KS], x2[KS];
+    bf16x8 x0[KS], x1[KS], x2[KS];  // (register-path lhs sets; unused in tail mode)
     auto load_x = [&](int k0, bf16x8 (&dst)[KS]) {
+        if constexpr (!TAIL) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, xrow[(k0 + 16 * ks) / 8 + h]);
+            for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, xrow[(k0 + 16 * ks) / 8 + h]);
+        }
     };
-    auto step = [&](const uint8_t* wbuf, const bf16x8 (&xf)[KS]) {
+    auto step = [&](const uint8_t* wbuf, const uint8_t* xbuf, const bf16x8 (&xr)[KS]) {
+        bf16x8 xf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (TAIL)
+                xf[ks] = *(const bf16x8*)(xbuf + x_rd[ks]);
+            else
+                xf[ks] = xr[ks];
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -221,17 +263,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // Step s uses stage s % 3.  At its top: wait until this wave's loads of step s have
-    // landed (each step's loads are NV + KS vector-memory operations, in issue order,
-    // and those of step s + 1 may stay in flight), barrier (everyone's W DMA landed;
-    // everyone is done with step s - 1, whose stage the next issue refills), then
-    // issue the loads of step s + 2.
+    // landed (each step's loads are NV + KS vector-memory operations -- in tail mode KS
+    // lhs DMAs, else KS lhs loads -- in issue order, and those of step s + 1 may stay in
+    // flight), barrier (everyone's DMA landed; everyone is done with step s - 1, whose
+    // stage the next issue refills), then issue the loads of step s + 2.
     constexpr int PER_STEP = NV + KS;
     static_assert(PER_STEP < 64, "vmcnt range");
+    static_assert(!TAIL || KS == 4, "tail mode: four lhs DMAs per wave per stage");
     const int n_steps = K / kRaggedTK;
-    issue(0, w0s);
+    issue(0, w0s, x0s);
     load_x(0, x0);
     if (n_steps > 1) {
-        issue(kRaggedTK, w1s);
+        issue(kRaggedTK, w1s, x1s);
         load_x(kRaggedTK, x1);
     }
     auto top = [&](int s) {
@@ -244,24 +287,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < n_steps; t += 3) {
         top(t);
         if (t + 2 < n_steps) {
-            issue((t + 2) * kRaggedTK, w2s);
+            issue((t + 2) * kRaggedTK, w2s, x2s);
             load_x((t + 2) * kRaggedTK, x2);
         }
-        step(w0s, x0);
+        step(w0s, x0s, x0);
         if (t + 1 >= n_steps) break;
         top(t + 1);
         if (t + 3 < n_steps) {
-            issue((t + 3) * kRaggedTK, w0s);
+            issue((t + 3) * kRaggedTK, w0s, x0s);
             load_x((t + 3) * kRaggedTK, x0);
         }
-        step(w1s, x1);
+        step(w1s, x1s, x1);
         if (t + 2 >= n_steps) break;
         top(t + 2);
         if (t + 4 < n_steps) {
-            issue((t + 4) * kRaggedTK, w1s);
+            issue((t + 4) * kRaggedTK, w1s, x1s);
             load_x((t + 4) * kRaggedTK, x1);
         }
-        step(w2s, x2);
+        step(w2s, x2s, x2);
     }
 
     // C^T[n][m]: lane (h, m) holds n = 32 md + 8 g4 + 4 h + u for u = 0..3
@@ -502,20 +545,20 @@ hipError_t launch_ragged_planned(const void* lhs, const void* rhs, void* out, in
         const int64_t tail_grid = 4 * (units < n_cu - 1 ? units : n_cu - 1);
         if (tail_grid == 0) return hipSuccess;
         if (out_f32)
-            hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w, items,
-                               n_items, out, M, K, N, (int)max_items, tail_cu);
+            hipLaunchKernelGGL((ragged_dot_kernel<1, 1>), dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w,
+                               items, n_items, out, M, K, N, (int)max_items, tail_cu);
         else
-            hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w, items,
-                               n_items, out, M, K, N, (int)max_items, tail_cu);
+            hipLaunchKernelGGL((ragged_dot_kernel<0, 1>), dim3((unsigned)tail_grid), dim3(256), 0, stream, x, w,
+                               items, n_items, out, M, K, N, (int)max_items, tail_cu);
         return hipGetLastError();
     }
     const int64_t grid = max_items * 2 * (N / kRaggedTN);
     if (out_f32)
-        hipLaunchKernelGGL(ragged_dot_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items, out,
-                           M, K, N, (int)max_items, 0);
+        hipLaunchKernelGGL((ragged_dot_kernel<1, 0>), dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items,
+                           out, M, K, N, (int)max_items, 0);
     else
-        hipLaunchKernelGGL(ragged_dot_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items, out,
-                           M, K, N, (int)max_items, 0);
+        hipLaunchKernelGGL((ragged_dot_kernel<0, 0>), dim3((unsigned)grid), dim3(256), 0, stream, x, w, items, n_items,
+                           out, M, K, N, (int)max_items, 0);
     return hipGetLastError();
 }
 
