@@ -237,6 +237,42 @@ def test_builtin_default_is_row_pair(D, bk, pair):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_largest_head(dtype):
+    """The largest head the boundary takes for D = 128: S = 2^22 - 128, so S*D*4 =
+    2^31 - 65536 sits just under the 32-bit byte range of the buffer one head is read
+    through (fp32: K and V of a head span it almost whole).  32767 key blocks per row,
+    1 GiB of mask: the diagonal, the last key block in every row (the highest K/V
+    addresses), two random blocks per row and one empty row; sampled rows, the first
+    and last query rows among them, against the oracle."""
+    ensure_built()
+    B, H, D, b = 1, 1, 128, 128
+    S = (1 << 22) - 128
+    n = S // b
+    assert S * D * 4 < (1 << 31) and (S + 128) * D * 4 == 1 << 31
+    say("largest head", dtype, (B, H, S, D))
+    q, k, v = rand_qkv(B, H, S, D, dtype, seed=73)
+    g = torch.Generator().manual_seed(73)
+    mask = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    i = torch.arange(n)
+    mask[0, 0, i, i] = 1
+    mask[0, 0, :, n - 1] = 1
+    for _ in range(2):
+        mask[0, 0, i, torch.randint(0, n, (n,), generator=g)] = 1
+    mask[0, 0, 5] = 0
+    qd, kd, vd, md = q.cuda(), k.cuda(), v.cuda(), mask.cuda()
+    out, lse = bs.fwd(qd, kd, vd, md, b, b)
+    torch.cuda.synchronize()
+    rows = np.union1d(W.sample_rows(B, H, S, b, 24, mask=mask), [5 * b, 5 * b + 77, S - 1])
+    ro, rl = oracle.fwd_rows(q, k, v, mask, b, b, 1.0 / np.sqrt(D), rows)
+    go = out.reshape(-1, D)[torch.as_tensor(rows, device=out.device)]
+    gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
+    kind = "bf16" if dtype == torch.bfloat16 else "f32"
+    say("  stats", compare(go, gl, ro, rl, kind, "largest head %s" % kind))
+    assert torch.all(out[0, 0, 5 * b:6 * b] == 0) and torch.all(torch.isinf(lse[0, 0, 5 * b:6 * b]))
+
+
 def test_rows_past_the_pair_limit():
     """Rows of more than 2048 key blocks (S = 262272, 128-key blocks, 2049 per row):
     the row-pair configs refuse the shape, the call with no config falls back to a
