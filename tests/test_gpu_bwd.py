@@ -252,3 +252,84 @@ def test_bwd_cut_key_blocks(D):
     torch.cuda.synchronize()
     for x, y in zip(g1, g2):
         assert torch.equal(x, y)
+
+
+def _key_bounds(dev, out, lse, mask, b, scale, j):
+    """The bounds of _bounds for dk_j and dv_j of one key of head 0 (fp64 torch on the
+    device, rows in chunks): every query row that sees the key contributes; P from
+    the forward's lse; the row's sum over keys of P |v| is bounded by max |v| (sum P
+    = 1), so the bound is looser than _bounds', never tighter."""
+    q, k, v, do = (t[0, 0] for t in dev[:4])
+    D = q.shape[-1]
+    blocks = torch.nonzero(mask[:, j // b]).flatten()
+    rows = (blocks[:, None] * b + torch.arange(b, device=q.device)).flatten()
+    sc = float(np.float32(scale))
+    vmax = v.double().abs().max(0).values
+    kj, vj = k[j].double(), v[j].double()
+    sum_dk_err = torch.zeros(D, dtype=torch.float64, device=q.device)
+    sum_ds_q = torch.zeros_like(sum_dk_err)
+    sum_p_do = torch.zeros_like(sum_dk_err)
+    for c in range(0, rows.numel(), 1 << 20):
+        r = rows[c:c + (1 << 20)]
+        qr, dor, outr = q[r].double(), do[r].double(), out[0, 0][r].double()
+        P = torch.exp(sc * (qr @ kj) - lse[0, 0][r].double())
+        dS = P * (dor @ vj - (dor * outr).sum(1))
+        E = (dor.abs() * (2 * U * vmax + U * outr.abs())).sum(1)
+        dp_err = D * 2.0 ** -24 * (dor.abs() @ vj.abs())
+        ds_err = U * dS.abs() + P * (E + dp_err) + 2.0 ** -20 * dS.abs()
+        sum_dk_err += (ds_err[:, None] * qr.abs()).sum(0)
+        sum_ds_q += (dS.abs()[:, None] * qr.abs()).sum(0)
+        sum_p_do += (P[:, None] * dor.abs()).sum(0)
+    acc = rows.numel() * 2.0 ** -24
+    b_dk = 2 * abs(sc) * (sum_dk_err + acc * sum_ds_q)
+    b_dv = 2 * (U + acc) * sum_p_do
+    return b_dk.cpu().numpy(), b_dv.cpu().numpy()
+
+
+@pytest.mark.timeout(900)
+def test_bwd_largest_head():
+    """The backward at the largest head the boundary takes for D = 128 (S = 2^22 -
+    128: 32767 key blocks per row, 1 GiB of mask): the diagonal, two random blocks
+    per row, an empty row, and the last key block seen by every query block, so its
+    column is cut into 256 pieces whose partial sums the reduce kernel adds.  dq on
+    sampled rows (the first and last among them), dk and dv on sampled keys (the
+    last key among them), each held to its bound against the oracle."""
+    ensure_built()
+    B, H, D, b = 1, 1, 128, 128
+    S = (1 << 22) - 128
+    n = S // b
+    scale = 1.0 / np.sqrt(D)
+    say("bwd largest head", (B, H, S, D))
+    q, k, v = rand_qkv(B, H, S, D, torch.bfloat16, seed=74)
+    do = torch.randn(B, H, S, D, generator=torch.Generator().manual_seed(75)).to(torch.bfloat16)
+    g = torch.Generator().manual_seed(74)
+    mask = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    i = torch.arange(n)
+    mask[0, 0, i, i] = 1
+    mask[0, 0, :, n - 1] = 1
+    for _ in range(2):
+        mask[0, 0, i, torch.randint(0, n, (n,), generator=g)] = 1
+    mask[0, 0, 5] = 0
+    dev = [t.cuda() for t in (q, k, v, do, mask)]
+    out, lse = bs.fwd(dev[0], dev[1], dev[2], dev[4], b, b, scale)
+    gq, gk, gv = bs.bwd(dev[0], dev[1], dev[2], out, lse, dev[3], dev[4], b, b, scale)
+    torch.cuda.synchronize()
+    assert torch.all(gq[0, 0, 5 * b:6 * b] == 0)
+    rng = np.random.default_rng(74)
+    q_rows = np.union1d(rng.choice(S, 14, replace=False), [0, 5 * b + 3, S - 1])
+    k_rows = np.union1d(rng.choice(S - b, 5, replace=False), [0, S - b, S - 1])
+    say("  oracle on", len(q_rows), "rows and", len(k_rows), "keys,", oracle.max_threads(), "threads")
+    rq, rk, rv = oracle.bwd_sample(q, k, v, do, mask, b, b, scale, q_rows, k_rows)
+    m = mask[0, 0].numpy() != 0
+    out_c = out[0, 0].float().cpu()
+    # dq bound: the sampled rows with every key (row-local quantities only)
+    fq = np.repeat(m[q_rows // b], b, axis=1)
+    bq_ = _bounds(q[0, 0].float()[q_rows], k[0, 0].float(), v[0, 0].float(), do[0, 0].float()[q_rows],
+                  out_c[q_rows], fq, scale, True)[0]
+    _check("dq", gq[0, 0][torch.as_tensor(q_rows, device="cuda")], rq, bq_, True, "largest head")
+    # dk, dv: the bound of _bounds per key, over every query row that sees it
+    for t, j in enumerate(k_rows):
+        b_k, b_v = _key_bounds(dev, out, lse, dev[4][0, 0], b, scale, int(j))
+        _check("dk", gk[0, 0, j:j + 1], rk[t:t + 1], b_k[None], True, "largest head key %d" % j)
+        _check("dv", gv[0, 0, j:j + 1], rv[t:t + 1], b_v[None], True, "largest head key %d" % j)
+    say("  done")
