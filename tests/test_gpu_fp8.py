@@ -319,3 +319,47 @@ def test_fp8_elem_workload_token_causal_sampled():
     keep = _keep_rows(st, pidx, pbits, w.block_q, w.block_k, rows, w.S)
     bound = _bound_keep(q, k, v, keep, w.scale, rows, ro)
     say("  max err", _check(go, gl, ro, rl, bound, "token-causal fp8, sampled"))
+
+
+@pytest.mark.timeout(600)
+def test_fp8_largest_head():
+    """The largest head the boundary takes for D = 128 (S = 2^22 - 128, 32767 key
+    blocks per row, 1 GiB of mask) in fp8: the diagonal, the last key block in every
+    row, two random blocks per row and an empty row; sampled rows (the first and last
+    among them) against their bound."""
+    ensure_built()
+    B, H, D, b = 1, 1, 128, 128
+    S = (1 << 22) - 128
+    n = S // b
+    scale = 1.0 / np.sqrt(D)
+    say("fwd_fp8 largest head", (B, H, S, D))
+    q, k, v = _fp8_inputs(B, H, S, D, 76)
+    g = torch.Generator().manual_seed(76)
+    mask = torch.zeros(B, H, n, n, dtype=torch.uint8)
+    i = torch.arange(n)
+    mask[0, 0, i, i] = 1
+    mask[0, 0, :, n - 1] = 1
+    for _ in range(2):
+        mask[0, 0, i, torch.randint(0, n, (n,), generator=g)] = 1
+    mask[0, 0, 5] = 0
+    out, lse = bs.fwd_fp8(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), b, b, scale)
+    torch.cuda.synchronize()
+    rows = np.union1d(W.sample_rows(B, H, S, b, 24, mask=mask), [5 * b, 5 * b + 77, S - 1])
+    ro, rl = oracle.fwd_rows(q, k, v, mask, b, b, scale, rows)
+    # the bound of _bound_rows, row by row on the row's own keys only
+    m = mask[0, 0].numpy() != 0
+    bound = np.zeros((len(rows), D))
+    for t, r in enumerate(rows):
+        keys = torch.as_tensor(np.nonzero(np.repeat(m[r // b], b))[0])
+        if keys.numel() == 0:
+            continue
+        kf, vf = k[0, 0][keys].double().numpy(), v[0, 0][keys].double().numpy()
+        sc = float(np.float32(scale)) * (kf @ q[0, 0, r].double().numpy())
+        w = np.exp(sc - sc.max())
+        w /= w.sum()
+        av = np.abs(vf)
+        bound[t] = 2.0 ** -4 * (w @ av) + 2.0 ** -10 * w.max() * av.sum(0) + D * 2.0 ** -24 * (w @ av)
+    bound = 2 * (bound + 2.0 ** -9 * np.abs(ro))
+    go = out.reshape(-1, D)[torch.as_tensor(rows, device=out.device)]
+    gl = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
+    say("  max err", _check(go, gl, ro, rl, bound, "fp8 largest head"))
