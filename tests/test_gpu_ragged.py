@@ -163,3 +163,40 @@ def test_ragged_planned_equals_one_shot():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.all(b[640:] == 0)
+
+
+@pytest.mark.timeout(600)
+def test_ragged_largest_expert():
+    """One expert's rhs just under the 2 GiB one buffer addresses (K 2048, N 524160:
+    K*N*2 = 2^31 - 2^19), two experts, so the second starts past byte 2^31 of rhs;
+    M 512 with 62 rows in no group.  Sampled rows of each group against the oracle
+    (the same function on the sampled rows alone: the product is row by row), each
+    element held to its bound; the rows in no group exactly 0."""
+    ensure_built()
+    M, K, N, G = 512, 2048, 524160, 2
+    assert K * N * 2 < (1 << 31) and (1 << 31) - K * N * 2 == 1 << 19
+    say("ragged largest expert", (M, K, N, G))
+    gen = torch.Generator().manual_seed(77)
+    x = torch.randn(M, K, generator=gen).to(torch.bfloat16)
+    gd = torch.Generator(device="cuda").manual_seed(77)
+    wd = torch.randn(G, K, N, generator=gd, device="cuda").to(torch.bfloat16)
+    sizes = torch.tensor([200, 250], dtype=torch.int32)
+    out = bs.ragged_dot(x.cuda(), wd, sizes.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(out[450:] == 0)
+    w = wd.cpu()
+    del wd
+    picks = [[0, 1, 117, 198, 199], [200, 201, 333, 448, 449]]
+    rows = np.array(picks[0] + picks[1])
+    sub_sizes = torch.tensor([len(picks[0]), len(picks[1])], dtype=torch.int32)
+    xs = x[torch.as_tensor(rows)]
+    say("  oracle on", len(rows), "rows,", oracle.max_threads(), "threads")
+    ref = oracle.ragged_dot(xs, w, sub_sizes)
+    mag = oracle.ragged_dot(xs.abs(), w.abs(), sub_sizes)  # |bf16| is exact
+    got = out[torch.as_tensor(rows, device="cuda")].double().cpu().numpy()
+    bound = K * 2.0 ** -24 * mag + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    rel = err[bound > 0] / bound[bound > 0]
+    assert rel.mean() < 0.5, float(rel.mean())
+    say("  max err", float(err.max()))
