@@ -20,8 +20,9 @@
 //                    layout of the first product).  A = V^T: lane (d + 32h) needs
 //                    V[key][d] for the same 32 keys in the same byte order; a
 //                    pre-pass (fp8_vt_kernel) writes V per 64-key tile as
-//                    vt[d][64] with byte 32h + 16t + 4g + u = V[32t + 8g + 4h + u][d],
-//                    so each lane reads 32 contiguous bytes.
+//                    vt[d][64] with byte 32h + 16t + 4g + u = V[32t + 8g + 4h + u][d]
+//                    (each lane then reads 32 contiguous bytes), stored in the
+//                    order of the LDS image below.
 // Element-level masks (ELEM = 1): the list entry of a partial block carries its bit
 // tile (kj | (tile + 1) << 16, as in the bf16 kernel); after the S MFMAs each lane
 // reads one 32-bit word of its query row per 32-key subtile and sets to -inf the
@@ -29,12 +30,15 @@
 // the word is shifted by 4h and bit 8g + u tested).  A row may have no kept score
 // yet (m = -inf): the exponent then uses m = 0 and the rescale factor is 0, so
 // dropped scores give exact zeros; a row that keeps nothing ends with 0 and -inf.
-// LDS: a K tile is (D/64) * 2 blocks of 2 KiB, block (t, m) holding lane l's
-// bytes K[32t + l%32][64m + 32(l/32) + 16p .. +15] in plane p at p*1024 + l*16; a
-// V^T tile is D/32 blocks, block md holding vt[32md + l%32][32(l/32) + 16p ..]
-// likewise.  Every LDS read is lane-linear 16 bytes (conflict free) and every
-// block is filled by two 1 KiB DMA instructions (buffer loads with the LDS flag,
-// one per plane) whose per-lane offset is the same for all of them.
+// LDS: a K tile is row-major, 64 rows of D bytes, with the 16-byte unit c of row r
+// at slot c ^ x(r), x(r) = (r / (256 / D)) % (D / 16).  Each 1 KiB DMA instruction
+// (a buffer load with the LDS flag) then reads 1024 / D whole rows, i.e. whole
+// 128-byte lines (the L2 -> CU path serves an instruction that touches 32 rows
+// for 32 bytes each at about a quarter of that rate), and an operand read (16
+// lanes, 16 consecutive rows, one unit) hits 16 distinct 16-byte bank groups.  A
+// V^T tile is D/32 blocks of 2 KiB, block md holding vt[32md + l%32][32(l/32) +
+// 16p .. +15] in plane p at p*1024 + l*16 (lane-linear reads); the pre-pass
+// stores it in exactly this order, so its DMA is a linear copy.
 #include "bf16_layout.h"
 #include "common.h"
 #include "kernels.h"
@@ -89,9 +93,12 @@ __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) {  // row i / 4, dwords 4 (i % 4) .. +3
-        const uint32_t* rp = tr + (i >> 2) * 17 + 4 * (i & 3);
-        ((u32x4*)(vt + base))[i] = u32x4{rp[0], rp[1], rp[2], rp[3]};
+    for (int i = threadIdx.x; i < 64 * D / 16; i += 256) {  // row d = i / 4, dwords 4q .. +3, q = i % 4
+        const int d = i >> 2, q = i & 3;
+        const uint32_t* rp = tr + d * 17 + 4 * q;
+        // LDS image: block d / 32, plane q % 2, lane 32 (q / 2) + d % 32
+        ((u32x4*)(vt + base))[(d >> 5) * 128 + (q & 1) * 64 + (q >> 1) * 32 + (d & 31)] =
+            u32x4{rp[0], rp[1], rp[2], rp[3]};
     }
 }
 
@@ -136,20 +143,36 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
     const uint8_t* kg = (const uint8_t*)a.k + head;
     const uint8_t* vg = (const uint8_t*)a.v + head;  // the vt copy
     const int nrec = a.S * D;
-    const int k_voff = l32 * D + 32 * h, v_voff = l32 * 64 + 32 * h;
-    // K instruction i: plane i & 1 of block (t, m) = (i >> 1) / MQ, (i >> 1) % MQ;
-    // V instruction i: plane i & 1 of block md = i >> 1.  Destination i KiB.
+    // K: instruction i fills rows RPI*i .. of the tile; lane l takes slot l % CPR of
+    // row l / CPR, i.e. unit (l % CPR) ^ x(row).  x(RPI*i + l/CPR) depends on i only
+    // through its parity (D = 128) or not at all (D = 64), and a wave's i all share
+    // the parity of the wave (WAVES is even): one lane offset per wave.
+    constexpr int CPR = D / 16, RPI = 1024 / D, XSH = D == 128 ? 1 : 2;
+    auto xsw = [](int row) { return (row >> XSH) & (CPR - 1); };
+    const int k_row = RPI * (wave_s & 1) + lane / CPR;
+    const int k_voff = (lane / CPR) * D + 16 * ((lane % CPR) ^ xsw(k_row));
+    // operand reads: lane (h, i) takes units 4m + 2h + p of row 32t + i (x(32t + i) = x(i))
+    int k_rd[MQ][2];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) k_rd[m][p] = l32 * D + 16 * ((4 * m + 2 * h + p) ^ xsw(l32));
+    auto k_frag = [&](const uint8_t* kbuf, int t, int m) -> i32x8 {
+        const u32x4 lo = *(const u32x4*)(kbuf + t * 32 * D + k_rd[m][0]);
+        const u32x4 hi = *(const u32x4*)(kbuf + t * 32 * D + k_rd[m][1]);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    // V: instruction i copies KiB i of the tile's LDS image.
     auto issue = [&](int key0, uint8_t* kbuf, uint8_t* vbuf) {
 #pragma unroll
         for (int j = 0; j < NK; ++j) {
             const int i = wave_s + j * WAVES;
-            const int p = i & 1, m = (i >> 1) % MQ, t = (i >> 1) / MQ;
-            dma16(kg, nrec, (BSATTN_LDS void*)(kbuf + i * 1024), k_voff, (key0 + 32 * t) * D + 64 * m + 16 * p);
+            dma16(kg, nrec, (BSATTN_LDS void*)(kbuf + i * 1024), k_voff, (key0 + RPI * i) * D);
         }
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int i = wave_s + j * WAVES;
-            dma16(vg, nrec, (BSATTN_LDS void*)(vbuf + i * 1024), v_voff, key0 * D + (i >> 1) * 2048 + 16 * (i & 1));
+            dma16(vg, nrec, (BSATTN_LDS void*)(vbuf + i * 1024), lane * 16, key0 * D + i * 1024);
         }
     };
 
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC,
         for (int t = 0; t < 2; ++t) {
             s[t] = f32x16{};
 #pragma unroll
-            for (int m = 0; m < MQ; ++m) s[t] = mfma_fp8(lds32(kbuf + (t * MQ + m) * 2048, lane), qf[m], s[t]);
+            for (int m = 0; m < MQ; ++m) s[t] = mfma_fp8(k_frag(kbuf, t, m), qf[m], s[t]);
         }
         if constexpr (ELEM) apply_tile(s, e, st);
         // row max over the 64 keys and the lazy move of the reference max
