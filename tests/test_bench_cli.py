@@ -68,3 +68,23 @@ def test_cpu_baseline_fields():
     assert cb["cores"] == n0 == oracle.max_threads()
     assert cb["nproc"] >= 1 and "query rows" in cb["sample"]
     assert cb["one_thread"]["value"] > 0 and cb["one_thread"]["unit"] == "TFLOP/s"
+
+
+def test_traffic_summaries_match_the_current_sources():
+    """Each committed counter summary (profiles/attn_traffic_*.json) was taken on the
+    current sources of its kernel family, so bench.py reports its traffic figure;
+    a kernel edit without new counters fails here instead of turning the figure
+    into null."""
+    import glob
+    import json
+    sys.path.insert(0, ROOT)
+    import bench
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "attn_traffic_*.json")))
+    assert paths
+    for p in paths:
+        name = os.path.basename(p)[len("attn_traffic_"):-len(".json")]
+        family = ("bwd" if name.endswith("_bwd") else "fp8" if name.endswith("_fp8")
+                  else "ragged" if name.startswith("ragged") else "fwd")
+        rec = json.load(open(p))
+        assert rec["kernel_source_hash"] == bench.kernel_source_hash(family), (name, family)
+        assert rec["by_config"], name
