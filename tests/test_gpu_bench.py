@@ -59,3 +59,24 @@ def test_bench_default_workload_is_causal():
     res = _bench("--config", "256,128,8,2")
     assert res["config"]["workload"] == "causal_bf16"
     assert res["config"]["active_blocks"] == 133120
+
+
+@pytest.mark.parametrize("args,dtype", [(("--workload", "dense_bf16", "--backward"), "bf16"),
+                                        (("--workload", "dense_bf16", "--fp8"), "fp8_e4m3"),
+                                        (("--workload", "causal_elem_bf16",), "bf16"),
+                                        (("--workload", "ragged_bf16",), "bf16")])
+def test_bench_other_modes(args, dtype):
+    """The backward, fp8, element-mask and ragged-dot lines keep the same contract:
+    one JSON line, the contract's fields, a roofline object whose frac is achieved
+    over peak, and the traffic figure of the committed counter summary (taken on
+    the current sources)."""
+    res = _bench(*args)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in res, key
+    assert res["n_gpus"] == 1 and res["steps"] == 3 and res["value"] > 0 and res["dtype"] == dtype
+    assert res["config"]["workload"].startswith(args[1])
+    rf = res["roofline"]
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9 and 0 < rf["frac"] < 1
+    assert rf["traffic"] is not None and rf["traffic"] > 0
+    assert rf["kernel_ms"] > 0
